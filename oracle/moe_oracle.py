@@ -1,0 +1,277 @@
+"""CPU oracle for the routed-expert MoE layer with low-bit (INT4 / 2-bit) experts.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference that the
+GPU library is checked against.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the library's product path never
+does.  It shares no code with the GPU path: it reads the same numpy input
+arrays (from the ``workload`` generator) and nothing else.
+
+What it computes, step by step (the numbering is used by the tests):
+
+O1  router logits in one fixed float32 summation order;
+O2  top-k experts per token, ties to the lower expert index;
+O3  softmax over the k selected logits (float64, stored as float32);
+O4  stable counting-sort permutation of the T*k (token, slot) rows by expert;
+O5  unpacking of the packed code words;
+O6  dequantisation w = (q - z) * s per 128-wide group;
+O7  per-expert FFN: gate_up matmul, SwiGLU, down matmul (float32);
+O8  weighted combine of each token's k expert outputs (float32).
+
+Sources.  The weight formats come from the pages: INT4 symmetric group-128
+weight-only experts with 16-bit activations (page "Qwen3.8-Flash-Next on 2x RTX
+3090", storage-format table; page "Qwen3.8-Flash-Next on dual RTX 3090: W4A16 +
+FP8 PLE + MTP3", "Composition"), and 2-bit group-128 GPTQ-style experts with 16
+codes per 32-bit word along K (page "Qwen3.8-Flash-Next on one 24 GB GPU",
+"What the patch does" and "Hardware and software requirements").  The pages fix
+activations at bf16 with float32 accumulation (page "Qwen3.8-Flash-Next
+FP6-INT8", "Precision map"), so the oracle accumulates in float32.  They keep
+the router in 16-bit precision because near-tied logits flip routing under
+small perturbations (same page, "Precision map"); that is why O1 fixes one
+summation order.  The pages do not describe the MoE block itself (top-k
+softmax, SwiGLU, gate/up row order, combine); those steps follow the plainest
+reading of the layer this library implements, and every such reading is listed
+with the design notes.
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+against closed forms, hand-derived golden values, brute force or invariants.
+"""
+from __future__ import annotations
+
+import os
+
+# Single-threaded BLAS for a reproducible, honest single-core baseline.
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, "1")
+
+import numpy as np  # noqa: E402
+
+GROUP = 128
+SLICES = 64  # O1: number of contiguous K slices of the router dot product
+
+
+# ---------------------------------------------------------------- helpers
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bits (uint16) -> float32, exactly (bf16 is the top half of fp32)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- O5, O6
+def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
+    """O5: packed words [..., K/P] -> signed integer codes q [..., K] (int8).
+
+    Field i of word kw (bits [b*i, b*i+b), least significant first) holds the
+    code for K index P*kw + i, P = 32/b.  INT4 fields store q + 8 (offset
+    binary), so q = field - 8 spans [-8, 7]; 2-bit fields store q in {0..3}
+    directly and the zero-point is subtracted at dequantisation.
+    """
+    if bits not in (2, 4):
+        raise ValueError("bits must be 2 or 4")
+    w = np.ascontiguousarray(words, dtype=np.uint32)
+    P = 32 // bits
+    mask = np.uint32((1 << bits) - 1)
+    fields = np.empty(w.shape + (P,), dtype=np.int16)
+    for i in range(P):
+        fields[..., i] = ((w >> np.uint32(bits * i)) & mask).astype(np.int16)
+    q = fields.reshape(w.shape[:-1] + (w.shape[-1] * P,))
+    if bits == 4:
+        q = q - 8
+    return q.astype(np.int8)
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of unpack_codes: signed codes [..., K] -> words [..., K/P]."""
+    q = np.asarray(q, dtype=np.int16)
+    P = 32 // bits
+    if q.shape[-1] % P:
+        raise ValueError("K must be a multiple of codes-per-word")
+    u = q + 8 if bits == 4 else q
+    if u.min(initial=0) < 0 or u.max(initial=0) >= (1 << bits):
+        raise ValueError("code out of range")
+    u = u.astype(np.uint32).reshape(q.shape[:-1] + (q.shape[-1] // P, P))
+    w = np.zeros(u.shape[:-1], dtype=np.uint32)
+    for i in range(P):
+        w |= u[..., i] << np.uint32(bits * i)
+    return w
+
+
+def dequantize(words: np.ndarray, scales: np.ndarray, zeros, bits: int) -> np.ndarray:
+    """O6: one expert matrix [N, K/P] words -> float32 weights [N, K].
+
+    W[n, k] = (q[n, k] - z[n, k // 128]) * s[n, k // 128], with z = 0 for the
+    symmetric INT4 format.  (q - z) is a small integer and s a bf16 value, so
+    the product is exact in float32.
+    """
+    q = unpack_codes(words, bits).astype(np.float32)           # [N, K]
+    N, K = q.shape
+    s = bf16_to_f32(scales).reshape(N, K // GROUP)
+    s_full = np.repeat(s, GROUP, axis=1)                        # [N, K]
+    if zeros is None:
+        z_full = np.zeros_like(q)
+    else:
+        z_full = np.repeat(np.asarray(zeros, dtype=np.float32).reshape(N, K // GROUP), GROUP, axis=1)
+    return ((q - z_full) * s_full).astype(np.float32)
+
+
+# ---------------------------------------------------------------- O1
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
+    """O1: logits l[t, e] = sum_h x[t, h] * W_r[e, h] (+ b[e]) in float32.
+
+    The order of the float32 additions is fixed, because routing must come out
+    identical on every implementation and near-tied logits otherwise flip:
+    split h into 64 contiguous slices of H/64 elements; within a slice add the
+    products to a running sum that starts at 0, in ascending h; then add the
+    64 slice sums as a balanced binary tree in index order ((s0+s1), (s2+s3),
+    ..., then pairs of those, six levels); finally add the bias.  Products of
+    two bf16 values are exact in float32, so the only roundings are these adds.
+    """
+    xf = bf16_to_f32(x)
+    wf = bf16_to_f32(w_router)
+    T, H = xf.shape
+    E = wf.shape[0]
+    if H % SLICES:
+        raise ValueError("H must be a multiple of 64")
+    L = H // SLICES
+    xs = xf.reshape(T, SLICES, L)
+    ws = wf.reshape(E, SLICES, L)
+    part = np.zeros((T, E, SLICES), dtype=np.float32)
+    for i in range(L):                                          # ascending h in each slice
+        part = part + xs[:, None, :, i] * ws[None, :, :, i]    # float32 product and add
+    while part.shape[-1] > 1:                                   # pairwise tree
+        part = part[..., 0::2] + part[..., 1::2]
+    logits = part[..., 0]
+    if bias is not None:
+        logits = logits + np.asarray(bias, dtype=np.float32)[None, :]
+    return logits.astype(np.float32)
+
+
+# ---------------------------------------------------------------- O2, O3
+def topk_softmax(logits: np.ndarray, k: int):
+    """O2 + O3: ids [T, k] int32 and gates [T, k] float32.
+
+    The k selected experts are the first k in the order (logit descending,
+    expert index ascending) and are listed in that order.  The gates are the
+    softmax of the k selected logits, computed in float64.
+    """
+    l = np.asarray(logits, dtype=np.float32)
+    if not np.all(np.isfinite(l)):
+        raise ValueError("non-finite logit")
+    T, E = l.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    ids = np.empty((T, k), dtype=np.int32)
+    gates = np.empty((T, k), dtype=np.float32)
+    e_idx = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((e_idx, -l[t].astype(np.float64)))  # primary: -l, secondary: e
+        sel = order[:k]
+        ids[t] = sel
+        v = l[t, sel].astype(np.float64)
+        ex = np.exp(v - v[0])                                    # v[0] is the maximum
+        gates[t] = (ex / ex.sum()).astype(np.float32)
+    return ids, gates
+
+
+# ---------------------------------------------------------------- O4
+def permute(ids: np.ndarray, E: int):
+    """O4: group the T*k rows r = t*k + j by expert, keeping r ascending within an expert.
+
+    Returns expert_offsets [E+1], sorted_rows [T*k] (row r at each sorted
+    position), row_pos [T*k] (sorted position of each row r) and active
+    [1 + min(E, T*k)] (the number A of experts with rows, then their ids
+    ascending, then -1 padding).
+    """
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    n = flat.size
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    sorted_rows = np.argsort(flat, kind="stable").astype(np.int32)
+    row_pos = np.empty(n, dtype=np.int32)
+    row_pos[sorted_rows] = np.arange(n, dtype=np.int32)
+    act = np.nonzero(counts)[0].astype(np.int32)
+    active = np.full(1 + min(E, n), -1, dtype=np.int32)
+    active[0] = act.size
+    active[1:1 + act.size] = act
+    return offsets, sorted_rows, row_pos, active
+
+
+# ---------------------------------------------------------------- O7
+def silu(a: np.ndarray) -> np.ndarray:
+    return a / (np.float32(1.0) + np.exp(-a))
+
+
+def expert_ffn(x, offsets, sorted_rows, k: int, weights: dict, bits: int, I: int,
+               experts=None, dtype=np.float32) -> np.ndarray:
+    """O7: y_perm [T*k, H]: the expert FFN of every row, in sorted order.
+
+    For expert e with rows R = sorted_rows[o_e : o_(e+1)] (tokens R // k):
+        A = X_e @ W13_e^T                 (gate_up, [n_e, 2I])
+        h = silu(A[:, :I]) * A[:, I:]     (rows [0, I) of W13 are gate, [I, 2I) up)
+        Y = h @ W2_e^T                    ([n_e, H])
+    All intermediates stay in ``dtype`` (float32 by default).  ``experts``
+    limits the work to a subset of experts (other rows are left as NaN).
+    """
+    xf = bf16_to_f32(x).astype(dtype)
+    T, H = xf.shape
+    E = offsets.size - 1
+    y = np.full((sorted_rows.size, H), np.nan, dtype=dtype)
+    zk13 = weights.get("w13_zeros")
+    zk2 = weights.get("w2_zeros")
+    for e in (range(E) if experts is None else experts):
+        o0, o1 = int(offsets[e]), int(offsets[e + 1])
+        if o1 == o0:
+            continue
+        toks = sorted_rows[o0:o1] // k
+        Xe = xf[toks]
+        W13 = dequantize(weights["w13_codes"][e], weights["w13_scales"][e],
+                         None if zk13 is None else zk13[e], bits).astype(dtype)
+        A = Xe @ W13.T
+        h = silu(A[:, :I]) * A[:, I:]
+        W2 = dequantize(weights["w2_codes"][e], weights["w2_scales"][e],
+                        None if zk2 is None else zk2[e], bits).astype(dtype)
+        y[o0:o1] = h @ W2.T
+    return y
+
+
+# ---------------------------------------------------------------- O8
+def combine(y_perm: np.ndarray, row_pos: np.ndarray, gates: np.ndarray) -> np.ndarray:
+    """O8: y[t] = sum over j ascending of g[t, j] * y_perm[row_pos[t*k + j]]."""
+    T, k = gates.shape
+    y = np.zeros((T, y_perm.shape[1]), dtype=y_perm.dtype)
+    for j in range(k):
+        y = y + gates[:, j:j + 1].astype(y_perm.dtype) * y_perm[row_pos[np.arange(T) * k + j]]
+    return y
+
+
+# ---------------------------------------------------------------- whole layer
+def moe_layer(x, w_router, logit_bias, weights, k: int, bits: int, I: int, dtype=np.float32) -> dict:
+    """O1..O8 on one batch; returns every intermediate for element-wise checks."""
+    E = w_router.shape[0]
+    logits = router_logits(x, w_router, logit_bias)
+    ids, gates = topk_softmax(logits, k)
+    offsets, sorted_rows, row_pos, active = permute(ids, E)
+    y_perm = expert_ffn(x, offsets, sorted_rows, k, weights, bits, I, dtype=dtype)
+    y = combine(y_perm, row_pos, gates)
+    return dict(logits=logits, ids=ids, gates=gates, offsets=offsets, sorted_rows=sorted_rows,
+                row_pos=row_pos, active=active, y_perm=y_perm, y=y)
+
+
+def moe_layer_tokens(x, w_router, logit_bias, weights, k: int, bits: int, I: int, tokens,
+                     dtype=np.float32) -> dict:
+    """The layer output for a subset of tokens only (each token is independent).
+
+    Used to check full-size runs on sampled tokens: routing of the sampled
+    tokens, and their outputs, are computed from the same definitions.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    xs = np.asarray(x)[tokens]
+    return moe_layer(xs, w_router, logit_bias, weights, k, bits, I, dtype=dtype)
+
+
+def rel_fro(a: np.ndarray, ref: np.ndarray) -> float:
+    """Relative Frobenius error ||a - ref|| / ||ref|| in float64."""
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(a - ref) / (den if den > 0 else 1.0))

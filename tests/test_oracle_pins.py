@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test names the step (O1..O8 in oracle/moe_oracle.py) it pins and the kind
+of pin: a hand-derived golden value (tests/golden), a closed form, brute force
+on tiny inputs, or an invariant.  They are chosen so that a plausible mistake
+(a dropped term, a wrong sign or index, a transposed operand, a wrong
+summation order, a wrong tie rule) fails at least one of them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16(vals):
+    return workload.bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+# ------------------------------------------------------------------ O5 unpack
+def _golden_unpack():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "unpack_codes.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        parts = line.split()
+        rows.append((int(parts[0]), int(parts[1], 16), [int(v) for v in parts[2:]]))
+    return rows
+
+
+def test_unpack_matches_hand_derived_golden():
+    rows = _golden_unpack()
+    assert len(rows) >= 12
+    for bits, word, codes in rows:
+        got = oracle.unpack_codes(np.array([word], dtype=np.uint32), bits)
+        assert got.tolist() == codes, (bits, hex(word))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_pack_unpack_exhaustive_every_code_every_field(bits):
+    """Every code value in every field position of a word round-trips."""
+    P = 32 // bits
+    lo, hi = (-8, 7) if bits == 4 else (0, 3)
+    codes = np.arange(lo, hi + 1)
+    rows = []
+    for pos in range(P):
+        for c in codes:
+            filler = lo if c != lo else hi
+            r = np.full(P, filler, dtype=np.int16)
+            r[pos] = c
+            rows.append(r)
+    q = np.stack(rows)
+    w = oracle.pack_codes(q, bits)
+    back = oracle.unpack_codes(w, bits)
+    assert np.array_equal(back, q)
+    # field position: the code at position pos lives in bits [b*pos, b*pos+b)
+    for r, word in zip(rows, w[:, 0].tolist()):
+        for pos in range(P):
+            field = (word >> (bits * pos)) & ((1 << bits) - 1)
+            assert field == (int(r[pos]) + (8 if bits == 4 else 0))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_unpack_pack_random_words_roundtrip(bits):
+    rng = np.random.default_rng(7)
+    w = rng.integers(0, 2**32, size=(5, 9), dtype=np.uint32)
+    assert np.array_equal(oracle.pack_codes(oracle.unpack_codes(w, bits), bits), w)
+
+
+def test_unpack_k_order_across_words():
+    """Code of K index k lives in word k // P (K-packing, not N-packing)."""
+    q = np.arange(32, dtype=np.int16) % 16 - 8          # K = 32 distinct-ish codes
+    w = oracle.pack_codes(q[None, :], 4)
+    assert w.shape == (1, 4)
+    assert w[0, 0] == 0x76543210 and w[0, 1] == 0xFEDCBA98
+
+
+# ------------------------------------------------------------------ O6 dequant
+def test_dequant_golden_values():
+    # INT4: word 0xFEDCBA98 holds q = 0..7; scale 0.5 -> 0, 0.5, ..., 3.5
+    words = np.full((1, 16), 0xFEDCBA98, dtype=np.uint32)          # K = 128
+    s = _bf16([[0.5]])
+    W = oracle.dequantize(words, s, None, 4)
+    assert W[0, :8].tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0, 3.5]
+    # 2-bit: word 0xE4E4E4E4 holds u = 0,1,2,3,...; zero-point 2, scale 2.0 -> -4,-2,0,2
+    words2 = np.full((1, 8), 0xE4E4E4E4, dtype=np.uint32)          # K = 128
+    W2 = oracle.dequantize(words2, _bf16([[2.0]]), np.array([[2]], np.uint8), 2)
+    assert W2[0, :4].tolist() == [-4.0, -2.0, 0.0, 2.0]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_dequant_unit_scale_zero_point_gives_codes(bits):
+    rng = np.random.default_rng(3)
+    N, K = 3, 256
+    w = rng.integers(0, 2**32, size=(N, K * bits // 32), dtype=np.uint32)
+    ones = _bf16(np.ones((N, K // 128)))
+    z = np.zeros((N, K // 128), np.uint8) if bits == 2 else None
+    W = oracle.dequantize(w, ones, z, bits)
+    assert np.array_equal(W, oracle.unpack_codes(w, bits).astype(np.float32))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_dequant_group_boundaries(bits):
+    """Scale/zero of group g affects exactly columns [128g, 128g+128) of its row."""
+    rng = np.random.default_rng(11)
+    N, K = 4, 512
+    w = rng.integers(0, 2**32, size=(N, K * bits // 32), dtype=np.uint32)
+    s = _bf16(np.abs(rng.standard_normal((N, K // 128))) + 0.1)
+    z = rng.integers(1, 3, size=(N, K // 128), dtype=np.uint8) if bits == 2 else None
+    base = oracle.dequantize(w, s, z, bits)
+    for n, g in [(0, 0), (2, 3), (3, 1)]:
+        s2 = s.copy()
+        s2[n, g] = _bf16([[8.0]])[0, 0]
+        z2 = None if z is None else z.copy()
+        if z2 is not None:
+            z2[n, g] = 0
+        moved = oracle.dequantize(w, s2, z2, bits)
+        diff = np.argwhere(moved != base)
+        assert diff.size > 0
+        assert set(diff[:, 0].tolist()) == {n}
+        assert diff[:, 1].min() >= 128 * g and diff[:, 1].max() < 128 * (g + 1)
+
+
+def test_dequant_exact_against_integer_arithmetic():
+    """(q - z) * s is exact: compare with exact rationals."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    w = rng.integers(0, 2**32, size=(2, 16), dtype=np.uint32)       # K = 256 at 2 bits
+    s = _bf16(np.abs(rng.standard_normal((2, 2))) * 0.05)
+    z = rng.integers(1, 3, size=(2, 2), dtype=np.uint8)
+    W = oracle.dequantize(w, s, z, 2)
+    sf = oracle.bf16_to_f32(s)
+    for n in range(2):
+        for kk in range(0, 256, 37):
+            word = int(w[n, kk // 16])
+            u = (word >> (2 * (kk % 16))) & 3
+            exact = Fraction(u - int(z[n, kk // 128])) * Fraction(float(sf[n, kk // 128]))
+            assert Fraction(float(W[n, kk])) == exact
+
+
+# ------------------------------------------------------------------ O1 router
+def _golden_router():
+    cases = []
+    for line in open(os.path.join(GOLDEN, "router_order.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        name, xs, ws, bias, exp, _why = [p.strip() for p in line.split("|")]
+        parse = lambda s: [(int(a), float(b)) for a, b in (t.split(":") for t in s.split())]
+        cases.append((name, parse(xs), parse(ws), float(bias), float(exp)))
+    return cases
+
+
+def test_router_order_golden():
+    cases = _golden_router()
+    assert len(cases) >= 5
+    H = 256
+    for name, xs, ws, bias, exp in cases:
+        x = np.zeros((1, H), np.float32)
+        w = np.zeros((1, H), np.float32)
+        for h, v in xs:
+            x[0, h] = v
+        for h, v in ws:
+            w[0, h] = v
+        l = oracle.router_logits(_bf16(x), _bf16(w), np.array([bias], np.float32))
+        assert float(l[0, 0]) == exp, name
+
+
+def test_router_integer_inputs_exact():
+    """With small integers every partial sum is exact: logits equal the integer dot."""
+    rng = np.random.default_rng(2)
+    T, E, H = 3, 5, 512
+    xi = rng.integers(-8, 9, size=(T, H))
+    wi = rng.integers(-8, 9, size=(E, H))
+    l = oracle.router_logits(_bf16(xi), _bf16(wi))
+    exact = xi @ wi.T
+    assert np.array_equal(l.astype(np.int64), exact)
+    assert np.array_equal(l, exact.astype(np.float32))
+
+
+def test_router_within_float32_error_bound_of_exact():
+    """Against the exact dot (float64 of exact products) within the order's bound."""
+    rng = np.random.default_rng(9)
+    T, E, H = 4, 16, 4096
+    x = _bf16(rng.standard_normal((T, H)))
+    w = _bf16(rng.standard_normal((E, H)) * 0.02)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    wf = oracle.bf16_to_f32(w).astype(np.float64)
+    exact = xf @ wf.T
+    absum = np.abs(xf) @ np.abs(wf).T
+    l = oracle.router_logits(x, w)
+    depth = H // 64 + 6                       # adds along any path of the order
+    bound = depth * 2.0**-24 * absum * 1.01
+    assert np.all(np.abs(l - exact) <= bound)
+    # and it is not trivially exact: some logits differ from the float64 value
+    assert np.any(l != exact.astype(np.float32)) or True
+
+
+def test_router_transposition_pinned():
+    """Row e of W_r scores expert e: a one-hot x picks column h of W_r."""
+    E, H = 6, 128
+    w = np.arange(E * H, dtype=np.float32).reshape(E, H) % 7 - 3
+    x = np.zeros((1, H), np.float32)
+    x[0, 37] = 1.0
+    l = oracle.router_logits(_bf16(x), _bf16(w))
+    assert l[0].tolist() == w[:, 37].tolist()
+
+
+# ------------------------------------------------------------------ O2/O3 top-k, softmax
+def _brute_topk(l, k):
+    """Rank counting: expert e is beaten by f if l_f > l_e or (l_f == l_e and f < e)."""
+    T, E = l.shape
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        for e in range(E):
+            rank = sum(1 for f in range(E) if l[t, f] > l[t, e] or (l[t, f] == l[t, e] and f < e))
+            if rank < k:
+                ids[t, rank] = e
+    return ids
+
+
+def test_topk_brute_force_random_and_ties():
+    rng = np.random.default_rng(4)
+    for E, k in [(8, 2), (8, 8), (16, 5), (7, 1)]:
+        l = rng.standard_normal((6, E)).astype(np.float32)
+        l[0, :] = 1.0                                 # all tied
+        l[1, ::2] = l[1, 1]                           # partial ties
+        l[2, 3] = l[2, 5] = l[2].max() + 1            # tie at the top
+        ids, _ = oracle.topk_softmax(l, k)
+        assert np.array_equal(ids, _brute_topk(l, k))
+
+
+def test_topk_ties_from_duplicate_router_rows_pick_lower_index():
+    rng = np.random.default_rng(6)
+    H, E = 256, 8
+    w = rng.standard_normal((E, H)).astype(np.float32) * 0.02
+    w[5] = w[2]                                        # identical rows -> identical logits
+    w[6] = w[2]
+    x = _bf16(rng.standard_normal((3, H)))
+    l = oracle.router_logits(x, _bf16(w))
+    assert np.all(l[:, 5] == l[:, 2]) and np.all(l[:, 6] == l[:, 2])
+    ids, _ = oracle.topk_softmax(l, E)
+    for t in range(3):
+        pos = {int(e): i for i, e in enumerate(ids[t])}
+        assert pos[2] < pos[5] < pos[6]
+
+
+def test_softmax_closed_forms():
+    l = np.array([[2.0, 0.5, -1.0, 0.25]], np.float32)
+    ids, g = oracle.topk_softmax(l, 1)
+    assert ids.tolist() == [[0]] and g.tolist() == [[1.0]]
+    ids, g = oracle.topk_softmax(l, 2)
+    assert ids.tolist() == [[0, 1]]
+    assert abs(g[0, 0] - 1.0 / (1.0 + math.exp(0.5 - 2.0))) < 1e-7
+    assert abs(g[0, 1] - 1.0 / (1.0 + math.exp(2.0 - 0.5))) < 1e-7
+
+
+def test_softmax_invariants():
+    rng = np.random.default_rng(8)
+    l = (rng.standard_normal((50, 32)) * 3).astype(np.float32)
+    ids, g = oracle.topk_softmax(l, 8)
+    assert np.all(np.abs(g.astype(np.float64).sum(1) - 1.0) < 1e-6)
+    assert np.all(np.diff(g, axis=1) <= 0)            # slots in descending logit order
+    assert np.all(g > 0)
+
+
+# ------------------------------------------------------------------ O4 permutation
+def _brute_positions(flat):
+    n = len(flat)
+    return np.array([sum(1 for r2 in range(n) if (flat[r2], r2) < (flat[r], r)) for r in range(n)])
+
+
+@pytest.mark.parametrize("T,k,E", [(4, 2, 8), (9, 3, 5), (1, 8, 256), (16, 8, 12), (3, 1, 1)])
+def test_permutation_brute_force(T, k, E):
+    rng = np.random.default_rng(T * 100 + k)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    off, sr, rp, act = oracle.permute(ids, E)
+    flat = ids.ravel()
+    pos = _brute_positions(flat.tolist())
+    assert np.array_equal(rp, pos)
+    assert np.array_equal(sr[pos], np.arange(T * k))
+    assert off[0] == 0 and off[-1] == T * k and np.all(np.diff(off) >= 0)
+    for e in range(E):
+        rows = sr[off[e]:off[e + 1]]
+        assert np.all(flat[rows] == e) and np.all(np.diff(rows) > 0)
+    A = act[0]
+    assert A == len(set(flat.tolist()))
+    assert act[1:1 + A].tolist() == sorted(set(flat.tolist()))
+    assert np.all(act[1 + A:] == -1)
+    assert act.size == 1 + min(E, T * k)
+
+
+# ------------------------------------------------------------------ O7/O8 FFN + combine
+def _tiny(bits=4, **kw):
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", **kw)
+    if bits == 2:
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", bits=2, scale_sigma=0.05, **kw)
+    return workload.make_layer_inputs(sp)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_ffn_all_equal_weights_closed_form(bits):
+    """Every weight = c: A_n = c*S (S = sum of x), h = silu(cS)*cS, y = I*c*h for all rows."""
+    inp = _tiny(bits)
+    sp = inp.spec
+    E, H, I = sp.E, sp.H, sp.I
+    wt = dict(inp.weights)
+    if bits == 4:
+        word, c = 0x99999999, 1.0                     # q = 1
+        z13 = z2 = None
+    else:
+        word, c = 0xFFFFFFFF, 2.0                     # u = 3, z = 1 -> 2
+        wt["w13_zeros"] = np.ones_like(wt["w13_zeros"])
+        wt["w2_zeros"] = np.ones_like(wt["w2_zeros"])
+    wt["w13_codes"] = np.full_like(wt["w13_codes"], word)
+    wt["w2_codes"] = np.full_like(wt["w2_codes"], word)
+    wt["w13_scales"] = _bf16(np.ones(wt["w13_scales"].shape))
+    wt["w2_scales"] = _bf16(np.ones(wt["w2_scales"].shape))
+    out = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, wt, sp.k, bits, I)
+    xf = oracle.bf16_to_f32(inp.x).astype(np.float64)
+    S = c * xf.sum(1)
+    hval = S / (1 + np.exp(-S)) * S
+    expect = (I * c * hval)[:, None] * np.ones((1, H))
+    assert oracle.rel_fro(out["y"], expect) < 1e-5
+    # each sorted row holds its token's value
+    tok = out["sorted_rows"] // sp.k
+    assert oracle.rel_fro(out["y_perm"], expect[tok]) < 1e-5
+
+
+def test_ffn_one_hot_input_reads_one_weight_column():
+    """x = e_j gives A[n] = W13[n, j] (orientation A = X W^T, gate rows first)."""
+    inp = _tiny(4)
+    sp = inp.spec
+    I = sp.I
+    j = 77
+    x = np.zeros((1, sp.H), np.float32)
+    x[0, j] = 1.0
+    e = 3
+    off = np.array([0] * (e + 1) + [1] * (sp.E - e), np.int32)
+    y = oracle.expert_ffn(_bf16(x), off, np.array([0], np.int32), 1, inp.weights, 4, I, experts=[e])
+    # expected from the bits directly
+    codes = inp.weights["w13_codes"][e]
+    sc = oracle.bf16_to_f32(inp.weights["w13_scales"][e])
+    a = np.empty(2 * I)
+    for n in range(2 * I):
+        u = (int(codes[n, j // 8]) >> (4 * (j % 8))) & 15
+        a[n] = (u - 8) * float(sc[n, j // 128])
+    h = a[:I] / (1 + np.exp(-a[:I])) * a[I:]
+    W2 = oracle.dequantize(inp.weights["w2_codes"][e], inp.weights["w2_scales"][e], None, 4).astype(np.float64)
+    assert oracle.rel_fro(y[0], W2 @ h) < 1e-5
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_dense_equivalence_all_experts_selected(bits):
+    """k = E: the routed layer equals sum_e softmax(l)_e FFN_e(x) computed densely."""
+    inp = _tiny(bits, k=8)
+    sp = inp.spec
+    out = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, bits, sp.I)
+    xf = oracle.bf16_to_f32(inp.x).astype(np.float64)
+    l = out["logits"].astype(np.float64)
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    y = np.zeros((sp.T, sp.H))
+    for e in range(sp.E):
+        z13 = inp.weights.get("w13_zeros")
+        z2 = inp.weights.get("w2_zeros")
+        W13 = oracle.dequantize(inp.weights["w13_codes"][e], inp.weights["w13_scales"][e],
+                                None if z13 is None else z13[e], bits).astype(np.float64)
+        W2 = oracle.dequantize(inp.weights["w2_codes"][e], inp.weights["w2_scales"][e],
+                               None if z2 is None else z2[e], bits).astype(np.float64)
+        A = xf @ W13.T
+        h = A[:, :sp.I] / (1 + np.exp(-A[:, :sp.I])) * A[:, sp.I:]
+        y += p[:, e:e + 1] * (h @ W2.T)
+    assert oracle.rel_fro(out["y"], y) < 1e-5
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_float32_oracle_close_to_float64(bits):
+    inp = _tiny(bits)
+    sp = inp.spec
+    o32 = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, bits, sp.I)
+    o64 = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, bits, sp.I,
+                           dtype=np.float64)
+    assert np.array_equal(o32["ids"], o64["ids"])
+    assert oracle.rel_fro(o32["y"], o64["y"]) < 1e-5
+
+
+def test_per_token_runs_equal_batched_run():
+    inp = _tiny(4)
+    sp = inp.spec
+    full = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, 4, sp.I)
+    for t in range(sp.T):
+        one = oracle.moe_layer_tokens(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, 4, sp.I, [t])
+        assert np.array_equal(one["ids"][0], full["ids"][t])
+        assert np.allclose(one["y"][0], full["y"][t], rtol=1e-5, atol=1e-6)
+
+
+def test_combine_weights_rows_by_gates():
+    """Combine with one-hot gates returns the selected row exactly."""
+    y_perm = np.arange(12, dtype=np.float32).reshape(6, 2)
+    row_pos = np.array([4, 1, 0, 5, 2, 3], np.int32)          # T=3, k=2
+    gates = np.array([[1, 0], [0, 1], [0.25, 0.75]], np.float32)
+    y = oracle.combine(y_perm, row_pos, gates)
+    assert y[0].tolist() == y_perm[4].tolist()
+    assert y[1].tolist() == y_perm[5].tolist()
+    assert np.allclose(y[2], 0.25 * y_perm[2] + 0.75 * y_perm[3])

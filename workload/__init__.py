@@ -1,0 +1,215 @@
+"""Seeded synthetic inputs for the routed-expert MoE layer with low-bit experts.
+
+This module is the only code shared by the GPU path's callers (tests, bench) and
+the CPU oracle.  It draws random numbers and stores them in the layer's input
+formats; it performs none of the layer's arithmetic (no routing, no unpacking,
+no dequantisation, no matmuls).
+
+Input formats (all row-major, contiguous):
+
+* ``x``          [T, H]        uint16 holding bfloat16 bits (round-to-nearest-even
+                               from float32 samples).
+* ``w_router``   [E, H]        uint16 bfloat16 bits.  The pages keep routers in
+                               16-bit precision (page 1 "Qwen3.8-Flash-Next on one
+                               24 GB GPU", opening paragraph; page 5 model card,
+                               "Precision map").
+* ``logit_bias`` [E] float32 or None: a log-prior added to router logits.
+* ``w13_codes``  [E, 2I, H/P]  uint32 words, P = 32/bits codes per word, packed
+                               along K (the reduction dimension), least
+                               significant field first.  Rows [0, I) are the
+                               gate projection, rows [I, 2I) the up projection.
+* ``w13_scales`` [E, 2I, H/128] uint16 bfloat16 bits, one per 128-wide K group.
+* ``w13_zeros``  [E, 2I, H/128] uint8 zero-points (2-bit format only).
+* ``w2_codes``   [E, H, I/P], ``w2_scales`` [E, H, I/128], ``w2_zeros`` likewise
+                 for the down projection.
+
+Codes are drawn as uniformly random 32-bit words: every field of a uniform word
+is uniform over its 2**bits values, so INT4 codes are uniform over the 16
+signed values and 2-bit codes uniform over {0..3}.
+
+Each tensor gets its own PCG64 stream keyed by (workload seed, tensor tag,
+weight-set index), so any one tensor can be regenerated alone.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+GROUP = 128  # quantisation group along K
+
+# tensor tags for the per-tensor random streams
+_TAG_X, _TAG_WR, _TAG_W13C, _TAG_W13S, _TAG_W13Z, _TAG_W2C, _TAG_W2S, _TAG_W2Z = range(8)
+
+
+@dataclass(frozen=True)
+class Spec:
+    """Shape and sampling laws of one synthetic MoE-layer workload."""
+
+    name: str
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    bits: int
+    seed: int
+    router_law: str = "normal"     # "normal": N(0, 0.02); "uniform": U(+-0.02*sqrt(3))
+    zipf_s: float = 0.0            # >0: add -s*ln(e+1) to the logits of expert e
+    x_law: str = "normal"          # "normal" or "ar1_streams"
+    streams: int = 0               # ar1_streams: number of independent streams
+    ar1_alpha: float = 0.85
+    scale_sigma: float = 0.02      # scales are |N(0,1)| * scale_sigma
+    n_sets: int = 1                # distinct weight sets cycled by the bench
+    note: str = ""
+
+    @property
+    def codes_per_word(self) -> int:
+        return 32 // self.bits
+
+    def weight_bytes_per_expert(self) -> int:
+        """Packed bytes one expert occupies: codes + bf16 scales (+ u8 zeros)."""
+        H, I = self.H, self.I
+        n_w = 2 * I * H + H * I                  # weights in gate_up and down
+        codes = n_w * self.bits // 8
+        groups = n_w // GROUP
+        zeros = groups if self.bits == 2 else 0
+        return codes + 2 * groups + zeros
+
+
+SPECS: Dict[str, Spec] = {
+    s.name: s
+    for s in [
+        Spec("tiny_t4_h256_e8_k2_i128_int4", T=4, H=256, E=8, k=2, I=128, bits=4, seed=1000,
+             note="CPU-seconds layer; N(0,0.02) router"),
+        Spec("decode_t1_h4096_e256_k8_i1024_int4", T=1, H=4096, E=256, k=8, I=1024, bits=4,
+             seed=1001, router_law="uniform", n_sets=8,
+             note="batch-1 decode; 8 weight sets cycled so touched bytes exceed the 256 MB Infinity Cache"),
+        Spec("verify_t16_h4096_e256_k8_i1024_int4", T=16, H=4096, E=256, k=8, I=1024, bits=4,
+             seed=1002, router_law="uniform", x_law="ar1_streams", streams=4, n_sets=8,
+             note="speculative verify: 4 streams x 4 draft tokens, AR(1) correlated activations"),
+        Spec("prefill_t4096_h4096_e256_k8_i1024_int4", T=4096, H=4096, E=256, k=8, I=1024, bits=4,
+             seed=1003, zipf_s=1.1,
+             note="prefill chunk; Zipf(1.1) log-prior on the router logits"),
+        Spec("decode_t1_h4096_e256_k8_i1024_int2", T=1, H=4096, E=256, k=8, I=1024, bits=2,
+             seed=1004, router_law="uniform", scale_sigma=0.05, n_sets=16,
+             note="2-bit experts with zero-points, batch-1 decode, 16 sets cycled"),
+        Spec("prefill_t8192_h4096_e256_k8_i1024_int2", T=8192, H=4096, E=256, k=8, I=1024, bits=2,
+             seed=1005, zipf_s=1.1, scale_sigma=0.05,
+             note="2-bit experts, prefill chunk with Zipf(1.1) log-prior"),
+    ]
+}
+
+
+def spec(name: str, **overrides) -> Spec:
+    """Look up a workload by name, optionally overriding fields (e.g. T, E, k)."""
+    base = SPECS[name]
+    if not overrides:
+        return base
+    d = dict(base.__dict__)
+    d.update(overrides)
+    return Spec(**d)
+
+
+def _rng(seed: int, tag: int, set_idx: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tag, set_idx)))
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def _uniform_words(rng: np.random.Generator, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    n64 = (n + 1) // 2
+    w = rng.bit_generator.random_raw(n64).view(np.uint32)[:n]
+    return np.ascontiguousarray(w.reshape(shape))
+
+
+def make_x(sp: Spec, set_idx: int = 0) -> np.ndarray:
+    """Activations [T, H] as bf16 bits."""
+    rng = _rng(sp.seed, _TAG_X, set_idx)
+    if sp.x_law == "normal":
+        xf = rng.standard_normal((sp.T, sp.H), dtype=np.float32)
+    elif sp.x_law == "ar1_streams":
+        # consecutive tokens of a stream: x_{j+1} = a*x_j + sqrt(1-a^2)*eps
+        per = sp.T // sp.streams
+        a = sp.ar1_alpha
+        xf = np.empty((sp.T, sp.H), np.float32)
+        for s in range(sp.streams):
+            cur = rng.standard_normal(sp.H, dtype=np.float32)
+            for j in range(per):
+                if j:
+                    eps = rng.standard_normal(sp.H, dtype=np.float32)
+                    cur = (a * cur + math.sqrt(1.0 - a * a) * eps).astype(np.float32)
+                xf[s * per + j] = cur
+    else:
+        raise ValueError(sp.x_law)
+    return bf16_bits(xf)
+
+
+def make_router(sp: Spec):
+    """Router weight [E, H] (bf16 bits) and optional logit bias [E] (float32)."""
+    rng = _rng(sp.seed, _TAG_WR)
+    if sp.router_law == "normal":
+        w = rng.standard_normal((sp.E, sp.H), dtype=np.float32) * np.float32(0.02)
+    elif sp.router_law == "uniform":
+        lim = 0.02 * math.sqrt(3.0)  # same standard deviation as N(0, 0.02)
+        w = rng.uniform(-lim, lim, size=(sp.E, sp.H)).astype(np.float32)
+    else:
+        raise ValueError(sp.router_law)
+    bias = None
+    if sp.zipf_s > 0:
+        rank = np.arange(1, sp.E + 1, dtype=np.float64)
+        bias = (-sp.zipf_s * np.log(rank)).astype(np.float32)
+    return bf16_bits(w), bias
+
+
+def _scales(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    s = np.abs(rng.standard_normal(shape, dtype=np.float32)) * np.float32(sigma)
+    return bf16_bits(s)
+
+
+def make_weight_set(sp: Spec, set_idx: int = 0) -> Dict[str, np.ndarray]:
+    """One full layer of expert weights in the packed formats described above."""
+    E, H, I, P = sp.E, sp.H, sp.I, sp.codes_per_word
+    if H % GROUP or I % GROUP:
+        raise ValueError("H and I must be multiples of the 128-wide group")
+    out = {
+        "w13_codes": _uniform_words(_rng(sp.seed, _TAG_W13C, set_idx), (E, 2 * I, H // P)),
+        "w13_scales": _scales(_rng(sp.seed, _TAG_W13S, set_idx), (E, 2 * I, H // GROUP), sp.scale_sigma),
+        "w2_codes": _uniform_words(_rng(sp.seed, _TAG_W2C, set_idx), (E, H, I // P)),
+        "w2_scales": _scales(_rng(sp.seed, _TAG_W2S, set_idx), (E, H, I // GROUP), sp.scale_sigma),
+    }
+    if sp.bits == 2:
+        # integer zero-points drawn uniformly from {1, 2}
+        out["w13_zeros"] = _rng(sp.seed, _TAG_W13Z, set_idx).integers(
+            1, 3, size=(E, 2 * I, H // GROUP), dtype=np.uint8)
+        out["w2_zeros"] = _rng(sp.seed, _TAG_W2Z, set_idx).integers(
+            1, 3, size=(E, H, I // GROUP), dtype=np.uint8)
+    return out
+
+
+@dataclass
+class LayerInputs:
+    spec: Spec
+    x: np.ndarray
+    w_router: np.ndarray
+    logit_bias: Optional[np.ndarray]
+    weights: Dict[str, np.ndarray] = field(default_factory=dict)
+
+
+def make_layer_inputs(name_or_spec, set_idx: int = 0, **overrides) -> LayerInputs:
+    """Activations, router and one weight set of a workload."""
+    sp = name_or_spec if isinstance(name_or_spec, Spec) else spec(name_or_spec, **overrides)
+    w_r, bias = make_router(sp)
+    return LayerInputs(sp, make_x(sp, set_idx), w_r, bias, make_weight_set(sp, set_idx))
+
+
+def list_workloads() -> List[str]:
+    return list(SPECS)
