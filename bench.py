@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-expert MoE layer with low-bit experts on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu-baseline]
+
+A step is one pass of the whole layer -- moe_route, moe_permute,
+moe_expert_ffn_w4a16/_w2a16, moe_combine, all through the C ABI -- over one
+batch of synthetic input already resident in HBM.  Decode workloads cycle
+through their distinct weight sets (and activations) step by step, so the
+expert bytes a step touches come from HBM rather than the 256 MB Infinity
+Cache.  By default each step is replayed from a HIP graph that holds its four
+calls (--eager launches them one by one instead).
+
+Printed: one JSON line with tokens/s over the timed steps, the roofline of
+the dominant kernel (the expert FFN: HBM-bound on packed weight bytes for
+decode, MFMA-bound on useful FLOPs for prefill) from HIP events on its own
+stream, and the CPU oracle's rate on a bounded sample of the same workload,
+timed on the host in a child process pinned to one core.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode HBM GB/s % peak; prefill MFMA % peak (1 GPU)"
+DEFAULT_WORKLOAD = "decode_t1_h4096_e256_k8_i1024_int4"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--eager", action="store_true", help="launch the four calls per step without a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ffn-only", action="store_true", help="time only the expert-FFN launches (for profiling)")
+    return ap.parse_args()
+
+
+def start_cpu_baseline(args):
+    if args.no_cpu_baseline:
+        return None
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    cmd = [sys.executable, "-m", "oracle.cpu_baseline", "--workload", args.workload, "--seconds", str(args.cpu_seconds)]
+    return subprocess.Popen(cmd, cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def finish_cpu_baseline(proc):
+    if proc is None:
+        return None
+    out, err = proc.communicate(timeout=600)
+    if proc.returncode != 0:
+        print(f"[bench] cpu baseline failed: {err[-500:]}", file=sys.stderr, flush=True)
+        return None
+    d = json.loads(out.strip().splitlines()[-1])
+    return {k: d[k] for k in ("value", "unit", "cores", "kind", "sample")}
+
+
+class Plan:
+    """Device buffers and pre-bound C-ABI calls for one workload."""
+
+    def __init__(self, sp, dev):
+        import numpy as np
+        import torch
+
+        import bit_quantized_moe_amd as bq
+        import workload
+
+        self.sp, self.dev, self.L = sp, dev, bq.lib()
+        T, H, E, k, I = sp.T, sp.H, sp.E, sp.k, sp.I
+        n = T * k
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            if a.dtype == np.uint32:
+                return torch.from_numpy(a.view(np.int32)).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        w_r, bias = workload.make_router(sp)
+        self.w_r = up(w_r)
+        self.bias = up(bias) if bias is not None else None
+        self.sets = []
+        t0 = time.time()
+        for s in range(sp.n_sets):
+            w = workload.make_weight_set(sp, s)
+            dw = {kk: up(v) for kk, v in w.items()}
+            del w
+            st = dict(w=dw, x=up(workload.make_x(sp, s)))
+            st["ids"] = torch.empty((T, k), dtype=torch.int32, device=dev)
+            st["gates"] = torch.empty((T, k), dtype=torch.float32, device=dev)
+            st["offsets"] = torch.empty(E + 1, dtype=torch.int32, device=dev)
+            st["sorted_rows"] = torch.empty(n, dtype=torch.int32, device=dev)
+            st["row_pos"] = torch.empty(n, dtype=torch.int32, device=dev)
+            st["active"] = torch.empty(1 + min(E, n), dtype=torch.int32, device=dev)
+            self.sets.append(st)
+        print(f"[bench] {sp.n_sets} weight set(s) generated and uploaded in {time.time() - t0:.1f} s", flush=True)
+        self.y_perm = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.ws_route = torch.zeros(self.L.moe_route_workspace_size(T, E), dtype=torch.uint8, device=dev)
+        self.ws_ffn = torch.zeros(self.L.moe_expert_ffn_workspace_size(T, k, E, H, I), dtype=torch.uint8, device=dev)
+        self.torch = torch
+
+    def _chk(self, s, name):
+        if s != 0:
+            raise RuntimeError(f"{name}: status {s}: {self.L.moe_last_error().decode()}")
+
+    def route_permute(self, i):
+        sp, st, L = self.sp, self.sets[i], self.L
+        stream = self.torch.cuda.current_stream(self.dev).cuda_stream
+        self._chk(L.moe_route(st["x"].data_ptr(), self.w_r.data_ptr(), self.bias.data_ptr() if self.bias is not None else None,
+                              sp.T, sp.H, sp.E, sp.k, st["ids"].data_ptr(), st["gates"].data_ptr(), None,
+                              self.ws_route.data_ptr(), self.ws_route.numel(), stream), "moe_route")
+        self._chk(L.moe_permute(st["ids"].data_ptr(), sp.T, sp.k, sp.E, st["offsets"].data_ptr(),
+                                st["sorted_rows"].data_ptr(), st["row_pos"].data_ptr(), st["active"].data_ptr(),
+                                None, 0, stream), "moe_permute")
+
+    def ffn(self, i):
+        sp, st, L = self.sp, self.sets[i], self.L
+        stream = self.torch.cuda.current_stream(self.dev).cuda_stream
+        w = st["w"]
+        common = (st["x"].data_ptr(), st["offsets"].data_ptr(), st["sorted_rows"].data_ptr(), st["active"].data_ptr(),
+                  sp.T, sp.k, sp.E, sp.H, sp.I)
+        if sp.bits == 4:
+            s = L.moe_expert_ffn_w4a16(*common, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
+                                       w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(), self.y_perm.data_ptr(),
+                                       self.ws_ffn.data_ptr(), self.ws_ffn.numel(), stream)
+        else:
+            s = L.moe_expert_ffn_w2a16(*common, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
+                                       w["w13_zeros"].data_ptr(), w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(),
+                                       w["w2_zeros"].data_ptr(), self.y_perm.data_ptr(), self.ws_ffn.data_ptr(),
+                                       self.ws_ffn.numel(), stream)
+        self._chk(s, "moe_expert_ffn")
+
+    def combine(self, i):
+        sp, st = self.sp, self.sets[i]
+        stream = self.torch.cuda.current_stream(self.dev).cuda_stream
+        self._chk(self.L.moe_combine(self.y_perm.data_ptr(), st["row_pos"].data_ptr(), st["gates"].data_ptr(), sp.T,
+                                     sp.k, sp.H, self.y.data_ptr(), stream), "moe_combine")
+
+    def step(self, i):
+        self.route_permute(i)
+        self.ffn(i)
+        self.combine(i)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the layer runs on a single MI355X and "
+                                   "has no multi-GPU path; run with --gpus 1"}))
+        sys.exit(2)
+    cpu = start_cpu_baseline(args)
+
+    import torch
+
+    import workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sp = workload.spec(args.workload)
+    plan = Plan(sp, dev)
+    nset = sp.n_sets
+    stream = torch.cuda.Stream(dev)
+
+    with torch.cuda.stream(stream):
+        for i in range(nset):      # eager warm-up; also fills every set's routing buffers
+            plan.step(i)
+        torch.cuda.synchronize(dev)
+
+        use_graph = not args.eager
+        graphs = []
+        if use_graph:
+            for i in range(nset):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    plan.step(i)
+                graphs.append(g)
+            torch.cuda.synchronize(dev)
+        run = (lambda i: graphs[i % nset].replay()) if use_graph else (lambda i: plan.step(i % nset))
+
+        # ---- whole-layer steps
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0 = time.perf_counter()
+        e0.record(stream)
+        if not args.ffn_only:
+            for i in range(args.steps):
+                run(i)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - c0
+        ms_step = e0.elapsed_time(e1) / max(1, args.steps)
+
+        # ---- dominant kernel: the expert FFN alone, back to back, one launch per set
+        fg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fg, stream=stream):
+            for i in range(nset):
+                plan.ffn(i)
+        reps = max(1, args.steps // nset)
+        for _ in range(2):
+            fg.replay()
+        torch.cuda.synchronize(dev)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(reps):
+            fg.replay()
+        f1.record(stream)
+        torch.cuda.synchronize(dev)
+        ffn_ms = f0.elapsed_time(f1) / (reps * nset)
+
+    # distinct experts per launch (decode bytes) from each set's routing
+    distinct = [int(st["active"][0].item()) for st in plan.sets]
+    mean_distinct = sum(distinct) / len(distinct)
+    bpe = sp.weight_bytes_per_expert()
+    decode = sp.T <= 16
+    if decode:
+        alg = mean_distinct * bpe
+        achieved = alg / (ffn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "ffn_decode_kernel (fused gate_up+SwiGLU+down GEMV)",
+                "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(ffn_ms * 1e3, 3),
+                "distinct_experts_per_launch": mean_distinct}
+    else:
+        flops = 2.0 * sp.T * sp.k * 3 * sp.H * sp.I
+        achieved = flops / (ffn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "expert FFN call (ffn_gemm_kernel gate_up+SwiGLU, then down)",
+                "algorithmic_flops_per_launch": flops, "avg_launch_us": round(ffn_ms * 1e3, 3)}
+
+    cpu_res = finish_cpu_baseline(cpu)
+    tok_s = sp.T / (ms_step * 1e-3) if ms_step > 0 else 0.0
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": sp.name, "T": sp.T, "H": sp.H, "E": sp.E, "top_k": sp.k, "I": sp.I,
+                   "weight_format": f"int{sp.bits} g128" + (" sym" if sp.bits == 4 else " + zero-point"),
+                   "weight_sets_cycled": nset, "launch": "hip graph per step" if use_graph else "eager",
+                   "wall_s_timed": round(wall, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu_res,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+"""Routed-expert MoE layer with low-bit (INT4 / 2-bit) experts on AMD MI355X.
+
+Python binding of ``libbqmoe.so`` (declared in include/bqmoe.h).  The binding
+only marshals arguments: it takes torch tensors for device memory, passes raw
+pointers and the current HIP stream, and raises on a non-OK status.  Every
+step of the layer runs in the library's HIP kernels; there is no fallback, so
+a missing library is an error.
+
+Tensor conventions: bf16 data as ``torch.bfloat16`` (or any 2-byte dtype
+holding bf16 bits), packed code words as ``torch.int32`` (bit patterns of the
+uint32 words), zero-points as ``torch.uint8``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+__all__ = [
+    "MoEError", "lib", "route", "permute", "expert_ffn", "combine", "unpack_codes",
+    "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbqmoe.so")
+
+_c_int, _c_i64, _c_size, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "moe_abi_version": (_c_int, []),
+    "moe_status_string": (ctypes.c_char_p, [_c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_route_workspace_size": (_c_size, [_c_int, _c_int]),
+    "moe_route": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "moe_permute_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
+    "moe_permute": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "moe_expert_ffn_workspace_size": (_c_size, [_c_int] * 5),
+    "moe_expert_ffn_w4a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 5 + [_vp, _c_size, _vp]),
+    "moe_expert_ffn_w2a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 7 + [_vp, _c_size, _vp]),
+    "moe_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_unpack_codes": (_c_int, [_vp, _c_int, _c_i64, _vp, _vp]),
+    "moe_dequant_bf16": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbqmoe.so (built by ``python -m bit_quantized_moe_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoEError(f"{LIB_PATH} is missing: build it with `python -m bit_quantized_moe_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, name: str) -> None:
+    if status != 0:
+        L = lib()
+        raise MoEError(f"{name}: {L.moe_status_string(status).decode()} ({status}): {L.moe_last_error().decode()}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise MoEError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor) -> torch.device:
+    if t.device.type != "cuda":
+        raise MoEError("the MoE library runs on the GPU: pass device tensors")
+    return t.device
+
+
+class Workspaces:
+    """Zero-initialised device workspaces, grown on demand and reused across calls.
+
+    Each workspace starts with a control block that the kernels leave zeroed,
+    so a buffer can be reused by consecutive calls on one stream.
+    """
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self._bufs: Dict[str, torch.Tensor] = {}
+
+    def get(self, name: str, nbytes: int) -> torch.Tensor:
+        b = self._bufs.get(name)
+        if b is None or b.numel() < nbytes:
+            b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._bufs[name] = b
+        return b
+
+
+def route(x: torch.Tensor, w_router: torch.Tensor, k: int, logit_bias: Optional[torch.Tensor] = None,
+          want_logits: bool = False, ws: Optional[Workspaces] = None):
+    """Router logits, top-k ids (int32 [T, k]) and softmax gates (float32 [T, k])."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = w_router.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    L = lib()
+    nbytes = L.moe_route_workspace_size(T, E)
+    w = (ws or Workspaces(dev)).get("route", nbytes)
+    _check(L.moe_route(_p(x), _p(w_router), _p(logit_bias), T, H, E, k, _p(ids), _p(gates), _p(logits),
+                       _p(w), w.numel(), _stream(dev)), "moe_route")
+    return (ids, gates, logits) if want_logits else (ids, gates)
+
+
+def permute(ids: torch.Tensor, E: int, ws: Optional[Workspaces] = None):
+    """Stable grouping of rows by expert: (offsets [E+1], sorted_rows, row_pos, active)."""
+    dev = _dev(ids)
+    T, k = ids.shape
+    n = T * k
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_rows = torch.empty(n, dtype=torch.int32, device=dev)
+    row_pos = torch.empty(n, dtype=torch.int32, device=dev)
+    active = torch.empty(1 + min(E, n), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.moe_permute_workspace_size(T, k, E)
+    w = (ws or Workspaces(dev)).get("permute", nbytes) if nbytes else None
+    _check(L.moe_permute(_p(ids), T, k, E, _p(offsets), _p(sorted_rows), _p(row_pos), _p(active), _p(w),
+                         0 if w is None else w.numel(), _stream(dev)), "moe_permute")
+    return offsets, sorted_rows, row_pos, active
+
+
+def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: Dict[str, torch.Tensor], bits: int,
+               I: int, ws: Optional[Workspaces] = None, y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-expert gate_up -> SwiGLU -> down on the sorted rows; bf16 [T*k, H]."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = offsets.numel() - 1
+    if y_perm is None:
+        y_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    L = lib()
+    nbytes = L.moe_expert_ffn_workspace_size(T, k, E, H, I)
+    w = (ws or Workspaces(dev)).get("ffn", nbytes)
+    st = _stream(dev)
+    if bits == 4:
+        s = L.moe_expert_ffn_w4a16(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I,
+                                   _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights["w2_codes"]),
+                                   _p(weights["w2_scales"]), _p(y_perm), _p(w), w.numel(), st)
+        _check(s, "moe_expert_ffn_w4a16")
+    elif bits == 2:
+        s = L.moe_expert_ffn_w2a16(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I,
+                                   _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights["w13_zeros"]),
+                                   _p(weights["w2_codes"]), _p(weights["w2_scales"]), _p(weights["w2_zeros"]),
+                                   _p(y_perm), _p(w), w.numel(), st)
+        _check(s, "moe_expert_ffn_w2a16")
+    else:
+        raise MoEError("bits must be 2 or 4")
+    return y_perm
+
+
+def combine(y_perm: torch.Tensor, row_pos: torch.Tensor, gates: torch.Tensor) -> torch.Tensor:
+    """Gate-weighted sum of each token's k expert rows; bf16 [T, H]."""
+    dev = _dev(y_perm)
+    T, k = gates.shape
+    H = y_perm.shape[1]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(lib().moe_combine(_p(y_perm), _p(row_pos), _p(gates), T, k, H, _p(y), _stream(dev)), "moe_combine")
+    return y
+
+
+def unpack_codes(words: torch.Tensor, bits: int) -> torch.Tensor:
+    """Signed codes of packed words (decode-path unpack routine); int8, K order."""
+    dev = _dev(words)
+    n = words.numel()
+    out = torch.empty(n * (32 // bits), dtype=torch.int8, device=dev)
+    _check(lib().moe_unpack_codes(_p(words), bits, n, _p(out), _stream(dev)), "moe_unpack_codes")
+    return out
+
+
+def dequant_bf16(words: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor], bits: int,
+                 N: int, K: int) -> torch.Tensor:
+    """[N, K] bf16 weights by the grouped-GEMM dequant routine."""
+    dev = _dev(words)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    _check(lib().moe_dequant_bf16(_p(words), _p(scales), _p(zeros), bits, N, K, _p(out), _stream(dev)),
+           "moe_dequant_bf16")
+    return out
+
+
+def moe_layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
+              weights: Dict[str, torch.Tensor], k: int, bits: int, I: int, ws: Optional[Workspaces] = None,
+              want_logits: bool = False) -> Dict[str, torch.Tensor]:
+    """The whole layer through the four library calls; returns every intermediate."""
+    ws = ws or Workspaces(x.device)
+    E = w_router.shape[0]
+    r = route(x, w_router, k, logit_bias, want_logits=want_logits, ws=ws)
+    ids, gates = r[0], r[1]
+    offsets, sorted_rows, row_pos, active = permute(ids, E, ws=ws)
+    y_perm = expert_ffn(x, offsets, sorted_rows, active, k, weights, bits, I, ws=ws)
+    y = combine(y_perm, row_pos, gates)
+    out = dict(ids=ids, gates=gates, offsets=offsets, sorted_rows=sorted_rows, row_pos=row_pos, active=active,
+               y_perm=y_perm, y=y)
+    if want_logits:
+        out["logits"] = r[2]
+    return out

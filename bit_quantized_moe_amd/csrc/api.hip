@@ -1,0 +1,242 @@
+// C ABI of the MoE library: host-side argument checks, workspace sizing,
+// dispatch to the kernel launchers and error reporting.  Nothing here touches
+// the GPU before every argument of a call has been checked.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+
+#include "bqmoe.h"
+#include "common.cuh"
+#include "internal.h"
+
+using namespace bqmoe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+bool g_dev_ok[kMaxDevices];
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status check_common_moe(int T, int H, int E, int k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+  if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E must be in [1, 1024] (got %d)", E);
+  if (k < 1 || k > 32 || k > E) return fail(MOE_ERR_INVALID_ARG, "k must be in [1, min(E, 32)] (got k=%d, E=%d)", k, E);
+  if (H < 128 || H % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H must be a positive multiple of 128 (got %d)", H);
+  if ((long long)T * k > (1LL << 24)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*k must be <= 2^24");
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace bqmoe {
+
+hipError_t current_device_info(DeviceInfo *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev_ok[dev]) {
+    DeviceInfo d;
+    d.device = dev;
+    e = hipDeviceGetAttribute(&d.num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_dev[dev] = d;
+    g_dev_ok[dev] = true;
+  }
+  *out = g_dev[dev];
+  return hipSuccess;
+}
+
+size_t ffn_workspace_bytes(int T, int k, int E, int H, int I) {
+  (void)E;
+  (void)H;
+  return round_up(ffn_ctl_bytes(T, k, E) + (size_t)T * k * I * sizeof(uint16_t), 256);
+}
+
+}  // namespace bqmoe
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MOE_ERR_MISALIGNED: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+size_t moe_route_workspace_size(int T, int E) {
+  if (T < 0 || E < 1) return 0;
+  return round_up(route_workspace_bytes(T, E), 256);
+}
+
+moe_status moe_route(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,
+                     int k, int32_t *topk_ids, float *topk_weights, float *logits, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  moe_status s = check_common_moe(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (!x || !w_router || !topk_ids || !topk_weights || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: x, w_router, topk_ids, topk_weights and workspace are required");
+  if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(MOE_ERR_MISALIGNED, "moe_route: x and w_router need 16-byte alignment");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "moe_route: workspace needs 256-byte alignment");
+  if (!aligned(topk_ids, 4) || !aligned(topk_weights, 4) || (logits && !aligned(logits, 4)) ||
+      (logit_bias && !aligned(logit_bias, 4)))
+    return fail(MOE_ERR_MISALIGNED, "moe_route: 4-byte arrays must be 4-byte aligned");
+  if (workspace_bytes < moe_route_workspace_size(T, E))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_route: workspace %zu < %zu bytes", workspace_bytes,
+                moe_route_workspace_size(T, E));
+  if (T == 0) return MOE_OK;
+  return from_hip(launch_route(x, w_router, logit_bias, T, H, E, k, topk_ids, topk_weights, logits, workspace,
+                               (hipStream_t)stream),
+                  "moe_route launch");
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return permute_workspace_bytes(T, k, E);
+}
+
+moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *expert_offsets, int32_t *sorted_rows,
+                       int32_t *row_pos, int32_t *active, void *workspace, size_t workspace_bytes, void *stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+  if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E must be in [1, 1024] (got %d)", E);
+  if (k < 1 || k > 32) return fail(MOE_ERR_INVALID_ARG, "k must be in [1, 32] (got %d)", k);
+  if ((long long)T * k > (1LL << 24)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*k must be <= 2^24");
+  if (!topk_ids || !expert_offsets || !sorted_rows || !row_pos || !active)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: all arrays are required");
+  if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_rows, 4) || !aligned(row_pos, 4) ||
+      !aligned(active, 4))
+    return fail(MOE_ERR_MISALIGNED, "moe_permute: int32 arrays must be 4-byte aligned");
+  const size_t need = moe_permute_workspace_size(T, k, E);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_permute: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (T == 0) return MOE_OK;
+  return from_hip(launch_permute(topk_ids, T, k, E, expert_offsets, sorted_rows, row_pos, active, workspace,
+                                 (hipStream_t)stream),
+                  "moe_permute launch");
+}
+
+size_t moe_expert_ffn_workspace_size(int T, int k, int E, int H, int I) {
+  if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return 0;
+  return ffn_workspace_bytes(T, k, E, H, I);
+}
+
+static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, const int32_t *expert_offsets,
+                             const int32_t *sorted_rows, const int32_t *active, int T, int k, int E, int H, int I,
+                             const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
+                             const uint32_t *w2_codes, const uint16_t *w2_scales, const uint8_t *w2_zeros,
+                             uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status s = check_common_moe(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
+  if (!x || !expert_offsets || !sorted_rows || !active || !w13_codes || !w13_scales || !w2_codes || !w2_scales ||
+      !y_perm || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+  if (bits == 2 && (!w13_zeros || !w2_zeros)) return fail(MOE_ERR_INVALID_ARG, "%s: zero-points are required", name);
+  if (!aligned(x, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16))
+    return fail(MOE_ERR_MISALIGNED, "%s: x and code arrays need 16-byte alignment", name);
+  if (!aligned(w13_scales, 2) || !aligned(w2_scales, 2) || !aligned(y_perm, 4) || !aligned(expert_offsets, 4) ||
+      !aligned(sorted_rows, 4) || !aligned(active, 4))
+    return fail(MOE_ERR_MISALIGNED, "%s: array alignment", name);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
+  const size_t need = moe_expert_ffn_workspace_size(T, k, E, H, I);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", name, workspace_bytes, need);
+  if (T == 0) return MOE_OK;
+  DeviceInfo dev;
+  hipError_t he = current_device_info(&dev);
+  if (he != hipSuccess) return from_hip(he, name);
+  FfnArgs a{x, expert_offsets, sorted_rows, active, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
+            w2_codes, w2_scales, w2_zeros, y_perm, workspace};
+  if (T <= kDecodeMaxT && decode_layout_ok(H, I, bits))
+    return from_hip(launch_ffn_decode(a, dev, (hipStream_t)stream), name);
+  return from_hip(launch_ffn_prefill(a, dev, (hipStream_t)stream), name);
+}
+
+moe_status moe_expert_ffn_w4a16(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                const int32_t *active, int T, int k, int E, int H, int I, const uint32_t *w13_codes,
+                                const uint16_t *w13_scales, const uint32_t *w2_codes, const uint16_t *w2_scales,
+                                uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream) {
+  return expert_ffn("moe_expert_ffn_w4a16", 4, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
+                    w13_scales, nullptr, w2_codes, w2_scales, nullptr, y_perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                const int32_t *active, int T, int k, int E, int H, int I, const uint32_t *w13_codes,
+                                const uint16_t *w13_scales, const uint8_t *w13_zeros, const uint32_t *w2_codes,
+                                const uint16_t *w2_scales, const uint8_t *w2_zeros, uint16_t *y_perm,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  return expert_ffn("moe_expert_ffn_w2a16", 2, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
+                    w13_scales, w13_zeros, w2_codes, w2_scales, w2_zeros, y_perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const float *topk_weights, int T, int k, int H,
+                       uint16_t *y, void *stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+  if (k < 1 || k > 32) return fail(MOE_ERR_INVALID_ARG, "k must be in [1, 32] (got %d)", k);
+  if (H < 8 || H % 8) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_combine: H must be a positive multiple of 8");
+  if (!y_perm || !row_pos || !topk_weights || !y) return fail(MOE_ERR_INVALID_ARG, "moe_combine: all arrays are required");
+  if (!aligned(y_perm, 16) || !aligned(y, 16) || !aligned(row_pos, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_ERR_MISALIGNED, "moe_combine: y_perm and y need 16-byte alignment");
+  if ((long long)T * k > (1LL << 24)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "T*k must be <= 2^24");
+  if (T == 0) return MOE_OK;
+  return from_hip(launch_combine(y_perm, row_pos, topk_weights, T, k, H, y, (hipStream_t)stream), "moe_combine launch");
+}
+
+moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, int8_t *out, void *stream) {
+  if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2 or 4 (got %d)", bits);
+  if (n_words < 0) return fail(MOE_ERR_INVALID_ARG, "n_words must be >= 0");
+  if (n_words > (1LL << 36)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "n_words too large");
+  if (!words || !out) return fail(MOE_ERR_INVALID_ARG, "moe_unpack_codes: words and out are required");
+  if (!aligned(words, 4)) return fail(MOE_ERR_MISALIGNED, "moe_unpack_codes: words must be 4-byte aligned");
+  if (n_words == 0) return MOE_OK;
+  return from_hip(launch_unpack(words, bits, n_words, out, (hipStream_t)stream), "moe_unpack_codes launch");
+}
+
+moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits, int N, int K,
+                            uint16_t *out, void *stream) {
+  if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2 or 4 (got %d)", bits);
+  if (N < 0 || K < 0) return fail(MOE_ERR_INVALID_ARG, "N and K must be >= 0");
+  if (K % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K must be a multiple of 128 (got %d)", K);
+  if ((long long)N * K > (1LL << 36)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "N*K too large");
+  if (!words || !scales || !out || (bits == 2 && !zeros))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dequant_bf16: a required pointer is NULL");
+  if (!aligned(words, 4) || !aligned(scales, 2) || !aligned(out, 4))
+    return fail(MOE_ERR_MISALIGNED, "moe_dequant_bf16: array alignment");
+  if (N == 0 || K == 0) return MOE_OK;
+  return from_hip(launch_dequant_bf16(words, scales, zeros, bits, N, K, out, (hipStream_t)stream),
+                  "moe_dequant_bf16 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Device helpers shared by the MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bqmoe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;  // quantisation group along K
+
+// Control block at the start of every workspace (int32 words).
+//   [0]      route: blocks finished (last-block top-k)
+//   [1]      ffn decode: blocks finished
+//   [2]      sticky error flags (bit 0: a bounded wait timed out)
+//   [64..]   ffn decode: per-active-expert completion counters, kCtrStride apart
+constexpr int kCtlRouteDone = 0;
+constexpr int kCtlFfnDone = 1;
+constexpr int kCtlError = 2;
+constexpr int kCtlCounters = 64;
+constexpr int kCtrStride = 32;   // ints between counters: one 128-byte line each
+constexpr int kCtlWords = 1024;  // minimum control block: 4 KiB
+constexpr size_t kCtlBytes = kCtlWords * 4;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// Two float32 -> packed bf16 pair (round to nearest even), lo in bits [0,16).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c for packed bf16 pairs, float32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+
+// ---------------------------------------------------------------- decode-path unpack
+// Offset form used by the GEMV kernels: OR-ing a code field u (< 128) into the
+// mantissa of bf16 128.0 (0x4300) gives exactly 128 + u.  For a 4-bit word the
+// pair i (i = 0..3) holds fields (i, i+4); for a 2-bit word pair i (0..7) holds
+// fields (i, i+8).  The dot product with activations arranged in the same
+// pairs, minus (128 + zero) * sum(x), gives the dot with (u - zero).
+// (a & mask) | magic in one v_and_or_b32 (gfx9 VOP3 takes no literal and one
+// SGPR, so the mask lives in a VGPR and the magic in an SGPR).
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t a, uint32_t mask_v, uint32_t magic_s) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask_v), "s"(magic_s));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i) {
+  return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+}
+__device__ __forceinline__ uint32_t int2_pair(uint32_t w, int i) {
+  return ((w >> (2 * i)) & 0x00030003u) | 0x43004300u;
+}
+
+// ---------------------------------------------------------------- GEMM-path dequant
+// Eight 4-bit fields of w -> four packed bf16 pairs of (u - zoff) * s, in K order.
+// (u - zoff) * s is exact in float32 (a small integer times a bf16 value); the
+// conversion to bf16 rounds to nearest even.
+__device__ __forceinline__ void dequant8_int4(uint32_t w, float s, float zs, uint32_t out[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // fields 0, 2, 4, 6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // fields 1, 3, 5, 7
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float f0 = (float)((lo >> (8 * b)) & 0xFFu);
+    const float f1 = (float)((hi >> (8 * b)) & 0xFFu);
+    out[b] = pack_bf16x2(__builtin_fmaf(f0, s, zs), __builtin_fmaf(f1, s, zs));
+  }
+}
+
+// Sixteen 2-bit fields of w -> eight packed bf16 pairs of (u - z) * s, in K order.
+// |u - z| <= 2 for z in {1, 2}, so the values are exact in bf16.
+__device__ __forceinline__ void dequant16_int2(uint32_t w, float s, float zs, uint32_t out[8]) {
+  const uint32_t f0 = w & 0x03030303u;          // fields 0, 4, 8, 12
+  const uint32_t f1 = (w >> 2) & 0x03030303u;   // fields 1, 5, 9, 13
+  const uint32_t f2 = (w >> 4) & 0x03030303u;   // fields 2, 6, 10, 14
+  const uint32_t f3 = (w >> 6) & 0x03030303u;   // fields 3, 7, 11, 15
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float a0 = (float)((f0 >> (8 * b)) & 0xFFu);
+    const float a1 = (float)((f1 >> (8 * b)) & 0xFFu);
+    const float a2 = (float)((f2 >> (8 * b)) & 0xFFu);
+    const float a3 = (float)((f3 >> (8 * b)) & 0xFFu);
+    out[2 * b + 0] = pack_bf16x2(__builtin_fmaf(a0, s, zs), __builtin_fmaf(a1, s, zs));
+    out[2 * b + 1] = pack_bf16x2(__builtin_fmaf(a2, s, zs), __builtin_fmaf(a3, s, zs));
+  }
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float wave_sum_xor(float v, int width) {
+  for (int d = width >> 1; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// Sum over the 64 lanes as a balanced pairwise tree in lane order:
+// ((v0+v1)+(v2+v3))+... .  The xor butterfly with distance 1 first forms the
+// level-1 pairs, distance 2 the level-2 pairs, and so on; float addition is
+// commutative, so every lane ends with the bits of the tree sum.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Load through the scalar cache.  Only for data that no wave writes during
+// the kernel, at a wave-uniform address.
+template <typename T>
+__device__ __forceinline__ T sload(const T *ptr) {
+  return *(const __attribute__((address_space(4))) T *)ptr;
+}
+
+#define BQ_DPP_ADD(v, ctrl) \
+  ((v) + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false)))
+
+// Sum of v over aligned groups of `width` lanes (1, 2, 4, ..., 64); every lane
+// of a group receives the group sum.  Lane distances 1 and 2 use quad
+// permutes, 4 and 8 the row (half-)mirror, 16 and 32 a cross-row shuffle.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  if (width >= 2) v = BQ_DPP_ADD(v, 0xB1);   // quad_perm [1,0,3,2]
+  if (width >= 4) v = BQ_DPP_ADD(v, 0x4E);   // quad_perm [2,3,0,1]
+  if (width >= 8) v = BQ_DPP_ADD(v, 0x141);  // row_half_mirror
+  if (width >= 16) v = BQ_DPP_ADD(v, 0x140); // row_mirror
+  if (width >= 32) v += __shfl_xor(v, 16, kWave);
+  if (width >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Bounded spin on a device-scope counter (device-coherent loads).  Returns
+// false on timeout.  Data published before the counter was raised must be
+// read with device-coherent loads as well (see the callers).
+__device__ __forceinline__ bool wait_counter_geq(int *ctr, int target, int max_spins) {
+  int spins = 0;
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > max_spins) return false;
+  }
+  return true;
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// stores) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+}  // namespace bqmoe

@@ -1,0 +1,63 @@
+// Host-side launchers of the MoE kernels.  Each returns the hipError_t of its
+// launch; argument checking happens in api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bqmoe {
+
+struct DeviceInfo {
+  int device = -1;
+  int num_cus = 0;
+};
+
+// Properties of the current device (cached per device, thread-safe).
+hipError_t current_device_info(DeviceInfo *out);
+
+// route.hip
+constexpr int kRouteSmallT = 32;  // T at or below: split-expert kernel + last-block top-k
+size_t route_workspace_bytes(int T, int E);
+hipError_t launch_route(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
+                        int k, int32_t *ids, float *gates, float *logits, void *ws, hipStream_t st);
+
+// permute.hip
+size_t permute_workspace_bytes(int T, int k, int E);
+hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *offsets, int32_t *sorted_rows,
+                          int32_t *row_pos, int32_t *active, void *ws, hipStream_t st);
+
+// ffn_decode.hip / ffn_prefill.hip
+constexpr int kDecodeMaxT = 16;  // T at or below uses the fused decode GEMV
+size_t ffn_workspace_bytes(int T, int k, int E, int H, int I);
+size_t ffn_ctl_bytes(int T, int k, int E);  // control block at the start of the FFN workspace (x256)
+bool decode_layout_ok(int H, int I, int bits);
+
+struct FfnArgs {
+  const uint16_t *x;
+  const int32_t *offsets;
+  const int32_t *sorted_rows;
+  const int32_t *active;
+  int T, k, E, H, I, bits;
+  const uint32_t *w13_codes;
+  const uint16_t *w13_scales;
+  const uint8_t *w13_zeros;
+  const uint32_t *w2_codes;
+  const uint16_t *w2_scales;
+  const uint8_t *w2_zeros;
+  uint16_t *y_perm;
+  void *ws;
+};
+hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
+hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
+
+// combine.hip
+hipError_t launch_combine(const uint16_t *y_perm, const int32_t *row_pos, const float *gates, int T, int k,
+                          int H, uint16_t *y, hipStream_t st);
+
+// unpack.hip
+hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_t *out, hipStream_t st);
+hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
+                               int N, int K, uint16_t *out, hipStream_t st);
+
+}  // namespace bqmoe

@@ -1,0 +1,84 @@
+// Diagnostic kernels that expose the two device dequantisation routines:
+//  - moe_unpack_codes: the offset-bf16 unpack of the decode GEMV kernels,
+//    converted back to signed integer codes;
+//  - moe_dequant_bf16: the bf16 (q - z) * s of the grouped-GEMM kernels.
+#include "common.cuh"
+#include "internal.h"
+
+namespace bqmoe {
+namespace {
+
+template <int BITS>
+__global__ void unpack_kernel(const uint32_t *__restrict__ words, int64_t n_words, int8_t *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_words) return;
+  const uint32_t w = words[i];
+  constexpr int P = 32 / BITS;
+  int8_t q[P];
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t pr = int4_pair(w, p);  // bf16 (128 + u) for fields p and p + 4
+      q[p] = (int8_t)((int)bf16lo(pr) - 136);
+      q[p + 4] = (int8_t)((int)bf16hi(pr) - 136);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t pr = int2_pair(w, p);  // fields p and p + 8
+      q[p] = (int8_t)((int)bf16lo(pr) - 128);
+      q[p + 8] = (int8_t)((int)bf16hi(pr) - 128);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) out[i * P + p] = q[p];
+}
+
+template <int BITS>
+__global__ void dequant_kernel(const uint32_t *__restrict__ words, const uint16_t *__restrict__ scales,
+                               const uint8_t *__restrict__ zeros, int N, int K, uint16_t *__restrict__ out) {
+  constexpr int P = 32 / BITS;
+  const int wpr = K / P;  // words per row
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)N * wpr) return;
+  const int n = (int)(i / wpr);
+  const int kw = (int)(i % wpr);
+  const int g = kw * P / kGroup;
+  const float s = bf16_to_f32(scales[(size_t)n * (K / kGroup) + g]);
+  const float z = (BITS == 4) ? 8.f : (float)zeros[(size_t)n * (K / kGroup) + g];
+  const uint32_t w = words[i];
+  uint32_t o[P / 2];
+  if constexpr (BITS == 4)
+    dequant8_int4(w, s, -z * s, o);
+  else
+    dequant16_int2(w, s, -z * s, o);
+  uint32_t *dst = (uint32_t *)(out + (size_t)n * K + (size_t)kw * P);
+#pragma unroll
+  for (int p = 0; p < P / 2; ++p) dst[p] = o[p];
+}
+
+}  // namespace
+
+hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_t *out, hipStream_t st) {
+  const int threads = 256;
+  const int64_t blocks = (n_words + threads - 1) / threads;
+  if (bits == 4)
+    unpack_kernel<4><<<(unsigned)blocks, threads, 0, st>>>(words, n_words, out);
+  else
+    unpack_kernel<2><<<(unsigned)blocks, threads, 0, st>>>(words, n_words, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
+                               int N, int K, uint16_t *out, hipStream_t st) {
+  const int threads = 256;
+  const int64_t n_words = (int64_t)N * K * bits / 32;
+  const int64_t blocks = (n_words + threads - 1) / threads;
+  if (bits == 4)
+    dequant_kernel<4><<<(unsigned)blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
+  else
+    dequant_kernel<2><<<(unsigned)blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
+  return hipGetLastError();
+}
+
+}  // namespace bqmoe

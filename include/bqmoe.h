@@ -1,0 +1,198 @@
+/*
+ * bqmoe.h -- C ABI of the routed-expert mixture-of-experts layer with low-bit
+ * (weight-only INT4 / 2-bit) experts, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, per batch of T tokens with hidden size H, E experts, top-k routing
+ * and expert intermediate size I:
+ *
+ *   moe_route       router logits, top-k experts and their softmax gates
+ *   moe_permute     stable grouping of the T*k (token, slot) rows by expert
+ *   moe_expert_ffn_w4a16 / _w2a16
+ *                   per-expert gate_up -> SwiGLU -> down with the expert weights
+ *                   dequantised on the fly from packed codes
+ *   moe_combine     gate-weighted sum of each token's k expert outputs
+ *
+ * Weight formats.  INT4 symmetric with one bf16 scale per 128 consecutive K
+ * (weight-only, activations stay 16-bit): page "Qwen3.8-Flash-Next on 2x RTX
+ * 3090", storage-format table; page "Qwen3.8-Flash-Next on dual RTX 3090: W4A16
+ * + FP8 PLE + MTP3", "Composition".  2-bit with group 128 and 16 codes per
+ * 32-bit word along K: page "Qwen3.8-Flash-Next on one 24 GB GPU", "What the
+ * patch does" and "Hardware and software requirements".  Field i of word kw
+ * (bits [b*i, b*i+b), least significant first) holds the code of K index
+ * P*kw + i, P = 32/b.  INT4 fields hold q + 8 with q in [-8, 7] and the weight
+ * is q*s; 2-bit fields hold u in {0..3} and the weight is (u - z)*s with an
+ * integer zero-point z per group.
+ *
+ * Conventions shared by every entry point:
+ *  - Every array argument is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or retains memory and never synchronises.
+ *  - Arrays are row-major and contiguous.  bf16 values are passed as uint16_t
+ *    holding the bfloat16 bit pattern.
+ *  - Each call checks its arguments on the host first; on any error it returns
+ *    a status != MOE_OK, enqueues nothing and moe_last_error() describes the
+ *    problem.  Otherwise it enqueues its kernels on `stream` (a hipStream_t
+ *    passed as void*; NULL = the default stream) and returns MOE_OK without
+ *    waiting.  A failed kernel launch returns MOE_ERR_HIP.
+ *  - T = 0 is a valid empty batch: the call checks its arguments and enqueues
+ *    nothing.
+ *  - Results are bitwise deterministic for given inputs on a given device.
+ *  - Workspaces: device memory of at least the size returned by the matching
+ *    *_workspace_size() function, 256-byte aligned.  Each workspace begins
+ *    with a control block that must be all-zero before the first call that
+ *    uses the buffer (allocate it zeroed); every call leaves it zeroed again.
+ *    Two calls that overlap in time must not share a workspace.
+ *  - Entry points are thread-safe; the only library state is a per-device
+ *    cache of device properties and a thread-local error string.
+ */
+#ifndef BQMOE_H
+#define BQMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,         /* null pointer, negative size, k outside [1, min(E, 32)] ... */
+    MOE_ERR_UNSUPPORTED_SHAPE = 2,   /* H or I not a multiple of 128, E > 1024, ... */
+    MOE_ERR_MISALIGNED = 3,          /* a pointer lacks the alignment its loads need */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 4,
+    MOE_ERR_HIP = 5                  /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+/* Library ABI version (MOE_ABI_VERSION at build time). */
+int moe_abi_version(void);
+
+/* Static text for a status code. */
+const char *moe_status_string(int status);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char *moe_last_error(void);
+
+/* ---------------------------------------------------------------- routing
+ * moe_route: logits l[t,e] = sum_h x[t,h] * w_router[e,h] (+ logit_bias[e]),
+ * then the k largest logits of each token, listed in order (logit descending,
+ * expert index ascending on ties), and their softmax gates.  The pages keep
+ * the router in 16-bit precision because a small logit perturbation changes
+ * routing on near-ties (page "Qwen3.8-Flash-Next FP6-INT8", "Precision map");
+ * to make the selection reproducible the float32 additions follow one fixed
+ * order: h is split into 64 contiguous slices of H/64 elements, each slice is
+ * summed in ascending h starting from 0, the 64 slice sums are added as a
+ * balanced pairwise tree in index order, then the bias is added.
+ *
+ *   x           [T, H] bf16, 16-byte aligned
+ *   w_router    [E, H] bf16, 16-byte aligned
+ *   logit_bias  [E] float32, or NULL for none (e.g. a log-prior over experts)
+ *   topk_ids    [T, k] int32 out
+ *   topk_weights[T, k] float32 out: exp(l_j - l_max) / sum over the k selected
+ *   logits      [T, E] float32 out, or NULL (exported for inspection)
+ * Requirements: H % 128 == 0, 1 <= E <= 1024, 1 <= k <= min(E, 32).
+ * Non-finite logits give unspecified (but in-bounds) ids.
+ */
+size_t moe_route_workspace_size(int T, int E);
+moe_status moe_route(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
+                     int T, int H, int E, int k,
+                     int32_t *topk_ids, float *topk_weights, float *logits,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------- permutation
+ * moe_permute: groups the n = T*k rows r = t*k + j (token t, slot j) by expert
+ * topk_ids[r], keeping r ascending inside each expert (a stable counting sort).
+ *
+ *   topk_ids       [T, k] int32 in
+ *   expert_offsets [E+1] int32 out: rows of expert e are sorted positions
+ *                  [expert_offsets[e], expert_offsets[e+1])
+ *   sorted_rows    [n] int32 out: the row r at each sorted position
+ *   row_pos        [n] int32 out: the sorted position of row r (inverse of
+ *                  sorted_rows); -1 for a row whose id is outside [0, E)
+ *   active         [1 + min(E, n)] int32 out: active[0] = A, the number of
+ *                  experts with at least one row, then their ids ascending,
+ *                  then -1 padding
+ * Rows whose id lies outside [0, E) are dropped (they get no sorted position).
+ */
+size_t moe_permute_workspace_size(int T, int k, int E);
+moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E,
+                       int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
+                       int32_t *active, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------- expert FFN
+ * moe_expert_ffn_w4a16: for every active expert e and each of its rows
+ * (sorted positions p in [expert_offsets[e], expert_offsets[e+1]), token
+ * t = sorted_rows[p] / k):
+ *     a = W13_e x_t                     gate_up, 2I outputs; rows [0, I) of
+ *                                       W13 are gate, rows [I, 2I) are up
+ *     h = silu(a[0:I]) * a[I:2I]        silu(v) = v / (1 + exp(-v))
+ *     y_perm[p] = W2_e h                down, H outputs, stored as bf16
+ * with W = q * s dequantised from INT4 symmetric group-128 codes.  The dot
+ * products accumulate in float32; h is rounded to bf16 before the down
+ * projection.  T <= 16 uses the decode path (one fused GEMV kernel streaming
+ * each selected expert's packed weights once); larger T uses grouped
+ * bf16-MFMA GEMMs.  The permutation arrays must come from moe_permute with
+ * the same T, k, E.
+ *
+ *   x           [T, H] bf16, 16-byte aligned
+ *   w13_codes   [E, 2I, H/8]  uint32, 16-byte aligned
+ *   w13_scales  [E, 2I, H/128] bf16
+ *   w2_codes    [E, H, I/8]   uint32, 16-byte aligned
+ *   w2_scales   [E, H, I/128] bf16
+ *   y_perm      [T*k, H] bf16 out, in sorted order (rows of dropped ids untouched)
+ * Requirements: H % 128 == 0, I % 128 == 0, 1 <= E <= 1024, 1 <= k <= 32.
+ */
+size_t moe_expert_ffn_workspace_size(int T, int k, int E, int H, int I);
+moe_status moe_expert_ffn_w4a16(const uint16_t *x, const int32_t *expert_offsets,
+                                const int32_t *sorted_rows, const int32_t *active,
+                                int T, int k, int E, int H, int I,
+                                const uint32_t *w13_codes, const uint16_t *w13_scales,
+                                const uint32_t *w2_codes, const uint16_t *w2_scales,
+                                uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* moe_expert_ffn_w2a16: as moe_expert_ffn_w4a16 with 2-bit codes (16 per
+ * uint32 along K: w13_codes [E, 2I, H/16], w2_codes [E, H, I/16]) and
+ * W = (u - z) * s, z an integer zero-point per (row, group):
+ *   w13_zeros [E, 2I, H/128] uint8, w2_zeros [E, H, I/128] uint8. */
+moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets,
+                                const int32_t *sorted_rows, const int32_t *active,
+                                int T, int k, int E, int H, int I,
+                                const uint32_t *w13_codes, const uint16_t *w13_scales,
+                                const uint8_t *w13_zeros,
+                                const uint32_t *w2_codes, const uint16_t *w2_scales,
+                                const uint8_t *w2_zeros,
+                                uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* ---------------------------------------------------------------- combine
+ * moe_combine: y[t] = sum over j = 0..k-1 (ascending) of
+ *   topk_weights[t, j] * y_perm[row_pos[t*k + j]]   in float32, stored as bf16.
+ * Rows with row_pos < 0 contribute nothing.
+ *   y_perm [T*k, H] bf16, row_pos [T*k] int32, topk_weights [T, k] float32,
+ *   y [T, H] bf16 out.  y_perm and y 16-byte aligned, H % 8 == 0.
+ */
+moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const float *topk_weights,
+                       int T, int k, int H, uint16_t *y, void *stream);
+
+/* ---------------------------------------------------------------- diagnostics
+ * moe_unpack_codes: the signed codes of n_words packed words, unpacked by the
+ * same device routine the decode kernels use (INT4: q = field - 8; 2-bit:
+ * u = field).  out holds n_words * 32/bits int8 values in K order.
+ */
+moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, int8_t *out,
+                            void *stream);
+
+/* moe_dequant_bf16: one [N, K] matrix dequantised to bf16 by the same device
+ * routine the grouped-GEMM kernels use: round-to-nearest-even of (q - z) * s.
+ *   words [N, K*bits/32] uint32 (16-byte aligned), scales [N, K/128] bf16,
+ *   zeros [N, K/128] uint8 (bits == 2 only, else NULL), out [N, K] bf16.
+ * Requirements: K % 128 == 0. */
+moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros,
+                            int bits, int N, int K, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BQMOE_H */

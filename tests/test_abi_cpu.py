@@ -1,0 +1,117 @@
+"""The C ABI on the host: the library loads, exports what include/bqmoe.h declares,
+and rejects bad arguments before touching the GPU (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_moe_amd as bq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "bqmoe.h")
+
+OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP = range(6)
+A = 1 << 20          # a fake, well-aligned device address: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = bq.lib()
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(bq._SIGS)
+
+
+def test_abi_version_and_status_strings():
+    L = bq.lib()
+    assert L.moe_abi_version() == 1
+    for s in range(6):
+        assert L.moe_status_string(s)
+    assert L.moe_status_string(99) == b"unknown status"
+
+
+def _route(T=4, H=256, E=8, k=2, x=A, w=A, ids=A, g=A, ws=A, wsb=1 << 20, bias=None, logits=None):
+    return bq.lib().moe_route(x, w, bias, T, H, E, k, ids, g, logits, ws, wsb, None)
+
+
+def test_route_argument_errors():
+    L = bq.lib()
+    assert _route(T=-1) == INVALID
+    assert _route(k=0) == INVALID
+    assert _route(k=9) == INVALID                 # k > E
+    assert _route(E=8, k=33) == INVALID
+    assert _route(E=2000) == SHAPE
+    assert _route(H=200) == SHAPE                 # not a multiple of 128
+    assert _route(x=None) == INVALID
+    assert b"required" in L.moe_last_error()
+    assert _route(x=A + 4) == MISALIGNED
+    assert _route(ws=A + 128) == MISALIGNED
+    assert _route(wsb=16) == WS_SMALL
+    assert b"workspace" in L.moe_last_error()
+    assert _route(T=0) == OK                      # empty batch: checked, nothing enqueued
+
+
+def test_route_workspace_size():
+    L = bq.lib()
+    assert L.moe_route_workspace_size(1, 256) >= 4096 + 256 * 4
+    assert L.moe_route_workspace_size(1, 256) % 256 == 0
+    assert L.moe_route_workspace_size(-1, 8) == 0
+
+
+def test_permute_argument_errors():
+    L = bq.lib()
+    f = lambda T=4, k=2, E=8, ids=A, off=A, sr=A, rp=A, act=A: L.moe_permute(ids, T, k, E, off, sr, rp, act, None, 0, None)
+    assert f(T=-2) == INVALID
+    assert f(k=0) == INVALID
+    assert f(E=0) == SHAPE
+    assert f(ids=None) == INVALID
+    assert f(off=A + 2) == MISALIGNED
+    assert f(T=0) == OK
+
+
+def _ffn(bits=4, T=2, k=2, E=8, H=256, I=128, x=A, codes=A, ws=A, wsb=1 << 24, zeros=A):
+    L = bq.lib()
+    if bits == 4:
+        return L.moe_expert_ffn_w4a16(x, A, A, A, T, k, E, H, I, codes, A, codes, A, A, ws, wsb, None)
+    return L.moe_expert_ffn_w2a16(x, A, A, A, T, k, E, H, I, codes, A, zeros, codes, A, zeros, A, ws, wsb, None)
+
+
+def test_ffn_argument_errors():
+    L = bq.lib()
+    assert _ffn(I=100) == SHAPE
+    assert _ffn(H=64) == SHAPE
+    assert _ffn(k=3, E=2) == INVALID
+    assert _ffn(x=None) == INVALID
+    assert _ffn(bits=2, zeros=None) == INVALID
+    assert _ffn(codes=A + 8) == MISALIGNED
+    assert _ffn(wsb=100) == WS_SMALL
+    assert _ffn(T=0) == OK
+    need = L.moe_expert_ffn_workspace_size(16, 8, 256, 4096, 1024)
+    assert need >= 4096 + 16 * 8 * 1024 * 2 and need % 256 == 0
+
+
+def test_combine_unpack_dequant_argument_errors():
+    L = bq.lib()
+    assert L.moe_combine(A, A, A, 4, 2, 100, A, None) == SHAPE       # H % 8
+    assert L.moe_combine(None, A, A, 4, 2, 128, A, None) == INVALID
+    assert L.moe_combine(A + 8, A, A, 4, 2, 128, A, None) == MISALIGNED
+    assert L.moe_combine(A, A, A, 0, 2, 128, A, None) == OK
+    assert L.moe_unpack_codes(A, 3, 10, A, None) == SHAPE
+    assert L.moe_unpack_codes(A, 4, -1, A, None) == INVALID
+    assert L.moe_unpack_codes(A, 4, 0, A, None) == OK
+    assert L.moe_dequant_bf16(A, A, None, 2, 4, 128, A, None) == INVALID  # 2-bit needs zeros
+    assert L.moe_dequant_bf16(A, A, None, 4, 4, 100, A, None) == SHAPE
+    assert L.moe_dequant_bf16(A, A, None, 4, 0, 128, A, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(bq.MoEError):
+        bq.route(torch.zeros((1, 256), dtype=torch.bfloat16), torch.zeros((8, 256), dtype=torch.bfloat16), 2)
