@@ -51,24 +51,44 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------- decode-path unpack
-// Offset form used by the GEMV kernels: OR-ing a code field u (< 128) into the
-// mantissa of bf16 128.0 (0x4300) gives exactly 128 + u.  For a 4-bit word the
-// pair i (i = 0..3) holds fields (i, i+4); for a 2-bit word pair i (0..7) holds
-// fields (i, i+8).  The dot product with activations arranged in the same
-// pairs, minus (128 + zero) * sum(x), gives the dot with (u - zero).
-// (a & mask) | magic in one v_and_or_b32 (gfx9 VOP3 takes no literal and one
-// SGPR, so the mask lives in a VGPR and the magic in an SGPR).
-__device__ __forceinline__ uint32_t and_or_b32(uint32_t a, uint32_t mask_v, uint32_t magic_s) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask_v), "s"(magic_s));
-  return r;
+// Offset form used by the GEMV kernels: a code field u (< 128) in the low byte
+// of a bf16 whose high byte is 0x43 is exactly the value 128 + u.  The fields
+// are isolated into bytes with one mask per shift, and v_perm_b32 pairs two
+// of those bytes with the 0x43 bytes of `magic` (0x43434343, passed in a
+// register).  The pairs come out in a fixed field order:
+//   INT4 word          -> fields 0 2 4 6 1 3 5 7
+//   INT2 word, half 0  -> fields 0 4 8 12 1 5 9 13
+//   INT2 word, half 1  -> fields 2 6 10 14 3 7 11 15
+// The activations are arranged in the same order, so that the dot product of
+// a pair sequence with them, minus (128 + zero) * sum(x), is sum((u - zero) x).
+constexpr int kOrder4[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+constexpr int kOrder2[16] = {0, 4, 8, 12, 1, 5, 9, 13, 2, 6, 10, 14, 3, 7, 11, 15};
+constexpr uint32_t kMagic43 = 0x43434343u;
+constexpr uint32_t kPermB01 = 0x04010400u;  // (byte 0, 0x43, byte 1, 0x43)
+constexpr uint32_t kPermB23 = 0x04030402u;  // (byte 2, 0x43, byte 3, 0x43)
+
+__device__ __forceinline__ u32x4 unpack4_pairs(uint32_t w, uint32_t magic) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  return u32x4{__builtin_amdgcn_perm(magic, lo, kPermB01), __builtin_amdgcn_perm(magic, lo, kPermB23),
+               __builtin_amdgcn_perm(magic, hi, kPermB01), __builtin_amdgcn_perm(magic, hi, kPermB23)};
+}
+__device__ __forceinline__ u32x4 unpack2_pairs(uint32_t w, int half, uint32_t magic) {
+  const uint32_t a = (w >> (4 * half)) & 0x03030303u, b = (w >> (4 * half + 2)) & 0x03030303u;
+  return u32x4{__builtin_amdgcn_perm(magic, a, kPermB01), __builtin_amdgcn_perm(magic, a, kPermB23),
+               __builtin_amdgcn_perm(magic, b, kPermB01), __builtin_amdgcn_perm(magic, b, kPermB23)};
 }
 
-__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int i) {
-  return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-}
-__device__ __forceinline__ uint32_t int2_pair(uint32_t w, int i) {
-  return ((w >> (2 * i)) & 0x00030003u) | 0x43004300u;
+// Natural-order bf16 activations d (pairs (x0,x1), (x2,x3), ...) -> the pair
+// order of the unpacked codes: o[i] = (x[ord[2i]], x[ord[2i+1]]).  N elements.
+template <int N>
+__device__ __forceinline__ void order_pairs(const uint32_t *d, uint32_t *o) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const int a = (N == 8) ? kOrder4[2 * i] : kOrder2[2 * i];
+    const int b = (N == 8) ? kOrder4[2 * i + 1] : kOrder2[2 * i + 1];
+    // a and b have the same parity in both orders
+    o[i] = __builtin_amdgcn_perm(d[b / 2], d[a / 2], (a & 1) ? 0x07060302u : 0x05040100u);
+  }
 }
 
 // ---------------------------------------------------------------- GEMM-path dequant
@@ -155,6 +175,15 @@ __device__ __forceinline__ bool wait_counter_geq(int *ctr, int target, int max_s
     if (++spins > max_spins) return false;
   }
   return true;
+}
+
+// Block barrier that orders LDS accesses only.  Unlike __syncthreads() it does
+// not first wait for this wave's outstanding global loads, so weights already
+// in flight stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Wait until this wave's outstanding vector-memory operations (including

@@ -7,39 +7,48 @@
 // page "Qwen3.8-Flash-Next FP6-INT8", "Step budget and hardware floors": the
 // expert GEMV is about 6 ms of each added decode stream) and dispatch to a GEMV
 // up to 16 rows (same page, "Quantization quality").  This kernel is a
-// from-scratch gfx950 design on the canonical K-packed layout:
+// from-scratch gfx950 design on the canonical K-packed layout.
 //
-//  * Phase 1 (gate_up + SwiGLU): a wave owns a contiguous run of items; an
-//    item is a (gate row i, up row I+i) pair of one expert.  Each lane reads
-//    whole 16-byte chunks of packed codes (global_load_dwordx4), dots them
-//    against bf16 activation pairs with v_dot2_f32_bf16, and a reduction over
-//    the row's lanes gives the row result; h = silu(gate) * up goes to the
-//    workspace as bf16.  The weights of the next item are in flight while the
-//    current one is computed.
-//  * Phase 2 (down): a wave owns a contiguous run of down rows.  Their weight
-//    chunks are requested as soon as the wave's phase-1 loads are out; before
-//    using h of an expert the wave waits until every phase-1 item of that
-//    expert is published.
+// Work items (a persistent grid walks them in order, phase-1 items first):
+//  * phase 1, (expert, 16 gate/up row pairs): the four waves of a block split
+//    the K groups of the 32 rows; every wave issues all of its weight loads
+//    (one 16-byte slice per lane, row and group) before any math;
+//  * phase 2, (expert, 128 down rows): each wave takes two sets of 16 rows
+//    over the full K.  The weight loads are issued first, then the block
+//    waits until every phase-1 item of the expert is published.
+//
+// The dot products run on the matrix cores: v_mfma_f32_16x16x32_bf16 with the
+// expert's routed activation rows as the 16-row A operand (a row repeated when
+// there are fewer) and the unpacked codes of 16 weight rows as B, so the K
+// reduction happens inside the MFMA accumulation and needs no cross-lane
+// shuffles.  Unpack: a code field u in the low byte under a 0x43 high byte is
+// the bf16 value 128 + u.  Per 128-wide group the accumulator holds
+// sum((128 + u) x), and s * (acc - (128 + zero) * sum(x)) = s * sum((u - zero) x)
+// (zero = 8 for INT4 offset-binary codes).  The activations are staged in LDS
+// in the K order the unpacked pairs come out in, with their per-group sums.
 //
 // Hand-off without cache flushes: h is written with device-coherent stores
-// (sc1), the writer waits for them to complete (vmcnt(0)) and then bumps the
-// expert's counter with a device-scope atomic; a reader polls the counter and
-// reads h with device-coherent loads.  Counters sit on separate 128-byte lines.
-// The grid never exceeds the co-resident block count and every wave finishes
-// its phase-1 items before it waits, so every wait ends; the waits are bounded
-// anyway and a timeout only raises an error flag.
-//
-// Unpack: OR-ing a code field u into the mantissa of bf16 128.0 gives exactly
-// 128 + u.  With activations arranged in the same (field i, field i + P/2)
-// pairs, sum((128 + u) x) - (128 + zero) * sum(x) = sum((u - zero) x), times
-// the group scale (zero = 8 for INT4 offset-binary codes).
+// (sc1); the block waits for them to complete (vmcnt(0)) and then bumps the
+// expert's counter with a device-scope atomic; a phase-2 block polls the
+// counter and reads h with device-coherent loads.  Counters sit on separate
+// 128-byte lines.  The grid never exceeds the co-resident block count and a
+// block finishes all of its phase-1 items before its first phase-2 item, so
+// every wait ends; the waits are bounded anyway and a timeout only raises an
+// error flag.
 #include <mutex>
+#include <type_traits>
 
 #include "common.cuh"
 #include "internal.h"
 
 namespace bqmoe {
 namespace {
+
+constexpr int kRows1 = 16;   // gate/up row pairs per phase-1 item
+constexpr int kRows2 = 128;  // down rows per phase-2 item (two sets of 16 per wave)
+constexpr int kChunkG = 8;   // K groups whose loads a wave keeps in flight together
+constexpr int kRMax = 4;     // routed rows staged per pass when T > 1
+constexpr int kRedFloats = 4 * 2 * 16 * 16;  // phase-1 cross-wave partials
 
 struct DecodeParams {
   const uint16_t *x;
@@ -56,382 +65,439 @@ struct DecodeParams {
   uint16_t *y_perm;
   uint16_t *hbuf;  // [T*k, I] bf16
   int *ctl;
-  int lpr1, rpw1, items1;  // phase 1: lanes per row, rows per wave pass, items per expert
-  int lpr2, rpw2, items2;  // phase 2
   int max_spins;
-  uint32_t magic;          // bf16 pair (128.0, 128.0); an argument so it sits in an SGPR
+  uint32_t magic;  // 0x43434343 (the bf16 high byte of 128); an argument so that it sits in an SGPR
 };
 
 __device__ __forceinline__ int *counter(int *ctl, int a) { return ctl + kCtlCounters + a * kCtrStride; }
 
-// bf16 activations of one 16-byte weight chunk, arranged as the unpack pairs.
-// INT4 chunk = 32 K (4 words); INT2 chunk = 64 K (4 words).
+// ---------------------------------------------------------------- operands
+// One chunk of natural-order bf16 activations (d: pairs (x0,x1), (x2,x3), ...)
+// in the field order of the unpacked codes: INT4 chunks of 8, INT2 chunks of 16.
 template <int BITS>
-struct ActChunk {
-  static constexpr int NP = (BITS == 4) ? 16 : 32;  // packed bf16 pairs
-  uint32_t p[NP];
-  float sum;
+__device__ __forceinline__ void permute_chunk(const uint32_t *d, uint32_t *o) {
+  order_pairs<BITS == 4 ? 8 : 16>(d, o);
+}
+
+// ---------------------------------------------------------------- LDS staging
+// Activation row r (K bf16) goes to LDS act + r * (K*2 + 16) in operand order,
+// in chunks of 8 (INT4) or 16 (INT2) elements; its per-group sums go to
+// Xs[g*16 + m] for the MFMA rows m that read it (row m reads activation row
+// min(m, R-1)).
+template <int BITS>
+constexpr int kChunkE = BITS == 4 ? 8 : 16;
+// Chunks of activation row 0 that every thread loads before its weights:
+// chunks t + 256 i, i < NPRE, of thread t (NPRE = 2 covers K = 4096 for INT4).
+// Vector memory loads retire in issue order, so only loads issued before the
+// weights can be waited for without waiting for the weights too.
+struct PreAct {
+  uint32_t d[8];
+};
+
+template <int BITS, bool COHERENT>
+__device__ __forceinline__ void load_act_chunk(const uint16_t *src, int q, uint32_t *d) {
+  const uint32_t *s32 = (const uint32_t *)(src + q * kChunkE<BITS>);
+  if constexpr (COHERENT) {
+#pragma unroll
+    for (int t = 0; t < kChunkE<BITS> / 2; ++t)
+      d[t] = __hip_atomic_load(s32 + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kChunkE<BITS> / 2; t += 4) {
+      const u32x4 v = *(const u32x4 *)(s32 + t);
+      d[t] = v[0];
+      d[t + 1] = v[1];
+      d[t + 2] = v[2];
+      d[t + 3] = v[3];
+    }
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_act_chunk(uint8_t *row, int q, const uint32_t *d) {
+  uint32_t o[kChunkE<BITS> / 2];
+  permute_chunk<BITS>(d, o);
+  uint32_t *dst = (uint32_t *)(row + q * kChunkE<BITS> * 2);
+#pragma unroll
+  for (int t = 0; t < kChunkE<BITS> / 2; t += 4) *(u32x4 *)(dst + t) = u32x4{o[t], o[t + 1], o[t + 2], o[t + 3]};
+}
+
+template <int BITS, int NPRE>
+__device__ __forceinline__ void pre_load(const uint16_t *src0, int K, PreAct &pa) {
+  const int nch = K / kChunkE<BITS>;
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    if (q < nch) load_act_chunk<BITS, false>(src0, q, pa.d + 4 * i);
+  }
+}
+
+// Stages rows 0..R-1 (src(r): row r's global address); chunks q < q0 of row 0
+// come from pa (q0 = 256 * NPRE or 0).  Ends with a block barrier.
+template <int BITS, bool COHERENT, int NPRE, typename Src>
+__device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int R, int K, int q0,
+                                           const PreAct *pa) {
+  const int pitch = K * 2 + 16;
+  const int nch = K / kChunkE<BITS>;
+  if (q0 > 0) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      const int q = threadIdx.x + 256 * i;
+      if (q < nch) store_act_chunk<BITS>(act, q, pa->d + 4 * i);
+    }
+  }
+  for (int r = 0; r < R; ++r) {
+    const uint16_t *s = src(r);
+    for (int q = (r == 0 ? q0 : 0) + threadIdx.x; q < nch; q += 256) {
+      uint32_t d[kChunkE<BITS> / 2];
+      load_act_chunk<BITS, COHERENT>(s, q, d);
+      store_act_chunk<BITS>(act + r * pitch, q, d);
+    }
+  }
+  lds_barrier();
+  // group sums: 8 threads per group, 16 elements each
+  const int G = K / kGroup;
+  for (int r = 0; r < R; ++r) {
+    for (int t = threadIdx.x; t < G * 8; t += 256) {
+      const int g = t / 8, part = t % 8;
+      const u32x4 *p = (const u32x4 *)(act + r * pitch + (g * kGroup + part * 16) * 2);
+      const u32x4 v0 = p[0], v1 = p[1];
+      float sum = 0.f;
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        sum = dot2_bf16(v0[z], 0x3F803F80u, sum);
+        sum = dot2_bf16(v1[z], 0x3F803F80u, sum);
+      }
+      sum = group_sum(sum, 8);
+      if (part == 0) {
+        if (r == R - 1) {
+          for (int m = r; m < 16; ++m) Xs[g * 16 + m] = sum;
+        } else {
+          Xs[g * 16 + r] = sum;
+        }
+      }
+    }
+  }
+  lds_barrier();
+}
+
+// ---------------------------------------------------------------- weights
+// A lane reads 32 consecutive K of one weight row per group: a 16-byte (INT4)
+// or 8-byte (INT2) slice at byte lsub * kGroupBytes / 4 of the group.
+template <int BITS>
+using Word = typename std::conditional<BITS == 4, u32x4, u32x2>::type;
+template <int BITS>
+constexpr int kGroupBytes = kGroup * BITS / 8;
+
+// kChunkG consecutive groups of one row (the lane's slices), their bf16 scales
+// (16 bytes) and, for INT2, their zero-points (8 bytes).
+template <int BITS>
+struct Chunk {
+  Word<BITS> w[kChunkG];
+  u32x4 s;
+  u32x2 z;
+};
+
+// Offsets (bytes) of a lane's first group in the expert's code, scale and
+// zero-point arrays.
+struct Off {
+  uint32_t c, s, z;
+};
+__device__ __forceinline__ Off row_off(int row, int G, int g0, int gbytes, int lsub) {
+  Off o;
+  o.z = (uint32_t)row * G + g0;
+  o.s = 2 * o.z;
+  o.c = o.z * gbytes + lsub * (gbytes / 4);
+  return o;
+}
+__device__ __forceinline__ Off add_groups(Off o, int dg, int gbytes) {
+  return Off{o.c + dg * gbytes, o.s + 2 * dg, o.z + dg};
+}
+
+// Expert-local arrays (wave-uniform bases).
+struct ExpertW {
+  const uint8_t *codes, *scales, *zeros;
 };
 
 template <int BITS>
-__device__ __forceinline__ void arrange_act(const uint32_t *d, ActChunk<BITS> &a) {
-  constexpr int ND = ActChunk<BITS>::NP;
-  if constexpr (BITS == 4) {
-    // word j covers 8 K: dwords (x0,x1)(x2,x3)(x4,x5)(x6,x7) -> pairs (x_i, x_{i+4})
+__device__ __forceinline__ void load_chunk(const ExpertW &x, Off o, Chunk<BITS> &ch) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a.p[4 * j + 0] = __builtin_amdgcn_perm(d[4 * j + 2], d[4 * j + 0], 0x05040100u);
-      a.p[4 * j + 1] = __builtin_amdgcn_perm(d[4 * j + 2], d[4 * j + 0], 0x07060302u);
-      a.p[4 * j + 2] = __builtin_amdgcn_perm(d[4 * j + 3], d[4 * j + 1], 0x05040100u);
-      a.p[4 * j + 3] = __builtin_amdgcn_perm(d[4 * j + 3], d[4 * j + 1], 0x07060302u);
-    }
-  } else {
-    // word j covers 16 K: dwords d[8j..8j+7] -> pairs (x_i, x_{i+8})
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = d[8 * j + i / 2], hi = d[8 * j + 4 + i / 2];
-        a.p[8 * j + i] = (i & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                                 : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-      }
-  }
-  float s = 0.f;
-#pragma unroll
-  for (int q = 0; q < ND; ++q) s = dot2_bf16(d[q], 0x3F803F80u, s);  // sum of the chunk's activations
-  a.sum = s;
+  for (int c = 0; c < kChunkG; ++c) ch.w[c] = *(const Word<BITS> *)(x.codes + o.c + c * kGroupBytes<BITS>);
+  ch.s = *(const u32x4 *)(x.scales + o.s);
+  if constexpr (BITS == 2) ch.z = *(const u32x2 *)(x.zeros + o.z);
 }
 
-// activations from ordinary memory (x)
+// B operand j (32 K of the lane's slice) of one group.
 template <int BITS>
-__device__ __forceinline__ void load_act(const uint16_t *src, ActChunk<BITS> &a) {
-  constexpr int ND = ActChunk<BITS>::NP;
-  uint32_t d[ND];
-#pragma unroll
-  for (int q = 0; q < ND / 4; ++q) {
-    const u32x4 v = *(const u32x4 *)(src + 8 * q);
-    d[4 * q + 0] = v[0];
-    d[4 * q + 1] = v[1];
-    d[4 * q + 2] = v[2];
-    d[4 * q + 3] = v[3];
-  }
-  arrange_act<BITS>(d, a);
+__device__ __forceinline__ bf16x8 b_op(Word<BITS> w, int j, uint32_t magic) {
+  if constexpr (BITS == 4)
+    return __builtin_bit_cast(bf16x8, unpack4_pairs(w[j], magic));
+  else
+    return __builtin_bit_cast(bf16x8, unpack2_pairs(w[j / 2], j & 1, magic));
 }
 
-// activations written by other blocks during this kernel (h): device-coherent loads
-template <int BITS>
-__device__ __forceinline__ void load_act_coherent(const uint16_t *src, ActChunk<BITS> &a) {
-  constexpr int ND = ActChunk<BITS>::NP;
-  uint32_t d[ND];
-  const uint32_t *s32 = (const uint32_t *)src;
+// C (16 activation rows x 16 weight rows) over one 128-wide group, for NR row
+// sets sharing the activations.  ap: the lane's activation bytes of the group
+// (row, K offset 32 * lsub).
+template <int BITS, int NR>
+__device__ __forceinline__ void group_mfma(const Word<BITS> *w, const uint8_t *ap, uint32_t magic,
+                                           f32x4 *cg) {
 #pragma unroll
-  for (int q = 0; q < ND; ++q) d[q] = __hip_atomic_load(s32 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  arrange_act<BITS>(d, a);
-}
-
-// sum over one chunk of (128 + u) * act
-template <int BITS>
-__device__ __forceinline__ float chunk_dot(const u32x4 &w, const ActChunk<BITS> &a, uint32_t mask, uint32_t magic) {
-  float acc = 0.f;
+  for (int r = 0; r < NR; ++r) cg[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t v = w[j];
-    if constexpr (BITS == 4) {
-      const uint32_t v4 = v >> 4;
-      acc = dot2_bf16(and_or_b32(v, mask, magic), a.p[4 * j + 0], acc);
-      acc = dot2_bf16(and_or_b32(v4, mask, magic), a.p[4 * j + 1], acc);
-      acc = dot2_bf16(and_or_b32(v >> 8, mask, magic), a.p[4 * j + 2], acc);
-      acc = dot2_bf16(and_or_b32(v4 >> 8, mask, magic), a.p[4 * j + 3], acc);
-    } else {
+    const bf16x8 a = *(const bf16x8 *)(ap + j * 16);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = dot2_bf16(and_or_b32(v >> (2 * i), mask, magic), a.p[8 * j + i], acc);
+    for (int r = 0; r < NR; ++r)
+      cg[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b_op<BITS>(w[r], j, magic), cg[r], 0, 0, 0);
+  }
+}
+
+// acc += s * (C - (128 + zero) * sum(x)), xs: the group sums of the lane's C rows.
+template <bool ONE>
+__device__ __forceinline__ void group_acc(f32x4 cg, float s, float zo, const float *xs, f32x4 &acc) {
+  if constexpr (ONE) {
+    acc[0] = __builtin_fmaf(s, __builtin_fmaf(-zo, xs[0], cg[0]), acc[0]);
+  } else {
+    const f32x4 v = *(const f32x4 *)xs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(s, __builtin_fmaf(-zo, v[i], cg[i]), acc[i]);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ float zero_off(uint32_t z) {
+  if constexpr (BITS == 4)
+    return 136.f;  // offset-binary code q + 8, plus the 128 of the unpack
+  else
+    return 128.f + (float)z;
+}
+
+// A full chunk (groups G0 .. G0+kChunkG-1) of NR row sets.  ap: activation
+// bytes of group G0 for the lane; xs: Xs + G0 * 16 (+ 4 * lsub unless ONE).
+template <int BITS, bool ONE, int NR>
+__device__ __forceinline__ void chunk_gemv(const Chunk<BITS> *ch, const uint8_t *ap, const float *xs, uint32_t magic,
+                                           f32x4 *acc) {
+#pragma unroll
+  for (int c = 0; c < kChunkG; ++c) {
+    Word<BITS> w[NR];
+    f32x4 cg[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[r] = ch[r].w[c];
+    group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float s = bf16_to_f32((ch[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
+      const float zo = zero_off<BITS>((ch[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
+      group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
     }
   }
-  return acc;
+}
+
+// One group at a time (shapes whose groups do not split into full chunks),
+// NR row sets at offsets o[r].
+template <int BITS, bool ONE, int NR>
+__device__ __forceinline__ void groups_gemv_slow(const ExpertW &x, const Off *o, int ng, const uint8_t *ap,
+                                                 const float *xs, uint32_t magic, f32x4 *acc) {
+  for (int c = 0; c < ng; ++c) {
+    Word<BITS> w[NR];
+    f32x4 cg[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[r] = *(const Word<BITS> *)(x.codes + o[r].c + c * kGroupBytes<BITS>);
+    group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float s = bf16_to_f32(*(const uint16_t *)(x.scales + o[r].s + 2 * c));
+      const float zo = zero_off<BITS>(BITS == 2 ? x.zeros[o[r].z + c] : 0u);
+      group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
+    }
+  }
+}
+
+// Per-expert metadata of active slot a (wave-uniform; through the scalar cache).
+struct Meta {
+  int e, o0, o1;
+};
+__device__ __forceinline__ Meta meta(const DecodeParams &p, int a, int nrows) {
+  Meta r;
+  r.e = min(max(sload(p.active + 1 + a), 0), p.E - 1);
+  r.o0 = min(max(sload(p.offsets + r.e), 0), nrows);
+  r.o1 = min(max(sload(p.offsets + r.e + 1), r.o0), nrows);
+  return r;
 }
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v)); }
 
-// One row's packed chunks for one lane, with scale and (2-bit) zero-point.
-template <int BITS, int MC>
-struct RowChunks {
-  u32x4 w[MC];
-  float s[MC];
-  float z[BITS == 2 ? MC : 1];  // 128 + zero-point (2-bit only; INT4 uses 136)
-};
-
-// lane-relative pointers of one weight row: codes at chunk lr (+c*lpr), scales at its groups
-template <int BITS, int MC>
-__device__ __forceinline__ void load_row(const uint32_t *codes_row, const uint16_t *scales_row,
-                                         const uint8_t *zeros_row, int lr, int lpr, RowChunks<BITS, MC> &rc) {
-  constexpr int KPC = 128 / BITS;  // K values per 16-byte chunk
-#pragma unroll
-  for (int c = 0; c < MC; ++c) {
-    const int ch = lr + c * lpr;
-    rc.w[c] = *(const u32x4 *)(codes_row + ch * 4);
-    const int g = ch * KPC / kGroup;
-    rc.s[c] = bf16_to_f32(scales_row[g]);
-    if constexpr (BITS == 2) rc.z[c] = 128.f + (float)zeros_row[g];
-  }
-}
-
-template <int BITS, int MC>
-__device__ __forceinline__ float row_partial(const RowChunks<BITS, MC> &rc, const ActChunk<BITS> *act, uint32_t mask,
-                                             uint32_t magic) {
-  float tot = 0.f;
-#pragma unroll
-  for (int c = 0; c < MC; ++c) {
-    const float raw = chunk_dot<BITS>(rc.w[c], act[c], mask, magic);
-    const float z = (BITS == 4) ? 136.f : rc.z[BITS == 2 ? c : 0];
-    tot += rc.s[c] * __builtin_fmaf(-z, act[c].sum, raw);
-  }
-  return tot;
-}
-
-// Per-expert metadata of active slot a, reloaded (through the scalar cache)
-// only when the slot changes.
-struct Meta {
-  int a = -1, e = 0, o0 = 0, o1 = 0;
-  __device__ __forceinline__ void get(const DecodeParams &p, int slot, int nrows) {
-    if (slot == a) return;
-    a = slot;
-    e = min(max(sload(p.active + 1 + slot), 0), p.E - 1);
-    o0 = min(max(sload(p.offsets + e), 0), nrows);
-    o1 = min(max(sload(p.offsets + e + 1), o0), nrows);
-  }
-};
-
-// Position (active slot, item within the expert) of a contiguous item run.
-struct Cursor {
-  int a, ib;
-  __device__ __forceinline__ void advance(int items) {
-    if (++ib == items) {
-      ib = 0;
-      ++a;
-    }
-  }
-};
-
-template <int BITS, int MC>
-struct PairBuf {
-  RowChunks<BITS, MC> g, u;
-};
-
-template <int BITS, int MC1, int MC2, bool ONE>
-struct Depth {
-  static constexpr int NTR = ONE ? 1 : 2;  // routed rows of one expert whose activations stay in registers
-  static constexpr int NB2 = 4;            // phase-2 items per load batch (two batches in flight)
-};
-
-// ONE: T == 1 (each expert has exactly one routed row, token 0)
-template <int BITS, int MC1, int MC2, bool ONE>
-__global__ void __launch_bounds__(256, 2) ffn_decode_kernel(DecodeParams p) {
-  constexpr int KPC = 128 / BITS;
-  constexpr int NTR = Depth<BITS, MC1, MC2, ONE>::NTR;
-  constexpr int NB2 = Depth<BITS, MC1, MC2, ONE>::NB2;
+// ONE: T == 1 (every active expert has exactly one routed row, of token 0).
+// FAST: every wave's phase-1 group range and the phase-2 K split into full
+// chunks of kChunkG groups (H % 4096 == 0 and I % 1024 == 0); the first chunk
+// of weights is then requested before the activations are staged.
+template <int BITS, bool ONE, bool FAST>
+__global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int s_last;
+  constexpr int RM = ONE ? 1 : kRMax;
+  constexpr int GB = kGroupBytes<BITS>;
+  // activation chunks per thread loaded ahead of the phase-1 weights
+  constexpr int NPRE = (BITS == 4 && ONE) ? 2 : 1;
   const uint32_t magic = p.magic;
-  const uint32_t mask = (BITS == 4) ? 0x000F000Fu : 0x00030003u;
   const int lane = lane_id();
-  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int W = gridDim.x * 4;
-  // With one token every active slot holds one of its k distinct experts, so
-  // the partition can use the host-known Amax (= k) without first reading A.
-  const int A = ONE ? p.Amax : min(max(sload(p.active), 0), p.Amax);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int m = lane % 16, lsub = lane / 16;
   const int nrows = p.T * p.k;
+  // With one token every active slot holds one of its k distinct experts, so
+  // the item partition uses Amax (= k) without first reading the count.
+  const int A = ONE ? p.Amax : min(max(sload(p.active), 0), p.Amax);
+  const int per1 = p.I / kRows1, per2 = p.H / kRows2;
+  const int n1 = A * per1, n2 = A * per2;
+  const int G1 = p.H / kGroup, G2 = p.I / kGroup;
+  const int Gw1 = (G1 + 3) / 4;  // phase-1 groups per wave
 
-  const int rs1 = lane / p.lpr1, lr1 = lane % p.lpr1;
-  const int rs2 = lane / p.lpr2, lr2 = lane % p.lpr2;
-  const int wpr1 = p.H * BITS / 32, gpr1 = p.H / kGroup;
-  const int wpr2 = p.I * BITS / 32, gpr2 = p.I / kGroup;
-  const int total1 = A * p.items1, total2 = A * p.items2;
-  const int per1 = (total1 + W - 1) / W, per2 = (total2 + W - 1) / W;
-  const int it1_0 = min(total1, gw * per1), it1_1 = min(total1, it1_0 + per1);
-  const int it2_0 = min(total2, gw * per2), it2_1 = min(total2, it2_0 + per2);
+  const int pitch1 = p.H * 2 + 16, pitch2 = p.I * 2 + 16;
+  const int pmax = pitch1 > pitch2 ? pitch1 : pitch2;
+  uint8_t *act = lds;
+  float *Xs = (float *)(lds + RM * pmax);
+  float *red = Xs + 16 * (G1 > G2 ? G1 : G2);
 
-  // ---------------------------------------------------------------- phase-2 loads
-  RowChunks<BITS, MC2> dwA[NB2], dwB[NB2];
-  Cursor c2l{it2_0 / max(p.items2, 1), it2_0 % max(p.items2, 1)};
-  Meta m2l;
-  int it2_loaded = it2_0;
-  auto load2 = [&](RowChunks<BITS, MC2>(&dw)[NB2]) {
-#pragma unroll
-    for (int j = 0; j < NB2; ++j) {
-      if (it2_loaded < it2_1) {
-        m2l.get(p, c2l.a, nrows);
-        const size_t row = (size_t)m2l.e * p.H + c2l.ib * p.rpw2 + rs2;
-        load_row<BITS, MC2>(p.w2c + row * wpr2, p.w2s + row * gpr2, BITS == 2 ? p.w2z + row * gpr2 : nullptr,
-                            lr2, p.lpr2, dw[j]);
-        c2l.advance(p.items2);
-        ++it2_loaded;
-      }
-    }
-  };
-
-  // ---------------------------------------------------------------- phase 1
-  // activations of the routed rows of the current expert (one token: loaded first)
-  ActChunk<BITS> xa[NTR][MC1];
-  Meta m1c;
-  int x_for = -1;
-  if constexpr (ONE) {
-#pragma unroll
-    for (int c = 0; c < MC1; ++c) load_act<BITS>(p.x + (lr1 + c * p.lpr1) * KPC, xa[0][c]);
-  }
-
-  Cursor c1l{it1_0 / max(p.items1, 1), it1_0 % max(p.items1, 1)};
-  Cursor c1c = c1l;
-  Meta m1l;
-  auto load1 = [&](PairBuf<BITS, MC1> &b) {
-    m1l.get(p, c1l.a, nrows);
-    const size_t row = (size_t)m1l.e * 2 * p.I + c1l.ib * p.rpw1 + rs1;
-    load_row<BITS, MC1>(p.w13c + row * wpr1, p.w13s + row * gpr1, BITS == 2 ? p.w13z + row * gpr1 : nullptr, lr1,
-                        p.lpr1, b.g);
-    const size_t rowu = row + p.I;
-    load_row<BITS, MC1>(p.w13c + rowu * wpr1, p.w13s + rowu * gpr1, BITS == 2 ? p.w13z + rowu * gpr1 : nullptr,
-                        lr1, p.lpr1, b.u);
-    c1l.advance(p.items1);
-  };
-
-  int cur_a = -1, done_in_a = 0;
-  auto publish = [&]() {
-    if (done_in_a) {
-      wait_vmem();
-      if (lane == 0) atomicAdd(counter(p.ctl, cur_a), done_in_a);
-    }
-  };
-  auto compute1 = [&](const PairBuf<BITS, MC1> &b) {
-    const int a = c1c.a;
-    const int i = c1c.ib * p.rpw1 + rs1;
-    if (a != cur_a) {
-      publish();
-      cur_a = a;
-      done_in_a = 0;
-    }
-    m1c.get(p, a, nrows);
-    if constexpr (ONE) {
-      const float gv = group_sum(row_partial<BITS, MC1>(b.g, xa[0], mask, magic), p.lpr1);
-      const float uv = group_sum(row_partial<BITS, MC1>(b.u, xa[0], mask, magic), p.lpr1);
-      if (lr1 == 0 && m1c.o1 > m1c.o0)
-        __hip_atomic_store(p.hbuf + (size_t)m1c.o0 * p.I + i, f32_to_bf16(silu_f(gv) * uv), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      if (x_for != a) {
-        x_for = a;
-#pragma unroll
-        for (int r = 0; r < NTR; ++r)
-          if (m1c.o0 + r < m1c.o1) {
-            const int t = min(max(sload(p.sorted_rows + m1c.o0 + r), 0) / p.k, p.T - 1);
-#pragma unroll
-            for (int c = 0; c < MC1; ++c) load_act<BITS>(p.x + (size_t)t * p.H + (lr1 + c * p.lpr1) * KPC, xa[r][c]);
-          }
-      }
-#pragma unroll
-      for (int r = 0; r < NTR; ++r)
-        if (m1c.o0 + r < m1c.o1) {
-          const float gv = group_sum(row_partial<BITS, MC1>(b.g, xa[r], mask, magic), p.lpr1);
-          const float uv = group_sum(row_partial<BITS, MC1>(b.u, xa[r], mask, magic), p.lpr1);
-          if (lr1 == 0)
-            __hip_atomic_store(p.hbuf + (size_t)(m1c.o0 + r) * p.I + i, f32_to_bf16(silu_f(gv) * uv),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int item = blockIdx.x; item < n1 + n2; item += gridDim.x) {
+    if (item < n1) {
+      // ============================================================ phase 1
+      const int a = item / per1, i0 = (item - a * per1) * kRows1;
+      const Meta md = meta(p, a, nrows);
+      const int g0 = wv * Gw1, ng = max(min(Gw1, G1 - g0), 0);
+      const size_t erows = (size_t)md.e * 2 * p.I;  // first row of the expert
+      const ExpertW xw = {(const uint8_t *)p.w13c + erows * (G1 * GB), (const uint8_t *)p.w13s + erows * (G1 * 2),
+                          p.w13z + erows * G1};
+      const Off o2[2] = {row_off(i0 + m, G1, g0, GB, lsub), row_off(p.I + i0 + m, G1, g0, GB, lsub)};
+      const int nch = ng / kChunkG;
+      // activation row of sorted position q
+      auto xrow = [&](int q) -> const uint16_t * {
+        const int t = ONE ? 0 : min(max(sload(p.sorted_rows + q), 0) / p.k, p.T - 1);
+        return p.x + (size_t)t * p.H;
+      };
+      PreAct pa;
+      int q0 = 0;
+      Chunk<BITS> wgu[2];
+      if constexpr (FAST) {
+        if (md.o0 < md.o1) {
+          pre_load<BITS, NPRE>(xrow(md.o0), p.H, pa);
+          q0 = 256 * NPRE;
         }
-      for (int q = m1c.o0 + NTR; q < m1c.o1; ++q) {  // more routed rows than are cached
-        const int t = min(max(sload(p.sorted_rows + q), 0) / p.k, p.T - 1);
-        ActChunk<BITS> act[MC1];
+        load_chunk<BITS>(xw, o2[0], wgu[0]);
+        load_chunk<BITS>(xw, o2[1], wgu[1]);
+      }
+      for (int rb = md.o0; rb < md.o1; rb += RM) {
+        const int R = ONE ? 1 : min(RM, md.o1 - rb);
+        stage_rows<BITS, false, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
+        const int arow = ONE ? 0 : min(m, R - 1);
+        const uint8_t *ap = act + arow * pitch1 + lsub * 64 + g0 * (kGroup * 2);
+        const float *xs = Xs + g0 * 16 + (ONE ? 0 : 4 * lsub);
+        f32x4 tgu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if constexpr (FAST) {
+          for (int ch = 0; ch < nch; ++ch) {
+            if (ch > 0) {
+              load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wgu[0]);
+              load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wgu[1]);
+            }
+            chunk_gemv<BITS, ONE, 2>(wgu, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, tgu);
+          }
+          if (nch > 1 && rb + RM < md.o1) {  // the next pass starts again from the first chunk
+            load_chunk<BITS>(xw, o2[0], wgu[0]);
+            load_chunk<BITS>(xw, o2[1], wgu[1]);
+          }
+        } else {
+          groups_gemv_slow<BITS, ONE, 2>(xw, o2, ng, ap, xs, magic, tgu);
+        }
+        const f32x4 tg = tgu[0], tu = tgu[1];
+        // cross-wave sum of the 16 x 16 gate / up partials: red[wave][gate|up][row][col]
+        float *rw = red + wv * 512;
 #pragma unroll
-        for (int c = 0; c < MC1; ++c) load_act<BITS>(p.x + (size_t)t * p.H + (lr1 + c * p.lpr1) * KPC, act[c]);
-        const float gv = group_sum(row_partial<BITS, MC1>(b.g, act, mask, magic), p.lpr1);
-        const float uv = group_sum(row_partial<BITS, MC1>(b.u, act, mask, magic), p.lpr1);
-        if (lr1 == 0)
-          __hip_atomic_store(p.hbuf + (size_t)q * p.I + i, f32_to_bf16(silu_f(gv) * uv), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < 4; ++i) {
+          rw[(4 * lsub + i) * 16 + m] = tg[i];
+          rw[256 + (4 * lsub + i) * 16 + m] = tu[i];
+        }
+        lds_barrier();
+        if (threadIdx.x < R * 16) {  // all in wave 0
+          const int mm = threadIdx.x / 16, n = threadIdx.x % 16;
+          float gv = 0.f, uv = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            gv += red[w * 512 + mm * 16 + n];
+            uv += red[w * 512 + 256 + mm * 16 + n];
+          }
+          __hip_atomic_store(p.hbuf + (size_t)(rb + mm) * p.I + i0 + n, f32_to_bf16(silu_f(gv) * uv),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (wv == 0) wait_vmem();  // h stores complete before thread 0 publishes
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        lds_barrier();
+      }
+      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), 1);
+    } else {
+      // ============================================================ phase 2
+      const int it = item - n1;
+      const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 32;
+      const Meta md = meta(p, a, nrows);
+      const size_t erows = (size_t)md.e * p.H;
+      const ExpertW xw = {(const uint8_t *)p.w2c + erows * (G2 * GB), (const uint8_t *)p.w2s + erows * (G2 * 2),
+                          p.w2z + erows * G2};
+      const Off o2[2] = {row_off(n0 + m, G2, 0, GB, lsub), row_off(n0 + 16 + m, G2, 0, GB, lsub)};
+      const int nch = G2 / kChunkG;
+      Chunk<BITS> wd[2];
+      if constexpr (FAST) {
+        load_chunk<BITS>(xw, o2[0], wd[0]);
+        load_chunk<BITS>(xw, o2[1], wd[1]);
+      }
+      if (threadIdx.x == 0) {
+        if (!wait_counter_geq(counter(p.ctl, a), per1, p.max_spins)) atomicOr(&p.ctl[kCtlError], 1);
+      }
+      for (int rb = md.o0; rb < md.o1; rb += RM) {
+        const int R = ONE ? 1 : min(RM, md.o1 - rb);
+        __syncthreads();  // holds the block until thread 0's wait has ended
+        stage_rows<BITS, true, 0>(act, Xs, [&](int r) { return (const uint16_t *)p.hbuf + (size_t)(rb + r) * p.I; }, R,
+                               p.I, 0, nullptr);
+        const int arow = ONE ? 0 : min(m, R - 1);
+        const uint8_t *ap = act + arow * pitch2 + lsub * 64;
+        const float *xs = Xs + (ONE ? 0 : 4 * lsub);
+        f32x4 ty[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if constexpr (FAST) {
+          for (int ch = 0; ch < nch; ++ch) {
+            if (ch > 0) {
+              load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wd[0]);
+              load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wd[1]);
+            }
+            chunk_gemv<BITS, ONE, 2>(wd, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, ty);
+          }
+          if (nch > 1 && rb + RM < md.o1) {
+            load_chunk<BITS>(xw, o2[0], wd[0]);
+            load_chunk<BITS>(xw, o2[1], wd[1]);
+          }
+        } else {
+          groups_gemv_slow<BITS, ONE, 2>(xw, o2, G2, ap, xs, magic, ty);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          uint16_t *yrow = p.y_perm + (size_t)rb * p.H + n0 + 16 * s2 + m;
+          if (ONE) {
+            if (lsub == 0) *yrow = f32_to_bf16(ty[s2][0]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int mm = 4 * lsub + i;
+              if (mm < R) yrow[(size_t)mm * p.H] = f32_to_bf16(ty[s2][i]);
+            }
+          }
+        }
+        lds_barrier();  // LDS is rewritten by the next pass
       }
     }
-    ++done_in_a;
-    c1c.advance(p.items1);
-  };
-
-  // one item ahead: the loads of item j+1 are issued before item j is computed;
-  // after the wave's last phase-1 load its first two phase-2 batches follow.
-  PairBuf<BITS, MC1> bA, bB;
-  bool p2_issued = false;
-  auto issue_p2 = [&]() {
-    if (!p2_issued) {
-      load2(dwA);
-      load2(dwB);
-      p2_issued = true;
-    }
-  };
-  if (it1_0 < it1_1) load1(bA);
-  for (int it = it1_0; it < it1_1; it += 2) {
-    if (it + 1 < it1_1) load1(bB); else issue_p2();
-    compute1(bA);
-    if (it + 1 < it1_1) {
-      if (it + 2 < it1_1) load1(bA); else issue_p2();
-      compute1(bB);
-    }
-  }
-  issue_p2();
-  publish();
-
-  // ---------------------------------------------------------------- phase 2
-  Cursor c2c{it2_0 / max(p.items2, 1), it2_0 % max(p.items2, 1)};
-  Meta m2c;
-  int ready_a = -1;
-  ActChunk<BITS> hc[NTR][MC2];
-  auto compute2 = [&](const RowChunks<BITS, MC2> &d) {
-    const int a = c2c.a;
-    const int n = c2c.ib * p.rpw2 + rs2;
-    m2c.get(p, a, nrows);
-    if (a != ready_a) {
-      int ok = 1;
-      if (lane == 0) ok = wait_counter_geq(counter(p.ctl, a), p.items1, p.max_spins) ? 1 : 0;
-      ok = __shfl(ok, 0, kWave);
-      if (!ok && lane == 0) atomicOr(&p.ctl[kCtlError], 1);
-      ready_a = a;
-#pragma unroll
-      for (int r = 0; r < NTR; ++r)
-        if (m2c.o0 + r < m2c.o1)
-#pragma unroll
-          for (int c = 0; c < MC2; ++c)
-            load_act_coherent<BITS>(p.hbuf + (size_t)(m2c.o0 + r) * p.I + (lr2 + c * p.lpr2) * KPC, hc[r][c]);
-    }
-#pragma unroll
-    for (int r = 0; r < NTR; ++r)
-      if (m2c.o0 + r < m2c.o1) {
-        const float yv = group_sum(row_partial<BITS, MC2>(d, hc[r], mask, magic), p.lpr2);
-        if (lr2 == 0) p.y_perm[(size_t)(m2c.o0 + r) * p.H + n] = f32_to_bf16(yv);
-      }
-    if constexpr (!ONE) {
-      for (int q = m2c.o0 + NTR; q < m2c.o1; ++q) {  // more routed rows than are cached
-        ActChunk<BITS> act[MC2];
-#pragma unroll
-        for (int c = 0; c < MC2; ++c)
-          load_act_coherent<BITS>(p.hbuf + (size_t)q * p.I + (lr2 + c * p.lpr2) * KPC, act[c]);
-        const float yv = group_sum(row_partial<BITS, MC2>(d, act, mask, magic), p.lpr2);
-        if (lr2 == 0) p.y_perm[(size_t)q * p.H + n] = f32_to_bf16(yv);
-      }
-    }
-    c2c.advance(p.items2);
-  };
-  for (int base = it2_0; base < it2_1; base += 2 * NB2) {
-#pragma unroll
-    for (int j = 0; j < NB2; ++j)
-      if (base + j < it2_1) compute2(dwA[j]);
-    if (base + 2 * NB2 < it2_1) load2(dwA);
-#pragma unroll
-    for (int j = 0; j < NB2; ++j)
-      if (base + NB2 + j < it2_1) compute2(dwB[j]);
-    if (base + 3 * NB2 < it2_1) load2(dwB);
   }
 
   // ---------------------------------------------------------------- counters reset
-  // The last block to finish re-zeroes the counters (no cache flush needed:
-  // every block has finished polling before it is counted).
-  __shared__ int s_last;
+  // The last block to finish re-zeroes the counters; every other block has
+  // finished polling before it is counted.
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&p.ctl[kCtlFfnDone], 1);
-    s_last = (prev == (int)gridDim.x - 1);
-  }
+  if (threadIdx.x == 0) s_last = atomicAdd(&p.ctl[kCtlFfnDone], 1) == (int)gridDim.x - 1;
   __syncthreads();
   if (s_last) {
     for (int a = threadIdx.x; a < p.Amax; a += blockDim.x)
@@ -440,52 +506,37 @@ __global__ void __launch_bounds__(256, 2) ffn_decode_kernel(DecodeParams p) {
   }
 }
 
-struct Layout {
-  int lpr, cpl, rpw;
-};
-
-Layout row_layout(int K, int bits) {
-  const int chunks = K * bits / 128;  // 16-byte chunks per row
-  Layout l;
-  l.lpr = chunks < kWave ? chunks : kWave;
-  l.cpl = chunks / l.lpr;
-  l.rpw = kWave / l.lpr;
-  return l;
-}
-
 template <int BITS, bool ONE>
-const void *decode_fn_mc(int mc1, int mc2) {
-  if (mc2 == 1) {
-    if (mc1 == 1) return (const void *)ffn_decode_kernel<BITS, 1, 1, ONE>;
-    if (mc1 == 2) return (const void *)ffn_decode_kernel<BITS, 2, 1, ONE>;
-    if (mc1 == 4) return (const void *)ffn_decode_kernel<BITS, 4, 1, ONE>;
-  } else if (mc2 == 2) {
-    if (mc1 == 1) return (const void *)ffn_decode_kernel<BITS, 1, 2, ONE>;
-    if (mc1 == 2) return (const void *)ffn_decode_kernel<BITS, 2, 2, ONE>;
-    if (mc1 == 4) return (const void *)ffn_decode_kernel<BITS, 4, 2, ONE>;
-  }
-  return nullptr;
+const void *decode_fn_fast(bool fast) {
+  return fast ? (const void *)ffn_decode_kernel<BITS, ONE, true> : (const void *)ffn_decode_kernel<BITS, ONE, false>;
 }
 
-const void *decode_kernel_fn(int bits, int mc1, int mc2, bool one) {
-  if (bits == 4) return one ? decode_fn_mc<4, true>(mc1, mc2) : decode_fn_mc<4, false>(mc1, mc2);
-  return one ? decode_fn_mc<2, true>(mc1, mc2) : decode_fn_mc<2, false>(mc1, mc2);
+const void *decode_kernel_fn(int bits, bool one, bool fast) {
+  if (bits == 4) return one ? decode_fn_fast<4, true>(fast) : decode_fn_fast<4, false>(fast);
+  return one ? decode_fn_fast<2, true>(fast) : decode_fn_fast<2, false>(fast);
 }
 
-// Co-resident blocks per CU of one decode instantiation (cached per device and kernel).
-int resident_blocks_per_cu(const void *fn, int device) {
+size_t decode_lds_bytes(int H, int I, bool one) {
+  const size_t kmax = H > I ? H : I;
+  return (size_t)(one ? 1 : kRMax) * (kmax * 2 + 16) + 16 * (kmax / kGroup) * 4 + kRedFloats * 4;
+}
+
+// Co-resident blocks per CU of one decode instantiation (cached per device, kernel and LDS size).
+int resident_blocks_per_cu(const void *fn, int device, size_t lds) {
   static std::mutex mu;
   static const void *c_fn[64];
   static int c_dev[64], c_nb[64], n_cached = 0;
+  static size_t c_lds[64];
   std::lock_guard<std::mutex> lk(mu);
   for (int i = 0; i < n_cached; ++i)
-    if (c_fn[i] == fn && c_dev[i] == device) return c_nb[i];
+    if (c_fn[i] == fn && c_dev[i] == device && c_lds[i] == lds) return c_nb[i];
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, lds) != hipSuccess) return 0;
   if (n_cached < 64) {
     c_fn[n_cached] = fn;
     c_dev[n_cached] = device;
     c_nb[n_cached] = nb;
+    c_lds[n_cached] = lds;
     ++n_cached;
   }
   return nb;
@@ -494,11 +545,8 @@ int resident_blocks_per_cu(const void *fn, int device) {
 }  // namespace
 
 bool decode_layout_ok(int H, int I, int bits) {
-  const Layout a = row_layout(H, bits), b = row_layout(I, bits);
-  const int ca = H * bits / 128, cb = I * bits / 128;
-  auto pow2 = [](int v) { return v > 0 && (v & (v - 1)) == 0; };
-  return (a.cpl == 1 || a.cpl == 2 || a.cpl == 4) && (b.cpl == 1 || b.cpl == 2) && ca % a.lpr == 0 &&
-         cb % b.lpr == 0 && pow2(a.lpr) && pow2(b.lpr) && I % a.rpw == 0 && H % b.rpw == 0;
+  (void)bits;
+  return I % kRows1 == 0 && H % kRows2 == 0 && decode_lds_bytes(H, I, false) <= 64 * 1024;
 }
 
 size_t ffn_ctl_bytes(int T, int k, int E) {
@@ -529,26 +577,20 @@ hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_
   p.y_perm = a.y_perm;
   p.ctl = (int *)a.ws;
   p.hbuf = (uint16_t *)((char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E));
-  const Layout l1 = row_layout(a.H, a.bits), l2 = row_layout(a.I, a.bits);
-  p.lpr1 = l1.lpr;
-  p.rpw1 = l1.rpw;
-  p.items1 = a.I / l1.rpw;
-  p.lpr2 = l2.lpr;
-  p.rpw2 = l2.rpw;
-  p.items2 = a.H / l2.rpw;
   p.max_spins = 1 << 22;
-  p.magic = 0x43004300u;
-  const void *fn = decode_kernel_fn(a.bits, l1.cpl, l2.cpl, a.T == 1);
-  if (!fn) return hipErrorInvalidConfiguration;
-  const int per_cu = resident_blocks_per_cu(fn, dev.device);
+  p.magic = kMagic43;
+  const bool one = a.T == 1;
+  const bool fast = (a.H / kGroup) % (4 * kChunkG) == 0 && (a.I / kGroup) % kChunkG == 0;
+  const void *fn = decode_kernel_fn(a.bits, one, fast);
+  const size_t lds = decode_lds_bytes(a.H, a.I, one);
+  const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
-  const long waves_needed = (long)p.Amax * (p.items1 > p.items2 ? p.items1 : p.items2);
-  long blocks = (waves_needed + 3) / 4;
+  long blocks = (long)p.Amax * (a.I / kRows1 + a.H / kRows2);
   const long resident = (long)dev.num_cus * per_cu;
   if (blocks > resident) blocks = resident;
   if (blocks < 1) blocks = 1;
   void *args[] = {&p};
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, st);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, lds, st);
 }
 
 }  // namespace bqmoe

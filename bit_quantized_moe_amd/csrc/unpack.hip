@@ -15,19 +15,23 @@ __global__ void unpack_kernel(const uint32_t *__restrict__ words, int64_t n_word
   const uint32_t w = words[i];
   constexpr int P = 32 / BITS;
   int8_t q[P];
+  // bf16 pairs (128 + u) in the field order of the unpack, back to field order
   if constexpr (BITS == 4) {
+    const u32x4 pr = unpack4_pairs(w, kMagic43);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t pr = int4_pair(w, p);  // bf16 (128 + u) for fields p and p + 4
-      q[p] = (int8_t)((int)bf16lo(pr) - 136);
-      q[p + 4] = (int8_t)((int)bf16hi(pr) - 136);
+      q[kOrder4[2 * p]] = (int8_t)((int)bf16lo(pr[p]) - 136);
+      q[kOrder4[2 * p + 1]] = (int8_t)((int)bf16hi(pr[p]) - 136);
     }
   } else {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const uint32_t pr = int2_pair(w, p);  // fields p and p + 8
-      q[p] = (int8_t)((int)bf16lo(pr) - 128);
-      q[p + 8] = (int8_t)((int)bf16hi(pr) - 128);
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 pr = unpack2_pairs(w, h, kMagic43);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        q[kOrder2[8 * h + 2 * p]] = (int8_t)((int)bf16lo(pr[p]) - 128);
+        q[kOrder2[8 * h + 2 * p + 1]] = (int8_t)((int)bf16hi(pr[p]) - 128);
+      }
     }
   }
 #pragma unroll

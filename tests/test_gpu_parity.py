@@ -218,6 +218,19 @@ def test_layer_mid_shapes(bits):
         _check_layer_exact(inp, got)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+def test_layer_decode_shapes_of_the_full_model(bits):
+    """H = 4096, I = 1024 (the decode kernel's full-chunk path) with few experts:
+    T = 1, a few tokens with experts holding 1-2 rows, and T = 16 with E = 8
+    (experts holding more rows than one pass stages)."""
+    for T, E, k in ((1, 8, 2), (3, 8, 2), (16, 8, 4)):
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=4096, I=1024, E=E, k=k, bits=bits,
+                           scale_sigma=0.02 if bits == 4 else 0.05, seed=1200 + T)
+        inp = workload.make_layer_inputs(sp)
+        got, _ = _layer(inp)
+        _check_layer_exact(inp, got)
+
+
 @pytest.mark.parametrize("T", [1, 8, 64])
 def test_layer_deterministic_and_workspace_left_zero(T):
     sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=512, I=256, E=16, k=4)
