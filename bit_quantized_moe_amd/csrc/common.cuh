@@ -20,10 +20,12 @@ constexpr int kGroup = 128;  // quantisation group along K
 //   [0]      route: blocks finished (last-block top-k)
 //   [1]      ffn decode: blocks finished
 //   [2]      sticky error flags (bit 0: a bounded wait timed out)
+//   [32]     route: selector blocks finished
 //   [64..]   ffn decode: per-active-expert completion counters, kCtrStride apart
 constexpr int kCtlRouteDone = 0;
 constexpr int kCtlFfnDone = 1;
 constexpr int kCtlError = 2;
+constexpr int kCtlRouteSel = 32;
 constexpr int kCtlCounters = 64;
 constexpr int kCtrStride = 32;   // ints between counters: one 128-byte line each
 constexpr int kCtlWords = 1024;  // minimum control block: 4 KiB
@@ -125,21 +127,6 @@ __device__ __forceinline__ void dequant16_int2(uint32_t w, float s, float zs, ui
 }
 
 // ---------------------------------------------------------------- wave helpers
-__device__ __forceinline__ float wave_sum_xor(float v, int width) {
-  for (int d = width >> 1; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
-
-// Sum over the 64 lanes as a balanced pairwise tree in lane order:
-// ((v0+v1)+(v2+v3))+... .  The xor butterfly with distance 1 first forms the
-// level-1 pairs, distance 2 the level-2 pairs, and so on; float addition is
-// commutative, so every lane ends with the bits of the tree sum.
-__device__ __forceinline__ float wave_tree_sum(float v) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
-
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Load through the scalar cache.  Only for data that no wave writes during
@@ -154,27 +141,28 @@ __device__ __forceinline__ T sload(const T *ptr) {
 
 // Sum of v over aligned groups of `width` lanes (1, 2, 4, ..., 64); every lane
 // of a group receives the group sum.  Lane distances 1 and 2 use quad
-// permutes, 4 and 8 the row (half-)mirror, 16 and 32 a cross-row shuffle.
+// permutes, 4 and 8 the row (half-)mirror, 16 a ds_swizzle xor inside each
+// half-wave, and the two halves are combined from v_readlane.  At every level
+// a lane adds the sums of the two halves of its group (in either operand
+// order, which float addition does not see), so the result is the balanced
+// pairwise tree over the lanes in index order, bit for bit the same in every
+// lane.
+__device__ __forceinline__ uint32_t xor16_lanes(uint32_t x) {
+  // bitmask swizzle: and 0x1f, or 0, xor 0x10 within each group of 32 lanes
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+}
 __device__ __forceinline__ float group_sum(float v, int width) {
   if (width >= 2) v = BQ_DPP_ADD(v, 0xB1);   // quad_perm [1,0,3,2]
   if (width >= 4) v = BQ_DPP_ADD(v, 0x4E);   // quad_perm [2,3,0,1]
   if (width >= 8) v = BQ_DPP_ADD(v, 0x141);  // row_half_mirror
   if (width >= 16) v = BQ_DPP_ADD(v, 0x140); // row_mirror
-  if (width >= 32) v += __shfl_xor(v, 16, kWave);
-  if (width >= 64) v += __shfl_xor(v, 32, kWave);
-  return v;
-}
-
-// Bounded spin on a device-scope counter (device-coherent loads).  Returns
-// false on timeout.  Data published before the counter was raised must be
-// read with device-coherent loads as well (see the callers).
-__device__ __forceinline__ bool wait_counter_geq(int *ctr, int target, int max_spins) {
-  int spins = 0;
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > max_spins) return false;
+  if (width >= 32) v += __builtin_bit_cast(float, xor16_lanes(__builtin_bit_cast(uint32_t, v)));
+  if (width >= 64) {
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    v = lo + hi;
   }
-  return true;
+  return v;
 }
 
 // Block barrier that orders LDS accesses only.  Unlike __syncthreads() it does

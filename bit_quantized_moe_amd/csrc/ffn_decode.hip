@@ -315,15 +315,34 @@ __device__ __forceinline__ void groups_gemv_slow(const ExpertW &x, const Off *o,
 }
 
 // Per-expert metadata of active slot a (wave-uniform; through the scalar cache).
+// With one token, the a-th active expert (ascending) owns sorted row a.
 struct Meta {
   int e, o0, o1;
 };
+template <bool ONE>
 __device__ __forceinline__ Meta meta(const DecodeParams &p, int a, int nrows) {
   Meta r;
   r.e = min(max(sload(p.active + 1 + a), 0), p.E - 1);
-  r.o0 = min(max(sload(p.offsets + r.e), 0), nrows);
-  r.o1 = min(max(sload(p.offsets + r.e + 1), r.o0), nrows);
+  if constexpr (ONE) {
+    r.o0 = min(a, nrows);
+    r.o1 = min(a + 1, nrows);
+  } else {
+    r.o0 = min(max(sload(p.offsets + r.e), 0), nrows);
+    r.o1 = min(max(sload(p.offsets + r.e + 1), r.o0), nrows);
+  }
   return r;
+}
+
+// Per-expert counter: bits [0, 16) count phase-1 items whose weight loads are
+// issued, bits [16, 32) phase-1 items whose h rows are published.
+constexpr int kIssued = 1, kPublished = 1 << 16;
+__device__ __forceinline__ bool wait_field_geq(int *ctr, int shift, int target, int max_spins) {
+  int spins = 0;
+  while (((__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> shift) & 0xFFFF) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > max_spins) return false;
+  }
+  return true;
 }
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v)); }
@@ -363,7 +382,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
     if (item < n1) {
       // ============================================================ phase 1
       const int a = item / per1, i0 = (item - a * per1) * kRows1;
-      const Meta md = meta(p, a, nrows);
+      const Meta md = meta<ONE>(p, a, nrows);
       const int g0 = wv * Gw1, ng = max(min(Gw1, G1 - g0), 0);
       const size_t erows = (size_t)md.e * 2 * p.I;  // first row of the expert
       const ExpertW xw = {(const uint8_t *)p.w13c + erows * (G1 * GB), (const uint8_t *)p.w13s + erows * (G1 * 2),
@@ -386,6 +405,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         load_chunk<BITS>(xw, o2[0], wgu[0]);
         load_chunk<BITS>(xw, o2[1], wgu[1]);
       }
+      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), kIssued);
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
         stage_rows<BITS, false, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
@@ -432,12 +452,12 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         lds_barrier();
       }
-      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), 1);
+      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), kPublished);
     } else {
       // ============================================================ phase 2
       const int it = item - n1;
       const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 32;
-      const Meta md = meta(p, a, nrows);
+      const Meta md = meta<ONE>(p, a, nrows);
       const size_t erows = (size_t)md.e * p.H;
       const ExpertW xw = {(const uint8_t *)p.w2c + erows * (G2 * GB), (const uint8_t *)p.w2s + erows * (G2 * 2),
                           p.w2z + erows * G2};
@@ -445,11 +465,16 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const int nch = G2 / kChunkG;
       Chunk<BITS> wd[2];
       if constexpr (FAST) {
+        // The down weights are needed last: request them only once every
+        // phase-1 item of the expert has its loads out, so that they queue
+        // behind the gate/up weights the hand-off waits for.
+        if (threadIdx.x == 0) wait_field_geq(counter(p.ctl, a), 0, per1, p.max_spins);
+        __syncthreads();
         load_chunk<BITS>(xw, o2[0], wd[0]);
         load_chunk<BITS>(xw, o2[1], wd[1]);
       }
       if (threadIdx.x == 0) {
-        if (!wait_counter_geq(counter(p.ctl, a), per1, p.max_spins)) atomicOr(&p.ctl[kCtlError], 1);
+        if (!wait_field_geq(counter(p.ctl, a), 16, per1, p.max_spins)) atomicOr(&p.ctl[kCtlError], 1);
       }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);

@@ -17,181 +17,204 @@
 namespace bqmoe {
 namespace {
 
-constexpr int kMaxE = 1024;
-constexpr int kMaxK = 32;
 
 // ------------------------------------------------------------ top-k of one token
-// One wave selects the k largest of lg[0..E) (ties: lower index first) and
-// writes ids / softmax gates.  COHERENT: lg is global memory written by other
-// blocks of this kernel, read with device-coherent loads; otherwise lg is LDS.
-template <bool COHERENT>
+// Selection order: logit descending, then expert index ascending.  A logit
+// becomes an order-preserving uint32 (with -0 folded into +0, so equal floats
+// give equal keys) and the pair (key, ~e) is compared as one 64-bit key, so a
+// plain maximum over the wave picks the next slot.
+__device__ __forceinline__ uint32_t ord_key(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ void key_max(uint32_t &hi, uint32_t &lo, uint32_t ohi, uint32_t olo) {
+  const bool take = (ohi > hi) || (ohi == hi && olo > lo);
+  hi = take ? ohi : hi;
+  lo = take ? olo : lo;
+}
+#define BQ_DPP_U32(v, ctrl) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), 0xF, 0xF, false))
+// Maximum (hi, lo) over the 64 lanes, in every lane.
+__device__ __forceinline__ void wave_key_max(uint32_t &hi, uint32_t &lo) {
+  key_max(hi, lo, BQ_DPP_U32(hi, 0xB1), BQ_DPP_U32(lo, 0xB1));
+  key_max(hi, lo, BQ_DPP_U32(hi, 0x4E), BQ_DPP_U32(lo, 0x4E));
+  key_max(hi, lo, BQ_DPP_U32(hi, 0x141), BQ_DPP_U32(lo, 0x141));
+  key_max(hi, lo, BQ_DPP_U32(hi, 0x140), BQ_DPP_U32(lo, 0x140));
+  key_max(hi, lo, xor16_lanes(hi), xor16_lanes(lo));
+  const uint32_t h0 = __builtin_amdgcn_readlane((int)hi, 0), l0 = __builtin_amdgcn_readlane((int)lo, 0);
+  const uint32_t h1 = __builtin_amdgcn_readlane((int)hi, 32), l1 = __builtin_amdgcn_readlane((int)lo, 32);
+  hi = h0;
+  lo = l0;
+  key_max(hi, lo, h1, l1);
+}
+
+// One wave selects the k largest of lg[0..E) and writes ids and softmax
+// gates.  NV = values per lane (E <= 64 * NV).  COHERENT: lg is global memory
+// written by other blocks of this kernel, read with device-coherent loads;
+// otherwise lg is LDS or ordinary memory.
+template <int NV, bool COHERENT>
 __device__ void topk_softmax_wave(const float *lg, int E, int k, int32_t *ids_out, float *g_out) {
   const int lane = lane_id();
-  float v[kMaxE / kWave];
+  uint32_t key[NV];
 #pragma unroll
-  for (int j = 0; j < kMaxE / kWave; ++j) {
+  for (int j = 0; j < NV; ++j) {
     const int e = lane + kWave * j;
-    if constexpr (COHERENT)
-      v[j] = (e < E) ? __hip_atomic_load(lg + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
-    else
-      v[j] = (e < E) ? lg[e] : -INFINITY;
+    float v = 0.f;
+    if (e < E) {
+      if constexpr (COHERENT)
+        v = __hip_atomic_load(lg + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        v = lg[e];
+    }
+    key[j] = (e < E) ? ord_key(v) : 0u;  // 0: below every finite logit; never selected while k <= E
   }
-  uint32_t used = 0;
+  uint32_t used = 0, my_hi = 0;
   int my_e = 0;
-  float my_v = 0.f;
   for (int slot = 0; slot < k; ++slot) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint32_t hi = 0, lo = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxE / kWave; ++j) {
+    for (int j = 0; j < NV; ++j) {
       const int e = lane + kWave * j;
-      const bool ok = (e < E) && !((used >> j) & 1u);
-      if (ok && (v[j] > bv || (v[j] == bv && e < be))) {
-        bv = v[j];
-        be = e;
-      }
+      if (e < E && !((used >> j) & 1u)) key_max(hi, lo, key[j], ~(uint32_t)e);
     }
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, kWave);
-      const int oe = __shfl_xor(be, d, kWave);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (be == 0x7fffffff) be = slot % E;  // only reachable with non-finite logits
+    wave_key_max(hi, lo);
+    const int be = (int)~lo;
     if ((be % kWave) == lane) used |= 1u << (be / kWave);
     if (lane == slot) {
       my_e = be;
-      my_v = bv;
+      my_hi = hi;
     }
   }
-  const float m = __shfl(my_v, 0, kWave);
-  const float ex = (lane < k) ? expf(my_v - m) : 0.f;
-  const float sum = wave_sum_xor(ex, kWave);
+  const float mine = key_value(my_hi);
+  const float m = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mine)));
+  const float ex = (lane < k) ? expf(mine - m) : 0.f;
+  const float sum = group_sum(ex, kWave);
   if (lane < k) {
     ids_out[lane] = my_e;
     g_out[lane] = ex / sum;
   }
 }
 
-// ------------------------------------------------------------ small T
-// Grid: ceil(E/4) blocks of 4 waves; wave -> one expert, lane s -> slice s.
-// The last block to finish runs top-k for every token.
-__device__ __forceinline__ void bf16x8_to_f32(const u32x4 &p, float *f) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f[2 * q] = bf16lo(p[q]);
-    f[2 * q + 1] = bf16hi(p[q]);
-  }
+template <bool COHERENT>
+__device__ __forceinline__ void topk_softmax_any(const float *lg, int E, int k, int32_t *ids_out, float *g_out) {
+  if (E <= 64)
+    topk_softmax_wave<1, COHERENT>(lg, E, k, ids_out, g_out);
+  else if (E <= 128)
+    topk_softmax_wave<2, COHERENT>(lg, E, k, ids_out, g_out);
+  else if (E <= 256)
+    topk_softmax_wave<4, COHERENT>(lg, E, k, ids_out, g_out);
+  else if (E <= 512)
+    topk_softmax_wave<8, COHERENT>(lg, E, k, ids_out, g_out);
+  else
+    topk_softmax_wave<16, COHERENT>(lg, E, k, ids_out, g_out);
 }
 
-template <int VEC>  // bf16 elements per load: 8 (16 B), 4 (8 B) or 2 (4 B)
-__global__ void __launch_bounds__(256) route_small_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ w, const float *bias,
-                                                          int T, int H, int E, int k, int32_t *ids,
-                                                          float *gates, float *lg, int *ctl) {
-  constexpr int MAXP = 8;  // 16-byte slice pieces held in registers (L <= 64)
-  const int wave = threadIdx.x / kWave;
+// ------------------------------------------------------------ small T
+// Grid: E blocks of one wave; block e computes the logits of expert e for
+// every token (lane s = slice s, sequential over its h), then counts itself
+// done.  Blocks 0 .. nsel-1 (nsel = min(T, E)) wait until every expert is
+// done and run top-k for tokens b, b + nsel, ...; the last of them to finish
+// re-zeroes the counters.  All E one-wave blocks are co-resident, so the wait
+// ends; it is bounded anyway and a timeout only raises the error flag.
+constexpr int kTB = 4;  // tokens whose activation slices are loaded together
+
+// VEC bf16 elements per load: 8 (16 B), 4 (8 B) or 2 (4 B); kept packed.
+template <int VEC>
+struct Vec {
+  uint32_t u[VEC / 2];
+};
+template <int VEC>
+__device__ __forceinline__ Vec<VEC> load_vec(const uint16_t *p) {
+  Vec<VEC> r;
+  if constexpr (VEC == 8) {
+    const u32x4 v = *(const u32x4 *)p;
+    r.u[0] = v[0], r.u[1] = v[1], r.u[2] = v[2], r.u[3] = v[3];
+  } else if constexpr (VEC == 4) {
+    const u32x2 v = *(const u32x2 *)p;
+    r.u[0] = v[0], r.u[1] = v[1];
+  } else {
+    r.u[0] = *(const uint32_t *)p;
+  }
+  return r;
+}
+// acc += x . w over the VEC elements, ascending (bf16 x bf16 is exact in fp32,
+// so each fma adds the exact product)
+template <int VEC>
+__device__ __forceinline__ float fma_vec(const Vec<VEC> &xv, const Vec<VEC> &wv, float acc) {
+#pragma unroll
+  for (int q = 0; q < VEC / 2; ++q) {
+    acc = __builtin_fmaf(bf16lo(xv.u[q]), bf16lo(wv.u[q]), acc);
+    acc = __builtin_fmaf(bf16hi(xv.u[q]), bf16hi(wv.u[q]), acc);
+  }
+  return acc;
+}
+
+template <int VEC>
+__global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ w, const float *bias, int T,
+                                                         int H, int E, int k, int32_t *ids, float *gates, float *lg,
+                                                         int *ctl, int max_spins) {
+  constexpr int NVC = 64 / VEC;  // loads per 64-element chunk of a slice
   const int lane = lane_id();
-  const int e = blockIdx.x * 4 + wave;
+  const int e = blockIdx.x;
   const int L = H / 64;
-  if (e < E) {
-    const uint16_t *wrow = w + (size_t)e * H + (size_t)lane * L;
-    const float b = bias ? bias[e] : 0.f;
-    if (VEC == 8 && L <= 8 * MAXP) {
-      // the whole slice of w and of one token's x in registers, all loads in flight together
-      const int np = L / 8;
-      u32x4 wp[MAXP];
+  const uint16_t *wrow = w + (size_t)e * H + (size_t)lane * L;
+  const float b = bias ? bias[e] : 0.f;
+  for (int t0 = 0; t0 < T; t0 += kTB) {
+    float acc[kTB];
 #pragma unroll
-      for (int q = 0; q < MAXP; ++q)
-        if (q < np) wp[q] = *(const u32x4 *)(wrow + 8 * q);
-      for (int t = 0; t < T; ++t) {
-        const uint16_t *xr = x + (size_t)t * H + (size_t)lane * L;
-        u32x4 xp[MAXP];
+    for (int tt = 0; tt < kTB; ++tt) acc[tt] = 0.f;
+    const int ntt = min(kTB, T - t0);
+    for (int c0 = 0; c0 < L; c0 += 64) {
+      const int nv = min(64, L - c0) / VEC;
+      // this chunk of the weight slice and of up to kTB tokens' activation slices
+      Vec<VEC> wv[NVC], xv[kTB][NVC];
 #pragma unroll
-        for (int q = 0; q < MAXP; ++q)
-          if (q < np) xp[q] = *(const u32x4 *)(xr + 8 * q);
-        float acc = 0.f;
+      for (int q = 0; q < NVC; ++q)
+        if (q < nv) wv[q] = load_vec<VEC>(wrow + c0 + q * VEC);
 #pragma unroll
-        for (int q = 0; q < MAXP; ++q)
-          if (q < np) {
-            float xf[8], wf[8];
-            bf16x8_to_f32(xp[q], xf);
-            bf16x8_to_f32(wp[q], wf);
+      for (int tt = 0; tt < kTB; ++tt)
+        if (tt < ntt) {
+          const uint16_t *xr = x + (size_t)(t0 + tt) * H + (size_t)lane * L + c0;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) acc = __builtin_fmaf(xf[r], wf[r], acc);  // ascending h
-          }
-        const float sum = wave_tree_sum(acc);  // pairwise tree over the 64 slice sums
-        if (lane == 0)
-          __hip_atomic_store(lg + (size_t)t * E + e, sum + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    } else {
-      for (int t0 = 0; t0 < T; t0 += 4) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < L; i += VEC) {
-          float wf[VEC];
-          if constexpr (VEC == 8) {
-            bf16x8_to_f32(*(const u32x4 *)(wrow + i), wf);
-          } else if constexpr (VEC == 4) {
-            const u32x2 pw = *(const u32x2 *)(wrow + i);
-            wf[0] = bf16lo(pw[0]);
-            wf[1] = bf16hi(pw[0]);
-            wf[2] = bf16lo(pw[1]);
-            wf[3] = bf16hi(pw[1]);
-          } else {
-            const uint32_t pw = *(const uint32_t *)(wrow + i);
-            wf[0] = bf16lo(pw);
-            wf[1] = bf16hi(pw);
-          }
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            if (t0 + tt < T) {
-              const uint16_t *xr = x + (size_t)(t0 + tt) * H + (size_t)lane * L + i;
-              float xf[VEC];
-              if constexpr (VEC == 8) {
-                bf16x8_to_f32(*(const u32x4 *)xr, xf);
-              } else if constexpr (VEC == 4) {
-                const u32x2 px = *(const u32x2 *)xr;
-                xf[0] = bf16lo(px[0]);
-                xf[1] = bf16hi(px[0]);
-                xf[2] = bf16lo(px[1]);
-                xf[3] = bf16hi(px[1]);
-              } else {
-                const uint32_t px = *(const uint32_t *)xr;
-                xf[0] = bf16lo(px);
-                xf[1] = bf16hi(px);
-              }
-#pragma unroll
-              for (int q = 0; q < VEC; ++q) acc[tt] = __builtin_fmaf(xf[q], wf[q], acc[tt]);
-            }
-          }
+          for (int q = 0; q < NVC; ++q)
+            if (q < nv) xv[tt][q] = load_vec<VEC>(xr + q * VEC);
         }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const float sum = wave_tree_sum(acc[tt]);  // pairwise tree over the 64 slice sums
-          if (lane == 0 && t0 + tt < T)
-            __hip_atomic_store(lg + (size_t)(t0 + tt) * E + e, sum + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int tt = 0; tt < kTB; ++tt)
+        if (tt < ntt) {
+#pragma unroll
+          for (int q = 0; q < NVC; ++q)
+            if (q < nv) acc[tt] = fma_vec<VEC>(xv[tt][q], wv[q], acc[tt]);
         }
-      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTB; ++tt) {
+      const float sum = group_sum(acc[tt], kWave);  // pairwise tree over the 64 slice sums
+      if (lane == 0 && t0 + tt < T)
+        __hip_atomic_store(lg + (size_t)(t0 + tt) * E + e, sum + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // The last block to finish selects the experts of every token.  Logits were
-  // stored device-coherently; each wave waits for its stores before the block
-  // is counted, and the last block reads them back device-coherently.
-  __shared__ int s_last;
-  wait_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&ctl[kCtlRouteDone], 1);
-    s_last = (prev == (int)gridDim.x - 1);
+  wait_vmem();  // the logit stores are complete before this expert counts as done
+  if (lane == 0) atomicAdd(&ctl[kCtlRouteDone], 1);
+  const int nsel = min(T, E);
+  if (e >= nsel) return;
+  int spins = 0;
+  while (__hip_atomic_load(&ctl[kCtlRouteDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < E) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > max_spins) {
+      if (lane == 0) atomicOr(&ctl[kCtlError], 1);
+      break;
+    }
   }
-  __syncthreads();
-  if (!s_last) return;
-  for (int t = wave; t < T; t += 4)
-    topk_softmax_wave<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
-  if (threadIdx.x == 0) __hip_atomic_store(&ctl[kCtlRouteDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int t = e; t < T; t += nsel)
+    topk_softmax_any<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
+  if (lane == 0 && atomicAdd(&ctl[kCtlRouteSel], 1) == nsel - 1) {
+    __hip_atomic_store(&ctl[kCtlRouteDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctl[kCtlRouteSel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ------------------------------------------------------------ large T
@@ -307,7 +330,7 @@ __global__ void __launch_bounds__(256) route_tiled_kernel(const uint16_t *__rest
   const int wave = tid / kWave;
   for (int t = wave; t < kTileT; t += 4) {
     const int tg = t_base + t;
-    if (tg < T) topk_softmax_wave<false>(lgs + t * E, E, k, ids + (size_t)tg * k, gates + (size_t)tg * k);
+    if (tg < T) topk_softmax_any<false>(lgs + t * E, E, k, ids + (size_t)tg * k, gates + (size_t)tg * k);
   }
 }
 
@@ -325,13 +348,14 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *w_router, const float
   if (T <= kRouteSmallT) {
     float *lg = logits ? logits : (float *)((char *)ws + kCtlBytes);
     const int L = H / 64;
-    dim3 grid((E + 3) / 4), block(256);
+    const int spins = 1 << 22;
+    dim3 grid(E), block(kWave);
     if (L % 8 == 0)
-      route_small_kernel<8><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl);
+      route_small_kernel<8><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl, spins);
     else if (L % 4 == 0)
-      route_small_kernel<4><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl);
+      route_small_kernel<4><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl, spins);
     else
-      route_small_kernel<2><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl);
+      route_small_kernel<2><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl, spins);
   } else {
     dim3 grid((T + kTileT - 1) / kTileT), block(256);
     route_tiled_kernel<<<grid, block, (size_t)kTileT * E * sizeof(float), st>>>(x, w_router, bias, T, H, E, k, ids,
