@@ -17,13 +17,13 @@ constexpr int kWave = 64;
 constexpr int kGroup = 128;  // quantisation group along K
 
 // Control block at the start of every workspace (int32 words).
-//   [0]      route: blocks finished (last-block top-k)
-//   [1]      ffn decode: blocks finished
-//   [2]      sticky error flags (bit 0: a bounded wait timed out)
-//   [32]     route: selector blocks finished
-//   [64..]   ffn decode: per-active-expert completion counters, kCtrStride apart
+//   [2]          sticky error flags (bit 0: a bounded wait timed out)
+//   route workspace:
+//   [32]         selector blocks finished
+//   [128 + 32 i] experts finished, i < 16 (one counter per 128-byte line)
+//   expert-FFN workspace:
+//   [64 ..]      per-active-expert counters, kCtrStride apart
 constexpr int kCtlRouteDone = 0;
-constexpr int kCtlFfnDone = 1;
 constexpr int kCtlError = 2;
 constexpr int kCtlRouteSel = 32;
 constexpr int kCtlCounters = 64;

@@ -31,10 +31,11 @@
 // (sc1); the block waits for them to complete (vmcnt(0)) and then bumps the
 // expert's counter with a device-scope atomic; a phase-2 block polls the
 // counter and reads h with device-coherent loads.  Counters sit on separate
-// 128-byte lines.  The grid never exceeds the co-resident block count and a
-// block finishes all of its phase-1 items before its first phase-2 item, so
-// every wait ends; the waits are bounded anyway and a timeout only raises an
-// error flag.
+// 128-byte lines, and the last phase-2 item of an expert re-zeroes them (no
+// kernel-wide counter: same-address atomics from every block serialise).  The
+// grid never exceeds the co-resident block count and a block finishes all of
+// its phase-1 items before its first phase-2 item, so every wait ends; the
+// waits are bounded anyway and a timeout only raises an error flag.
 #include <mutex>
 #include <type_traits>
 
@@ -69,7 +70,10 @@ struct DecodeParams {
   uint32_t magic;  // 0x43434343 (the bf16 high byte of 128); an argument so that it sits in an SGPR
 };
 
+// Per active slot a: published phase-1 items, and finished phase-2 items
+// (slot Amax + a), each on its own 128-byte line.
 __device__ __forceinline__ int *counter(int *ctl, int a) { return ctl + kCtlCounters + a * kCtrStride; }
+__device__ __forceinline__ int *done2(int *ctl, int amax, int a) { return ctl + kCtlCounters + (amax + a) * kCtrStride; }
 
 // ---------------------------------------------------------------- operands
 // One chunk of natural-order bf16 activations (d: pairs (x0,x1), (x2,x3), ...)
@@ -333,12 +337,9 @@ __device__ __forceinline__ Meta meta(const DecodeParams &p, int a, int nrows) {
   return r;
 }
 
-// Per-expert counter: bits [0, 16) count phase-1 items whose weight loads are
-// issued, bits [16, 32) phase-1 items whose h rows are published.
-constexpr int kIssued = 1, kPublished = 1 << 16;
-__device__ __forceinline__ bool wait_field_geq(int *ctr, int shift, int target, int max_spins) {
+__device__ __forceinline__ bool wait_geq(int *ctr, int target, int max_spins) {
   int spins = 0;
-  while (((__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> shift) & 0xFFFF) < target) {
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     __builtin_amdgcn_s_sleep(1);
     if (++spins > max_spins) return false;
   }
@@ -354,7 +355,6 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v))
 template <int BITS, bool ONE, bool FAST>
 __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int s_last;
   constexpr int RM = ONE ? 1 : kRMax;
   constexpr int GB = kGroupBytes<BITS>;
   // activation chunks per thread loaded ahead of the phase-1 weights
@@ -405,7 +405,6 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         load_chunk<BITS>(xw, o2[0], wgu[0]);
         load_chunk<BITS>(xw, o2[1], wgu[1]);
       }
-      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), kIssued);
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
         stage_rows<BITS, false, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
@@ -452,7 +451,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         lds_barrier();
       }
-      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), kPublished);
+      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), 1);
     } else {
       // ============================================================ phase 2
       const int it = item - n1;
@@ -465,16 +464,11 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const int nch = G2 / kChunkG;
       Chunk<BITS> wd[2];
       if constexpr (FAST) {
-        // The down weights are needed last: request them only once every
-        // phase-1 item of the expert has its loads out, so that they queue
-        // behind the gate/up weights the hand-off waits for.
-        if (threadIdx.x == 0) wait_field_geq(counter(p.ctl, a), 0, per1, p.max_spins);
-        __syncthreads();
         load_chunk<BITS>(xw, o2[0], wd[0]);
         load_chunk<BITS>(xw, o2[1], wd[1]);
       }
       if (threadIdx.x == 0) {
-        if (!wait_field_geq(counter(p.ctl, a), 16, per1, p.max_spins)) atomicOr(&p.ctl[kCtlError], 1);
+        if (!wait_geq(counter(p.ctl, a), per1, p.max_spins)) atomicOr(&p.ctl[kCtlError], 1);
       }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
@@ -515,19 +509,13 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         }
         lds_barrier();  // LDS is rewritten by the next pass
       }
+      // The last phase-2 item of the expert re-zeroes its two counters: every
+      // phase-1 item has published and every phase-2 item has passed its wait.
+      if (threadIdx.x == 0 && atomicAdd(done2(p.ctl, p.Amax, a), 1) == per2 - 1) {
+        __hip_atomic_store(counter(p.ctl, a), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(done2(p.ctl, p.Amax, a), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-  }
-
-  // ---------------------------------------------------------------- counters reset
-  // The last block to finish re-zeroes the counters; every other block has
-  // finished polling before it is counted.
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&p.ctl[kCtlFfnDone], 1) == (int)gridDim.x - 1;
-  __syncthreads();
-  if (s_last) {
-    for (int a = threadIdx.x; a < p.Amax; a += blockDim.x)
-      __hip_atomic_store(counter(p.ctl, a), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) __hip_atomic_store(&p.ctl[kCtlFfnDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -576,7 +564,7 @@ bool decode_layout_ok(int H, int I, int bits) {
 
 size_t ffn_ctl_bytes(int T, int k, int E) {
   const long amax = E < (long)T * k ? E : (long)T * k;
-  size_t b = (size_t)(kCtlCounters + amax * kCtrStride) * 4;
+  size_t b = (size_t)(kCtlCounters + 2 * amax * kCtrStride) * 4;
   if (b < kCtlBytes) b = kCtlBytes;
   return (b + 255) / 256 * 256;
 }

@@ -114,11 +114,13 @@ __device__ __forceinline__ void topk_softmax_any(const float *lg, int E, int k, 
 // ------------------------------------------------------------ small T
 // Grid: E blocks of one wave; block e computes the logits of expert e for
 // every token (lane s = slice s, sequential over its h), then counts itself
-// done.  Blocks 0 .. nsel-1 (nsel = min(T, E)) wait until every expert is
+// done (control words 128, 160, ..., one counter per 128-byte line).  Blocks 0 .. nsel-1 (nsel = min(T, E)) wait until every expert is
 // done and run top-k for tokens b, b + nsel, ...; the last of them to finish
 // re-zeroes the counters.  All E one-wave blocks are co-resident, so the wait
 // ends; it is bounded anyway and a timeout only raises the error flag.
 constexpr int kTB = 4;  // tokens whose activation slices are loaded together
+constexpr int kRouteDoneN = 16;  // done counters, one 128-byte line each
+__device__ __forceinline__ int route_done(int i) { return kCtlRouteDone + 32 * (4 + i); }
 
 // VEC bf16 elements per load: 8 (16 B), 4 (8 B) or 2 (4 B); kept packed.
 template <int VEC>
@@ -198,11 +200,18 @@ __global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restr
     }
   }
   wait_vmem();  // the logit stores are complete before this expert counts as done
-  if (lane == 0) atomicAdd(&ctl[kCtlRouteDone], 1);
+  // Experts count themselves done on kRouteDoneN counters (same-address
+  // atomics from every block would serialise).
+  if (lane == 0) atomicAdd(&ctl[route_done(e % kRouteDoneN)], 1);
   const int nsel = min(T, E);
   if (e >= nsel) return;
   int spins = 0;
-  while (__hip_atomic_load(&ctl[kCtlRouteDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < E) {
+  for (;;) {
+    const int c = (lane < kRouteDoneN)
+                      ? __hip_atomic_load(&ctl[route_done(lane)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : 0;
+    const int done = __builtin_amdgcn_readfirstlane((int)group_sum((float)c, kRouteDoneN));
+    if (done >= E) break;
     __builtin_amdgcn_s_sleep(1);
     if (++spins > max_spins) {
       if (lane == 0) atomicOr(&ctl[kCtlError], 1);
@@ -212,7 +221,8 @@ __global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restr
   for (int t = e; t < T; t += nsel)
     topk_softmax_any<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
   if (lane == 0 && atomicAdd(&ctl[kCtlRouteSel], 1) == nsel - 1) {
-    __hip_atomic_store(&ctl[kCtlRouteDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < kRouteDoneN; ++i)
+      __hip_atomic_store(&ctl[route_done(i)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&ctl[kCtlRouteSel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
