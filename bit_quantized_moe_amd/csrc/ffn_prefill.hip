@@ -14,21 +14,25 @@
 //    M-tile) is derived on the device from the permutation offsets, so the
 //    host launches an upper bound of M-tile slots and surplus blocks exit;
 //  * A rows (gathered activations for G1, contiguous h rows for G2) and the B
-//    tile, dequantised once per block to bf16 (q - z) * s, are staged in LDS
-//    with an XOR swizzle of 16-byte chunks so the MFMA operand reads are
-//    conflict-free;
+//    tile, dequantised once per block to bf16 (q - z) * s, go through two LDS
+//    buffers with an XOR swizzle of 16-byte chunks, so both the staging
+//    writes and the MFMA operand reads are free of bank conflicts;
 //  * 4 waves in a 2 x 2 arrangement each own a 64 x 64 sub-tile computed with
 //    v_mfma_f32_16x16x32_bf16 (float32 accumulation);
-//  * global loads of the next K tile are issued before the MFMAs of the
-//    current one (register staging).
+//  * software pipeline with one barrier per K tile of 64: while the MFMAs
+//    read one buffer, the next tile is dequantised into the other and global
+//    loads run kStages tiles ahead in registers.
 #include "common.cuh"
 #include "internal.h"
 
 namespace bqmoe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kRowBytes = BK * 2;  // one LDS row: 128 bf16 = 16 chunks of 16 B
+constexpr int BM = 128, BN = 128;
+constexpr int BK = 64;                       // K per tile: half a quantisation group
+constexpr int kRowBytes = BK * 2;            // one LDS row: 64 bf16 = 8 chunks of 16 B
+constexpr int kTileBytes = 128 * kRowBytes;  // 16 KiB per operand tile
+constexpr int kStages = 3;                   // K tiles held in registers ahead of LDS
 
 struct GemmParams {
   const uint16_t *a_src;   // G1: x [T, H]; G2: h [T*k, I]
@@ -42,9 +46,13 @@ struct GemmParams {
   const uint8_t *zeros;
   uint16_t *out;           // G1: h; G2: y_perm
   int n_rows_w;            // rows of one expert's weight matrix: 2I (G1) or H (G2)
+  int n_blocks;            // N tiles: I / 64 (G1) or H / BN (G2)
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
+// LDS position of 16-byte chunk `chunk` of tile row `row`.  Eight lanes that
+// read (or write) the same chunk of eight consecutive rows, or eight chunks
+// of one row, touch eight distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
 
 // Find the (expert, M-tile) of M-tile slot `slot`; returns false past the end.
 __device__ bool find_tile(const GemmParams &p, int slot, int *e_out, int *m0_out, int *n_e_out) {
@@ -95,110 +103,135 @@ __device__ bool find_tile(const GemmParams &p, int slot, int *e_out, int *m0_out
 
 template <int BITS, bool GATEUP>
 __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[BN * kRowBytes];
+  // two LDS buffers, each an A tile then a B tile (BM and BN rows of BK bf16)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kTileBytes];
+  // Blocks are dealt to the 8 XCDs round-robin; the n_blocks N tiles of one
+  // M tile go to consecutive blocks of the same XCD, so the A tile is read
+  // into that XCD's L2 once and reused by all of them.
+  const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int nb = local % p.n_blocks;
+  const int mslot = (local / p.n_blocks) * 8 + xcd;
   int e, m0, rows;
-  if (!find_tile(p, blockIdx.x, &e, &m0, &rows)) return;
+  if (!find_tile(p, mslot, &e, &m0, &rows)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;
-  const int nb = blockIdx.y;
 
-  // ---- this thread's global sources
-  // A: tile row ra = tid / 2, K half (tid % 2) * 64 .. +64 (8 chunks of 8 bf16)
-  const int ra = tid / 2, ha = tid % 2;
-  const uint16_t *a_row = nullptr;
-  if (ra < rows) {
-    const int q = m0 + ra;
-    const size_t src_row = GATEUP ? (size_t)min(max(p.sorted_rows[q], 0) / p.k, p.T - 1) : (size_t)q;
-    a_row = p.a_src + src_row * p.K + ha * 64;
-  }
-  // B: tile column cb = tid / 2 (a weight row), K half (tid % 2) * 64 .. +64
-  const int cb = tid / 2, hb = tid % 2;
-  int wrow;
-  if (GATEUP) {
-    const int wn_b = cb / 64, cc = cb % 64;
-    const int i = nb * 64 + wn_b * 32 + (cc % 32);
-    wrow = (cc < 32) ? i : p.I + i;
-  } else {
-    wrow = nb * BN + cb;
-  }
-  constexpr int WPH = 64 * BITS / 32;  // words per half row of the K tile: 8 (INT4) or 4 (INT2)
-  const size_t wrow_g = (size_t)e * p.n_rows_w + wrow;
-  const uint32_t *b_row = p.codes + wrow_g * (p.K * BITS / 32) + hb * WPH;
-  const uint16_t *s_row = p.scales + wrow_g * (p.K / kGroup);
-  const uint8_t *z_row = (BITS == 2) ? p.zeros + wrow_g * (p.K / kGroup) : nullptr;
-
-  u32x4 a_reg[8];
-  u32x4 b_reg[WPH / 4];
-  float s_reg = 0.f, z_reg = 0.f;
-  auto load_global = [&](int kt) {
-    if (a_row) {
+  // ---- staging map.  A: thread -> rows (tid >> 3) + 32 j (j < 4), chunk tid & 7.
+  constexpr int WPT = BK * BITS / 32;         // code words per tile row: 8 (INT4) or 4 (INT2)
+  constexpr int TPR = WPT;                    // threads per B row (one word each)
+  constexpr int NBR = 128 / (256 / TPR);      // B rows per thread: 4 (INT4) or 2 (INT2)
+  const int ar = tid >> 3, ac = tid & 7;
+  // Element offset of the thread's A chunk in a_src.  Rows past the tile read
+  // the tile's last row instead: every load is unconditional (branches around
+  // loads defeat the compiler's load counting), and those rows only feed C
+  // rows that the epilogue never stores.
+  int a_off[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a_reg[c] = *(const u32x4 *)(a_row + kt * BK + c * 8);
+  for (int j = 0; j < 4; ++j) {
+    const int q = m0 + min(ar + 32 * j, rows - 1);
+    const int src = GATEUP ? min(max(p.sorted_rows[q], 0) / p.k, p.T - 1) : q;
+    a_off[j] = src * p.K + ac * 8;
+  }
+  // B: thread -> weight rows (tid / TPR) + (256 / TPR) j (j < NBR), word tid % TPR
+  const int br0 = tid / TPR, bw = tid % TPR;
+  uint32_t b_off[NBR], s_off[NBR];            // word offset in the codes, element offset in the scales
+#pragma unroll
+  for (int j = 0; j < NBR; ++j) {
+    const int cb = br0 + (256 / TPR) * j;
+    int wrow;
+    if (GATEUP) {  // wave column wn gets 32 gate rows then the 32 matching up rows
+      const int wn_b = cb / 64, cc = cb % 64;
+      const int i = nb * 64 + wn_b * 32 + (cc % 32);
+      wrow = (cc < 32) ? i : p.I + i;
     } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) a_reg[c] = u32x4{0u, 0u, 0u, 0u};
+      wrow = nb * BN + cb;
     }
+    const uint32_t wrow_g = (uint32_t)e * p.n_rows_w + wrow;
+    b_off[j] = wrow_g * (uint32_t)(p.K * BITS / 32) + bw;
+    s_off[j] = wrow_g * (uint32_t)(p.K / kGroup);
+  }
+
+  // ---- register stages
+  u32x4 a_st[kStages][4];
+  uint32_t b_st[kStages][NBR];
+  uint32_t sc_st[kStages][NBR], z_st[kStages][NBR];  // raw bf16 scale / zero-point (no math on a load in flight)
+  auto load_tile = [&](int kt, int s) {
 #pragma unroll
-    for (int c = 0; c < WPH / 4; ++c) b_reg[c] = *(const u32x4 *)(b_row + (size_t)kt * (BK * BITS / 32) + c * 4);
-    s_reg = bf16_to_f32(s_row[kt]);
-    z_reg = (BITS == 4) ? 8.f : (float)z_row[kt];
+    for (int j = 0; j < 4; ++j) a_st[s][j] = *(const u32x4 *)(p.a_src + a_off[j] + kt * BK);
+#pragma unroll
+    for (int j = 0; j < NBR; ++j) {
+      b_st[s][j] = p.codes[b_off[j] + kt * WPT];
+      sc_st[s][j] = p.scales[s_off[j] + kt / 2];
+      if constexpr (BITS == 2) z_st[s][j] = p.zeros[s_off[j] + kt / 2];
+    }
   };
-  auto store_lds = [&]() {
+  auto store_tile = [&](int s, uint8_t *buf) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) *(u32x4 *)(lds_a + swz(ra, ha * 8 + c)) = a_reg[c];
-    const float zs = -z_reg * s_reg;
-    if constexpr (BITS == 4) {
+    for (int j = 0; j < 4; ++j) *(u32x4 *)(buf + swz(ar + 32 * j, ac)) = a_st[s][j];
+    uint8_t *bb = buf + kTileBytes;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t o[4];
-          dequant8_int4(b_reg[c][j], s_reg, zs, o);
-          *(u32x4 *)(lds_b + swz(cb, hb * 8 + c * 4 + j)) = u32x4{o[0], o[1], o[2], o[3]};
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NBR; ++j) {
+      const int cb = br0 + (256 / TPR) * j;
+      const float sc = bf16_to_f32(sc_st[s][j]);
+      const float zs = -((BITS == 4) ? 8.f : (float)z_st[s][j]) * sc;
+      if constexpr (BITS == 4) {
+        uint32_t o[4];
+        dequant8_int4(b_st[s][j], sc, zs, o);
+        *(u32x4 *)(bb + swz(cb, bw)) = u32x4{o[0], o[1], o[2], o[3]};
+      } else {
         uint32_t o[8];
-        dequant16_int2(b_reg[0][j], s_reg, zs, o);
-        *(u32x4 *)(lds_b + swz(cb, hb * 8 + 2 * j)) = u32x4{o[0], o[1], o[2], o[3]};
-        *(u32x4 *)(lds_b + swz(cb, hb * 8 + 2 * j + 1)) = u32x4{o[4], o[5], o[6], o[7]};
+        dequant16_int2(b_st[s][j], sc, zs, o);
+        *(u32x4 *)(bb + swz(cb, 2 * bw)) = u32x4{o[0], o[1], o[2], o[3]};
+        *(u32x4 *)(bb + swz(cb, 2 * bw + 1)) = u32x4{o[4], o[5], o[6], o[7]};
       }
     }
   };
-
   f32x4 acc[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // ---- pipeline: one barrier per K tile.  While the MFMAs read buffer kt & 1,
+  // tile kt + 1 is dequantised into the other buffer and tile kt + 1 + kStages
+  // is requested from global memory.  Tile t lives in register stage
+  // t % kStages; the K loop is unrolled by kStages so that every stage index
+  // is a constant (a register copy between stages would wait for its load).
   const int nk = p.K / BK;
-  load_global(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    store_lds();
-    __syncthreads();
-    if (kt + 1 < nk) load_global(kt + 1);
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int ch = kk * 4 + lane / 16;
-      bf16x8 af[4], bfr[4];
+  for (int s = 0; s < kStages; ++s) load_tile(min(s, nk - 1), s);
+  store_tile(0, lds[0]);
+  load_tile(min(kStages, nk - 1), 0);
+  __syncthreads();
+  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *(const bf16x8 *)(lds_a + swz(wm * 64 + mi * 16 + lane % 16, ch));
+    for (int d = 0; d < kStages; ++d) {
+      const int kt = kt0 + d;
+      if (kt >= nk) break;
+      const uint8_t *ba = lds[kt & 1], *bb = lds[kt & 1] + kTileBytes;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bfr[ni] = *(const bf16x8 *)(lds_b + swz(wn * 64 + ni * 16 + lane % 16, ch));
+      for (int kk = 0; kk < BK / 32; ++kk) {
+        const int ch = kk * 4 + lane / 16;
+        bf16x8 af[4], bfr[4];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 4; ++mi) af[mi] = *(const bf16x8 *)(ba + swz(wm * 64 + mi * 16 + lane % 16, ch));
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < 4; ++ni) bfr[ni] = *(const bf16x8 *)(bb + swz(wn * 64 + ni * 16 + lane % 16, ch));
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      }
+      const int sn = (d + 1) % kStages;  // stage of tile kt + 1 (a constant once unrolled)
+      // Past the end the last tile is stored and loaded again: harmless, and
+      // it keeps the loop free of branches around memory operations.
+      store_tile(sn, lds[(kt + 1) & 1]);
+      load_tile(min(kt + 1 + kStages, nk - 1), sn);
+      __syncthreads();
     }
   }
 
@@ -233,7 +266,8 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
 hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t st) {
   const int nrows = a.T * a.k;
   const int Amax = a.E < nrows ? a.E : nrows;
-  const long slots = ((long)nrows + (long)Amax * (BM - 1)) / BM;
+  long slots = ((long)nrows + (long)Amax * (BM - 1)) / BM;
+  slots = (slots + 7) / 8 * 8;  // whole rounds of the 8 XCDs
   uint16_t *hbuf = (uint16_t *)((char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E));
 
   GemmParams g1;
@@ -262,7 +296,9 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   g2.out = a.y_perm;
   g2.n_rows_w = a.H;
 
-  dim3 grid1((unsigned)slots, a.I / 64), grid2((unsigned)slots, a.H / BN);
+  g1.n_blocks = a.I / 64;
+  g2.n_blocks = a.H / BN;
+  dim3 grid1((unsigned)(slots * g1.n_blocks)), grid2((unsigned)(slots * g2.n_blocks));
   if (a.bits == 4) {
     ffn_gemm_kernel<4, true><<<grid1, 256, 0, st>>>(g1);
     ffn_gemm_kernel<4, false><<<grid2, 256, 0, st>>>(g2);
