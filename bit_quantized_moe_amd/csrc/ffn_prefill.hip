@@ -201,6 +201,9 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   // t % kStages; the K loop is unrolled by kStages so that every stage index
   // is a constant (a register copy between stages would wait for its load).
   const int nk = p.K / BK;
+  // Rows of this wave's half of the tile that hold data: 16-row MFMA blocks
+  // past them are skipped (an expert's last tile is often mostly empty).
+  const int mvalid = __builtin_amdgcn_readfirstlane(rows - wm * 64);
 #pragma unroll
   for (int s = 0; s < kStages; ++s) load_tile(min(s, nk - 1), s);
   store_tile(0, lds[0]);
@@ -217,14 +220,17 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
         const int ch = kk * 4 + lane / 16;
         bf16x8 af[4], bfr[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) af[mi] = *(const bf16x8 *)(ba + swz(wm * 64 + mi * 16 + lane % 16, ch));
+        for (int mi = 0; mi < 4; ++mi)
+          if (mi * 16 < mvalid) af[mi] = *(const bf16x8 *)(ba + swz(wm * 64 + mi * 16 + lane % 16, ch));
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) bfr[ni] = *(const bf16x8 *)(bb + swz(wn * 64 + ni * 16 + lane % 16, ch));
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
+          if (mi * 16 < mvalid) {
 #pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+            for (int ni = 0; ni < 4; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          }
       }
       const int sn = (d + 1) % kStages;  // stage of tile kt + 1 (a constant once unrolled)
       // Past the end the last tile is stored and loaded again: harmless, and
