@@ -158,7 +158,7 @@ class Plan:
         print(f"[bench] {sp.n_sets} weight set(s) generated and uploaded in {time.time() - t0:.1f} s", flush=True)
         self.y_perm = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        self.ws_route = torch.zeros(self.L.moe_route_workspace_size(T, E), dtype=torch.uint8, device=dev)
+        self.ws_route = torch.zeros(self.L.moe_route_permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.zeros(self.L.moe_expert_ffn_workspace_size(T, k, E, H, I), dtype=torch.uint8, device=dev)
         self.torch = torch
 
@@ -169,12 +169,11 @@ class Plan:
     def route_permute(self, i):
         sp, st, L = self.sp, self.sets[i], self.L
         stream = self.torch.cuda.current_stream(self.dev).cuda_stream
-        self._chk(L.moe_route(st["x"].data_ptr(), self.w_r.data_ptr(), self.bias.data_ptr() if self.bias is not None else None,
-                              sp.T, sp.H, sp.E, sp.k, st["ids"].data_ptr(), st["gates"].data_ptr(), None,
-                              self.ws_route.data_ptr(), self.ws_route.numel(), stream), "moe_route")
-        self._chk(L.moe_permute(st["ids"].data_ptr(), sp.T, sp.k, sp.E, st["offsets"].data_ptr(),
-                                st["sorted_rows"].data_ptr(), st["row_pos"].data_ptr(), st["active"].data_ptr(),
-                                None, 0, stream), "moe_permute")
+        self._chk(L.moe_route_permute(st["x"].data_ptr(), self.w_r.data_ptr(),
+                                      self.bias.data_ptr() if self.bias is not None else None, sp.T, sp.H, sp.E, sp.k,
+                                      st["ids"].data_ptr(), st["gates"].data_ptr(), None, st["offsets"].data_ptr(),
+                                      st["sorted_rows"].data_ptr(), st["row_pos"].data_ptr(), st["active"].data_ptr(),
+                                      self.ws_route.data_ptr(), self.ws_route.numel(), stream), "moe_route_permute")
 
     def ffn(self, i):
         sp, st, L = self.sp, self.sets[i], self.L

@@ -19,7 +19,7 @@ from typing import Dict, Optional
 import torch
 
 __all__ = [
-    "MoEError", "lib", "route", "permute", "expert_ffn", "combine", "unpack_codes",
+    "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "combine", "unpack_codes",
     "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH",
 ]
 
@@ -35,6 +35,8 @@ _SIGS = {
     "moe_route": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_permute_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_permute": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "moe_route_permute_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
+    "moe_route_permute": (_c_int, [_vp, _vp, _vp] + [_c_int] * 4 + [_vp] * 7 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_workspace_size": (_c_size, [_c_int] * 5),
     "moe_expert_ffn_w4a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 5 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 7 + [_vp, _c_size, _vp]),
@@ -142,6 +144,34 @@ def permute(ids: torch.Tensor, E: int, ws: Optional[Workspaces] = None):
     return offsets, sorted_rows, row_pos, active
 
 
+def route_permute(x: torch.Tensor, w_router: torch.Tensor, k: int, logit_bias: Optional[torch.Tensor] = None,
+                  want_logits: bool = False, ws: Optional[Workspaces] = None) -> Dict[str, torch.Tensor]:
+    """route() then permute() in one library call (one launch for small batches).
+
+    Returns ids, gates, offsets, sorted_rows, row_pos, active (and logits)."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = w_router.shape[0]
+    n = T * k
+    out = dict(
+        ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+        gates=torch.empty((T, k), dtype=torch.float32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        sorted_rows=torch.empty(n, dtype=torch.int32, device=dev),
+        row_pos=torch.empty(n, dtype=torch.int32, device=dev),
+        active=torch.empty(1 + min(E, n), dtype=torch.int32, device=dev),
+    )
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    L = lib()
+    w = (ws or Workspaces(dev)).get("route", L.moe_route_permute_workspace_size(T, k, E))
+    _check(L.moe_route_permute(_p(x), _p(w_router), _p(logit_bias), T, H, E, k, _p(out["ids"]), _p(out["gates"]),
+                               _p(logits), _p(out["offsets"]), _p(out["sorted_rows"]), _p(out["row_pos"]),
+                               _p(out["active"]), _p(w), w.numel(), _stream(dev)), "moe_route_permute")
+    if want_logits:
+        out["logits"] = logits
+    return out
+
+
 def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: Dict[str, torch.Tensor], bits: int,
                I: int, ws: Optional[Workspaces] = None, y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-expert gate_up -> SwiGLU -> down on the sorted rows; bf16 [T*k, H]."""
@@ -202,16 +232,10 @@ def dequant_bf16(words: torch.Tensor, scales: torch.Tensor, zeros: Optional[torc
 def moe_layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
               weights: Dict[str, torch.Tensor], k: int, bits: int, I: int, ws: Optional[Workspaces] = None,
               want_logits: bool = False) -> Dict[str, torch.Tensor]:
-    """The whole layer through the four library calls; returns every intermediate."""
+    """The whole layer: moe_route_permute, the expert FFN and moe_combine; returns every intermediate."""
     ws = ws or Workspaces(x.device)
-    E = w_router.shape[0]
-    r = route(x, w_router, k, logit_bias, want_logits=want_logits, ws=ws)
-    ids, gates = r[0], r[1]
-    offsets, sorted_rows, row_pos, active = permute(ids, E, ws=ws)
-    y_perm = expert_ffn(x, offsets, sorted_rows, active, k, weights, bits, I, ws=ws)
-    y = combine(y_perm, row_pos, gates)
-    out = dict(ids=ids, gates=gates, offsets=offsets, sorted_rows=sorted_rows, row_pos=row_pos, active=active,
-               y_perm=y_perm, y=y)
-    if want_logits:
-        out["logits"] = r[2]
+    out = route_permute(x, w_router, k, logit_bias, want_logits=want_logits, ws=ws)
+    y_perm = expert_ffn(x, out["offsets"], out["sorted_rows"], out["active"], k, weights, bits, I, ws=ws)
+    out["y_perm"] = y_perm
+    out["y"] = combine(y_perm, out["row_pos"], out["gates"])
     return out

@@ -147,6 +147,43 @@ moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *ex
                   "moe_permute launch");
 }
 
+size_t moe_route_permute_workspace_size(int T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  const size_t r = moe_route_workspace_size(T, E), p = round_up(permute_workspace_bytes(T, k, E), 256);
+  return r > p ? r : p;
+}
+
+moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H,
+                             int E, int k, int32_t *topk_ids, float *topk_weights, float *logits,
+                             int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos, int32_t *active,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status s = check_common_moe(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (!x || !w_router || !topk_ids || !topk_weights || !workspace || !expert_offsets || !sorted_rows || !row_pos ||
+      !active)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: a required pointer is NULL");
+  if (!aligned(x, 16) || !aligned(w_router, 16))
+    return fail(MOE_ERR_MISALIGNED, "moe_route_permute: x and w_router need 16-byte alignment");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "moe_route_permute: workspace needs 256-byte alignment");
+  if (!aligned(topk_ids, 4) || !aligned(topk_weights, 4) || (logits && !aligned(logits, 4)) ||
+      (logit_bias && !aligned(logit_bias, 4)) || !aligned(expert_offsets, 4) || !aligned(sorted_rows, 4) ||
+      !aligned(row_pos, 4) || !aligned(active, 4))
+    return fail(MOE_ERR_MISALIGNED, "moe_route_permute: 4-byte arrays must be 4-byte aligned");
+  const size_t need = moe_route_permute_workspace_size(T, k, E);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_route_permute: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (T == 0) return MOE_OK;
+  const hipStream_t st = (hipStream_t)stream;
+  if (route_groups_rows(T, k))
+    return from_hip(launch_route_group(x, w_router, logit_bias, T, H, E, k, topk_ids, topk_weights, logits,
+                                       expert_offsets, sorted_rows, row_pos, active, workspace, st),
+                    "moe_route_permute launch");
+  hipError_t e = launch_route(x, w_router, logit_bias, T, H, E, k, topk_ids, topk_weights, logits, workspace, st);
+  if (e != hipSuccess) return from_hip(e, "moe_route_permute: route launch");
+  return from_hip(launch_permute(topk_ids, T, k, E, expert_offsets, sorted_rows, row_pos, active, workspace, st),
+                  "moe_route_permute: permute launch");
+}
+
 size_t moe_expert_ffn_workspace_size(int T, int k, int E, int H, int I) {
   if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return 0;
   return ffn_workspace_bytes(T, k, E, H, I);

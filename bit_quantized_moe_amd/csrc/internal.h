@@ -21,6 +21,12 @@ constexpr int kRouteSmallT = 32;  // T at or below: split-expert kernel + last-b
 size_t route_workspace_bytes(int T, int E);
 hipError_t launch_route(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
                         int k, int32_t *ids, float *gates, float *logits, void *ws, hipStream_t st);
+// Router launch that also groups the rows by expert (the outputs of
+// launch_permute), for shapes where route_groups_rows(T, k) holds.
+bool route_groups_rows(int T, int k);
+hipError_t launch_route_group(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
+                              int k, int32_t *ids, float *gates, float *logits, int32_t *offsets,
+                              int32_t *sorted_rows, int32_t *row_pos, int32_t *active, void *ws, hipStream_t st);
 
 // permute.hip
 size_t permute_workspace_bytes(int T, int k, int E);

@@ -54,8 +54,10 @@ __device__ __forceinline__ void wave_key_max(uint32_t &hi, uint32_t &lo) {
 // gates.  NV = values per lane (E <= 64 * NV).  COHERENT: lg is global memory
 // written by other blocks of this kernel, read with device-coherent loads;
 // otherwise lg is LDS or ordinary memory.
-template <int NV, bool COHERENT>
-__device__ void topk_softmax_wave(const float *lg, int E, int k, int32_t *ids_out, float *g_out) {
+// PUBLISH: ids are stored with device-coherent stores (read back by another
+// block).  key_lds, when given, receives a copy of the ids.
+template <int NV, bool COHERENT, bool PUBLISH>
+__device__ void topk_softmax_wave(const float *lg, int E, int k, int32_t *ids_out, float *g_out, int *key_lds) {
   const int lane = lane_id();
   uint32_t key[NV];
 #pragma unroll
@@ -92,23 +94,111 @@ __device__ void topk_softmax_wave(const float *lg, int E, int k, int32_t *ids_ou
   const float ex = (lane < k) ? expf(mine - m) : 0.f;
   const float sum = group_sum(ex, kWave);
   if (lane < k) {
-    ids_out[lane] = my_e;
+    if constexpr (PUBLISH)
+      __hip_atomic_store(ids_out + lane, my_e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      ids_out[lane] = my_e;
     g_out[lane] = ex / sum;
+    if (key_lds) key_lds[lane] = my_e;
   }
 }
 
-template <bool COHERENT>
-__device__ __forceinline__ void topk_softmax_any(const float *lg, int E, int k, int32_t *ids_out, float *g_out) {
+template <bool COHERENT, bool PUBLISH = false>
+__device__ __forceinline__ void topk_softmax_any(const float *lg, int E, int k, int32_t *ids_out, float *g_out,
+                                                 int *key_lds = nullptr) {
   if (E <= 64)
-    topk_softmax_wave<1, COHERENT>(lg, E, k, ids_out, g_out);
+    topk_softmax_wave<1, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
   else if (E <= 128)
-    topk_softmax_wave<2, COHERENT>(lg, E, k, ids_out, g_out);
+    topk_softmax_wave<2, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
   else if (E <= 256)
-    topk_softmax_wave<4, COHERENT>(lg, E, k, ids_out, g_out);
+    topk_softmax_wave<4, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
   else if (E <= 512)
-    topk_softmax_wave<8, COHERENT>(lg, E, k, ids_out, g_out);
+    topk_softmax_wave<8, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
   else
-    topk_softmax_wave<16, COHERENT>(lg, E, k, ids_out, g_out);
+    topk_softmax_wave<16, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
+}
+
+// ------------------------------------------------------------ grouping by expert
+// The stable grouping of n rows by expert (the result of moe_permute), done by
+// one wave in LDS: a histogram, one exclusive scan for the offsets and the
+// active list, then placement of the rows 64 at a time in row order.  Within a
+// batch of 64, lanes with the same key find each other by bit-plane ballots,
+// so a lane's rank among them is the number of lower lanes with its key.
+// key[r] is the expert of row r, or E for a dropped row; cur holds E ints.
+constexpr int kFusedRows = 256;  // largest T*k grouped inside the router launch
+
+__device__ int wave_exclusive_scan(int v, int *total) {
+  const int lane = lane_id();
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  *total = __shfl(inc, kWave - 1, kWave);
+  return inc - v;
+}
+
+__device__ void wave_group_rows(const int *key, int n, int E, int *cur, int32_t *offsets, int32_t *sorted_rows,
+                                int32_t *row_pos, int32_t *active, int n_active_slots) {
+  const int lane = lane_id();
+  for (int e = lane; e < E; e += kWave) cur[e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int r = lane; r < n; r += kWave) {
+    const int kk = key[r];
+    if (kk < E) atomicAdd(&cur[kk], 1);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane owns the experts [e0, e1)
+  const int seg = (E + kWave - 1) / kWave;
+  const int e0 = min(E, lane * seg), e1 = min(E, e0 + seg);
+  int rows = 0, acts = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = cur[e];
+    rows += c;
+    acts += c > 0;
+  }
+  int n_valid = 0, n_act = 0;
+  int base = wave_exclusive_scan(rows, &n_valid);
+  int abase = wave_exclusive_scan(acts, &n_act);
+  __builtin_amdgcn_wave_barrier();
+  for (int e = e0; e < e1; ++e) {
+    const int c = cur[e];
+    offsets[e] = base;
+    cur[e] = base;
+    if (c > 0) active[1 + abase++] = e;
+    base += c;
+  }
+  if (lane == 0) {
+    offsets[E] = n_valid;
+    active[0] = n_act;
+  }
+  for (int i = 1 + n_act + lane; i < n_active_slots; i += kWave) active[i] = -1;
+  __builtin_amdgcn_wave_barrier();
+  int nbits = 1;
+  while ((1 << nbits) < E + 2) ++nbits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int rb = 0; rb < n; rb += kWave) {
+    const int r = rb + lane;
+    const int kk = (r < n) ? key[r] : E + 1;  // E + 1: lanes past the last row
+    uint64_t peers = __ballot(1);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot((kk >> b) & 1);
+      peers &= ((kk >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    if (kk < E) {
+      const int pos = cur[kk] + rank;
+      sorted_rows[pos] = r;
+      row_pos[r] = pos;
+    } else if (kk == E) {
+      row_pos[r] = -1;
+    }
+    // every lane has read its cursor before the first lane of each key moves it
+    __builtin_amdgcn_wave_barrier();
+    if (rank == 0 && kk < E) cur[kk] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 // ------------------------------------------------------------ small T
@@ -153,11 +243,18 @@ __device__ __forceinline__ float fma_vec(const Vec<VEC> &xv, const Vec<VEC> &wv,
   return acc;
 }
 
-template <int VEC>
+// Outputs of the grouping by expert, when the router launch also groups the
+// rows (T*k <= kFusedRows).
+struct GroupOut {
+  int32_t *offsets, *sorted_rows, *row_pos, *active;
+  int n_active_slots;
+};
+
+template <int VEC, bool GROUP>
 __global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ w, const float *bias, int T,
                                                          int H, int E, int k, int32_t *ids, float *gates, float *lg,
-                                                         int *ctl, int max_spins) {
+                                                         int *ctl, int max_spins, GroupOut go) {
   constexpr int NVC = 64 / VEC;  // loads per 64-element chunk of a slice
   const int lane = lane_id();
   const int e = blockIdx.x;
@@ -218,12 +315,43 @@ __global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restr
       break;
     }
   }
-  for (int t = e; t < T; t += nsel)
-    topk_softmax_any<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
-  if (lane == 0 && atomicAdd(&ctl[kCtlRouteSel], 1) == nsel - 1) {
+  extern __shared__ int group_lds[];  // GROUP: key[kFusedRows], then cur[E]
+  int *key = group_lds, *cur = group_lds + kFusedRows;
+  if constexpr (!GROUP) {
+    for (int t = e; t < T; t += nsel)
+      topk_softmax_any<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
+  } else {
+    // One selector keeps every token's ids in LDS; several publish them for
+    // the last one to read back.
+    if (nsel == 1) {
+      for (int t = 0; t < T; ++t)
+        topk_softmax_any<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, key + t * k);
+    } else {
+      for (int t = e; t < T; t += nsel)
+        topk_softmax_any<true, true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
+      wait_vmem();  // the ids are stored before this selector counts itself done
+    }
+  }
+  int last = 1;
+  if (nsel > 1) {
+    last = 0;
+    if (lane == 0) last = atomicAdd(&ctl[kCtlRouteSel], 1) == nsel - 1;
+    last = __builtin_amdgcn_readfirstlane(last);
+  }
+  if (!last) return;
+  if (lane == 0) {
     for (int i = 0; i < kRouteDoneN; ++i)
       __hip_atomic_store(&ctl[route_done(i)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&ctl[kCtlRouteSel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if constexpr (GROUP) {
+    const int n = T * k;
+    if (nsel > 1) {
+      for (int r = lane; r < n; r += kWave)
+        key[r] = __hip_atomic_load(ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_wave_barrier();
+    }
+    wave_group_rows(key, n, E, cur, go.offsets, go.sorted_rows, go.row_pos, go.active, go.n_active_slots);
   }
 }
 
@@ -352,20 +480,42 @@ size_t route_workspace_bytes(int T, int E) {
   return b;
 }
 
+template <bool GROUP>
+static void launch_route_small(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
+                               int k, int32_t *ids, float *gates, float *logits, void *ws, const GroupOut &go,
+                               hipStream_t st) {
+  int *ctl = (int *)ws;
+  float *lg = logits ? logits : (float *)((char *)ws + kCtlBytes);
+  const int L = H / 64;
+  const int spins = 1 << 22;
+  dim3 grid(E), block(kWave);
+  const size_t lds = GROUP ? (size_t)(kFusedRows + E) * sizeof(int) : 0;
+  if (L % 8 == 0)
+    route_small_kernel<8, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl,
+                                                           spins, go);
+  else if (L % 4 == 0)
+    route_small_kernel<4, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl,
+                                                           spins, go);
+  else
+    route_small_kernel<2, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl,
+                                                           spins, go);
+}
+
+bool route_groups_rows(int T, int k) { return T <= kRouteSmallT && T * k <= kFusedRows; }
+
+hipError_t launch_route_group(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
+                              int k, int32_t *ids, float *gates, float *logits, int32_t *offsets,
+                              int32_t *sorted_rows, int32_t *row_pos, int32_t *active, void *ws, hipStream_t st) {
+  const int n = T * k;
+  const GroupOut go{offsets, sorted_rows, row_pos, active, 1 + (E < n ? E : n)};
+  launch_route_small<true>(x, w_router, bias, T, H, E, k, ids, gates, logits, ws, go, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
                         int k, int32_t *ids, float *gates, float *logits, void *ws, hipStream_t st) {
-  int *ctl = (int *)ws;
   if (T <= kRouteSmallT) {
-    float *lg = logits ? logits : (float *)((char *)ws + kCtlBytes);
-    const int L = H / 64;
-    const int spins = 1 << 22;
-    dim3 grid(E), block(kWave);
-    if (L % 8 == 0)
-      route_small_kernel<8><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl, spins);
-    else if (L % 4 == 0)
-      route_small_kernel<4><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl, spins);
-    else
-      route_small_kernel<2><<<grid, block, 0, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl, spins);
+    launch_route_small<false>(x, w_router, bias, T, H, E, k, ids, gates, logits, ws, GroupOut{}, st);
   } else {
     dim3 grid((T + kTileT - 1) / kTileT), block(256);
     route_tiled_kernel<<<grid, block, (size_t)kTileT * E * sizeof(float), st>>>(x, w_router, bias, T, H, E, k, ids,

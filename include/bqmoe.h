@@ -120,6 +120,23 @@ moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E,
                        int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
                        int32_t *active, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- route + permutation
+ * moe_route_permute: moe_route, then moe_permute on its topk_ids, with the
+ * outputs of both bit for bit (same arguments, same meaning).  For T <= 32
+ * and T*k <= 256 both steps run in one launch: the block that finishes the
+ * top-k last groups the rows by expert in LDS, which saves a launch on the
+ * decode path.  Other shapes run the two launches in order.  topk_ids are
+ * always valid expert ids here, so row_pos has no -1 entries.
+ * The workspace (moe_route_permute_workspace_size bytes, 256-byte aligned)
+ * starts with the router's control block; the library leaves it zeroed.
+ */
+size_t moe_route_permute_workspace_size(int T, int k, int E);
+moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
+                             int T, int H, int E, int k,
+                             int32_t *topk_ids, float *topk_weights, float *logits,
+                             int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
+                             int32_t *active, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------- expert FFN
  * moe_expert_ffn_w4a16: for every active expert e and each of its rows
  * (sorted positions p in [expert_offsets[e], expert_offsets[e+1]), token

@@ -76,6 +76,28 @@ def test_permute_argument_errors():
     assert f(T=0) == OK
 
 
+def test_route_permute_argument_errors():
+    L = bq.lib()
+
+    def f(T=4, H=256, E=8, k=2, x=A, ids=A, off=A, act=A, ws=A, wsb=1 << 20):
+        return L.moe_route_permute(x, A, None, T, H, E, k, ids, A, None, off, A, A, act, ws, wsb, None)
+    assert f(T=-1) == INVALID
+    assert f(k=9) == INVALID                      # k > E
+    assert f(E=2000) == SHAPE
+    assert f(H=200) == SHAPE
+    assert f(x=None) == INVALID
+    assert f(off=None) == INVALID                 # the permutation outputs are required
+    assert f(act=A + 2) == MISALIGNED
+    assert f(ws=A + 128) == MISALIGNED
+    assert f(wsb=16) == WS_SMALL
+    assert f(T=0) == OK
+    # the workspace covers both the router's and the grouping's needs
+    for T, k, E in [(1, 8, 256), (16, 8, 256), (4096, 8, 256), (33, 32, 1024)]:
+        need = L.moe_route_permute_workspace_size(T, k, E)
+        assert need % 256 == 0
+        assert need >= L.moe_route_workspace_size(T, E) and need >= L.moe_permute_workspace_size(T, k, E)
+
+
 def _ffn(bits=4, T=2, k=2, E=8, H=256, I=128, x=A, codes=A, ws=A, wsb=1 << 24, zeros=A):
     L = bq.lib()
     if bits == 4:

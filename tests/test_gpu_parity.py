@@ -150,6 +150,37 @@ def test_permute_bit_exact(T, k, E, bad):
     assert np.all(act[1 + len(exp_act):] == -1)
 
 
+@pytest.mark.parametrize("T,H,E,k", [(1, 4096, 256, 8), (16, 4096, 256, 8), (32, 512, 256, 8), (33, 256, 64, 8),
+                                     (3, 256, 1024, 32), (32, 384, 7, 7), (5, 256, 1, 1), (8, 256, 300, 32),
+                                     (2, 4096, 8, 2), (9, 1024, 100, 29)])
+def test_route_permute_matches_route_then_permute(T, H, E, k):
+    """The one-launch router + grouping gives the outputs of moe_route and moe_permute bit for bit."""
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, E=E, k=k, seed=300 + T + E)
+    w_r, _ = workload.make_router(sp)
+    bias = (np.random.default_rng(E).standard_normal(E) * 0.01).astype(np.float32)
+    ws = bq.Workspaces("cuda:0")
+    wd, bd = to_dev(w_r), to_dev(bias)
+    for s in range(3):                                  # reused workspace: the control block is left zeroed
+        x = workload.make_x(sp, s)
+        got = {n: to_np(v) for n, v in bq.route_permute(to_dev(x), wd, k, bd, want_logits=True, ws=ws).items()}
+        ref_l = oracle.router_logits(x, w_r, bias)
+        assert np.array_equal(got["logits"].view(np.uint32), ref_l.view(np.uint32)), "router logits differ"
+        ref_ids, ref_g = oracle.topk_softmax(ref_l, k)
+        assert np.array_equal(got["ids"], ref_ids)
+        assert np.max(np.abs(got["gates"] - ref_g)) <= 1e-6
+        r_off, r_sr, r_rp, r_act = oracle.permute(ref_ids, E)
+        assert np.array_equal(got["offsets"], r_off), "offsets"
+        assert np.array_equal(got["sorted_rows"], r_sr), "sorted_rows"
+        assert np.array_equal(got["row_pos"], r_rp), "row_pos"
+        assert np.array_equal(got["active"][:1 + got["active"][0]], r_act[:1 + r_act[0]]), "active"
+        assert np.all(got["active"][1 + got["active"][0]:] == -1)
+        sep_ids, sep_g = bq.route(to_dev(x), wd, k, bd, ws=ws)
+        sep = [to_np(v) for v in bq.permute(sep_ids, E, ws=ws)]
+        assert np.array_equal(to_np(sep_ids), got["ids"]) and np.array_equal(to_np(sep_g), got["gates"])
+        for a, b in zip(sep, [got["offsets"], got["sorted_rows"], got["row_pos"], got["active"]]):
+            assert np.array_equal(a, b)
+
+
 def test_combine_matches_oracle():
     rng = np.random.default_rng(3)
     T, k, H = 37, 8, 4096
