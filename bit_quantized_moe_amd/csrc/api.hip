@@ -73,7 +73,9 @@ hipError_t current_device_info(DeviceInfo *out) {
 size_t ffn_workspace_bytes(int T, int k, int E, int H, int I) {
   (void)E;
   (void)H;
-  return round_up(ffn_ctl_bytes(T, k, E) + (size_t)T * k * I * sizeof(uint16_t), 256);
+  // h: 32-bit tagged words on the decode path, bf16 on the grouped-GEMM path
+  const size_t h_elem = T <= kDecodeMaxT ? sizeof(uint32_t) : sizeof(uint16_t);
+  return round_up(ffn_ctl_bytes(T, k, E) + (size_t)T * k * I * h_elem, 256);
 }
 
 }  // namespace bqmoe
@@ -218,6 +220,9 @@ static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, cons
             w2_codes, w2_scales, w2_zeros, y_perm, workspace};
   if (T <= kDecodeMaxT && decode_layout_ok(H, I, bits))
     return from_hip(launch_ffn_decode(a, dev, (hipStream_t)stream), name);
+  // the grouped GEMMs address x and one expert's codes with 32-bit byte offsets
+  if ((long long)T * H > (1LL << 30) || (long long)I * H > (1LL << 30))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: T*H and I*H must be <= 2^30 on the grouped-GEMM path (T=%d)", name, T);
   return from_hip(launch_ffn_prefill(a, dev, (hipStream_t)stream), name);
 }
 

@@ -27,12 +27,14 @@
 // (zero = 8 for INT4 offset-binary codes).  The activations are staged in LDS
 // in the K order the unpacked pairs come out in, with their per-group sums.
 //
-// Hand-off without cache flushes: h is written with device-coherent stores
-// (sc1); the block waits for them to complete (vmcnt(0)) and then bumps the
-// expert's counter with a device-scope atomic; a phase-2 block polls the
-// counter and reads h with device-coherent loads.  Counters sit on separate
-// 128-byte lines, and the last phase-2 item of an expert re-zeroes them (no
-// kernel-wide counter: same-address atomics from every block serialise).  The
+// Hand-off without cache flushes or counters on the critical path: phase 1
+// writes each h value as a 32-bit word, the bf16 bits under a nonzero tag, with
+// a device-coherent (sc1) store; a phase-2 block reads h with device-coherent
+// loads and simply reads again until every word it needs carries the tag.
+// Every word is self-validating, so no store has to be waited for and no
+// counter bumped before the data can be used.  The last phase-2 item of an
+// expert (a per-expert done counter on its own 128-byte line) clears the
+// expert's h words, so the buffer is all-zero again when the kernel ends.  The
 // grid never exceeds the co-resident block count and a block finishes all of
 // its phase-1 items before its first phase-2 item, so every wait ends; the
 // waits are bounded anyway and a timeout only raises an error flag.
@@ -64,16 +66,15 @@ struct DecodeParams {
   const uint16_t *w2s;
   const uint8_t *w2z;
   uint16_t *y_perm;
-  uint16_t *hbuf;  // [T*k, I] bf16
+  uint32_t *hbuf;  // [T*k, I] words: kHReady | bf16 bits once written, 0 before
   int *ctl;
   int max_spins;
   uint32_t magic;  // 0x43434343 (the bf16 high byte of 128); an argument so that it sits in an SGPR
 };
 
-// Per active slot a: published phase-1 items, and finished phase-2 items
-// (slot Amax + a), each on its own 128-byte line.
-__device__ __forceinline__ int *counter(int *ctl, int a) { return ctl + kCtlCounters + a * kCtrStride; }
-__device__ __forceinline__ int *done2(int *ctl, int amax, int a) { return ctl + kCtlCounters + (amax + a) * kCtrStride; }
+// Per active slot a: finished phase-2 items, on its own 128-byte line.
+__device__ __forceinline__ int *done2(int *ctl, int a) { return ctl + kCtlCounters + a * kCtrStride; }
+constexpr uint32_t kHReady = 1u << 16;  // tag of a written h word
 
 // ---------------------------------------------------------------- operands
 // One chunk of natural-order bf16 activations (d: pairs (x0,x1), (x2,x3), ...)
@@ -98,22 +99,16 @@ struct PreAct {
   uint32_t d[8];
 };
 
-template <int BITS, bool COHERENT>
+template <int BITS>
 __device__ __forceinline__ void load_act_chunk(const uint16_t *src, int q, uint32_t *d) {
   const uint32_t *s32 = (const uint32_t *)(src + q * kChunkE<BITS>);
-  if constexpr (COHERENT) {
 #pragma unroll
-    for (int t = 0; t < kChunkE<BITS> / 2; ++t)
-      d[t] = __hip_atomic_load(s32 + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-#pragma unroll
-    for (int t = 0; t < kChunkE<BITS> / 2; t += 4) {
-      const u32x4 v = *(const u32x4 *)(s32 + t);
-      d[t] = v[0];
-      d[t + 1] = v[1];
-      d[t + 2] = v[2];
-      d[t + 3] = v[3];
-    }
+  for (int t = 0; t < kChunkE<BITS> / 2; t += 4) {
+    const u32x4 v = *(const u32x4 *)(s32 + t);
+    d[t] = v[0];
+    d[t + 1] = v[1];
+    d[t + 2] = v[2];
+    d[t + 3] = v[3];
   }
 }
 
@@ -132,34 +127,16 @@ __device__ __forceinline__ void pre_load(const uint16_t *src0, int K, PreAct &pa
 #pragma unroll
   for (int i = 0; i < NPRE; ++i) {
     const int q = threadIdx.x + 256 * i;
-    if (q < nch) load_act_chunk<BITS, false>(src0, q, pa.d + 4 * i);
+    if (q < nch) load_act_chunk<BITS>(src0, q, pa.d + 4 * i);
   }
 }
 
-// Stages rows 0..R-1 (src(r): row r's global address); chunks q < q0 of row 0
-// come from pa (q0 = 256 * NPRE or 0).  Ends with a block barrier.
-template <int BITS, bool COHERENT, int NPRE, typename Src>
-__device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int R, int K, int q0,
-                                           const PreAct *pa) {
+// Per-group sums of the staged rows 0..R-1 (8 threads per group, 16 elements
+// each) into Xs; starts and ends with a block barrier.
+template <int BITS>
+__device__ __forceinline__ void stage_group_sums(const uint8_t *act, float *Xs, int R, int K) {
   const int pitch = K * 2 + 16;
-  const int nch = K / kChunkE<BITS>;
-  if (q0 > 0) {
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i) {
-      const int q = threadIdx.x + 256 * i;
-      if (q < nch) store_act_chunk<BITS>(act, q, pa->d + 4 * i);
-    }
-  }
-  for (int r = 0; r < R; ++r) {
-    const uint16_t *s = src(r);
-    for (int q = (r == 0 ? q0 : 0) + threadIdx.x; q < nch; q += 256) {
-      uint32_t d[kChunkE<BITS> / 2];
-      load_act_chunk<BITS, COHERENT>(s, q, d);
-      store_act_chunk<BITS>(act + r * pitch, q, d);
-    }
-  }
   lds_barrier();
-  // group sums: 8 threads per group, 16 elements each
   const int G = K / kGroup;
   for (int r = 0; r < R; ++r) {
     for (int t = threadIdx.x; t < G * 8; t += 256) {
@@ -183,6 +160,69 @@ __device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int
     }
   }
   lds_barrier();
+}
+
+// Stages activation rows 0..R-1 (src(r): row r's global address); chunks
+// q < q0 of row 0 come from pa (q0 = 256 * NPRE or 0).  Ends with a block barrier.
+template <int BITS, int NPRE, typename Src>
+__device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int R, int K, int q0,
+                                           const PreAct *pa) {
+  const int pitch = K * 2 + 16;
+  const int nch = K / kChunkE<BITS>;
+  if (q0 > 0) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      const int q = threadIdx.x + 256 * i;
+      if (q < nch) store_act_chunk<BITS>(act, q, pa->d + 4 * i);
+    }
+  }
+  for (int r = 0; r < R; ++r) {
+    const uint16_t *s = src(r);
+    for (int q = (r == 0 ? q0 : 0) + threadIdx.x; q < nch; q += 256) {
+      uint32_t d[kChunkE<BITS> / 2];
+      load_act_chunk<BITS>(s, q, d);
+      store_act_chunk<BITS>(act + r * pitch, q, d);
+    }
+  }
+  stage_group_sums<BITS>(act, Xs, R, K);
+}
+
+// Stages h rows 0..R-1 (h0: row 0's words, rows I words apart) once phase 1
+// has written them: each thread reads its chunks with device-coherent loads
+// until every word carries kHReady.  Returns false if a wait timed out.
+template <int BITS>
+__device__ __forceinline__ bool stage_h_rows(uint8_t *act, float *Xs, const uint32_t *h0, int R, int I,
+                                             int max_spins) {
+  constexpr int CE = kChunkE<BITS>;
+  const int pitch = I * 2 + 16;
+  const int nch = I / CE;
+  bool ok = true;
+  for (int r = 0; r < R; ++r) {
+    for (int q = threadIdx.x; q < nch; q += 256) {
+      const uint32_t *src = h0 + (size_t)r * I + q * CE;
+      uint32_t w[CE];
+      for (int spins = 0;; ++spins) {
+        uint32_t all = kHReady;
+#pragma unroll
+        for (int t = 0; t < CE; ++t) {
+          w[t] = __hip_atomic_load(src + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          all &= w[t];
+        }
+        if (all) break;
+        if (spins >= max_spins) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      uint32_t d[CE / 2];
+#pragma unroll
+      for (int t = 0; t < CE / 2; ++t) d[t] = (w[2 * t] & 0xFFFFu) | (w[2 * t + 1] << 16);
+      store_act_chunk<BITS>(act + r * pitch, q, d);
+    }
+  }
+  stage_group_sums<BITS>(act, Xs, R, I);
+  return ok;
 }
 
 // ---------------------------------------------------------------- weights
@@ -337,15 +377,6 @@ __device__ __forceinline__ Meta meta(const DecodeParams &p, int a, int nrows) {
   return r;
 }
 
-__device__ __forceinline__ bool wait_geq(int *ctr, int target, int max_spins) {
-  int spins = 0;
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > max_spins) return false;
-  }
-  return true;
-}
-
 __device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v)); }
 
 // ONE: T == 1 (every active expert has exactly one routed row, of token 0).
@@ -407,7 +438,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
-        stage_rows<BITS, false, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
+        stage_rows<BITS, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
         const int arow = ONE ? 0 : min(m, R - 1);
         const uint8_t *ap = act + arow * pitch1 + lsub * 64 + g0 * (kGroup * 2);
         const float *xs = Xs + g0 * 16 + (ONE ? 0 : 4 * lsub);
@@ -444,14 +475,12 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
             gv += red[w * 512 + mm * 16 + n];
             uv += red[w * 512 + 256 + mm * 16 + n];
           }
-          __hip_atomic_store(p.hbuf + (size_t)(rb + mm) * p.I + i0 + n, f32_to_bf16(silu_f(gv) * uv),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(p.hbuf + (size_t)(rb + mm) * p.I + i0 + n,
+                             kHReady | (uint32_t)f32_to_bf16(silu_f(gv) * uv), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (wv == 0) wait_vmem();  // h stores complete before thread 0 publishes
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         lds_barrier();
       }
-      if (threadIdx.x == 0) atomicAdd(counter(p.ctl, a), 1);
     } else {
       // ============================================================ phase 2
       const int it = item - n1;
@@ -467,14 +496,10 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         load_chunk<BITS>(xw, o2[0], wd[0]);
         load_chunk<BITS>(xw, o2[1], wd[1]);
       }
-      if (threadIdx.x == 0) {
-        if (!wait_geq(counter(p.ctl, a), per1, p.max_spins)) atomicOr(&p.ctl[kCtlError], 1);
-      }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
-        __syncthreads();  // holds the block until thread 0's wait has ended
-        stage_rows<BITS, true, 0>(act, Xs, [&](int r) { return (const uint16_t *)p.hbuf + (size_t)(rb + r) * p.I; }, R,
-                               p.I, 0, nullptr);
+        if (!stage_h_rows<BITS>(act, Xs, p.hbuf + (size_t)rb * p.I, R, p.I, p.max_spins))
+          atomicOr(&p.ctl[kCtlError], 1);
         const int arow = ONE ? 0 : min(m, R - 1);
         const uint8_t *ap = act + arow * pitch2 + lsub * 64;
         const float *xs = Xs + (ONE ? 0 : 4 * lsub);
@@ -509,12 +534,19 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         }
         lds_barrier();  // LDS is rewritten by the next pass
       }
-      // The last phase-2 item of the expert re-zeroes its two counters: every
-      // phase-1 item has published and every phase-2 item has passed its wait.
-      if (threadIdx.x == 0 && atomicAdd(done2(p.ctl, p.Amax, a), 1) == per2 - 1) {
-        __hip_atomic_store(counter(p.ctl, a), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(done2(p.ctl, p.Amax, a), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // The last phase-2 item of the expert clears the expert's h words and
+      // its done counter: every phase-2 item has read h by then.
+      int *flag = (int *)red;
+      if (threadIdx.x == 0) *flag = atomicAdd(done2(p.ctl, a), 1) == per2 - 1;
+      lds_barrier();
+      if (*flag) {
+        const int n = (md.o1 - md.o0) * p.I;
+        uint32_t *h = p.hbuf + (size_t)md.o0 * p.I;
+        for (int i = threadIdx.x; i < n; i += 256)
+          __hip_atomic_store(h + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(done2(p.ctl, a), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      lds_barrier();  // the flag is read before the next item reuses LDS
     }
   }
 }
@@ -564,7 +596,7 @@ bool decode_layout_ok(int H, int I, int bits) {
 
 size_t ffn_ctl_bytes(int T, int k, int E) {
   const long amax = E < (long)T * k ? E : (long)T * k;
-  size_t b = (size_t)(kCtlCounters + 2 * amax * kCtrStride) * 4;
+  size_t b = (size_t)(kCtlCounters + amax * kCtrStride) * 4;
   if (b < kCtlBytes) b = kCtlBytes;
   return (b + 255) / 256 * 256;
 }
@@ -589,7 +621,7 @@ hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_
   p.w2z = a.w2_zeros;
   p.y_perm = a.y_perm;
   p.ctl = (int *)a.ws;
-  p.hbuf = (uint16_t *)((char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E));
+  p.hbuf = (uint32_t *)((char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E));
   p.max_spins = 1 << 22;
   p.magic = kMagic43;
   const bool one = a.T == 1;

@@ -267,6 +267,13 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
     }
 }
 
+// Re-zeroes h after the down GEMM has read it: the workspace is all-zero
+// between calls, which the decode path's tagged h words rely on.
+__global__ void __launch_bounds__(256) zero_kernel(u32x4 *p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 }  // namespace
 
 hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t st) {
@@ -312,6 +319,10 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
     ffn_gemm_kernel<2, true><<<grid1, 256, 0, st>>>(g1);
     ffn_gemm_kernel<2, false><<<grid2, 256, 0, st>>>(g2);
   }
+  // h is T*k*I bf16 (I % 128 == 0, so a whole number of 16-byte chunks)
+  const size_t n16 = (size_t)nrows * a.I * sizeof(uint16_t) / 16;
+  const size_t zb = (n16 + 255) / 256;
+  zero_kernel<<<(unsigned)(zb < 2048 ? zb : 2048), 256, 0, st>>>((u32x4 *)hbuf, n16);
   return hipGetLastError();
 }
 

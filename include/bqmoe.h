@@ -158,7 +158,12 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  *   w2_codes    [E, H, I/8]   uint32, 16-byte aligned
  *   w2_scales   [E, H, I/128] bf16
  *   y_perm      [T*k, H] bf16 out, in sorted order (rows of dropped ids untouched)
- * Requirements: H % 128 == 0, I % 128 == 0, 1 <= E <= 1024, 1 <= k <= 32.
+ *   workspace   moe_expert_ffn_workspace_size bytes; all of it must be zero
+ *               before the first call (allocate it zeroed) and every call
+ *               leaves all of it zero again (the decode path tells written
+ *               intermediate values from unwritten ones by a nonzero tag)
+ * Requirements: H % 128 == 0, I % 128 == 0, 1 <= E <= 1024, 1 <= k <= 32;
+ * for T > 16 also T*H <= 2^30 and I*H <= 2^30 (32-bit offsets in the GEMMs).
  */
 size_t moe_expert_ffn_workspace_size(int T, int k, int E, int H, int I);
 moe_status moe_expert_ffn_w4a16(const uint16_t *x, const int32_t *expert_offsets,
