@@ -21,7 +21,9 @@
 //    v_mfma_f32_16x16x32_bf16 (float32 accumulation);
 //  * software pipeline with one barrier per K tile of 64: while the MFMAs
 //    read one buffer, the next tile is dequantised into the other and global
-//    loads run kStages tiles ahead in registers.
+//    loads run S tiles ahead in registers.
+#include <type_traits>
+
 #include "common.cuh"
 #include "internal.h"
 
@@ -32,7 +34,7 @@ constexpr int BM = 128, BN = 128;
 constexpr int BK = 64;                       // K per tile: half a quantisation group
 constexpr int kRowBytes = BK * 2;            // one LDS row: 64 bf16 = 8 chunks of 16 B
 constexpr int kTileBytes = 128 * kRowBytes;  // 16 KiB per operand tile
-constexpr int kStages = 3;                   // K tiles held in registers ahead of LDS
+constexpr int kBufWord3 = 0x00020000;        // buffer resource word 3: raw 32-bit access
 
 struct GemmParams {
   const uint16_t *a_src;   // G1: x [T, H]; G2: h [T*k, I]
@@ -101,7 +103,11 @@ __device__ bool find_tile(const GemmParams &p, int slot, int *e_out, int *m0_out
   return s_info[0] >= 0;
 }
 
-template <int BITS, bool GATEUP>
+template <int N>
+using IntC = std::integral_constant<int, N>;
+
+// S: K tiles held in registers ahead of LDS (K / BK must be a multiple of S).
+template <int BITS, bool GATEUP, int S>
 __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   // two LDS buffers, each an A tile then a B tile (BM and BN rows of BK bf16)
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kTileBytes];
@@ -119,152 +125,175 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   const int wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;
 
-  // ---- staging map.  A: thread -> rows (tid >> 3) + 32 j (j < 4), chunk tid & 7.
-  constexpr int WPT = BK * BITS / 32;         // code words per tile row: 8 (INT4) or 4 (INT2)
-  constexpr int TPR = WPT;                    // threads per B row (one word each)
-  constexpr int NBR = 128 / (256 / TPR);      // B rows per thread: 4 (INT4) or 2 (INT2)
+  // Loads go through buffer resources: one 32-bit byte offset per stream and
+  // the K-tile step in the scalar offset.  G2 rows are contiguous from the
+  // tile's first row; G1 rows are gathered tokens.
+  const uint16_t *a_base = GATEUP ? p.a_src : p.a_src + (size_t)m0 * p.K;
+  const uint32_t a_bytes = (uint32_t)(GATEUP ? p.T : rows) * (uint32_t)p.K * 2u;
+  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc((void *)a_base, (short)0, (int)a_bytes, kBufWord3);
+  // A staging: thread -> rows (tid >> 3) + 32 j (j < 4), chunk tid & 7.  Rows
+  // past the tile read the tile's last row instead: every load is
+  // unconditional (branches around loads defeat the compiler's load
+  // counting), and those rows only feed C rows that are never stored.
   const int ar = tid >> 3, ac = tid & 7;
-  // Element offset of the thread's A chunk in a_src.  Rows past the tile read
-  // the tile's last row instead: every load is unconditional (branches around
-  // loads defeat the compiler's load counting), and those rows only feed C
-  // rows that the epilogue never stores.
-  int a_off[4];
+  uint32_t a_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int q = m0 + min(ar + 32 * j, rows - 1);
-    const int src = GATEUP ? min(max(p.sorted_rows[q], 0) / p.k, p.T - 1) : q;
-    a_off[j] = src * p.K + ac * 8;
+    const int r = min(ar + 32 * j, rows - 1);
+    const int src = GATEUP ? min(max(p.sorted_rows[m0 + r], 0) / p.k, p.T - 1) : r;
+    a_off[j] = (uint32_t)(src * p.K + ac * 8) * 2u;
   }
-  // B: thread -> weight rows (tid / TPR) + (256 / TPR) j (j < NBR), word tid % TPR
-  const int br0 = tid / TPR, bw = tid % TPR;
-  uint32_t b_off[NBR], s_off[NBR];            // word offset in the codes, element offset in the scales
-#pragma unroll
-  for (int j = 0; j < NBR; ++j) {
-    const int cb = br0 + (256 / TPR) * j;
-    int wrow;
-    if (GATEUP) {  // wave column wn gets 32 gate rows then the 32 matching up rows
-      const int wn_b = cb / 64, cc = cb % 64;
-      const int i = nb * 64 + wn_b * 32 + (cc % 32);
-      wrow = (cc < 32) ? i : p.I + i;
-    } else {
-      wrow = nb * BN + cb;
-    }
-    const uint32_t wrow_g = (uint32_t)e * p.n_rows_w + wrow;
-    b_off[j] = wrow_g * (uint32_t)(p.K * BITS / 32) + bw;
-    s_off[j] = wrow_g * (uint32_t)(p.K / kGroup);
+  // B staging: thread -> weight row tid / 2 of the tile, code words
+  // (tid % 2) * WPL .. + WPL of the K tile, i.e. LDS chunks (tid % 2) * 4 .. + 4.
+  // G1 tiles give each wave column 32 gate rows then the 32 matching up rows.
+  constexpr int WPT = BK * BITS / 32;         // code words per tile row: 8 (INT4) or 4 (INT2)
+  constexpr int WPL = WPT / 2;                // words per thread: 4 (INT4) or 2 (INT2)
+  const int br = tid >> 1, bh = tid & 1;
+  int wrow;
+  if (GATEUP) {
+    const int wn_b = br / 64, cc = br % 64;
+    const int i = nb * 64 + wn_b * 32 + (cc % 32);
+    wrow = (cc < 32) ? i : p.I + i;
+  } else {
+    wrow = nb * BN + br;
   }
-
-  // ---- register stages
-  u32x4 a_st[kStages][4];
-  uint32_t b_st[kStages][NBR];
-  uint32_t sc_st[kStages][NBR], z_st[kStages][NBR];  // raw bf16 scale / zero-point (no math on a load in flight)
-  auto load_tile = [&](int kt, int s) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a_st[s][j] = *(const u32x4 *)(p.a_src + a_off[j] + kt * BK);
-#pragma unroll
-    for (int j = 0; j < NBR; ++j) {
-      b_st[s][j] = p.codes[b_off[j] + kt * WPT];
-      sc_st[s][j] = p.scales[s_off[j] + kt / 2];
-      if constexpr (BITS == 2) z_st[s][j] = p.zeros[s_off[j] + kt / 2];
-    }
-  };
-  auto store_tile = [&](int s, uint8_t *buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)(buf + swz(ar + 32 * j, ac)) = a_st[s][j];
-    uint8_t *bb = buf + kTileBytes;
-#pragma unroll
-    for (int j = 0; j < NBR; ++j) {
-      const int cb = br0 + (256 / TPR) * j;
-      const float sc = bf16_to_f32(sc_st[s][j]);
-      const float zs = -((BITS == 4) ? 8.f : (float)z_st[s][j]) * sc;
-      if constexpr (BITS == 4) {
-        uint32_t o[4];
-        dequant8_int4(b_st[s][j], sc, zs, o);
-        *(u32x4 *)(bb + swz(cb, bw)) = u32x4{o[0], o[1], o[2], o[3]};
-      } else {
-        uint32_t o[8];
-        dequant16_int2(b_st[s][j], sc, zs, o);
-        *(u32x4 *)(bb + swz(cb, 2 * bw)) = u32x4{o[0], o[1], o[2], o[3]};
-        *(u32x4 *)(bb + swz(cb, 2 * bw + 1)) = u32x4{o[4], o[5], o[6], o[7]};
-      }
-    }
-  };
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int wpr = p.K * BITS / 32, gpr = p.K / kGroup;  // code words and groups per weight row
+  const size_t erow0 = (size_t)e * p.n_rows_w;          // the expert's first weight row
+  const __amdgpu_buffer_rsrc_t b_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(p.codes + erow0 * wpr), (short)0, p.n_rows_w * wpr * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t s_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(p.scales + erow0 * gpr), (short)0, p.n_rows_w * gpr * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t z_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(BITS == 2 ? p.zeros + erow0 * gpr : p.zeros), (short)0, BITS == 2 ? p.n_rows_w * gpr : 0, kBufWord3);
+  const uint32_t b_off = (uint32_t)(wrow * wpr + bh * WPL) * 4u;  // bytes
+  const uint32_t s_off = (uint32_t)(wrow * gpr);                  // elements
 
   // ---- pipeline: one barrier per K tile.  While the MFMAs read buffer kt & 1,
-  // tile kt + 1 is dequantised into the other buffer and tile kt + 1 + kStages
-  // is requested from global memory.  Tile t lives in register stage
-  // t % kStages; the K loop is unrolled by kStages so that every stage index
-  // is a constant (a register copy between stages would wait for its load).
+  // tile kt + 1 is dequantised into the other buffer and tile kt + 1 + S is
+  // requested from global memory.  Tile t lives in register stage t % S; the
+  // K loop is unrolled by S so that every stage index is a constant (a
+  // register copy between stages would wait for its load), and it has no
+  // exits: K / BK is a multiple of S.
+  //
+  // MV = 16-row MFMA blocks of this wave's 64 rows that hold data (an
+  // expert's last tile is often mostly empty).  It is a template constant of
+  // the loop, so the loop body has no branches; waves of one block may run
+  // different variants (they meet at the same barriers).
   const int nk = p.K / BK;
-  // Rows of this wave's half of the tile that hold data: 16-row MFMA blocks
-  // past them are skipped (an expert's last tile is often mostly empty).
-  const int mvalid = __builtin_amdgcn_readfirstlane(rows - wm * 64);
-#pragma unroll
-  for (int s = 0; s < kStages; ++s) load_tile(min(s, nk - 1), s);
-  store_tile(0, lds[0]);
-  load_tile(min(kStages, nk - 1), 0);
-  __syncthreads();
-  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
-#pragma unroll
-    for (int d = 0; d < kStages; ++d) {
-      const int kt = kt0 + d;
-      if (kt >= nk) break;
-      const uint8_t *ba = lds[kt & 1], *bb = lds[kt & 1] + kTileBytes;
-#pragma unroll
-      for (int kk = 0; kk < BK / 32; ++kk) {
-        const int ch = kk * 4 + lane / 16;
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          if (mi * 16 < mvalid) af[mi] = *(const bf16x8 *)(ba + swz(wm * 64 + mi * 16 + lane % 16, ch));
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) bfr[ni] = *(const bf16x8 *)(bb + swz(wn * 64 + ni * 16 + lane % 16, ch));
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          if (mi * 16 < mvalid) {
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-          }
-      }
-      const int sn = (d + 1) % kStages;  // stage of tile kt + 1 (a constant once unrolled)
-      // Past the end the last tile is stored and loaded again: harmless, and
-      // it keeps the loop free of branches around memory operations.
-      store_tile(sn, lds[(kt + 1) & 1]);
-      load_tile(min(kt + 1 + kStages, nk - 1), sn);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: C[m][n] of (mi, ni, r) is m = 4*(lane/16) + r, n = lane % 16
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = wm * 64 + mi * 16 + 4 * (lane / 16) + r;
-      if (m >= rows) continue;
-      const size_t orow = (size_t)(m0 + m);
-      if (GATEUP) {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const float g = acc[mi][ni][r], u = acc[mi][ni + 2][r];
-          const float hv = g / (1.f + __expf(-g)) * u;
-          const int col = nb * 64 + wn * 32 + ni * 16 + lane % 16;
-          p.out[orow * p.I + col] = f32_to_bf16(hv);
-        }
+  const int mvalid = rows - wm * 64;
+  const int mv = __builtin_amdgcn_readfirstlane(mvalid <= 0 ? 0 : mvalid >= 64 ? 4 : (mvalid + 15) / 16);
+  auto run = [&](auto mv_c) {
+    constexpr int MV = decltype(mv_c)::value;
+    // ---- register stages
+    u32x4 a_st[S][4];
+    uint32_t b_st[S][WPL];
+    uint32_t sc_st[S], z_st[S];  // raw bf16 scale / zero-point (no math on a load in flight)
+    auto load_tile = [&](int kt, int s) {
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) a_st[s][j] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[j], kt * (BK * 2), 0);
+      if constexpr (BITS == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off, kt * (WPT * 4), 0);
+  #pragma unroll
+        for (int w = 0; w < 4; ++w) b_st[s][w] = v[w];
       } else {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = nb * BN + wn * 64 + ni * 16 + lane % 16;
-          p.out[orow * p.H + col] = f32_to_bf16(acc[mi][ni][r]);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(b_rs, b_off, kt * (WPT * 4), 0);
+        b_st[s][0] = v[0];
+        b_st[s][1] = v[1];
+      }
+      sc_st[s] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off * 2u, (kt / 2) * 2, 0);
+      if constexpr (BITS == 2) z_st[s] = __builtin_amdgcn_raw_buffer_load_b8(z_rs, s_off, kt / 2, 0);
+    };
+    auto store_tile = [&](int s, uint8_t *buf) {
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) *(u32x4 *)(buf + swz(ar + 32 * j, ac)) = a_st[s][j];
+      uint8_t *bb = buf + kTileBytes;
+      const float sc = bf16_to_f32(sc_st[s]);
+      const float zs = -((BITS == 4) ? 8.f : (float)z_st[s]) * sc;
+  #pragma unroll
+      for (int w = 0; w < WPL; ++w) {
+        if constexpr (BITS == 4) {
+          uint32_t o[4];
+          dequant8_int4(b_st[s][w], sc, zs, o);
+          *(u32x4 *)(bb + swz(br, bh * 4 + w)) = u32x4{o[0], o[1], o[2], o[3]};
+        } else {
+          uint32_t o[8];
+          dequant16_int2(b_st[s][w], sc, zs, o);
+          *(u32x4 *)(bb + swz(br, bh * 4 + 2 * w)) = u32x4{o[0], o[1], o[2], o[3]};
+          *(u32x4 *)(bb + swz(br, bh * 4 + 2 * w + 1)) = u32x4{o[4], o[5], o[6], o[7]};
         }
       }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < S; ++s) load_tile(min(s, nk - 1), s);
+    store_tile(0, lds[0]);
+    load_tile(min(S, nk - 1), 0);
+    __syncthreads();
+    for (int kt0 = 0; kt0 < nk; kt0 += S) {
+#pragma unroll
+      for (int d = 0; d < S; ++d) {
+        const int kt = kt0 + d;
+        const uint8_t *ba = lds[kt & 1], *bb = lds[kt & 1] + kTileBytes;
+        if constexpr (MV > 0) {
+#pragma unroll
+          for (int kk = 0; kk < BK / 32; ++kk) {
+            const int ch = kk * 4 + lane / 16;
+            bf16x8 af[MV], bfr[4];
+#pragma unroll
+            for (int mi = 0; mi < MV; ++mi) af[mi] = *(const bf16x8 *)(ba + swz(wm * 64 + mi * 16 + lane % 16, ch));
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) bfr[ni] = *(const bf16x8 *)(bb + swz(wn * 64 + ni * 16 + lane % 16, ch));
+#pragma unroll
+            for (int mi = 0; mi < MV; ++mi)
+#pragma unroll
+              for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          }
+        }
+        const int sn = (d + 1) % S;  // stage of tile kt + 1 (a constant once unrolled)
+        // Past the end the last tile is stored and loaded again: harmless, and
+        // it keeps the loop free of branches around memory operations.
+        store_tile(sn, lds[(kt + 1) & 1]);
+        load_tile(min(kt + 1 + S, nk - 1), sn);
+        __syncthreads();
+      }
     }
+    // ---- epilogue: C[m][n] of (mi, ni, r) is m = 4*(lane/16) + r, n = lane % 16
+#pragma unroll
+    for (int mi = 0; mi < MV; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = wm * 64 + mi * 16 + 4 * (lane / 16) + r;
+        if (m >= rows) continue;
+        const size_t orow = (size_t)(m0 + m);
+        if (GATEUP) {
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) {
+            const float g = acc[mi][ni][r], u = acc[mi][ni + 2][r];
+            const float hv = g / (1.f + __expf(-g)) * u;
+            const int col = nb * 64 + wn * 32 + ni * 16 + lane % 16;
+            p.out[orow * p.I + col] = f32_to_bf16(hv);
+          }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) {
+            const int col = nb * BN + wn * 64 + ni * 16 + lane % 16;
+            p.out[orow * p.H + col] = f32_to_bf16(acc[mi][ni][r]);
+          }
+        }
+      }
+  };
+  switch (mv) {
+    case 4: run(IntC<4>{}); break;
+    case 3: run(IntC<3>{}); break;
+    case 2: run(IntC<2>{}); break;
+    case 1: run(IntC<1>{}); break;
+    default: run(IntC<0>{}); break;
+  }
 }
 
 // Re-zeroes h after the down GEMM has read it: the workspace is all-zero
@@ -312,12 +341,13 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   g1.n_blocks = a.I / 64;
   g2.n_blocks = a.H / BN;
   dim3 grid1((unsigned)(slots * g1.n_blocks)), grid2((unsigned)(slots * g2.n_blocks));
+  // two register stages: K % 128 == 0 makes K / BK even
   if (a.bits == 4) {
-    ffn_gemm_kernel<4, true><<<grid1, 256, 0, st>>>(g1);
-    ffn_gemm_kernel<4, false><<<grid2, 256, 0, st>>>(g2);
+    ffn_gemm_kernel<4, true, 2><<<grid1, 256, 0, st>>>(g1);
+    ffn_gemm_kernel<4, false, 2><<<grid2, 256, 0, st>>>(g2);
   } else {
-    ffn_gemm_kernel<2, true><<<grid1, 256, 0, st>>>(g1);
-    ffn_gemm_kernel<2, false><<<grid2, 256, 0, st>>>(g2);
+    ffn_gemm_kernel<2, true, 2><<<grid1, 256, 0, st>>>(g1);
+    ffn_gemm_kernel<2, false, 2><<<grid2, 256, 0, st>>>(g2);
   }
   // h is T*k*I bf16 (I % 128 == 0, so a whole number of 16-byte chunks)
   const size_t n16 = (size_t)nrows * a.I * sizeof(uint16_t) / 16;
