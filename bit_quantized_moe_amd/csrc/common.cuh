@@ -19,11 +19,9 @@ constexpr int kGroup = 128;  // quantisation group along K
 // Control block at the start of every workspace (int32 words).
 //   [2]          sticky error flags (bit 0: a bounded wait timed out)
 //   route workspace:
-//   [32]         selector blocks finished
-//   [128 + 32 i] experts finished, i < 16 (one counter per 128-byte line)
+//   [32]         selector blocks finished (several selectors grouping rows)
 //   expert-FFN workspace:
 //   [64 ..]      per-active-expert counters, kCtrStride apart
-constexpr int kCtlRouteDone = 0;
 constexpr int kCtlError = 2;
 constexpr int kCtlRouteSel = 32;
 constexpr int kCtlCounters = 64;

@@ -50,28 +50,19 @@ __device__ __forceinline__ void wave_key_max(uint32_t &hi, uint32_t &lo) {
   key_max(hi, lo, h1, l1);
 }
 
-// One wave selects the k largest of lg[0..E) and writes ids and softmax
-// gates.  NV = values per lane (E <= 64 * NV).  COHERENT: lg is global memory
-// written by other blocks of this kernel, read with device-coherent loads;
-// otherwise lg is LDS or ordinary memory.
+// One wave selects the k largest logits and writes ids and softmax gates.
+// NV = values per lane (E <= 64 * NV); load(v) fills v[j] with the logit of
+// expert lane + 64 j (any value where that index is >= E).
 // PUBLISH: ids are stored with device-coherent stores (read back by another
 // block).  key_lds, when given, receives a copy of the ids.
-template <int NV, bool COHERENT, bool PUBLISH>
-__device__ void topk_softmax_wave(const float *lg, int E, int k, int32_t *ids_out, float *g_out, int *key_lds) {
+template <int NV, bool PUBLISH, typename Load>
+__device__ void topk_softmax_wave(Load load, int E, int k, int32_t *ids_out, float *g_out, int *key_lds) {
   const int lane = lane_id();
+  float v[NV];
+  load(v);
   uint32_t key[NV];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int e = lane + kWave * j;
-    float v = 0.f;
-    if (e < E) {
-      if constexpr (COHERENT)
-        v = __hip_atomic_load(lg + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        v = lg[e];
-    }
-    key[j] = (e < E) ? ord_key(v) : 0u;  // 0: below every finite logit; never selected while k <= E
-  }
+  for (int j = 0; j < NV; ++j) key[j] = (lane + kWave * j < E) ? ord_key(v[j]) : 0u;  // 0: never selected (k <= E)
   uint32_t used = 0, my_hi = 0;
   int my_e = 0;
   for (int slot = 0; slot < k; ++slot) {
@@ -103,19 +94,19 @@ __device__ void topk_softmax_wave(const float *lg, int E, int k, int32_t *ids_ou
   }
 }
 
-template <bool COHERENT, bool PUBLISH = false>
-__device__ __forceinline__ void topk_softmax_any(const float *lg, int E, int k, int32_t *ids_out, float *g_out,
+template <bool PUBLISH = false, typename Load>
+__device__ __forceinline__ void topk_softmax_any(Load load, int E, int k, int32_t *ids_out, float *g_out,
                                                  int *key_lds = nullptr) {
   if (E <= 64)
-    topk_softmax_wave<1, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
+    topk_softmax_wave<1, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
   else if (E <= 128)
-    topk_softmax_wave<2, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
+    topk_softmax_wave<2, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
   else if (E <= 256)
-    topk_softmax_wave<4, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
+    topk_softmax_wave<4, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
   else if (E <= 512)
-    topk_softmax_wave<8, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
+    topk_softmax_wave<8, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
   else
-    topk_softmax_wave<16, COHERENT, PUBLISH>(lg, E, k, ids_out, g_out, key_lds);
+    topk_softmax_wave<16, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
 }
 
 // ------------------------------------------------------------ grouping by expert
@@ -201,16 +192,57 @@ __device__ void wave_group_rows(const int *key, int n, int E, int *cur, int32_t 
   }
 }
 
+// The same grouping for n <= 64 rows, in registers: lane r holds row r's key
+// (E for a dropped row, E + 1 past the last row) and every count is a loop
+// over the n keys read back one lane at a time.
+__device__ void wave_group_rows_small(int kr, int n, int E, int32_t *offsets, int32_t *sorted_rows, int32_t *row_pos,
+                                      int32_t *active, int n_active_slots) {
+  const int lane = lane_id();
+  int pos = 0;
+  bool first = true;  // no lower row has this key
+  for (int q = 0; q < n; ++q) {
+    const int kq = __builtin_amdgcn_readlane(kr, q);
+    pos += (kq < kr) || (kq == kr && q < lane);
+    first = first && !(kq == kr && q < lane);
+  }
+  if (lane < n) {
+    if (kr < E) {
+      sorted_rows[pos] = lane;
+      row_pos[lane] = pos;
+    } else {
+      row_pos[lane] = -1;
+    }
+  }
+  // heads: the first row of every expert that has rows
+  const uint64_t heads = __ballot(lane < n && kr < E && first);
+  const int n_act = __popcll(heads);
+  for (int e = lane; e <= E; e += kWave) {
+    int below = 0, act_below = 0, here = 0;
+    for (int q = 0; q < n; ++q) {
+      const int kq = __builtin_amdgcn_readlane(kr, q);
+      below += kq < e;
+      act_below += ((heads >> q) & 1ull) && kq < e;
+      here += kq == e;
+    }
+    offsets[e] = below;
+    if (e < E && here > 0) active[1 + act_below] = e;
+  }
+  for (int i = 1 + n_act + lane; i < n_active_slots; i += kWave) active[i] = -1;
+  if (lane == 0) active[0] = n_act;
+}
+
 // ------------------------------------------------------------ small T
 // Grid: E blocks of one wave; block e computes the logits of expert e for
-// every token (lane s = slice s, sequential over its h), then counts itself
-// done (control words 128, 160, ..., one counter per 128-byte line).  Blocks 0 .. nsel-1 (nsel = min(T, E)) wait until every expert is
-// done and run top-k for tokens b, b + nsel, ...; the last of them to finish
-// re-zeroes the counters.  All E one-wave blocks are co-resident, so the wait
-// ends; it is bounded anyway and a timeout only raises the error flag.
+// every token (lane s = slice s, sequential over its h) and stores each as a
+// 64-bit word, the float bits under a nonzero tag, with a device-coherent
+// store.  Blocks 0 .. nsel-1 (nsel = min(T, E)) run the top-k of tokens
+// b, b + nsel, ...: they read the token's E words until every one carries the
+// tag (each word is self-validating, so no counter and no store wait are
+// needed), then clear them for the next call.  All E one-wave blocks are
+// co-resident, so the wait ends; it is bounded anyway and a timeout only
+// raises the error flag.
 constexpr int kTB = 4;  // tokens whose activation slices are loaded together
-constexpr int kRouteDoneN = 16;  // done counters, one 128-byte line each
-__device__ __forceinline__ int route_done(int i) { return kCtlRouteDone + 32 * (4 + i); }
+constexpr uint64_t kLogitTag = 1ull << 32;
 
 // VEC bf16 elements per load: 8 (16 B), 4 (8 B) or 2 (4 B); kept packed.
 template <int VEC>
@@ -253,8 +285,9 @@ struct GroupOut {
 template <int VEC, bool GROUP>
 __global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ w, const float *bias, int T,
-                                                         int H, int E, int k, int32_t *ids, float *gates, float *lg,
-                                                         int *ctl, int max_spins, GroupOut go) {
+                                                         int H, int E, int k, int32_t *ids, float *gates,
+                                                         uint64_t *tl, float *lg_out, int *ctl, int max_spins,
+                                                         GroupOut go) {
   constexpr int NVC = 64 / VEC;  // loads per 64-element chunk of a slice
   const int lane = lane_id();
   const int e = blockIdx.x;
@@ -293,65 +326,93 @@ __global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restr
     for (int tt = 0; tt < kTB; ++tt) {
       const float sum = group_sum(acc[tt], kWave);  // pairwise tree over the 64 slice sums
       if (lane == 0 && t0 + tt < T)
-        __hip_atomic_store(lg + (size_t)(t0 + tt) * E + e, sum + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(tl + (size_t)(t0 + tt) * E + e, kLogitTag | __float_as_uint(sum + b), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  wait_vmem();  // the logit stores are complete before this expert counts as done
-  // Experts count themselves done on kRouteDoneN counters (same-address
-  // atomics from every block would serialise).
-  if (lane == 0) atomicAdd(&ctl[route_done(e % kRouteDoneN)], 1);
   const int nsel = min(T, E);
   if (e >= nsel) return;
-  int spins = 0;
-  for (;;) {
-    const int c = (lane < kRouteDoneN)
-                      ? __hip_atomic_load(&ctl[route_done(lane)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : 0;
-    const int done = __builtin_amdgcn_readfirstlane((int)group_sum((float)c, kRouteDoneN));
-    if (done >= E) break;
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > max_spins) {
-      if (lane == 0) atomicOr(&ctl[kCtlError], 1);
-      break;
-    }
-  }
-  extern __shared__ int group_lds[];  // GROUP: key[kFusedRows], then cur[E]
-  int *key = group_lds, *cur = group_lds + kFusedRows;
+  // Loader of token t's logits: poll the tagged words, then clear them.
+  auto logits_of = [&](int t) {
+    return [=](auto &v) {
+      constexpr int NV = sizeof(v) / sizeof(v[0]);
+      uint64_t *row = tl + (size_t)t * E;
+      uint64_t wv[NV];
+      for (int spins = 0;; ++spins) {
+        bool ready = true;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int ee = lane + kWave * j;
+          wv[j] = ee < E ? __hip_atomic_load(row + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kLogitTag;
+          ready = ready && (wv[j] & kLogitTag);
+        }
+        if (__ballot(!ready) == 0) break;
+        if (spins >= max_spins) {
+          if (lane == 0) atomicOr(&ctl[kCtlError], 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int ee = lane + kWave * j;
+        v[j] = __uint_as_float((uint32_t)wv[j]);
+        if (ee < E) {
+          __hip_atomic_store(row + ee, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lg_out) lg_out[(size_t)t * E + ee] = v[j];
+        }
+      }
+    };
+  };
+  extern __shared__ int group_lds[];  // GROUP with several selectors: key[kFusedRows], then cur[E]
   if constexpr (!GROUP) {
     for (int t = e; t < T; t += nsel)
-      topk_softmax_any<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
+      topk_softmax_any(logits_of(t), E, k, ids + (size_t)t * k, gates + (size_t)t * k);
   } else {
-    // One selector keeps every token's ids in LDS; several publish them for
-    // the last one to read back.
-    if (nsel == 1) {
-      for (int t = 0; t < T; ++t)
-        topk_softmax_any<true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, key + t * k);
-    } else {
-      for (int t = e; t < T; t += nsel)
-        topk_softmax_any<true, true>(lg + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k);
-      wait_vmem();  // the ids are stored before this selector counts itself done
-    }
-  }
-  int last = 1;
-  if (nsel > 1) {
-    last = 0;
-    if (lane == 0) last = atomicAdd(&ctl[kCtlRouteSel], 1) == nsel - 1;
-    last = __builtin_amdgcn_readfirstlane(last);
-  }
-  if (!last) return;
-  if (lane == 0) {
-    for (int i = 0; i < kRouteDoneN; ++i)
-      __hip_atomic_store(&ctl[route_done(i)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ctl[kCtlRouteSel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if constexpr (GROUP) {
     const int n = T * k;
-    if (nsel > 1) {
-      for (int r = lane; r < n; r += kWave)
-        key[r] = __hip_atomic_load(ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (nsel == 1) {
+      // One selector: every id is in its LDS; at n <= 64 the grouping runs in registers.
+      for (int t = 0; t < T; ++t)
+        topk_softmax_any(logits_of(t), E, k, ids + (size_t)t * k, gates + (size_t)t * k, group_lds + t * k);
       __builtin_amdgcn_wave_barrier();
+      if (n <= kWave) {
+        int kr = E + 1;
+        if (lane < n) {
+          const int id = group_lds[lane];
+          kr = (id >= 0 && id < E) ? id : E;
+        }
+        wave_group_rows_small(kr, n, E, go.offsets, go.sorted_rows, go.row_pos, go.active, go.n_active_slots);
+      } else {
+        wave_group_rows(group_lds, n, E, group_lds + kFusedRows, go.offsets, go.sorted_rows, go.row_pos, go.active,
+                        go.n_active_slots);
+      }
+      return;
     }
-    wave_group_rows(key, n, E, cur, go.offsets, go.sorted_rows, go.row_pos, go.active, go.n_active_slots);
+    // Several selectors publish their ids; the last one to finish reads them
+    // back and groups the rows.
+    for (int t = e; t < T; t += nsel)
+      topk_softmax_any<true>(logits_of(t), E, k, ids + (size_t)t * k, gates + (size_t)t * k);
+    wait_vmem();  // the ids are stored before this selector counts itself done
+    int last = 0;
+    if (lane == 0) last = atomicAdd(&ctl[kCtlRouteSel], 1) == nsel - 1;
+    if (!__builtin_amdgcn_readfirstlane(last)) return;
+    if (lane == 0) __hip_atomic_store(&ctl[kCtlRouteSel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n <= kWave) {
+      int kr = E + 1;
+      if (lane < n) {
+        const int id = __hip_atomic_load(ids + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        kr = (id >= 0 && id < E) ? id : E;
+      }
+      wave_group_rows_small(kr, n, E, go.offsets, go.sorted_rows, go.row_pos, go.active, go.n_active_slots);
+    } else {
+      int *key = group_lds, *cur = group_lds + kFusedRows;
+      for (int r = lane; r < n; r += kWave) {
+        const int id = __hip_atomic_load(ids + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        key[r] = (id >= 0 && id < E) ? id : E;
+      }
+      __builtin_amdgcn_wave_barrier();
+      wave_group_rows(key, n, E, cur, go.offsets, go.sorted_rows, go.row_pos, go.active, go.n_active_slots);
+    }
   }
 }
 
@@ -468,7 +529,19 @@ __global__ void __launch_bounds__(256) route_tiled_kernel(const uint16_t *__rest
   const int wave = tid / kWave;
   for (int t = wave; t < kTileT; t += 4) {
     const int tg = t_base + t;
-    if (tg < T) topk_softmax_any<false>(lgs + t * E, E, k, ids + (size_t)tg * k, gates + (size_t)tg * k);
+    if (tg < T) {
+      const float *row = lgs + t * E;
+      topk_softmax_any(
+          [&](auto &v) {
+            constexpr int NV = sizeof(v) / sizeof(v[0]);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+              const int ee = lane_id() + kWave * j;
+              v[j] = ee < E ? row[ee] : 0.f;
+            }
+          },
+          E, k, ids + (size_t)tg * k, gates + (size_t)tg * k);
+    }
   }
 }
 
@@ -476,7 +549,7 @@ __global__ void __launch_bounds__(256) route_tiled_kernel(const uint16_t *__rest
 
 size_t route_workspace_bytes(int T, int E) {
   size_t b = kCtlBytes;
-  if (T <= kRouteSmallT) b += (size_t)T * E * sizeof(float);
+  if (T <= kRouteSmallT) b += (size_t)T * E * sizeof(uint64_t);  // tagged logits
   return b;
 }
 
@@ -485,20 +558,20 @@ static void launch_route_small(const uint16_t *x, const uint16_t *w_router, cons
                                int k, int32_t *ids, float *gates, float *logits, void *ws, const GroupOut &go,
                                hipStream_t st) {
   int *ctl = (int *)ws;
-  float *lg = logits ? logits : (float *)((char *)ws + kCtlBytes);
+  uint64_t *tl = (uint64_t *)((char *)ws + kCtlBytes);
   const int L = H / 64;
   const int spins = 1 << 22;
   dim3 grid(E), block(kWave);
   const size_t lds = GROUP ? (size_t)(kFusedRows + E) * sizeof(int) : 0;
   if (L % 8 == 0)
-    route_small_kernel<8, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl,
-                                                           spins, go);
+    route_small_kernel<8, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, tl, logits,
+                                                           ctl, spins, go);
   else if (L % 4 == 0)
-    route_small_kernel<4, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl,
-                                                           spins, go);
+    route_small_kernel<4, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, tl, logits,
+                                                           ctl, spins, go);
   else
-    route_small_kernel<2, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, lg, ctl,
-                                                           spins, go);
+    route_small_kernel<2, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, tl, logits,
+                                                           ctl, spins, go);
 }
 
 bool route_groups_rows(int T, int k) { return T <= kRouteSmallT && T * k <= kFusedRows; }

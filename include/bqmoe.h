@@ -37,10 +37,12 @@
  *    nothing.
  *  - Results are bitwise deterministic for given inputs on a given device.
  *  - Workspaces: device memory of at least the size returned by the matching
- *    *_workspace_size() function, 256-byte aligned.  Each workspace begins
- *    with a control block that must be all-zero before the first call that
- *    uses the buffer (allocate it zeroed); every call leaves it zeroed again.
- *    Two calls that overlap in time must not share a workspace.
+ *    *_workspace_size() function, 256-byte aligned.  A workspace must be
+ *    all-zero before the first call that uses it (allocate it zeroed); every
+ *    call leaves it all-zero again, because kernels tell values written in
+ *    this call from unwritten ones by a nonzero tag.  Two calls that overlap
+ *    in time must not share a workspace.  After a call that reported an
+ *    error, zero the workspace again.
  *  - Entry points are thread-safe; the only library state is a per-device
  *    cache of device properties and a thread-local error string.
  */
@@ -128,7 +130,7 @@ moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E,
  * decode path.  Other shapes run the two launches in order.  topk_ids are
  * always valid expert ids here, so row_pos has no -1 entries.
  * The workspace (moe_route_permute_workspace_size bytes, 256-byte aligned)
- * starts with the router's control block; the library leaves it zeroed.
+ * starts with the router's control block; the library leaves all of it zero.
  */
 size_t moe_route_permute_workspace_size(int T, int k, int E);
 moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
