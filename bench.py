@@ -3,19 +3,23 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu-baseline]
 
-A step is one pass of the whole layer -- moe_route, moe_permute,
-moe_expert_ffn_w4a16/_w2a16, moe_combine, all through the C ABI -- over one
-batch of synthetic input already resident in HBM.  Decode workloads cycle
-through their distinct weight sets (and activations) step by step, so the
-expert bytes a step touches come from HBM rather than the 256 MB Infinity
-Cache.  By default each step is replayed from a HIP graph that holds its four
-calls (--eager launches them one by one instead).
+A step is one pass of the whole layer over one batch of synthetic input
+already resident in HBM, through the C ABI: for T <= 4 one moe_layer_w4a16 /
+_w2a16 call (router, grouping, expert FFN and combine in one launch; --stages
+runs the stage calls instead), for larger T moe_route_permute,
+moe_expert_ffn_w4a16/_w2a16 and moe_combine.  Decode workloads cycle through
+their distinct weight sets (and activations) step by step, so the expert bytes
+a step touches come from HBM rather than the 256 MB Infinity Cache.  By
+default each step is replayed from a HIP graph (--eager launches the calls one
+by one instead).
 
 Printed: one JSON line with tokens/s over the timed steps, the roofline of
-the dominant kernel (the expert FFN: HBM-bound on packed weight bytes for
-decode, MFMA-bound on useful FLOPs for prefill) from HIP events on its own
-stream, and the CPU oracle's rate on a bounded sample of the same workload,
-timed on the host in a child process pinned to one core.
+the dominant kernel (decode: the one-launch layer kernel, HBM-bound on the
+packed weight bytes of the selected experts plus the router weights; prefill:
+the expert-FFN GEMMs, MFMA-bound on useful FLOPs) from HIP events on its own
+stream, the expert-FFN stage launched alone (decode), and the CPU oracle's
+rate on a bounded sample of the same workload, timed on the host in a child
+process pinned to one core.
 """
 from __future__ import annotations
 
@@ -33,6 +37,7 @@ METRIC = "MoE-layer tokens/s; decode HBM GB/s % peak; prefill MFMA % peak (1 GPU
 DEFAULT_WORKLOAD = "decode_t1_h4096_e256_k8_i1024_int4"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FUSED_MAX_T = 4  # decode batches up to this size run as one moe_layer launch; larger ones as the stages
 
 
 def parse():
@@ -44,7 +49,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch the four calls per step without a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--ffn-only", action="store_true", help="time only the expert-FFN launches (for profiling)")
+    ap.add_argument("--ffn-only", action="store_true", help="time only the expert-FFN stage launches (for profiling)")
+    ap.add_argument("--stages", action="store_true", help="decode: run the stage calls instead of the one-launch layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (to scale the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
@@ -70,7 +76,10 @@ def copy_calibration():
 # while these files are unchanged since the counters were taken.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "decode": ["bit_quantized_moe_amd/csrc/ffn_decode.hip", "bit_quantized_moe_amd/csrc/common.cuh"],
+    "decode": ["bit_quantized_moe_amd/csrc/ffn_decode.hip", "bit_quantized_moe_amd/csrc/common.cuh",
+               "bit_quantized_moe_amd/csrc/route_dev.cuh"],
+    "layer": ["bit_quantized_moe_amd/csrc/ffn_decode.hip", "bit_quantized_moe_amd/csrc/common.cuh",
+              "bit_quantized_moe_amd/csrc/route_dev.cuh"],
     "prefill": ["bit_quantized_moe_amd/csrc/ffn_prefill.hip", "bit_quantized_moe_amd/csrc/common.cuh"],
 }
 
@@ -89,7 +98,7 @@ def stored_traffic(workload, kind):
     """HBM bytes per launch measured with FETCH_SIZE / WRITE_SIZE (scaled by a plain copy), or None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(workload)
+            rec = json.load(f).get(workload if kind != "layer" else workload + ":layer")
     except (OSError, ValueError):
         return None
     if not rec or rec.get("sources_sha256") != sources_digest(kind):
@@ -119,7 +128,7 @@ def finish_cpu_baseline(proc):
 class Plan:
     """Device buffers and pre-bound C-ABI calls for one workload."""
 
-    def __init__(self, sp, dev):
+    def __init__(self, sp, dev, fused=False):
         import numpy as np
         import torch
 
@@ -127,6 +136,7 @@ class Plan:
         import workload
 
         self.sp, self.dev, self.L = sp, dev, bq.lib()
+        self.fused = fused
         T, H, E, k, I = sp.T, sp.H, sp.E, sp.k, sp.I
         n = T * k
 
@@ -160,6 +170,8 @@ class Plan:
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.ws_route = torch.zeros(self.L.moe_route_permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.zeros(self.L.moe_expert_ffn_workspace_size(T, k, E, H, I), dtype=torch.uint8, device=dev)
+        self.ws_layer = (torch.zeros(self.L.moe_layer_workspace_size(T, k, E, H, I), dtype=torch.uint8, device=dev)
+                         if fused else None)
         self.torch = torch
 
     def _chk(self, s, name):
@@ -198,10 +210,33 @@ class Plan:
         self._chk(self.L.moe_combine(self.y_perm.data_ptr(), st["row_pos"].data_ptr(), st["gates"].data_ptr(), sp.T,
                                      sp.k, sp.H, self.y.data_ptr(), stream), "moe_combine")
 
-    def step(self, i):
+    def layer(self, i):
+        sp, st, L = self.sp, self.sets[i], self.L
+        stream = self.torch.cuda.current_stream(self.dev).cuda_stream
+        w = st["w"]
+        head = (st["x"].data_ptr(), self.w_r.data_ptr(), self.bias.data_ptr() if self.bias is not None else None,
+                sp.T, sp.H, sp.E, sp.k, sp.I)
+        tail = (self.y.data_ptr(), st["ids"].data_ptr(), st["gates"].data_ptr(), self.ws_layer.data_ptr(),
+                self.ws_layer.numel(), stream)
+        if sp.bits == 4:
+            s = L.moe_layer_w4a16(*head, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
+                                  w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(), *tail)
+        else:
+            s = L.moe_layer_w2a16(*head, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
+                                  w["w13_zeros"].data_ptr(), w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(),
+                                  w["w2_zeros"].data_ptr(), *tail)
+        self._chk(s, "moe_layer")
+
+    def stages(self, i):
         self.route_permute(i)
         self.ffn(i)
         self.combine(i)
+
+    def step(self, i):
+        if self.fused:
+            self.layer(i)
+        else:
+            self.stages(i)
 
 
 def main():
@@ -222,13 +257,34 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sp = workload.spec(args.workload)
-    plan = Plan(sp, dev)
+    fused = sp.T <= FUSED_MAX_T and not args.stages
+    plan = Plan(sp, dev, fused=fused)
     nset = sp.n_sets
     stream = torch.cuda.Stream(dev)
 
+    def time_graph(fn):
+        """Average time of fn(i) (one launch) over back-to-back replays of a graph of all sets."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(nset):
+                fn(i)
+        reps = max(1, args.steps // nset)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        return a.elapsed_time(b) / (reps * nset)
+
     with torch.cuda.stream(stream):
-        for i in range(nset):      # eager warm-up; also fills every set's routing buffers
-            plan.step(i)
+        for i in range(nset):      # eager warm-up; fills every set's routing buffers (the FFN stage reads them)
+            plan.stages(i)
+            if fused:
+                plan.layer(i)
         torch.cuda.synchronize(dev)
 
         use_graph = not args.eager
@@ -257,36 +313,33 @@ def main():
         wall = time.perf_counter() - c0
         ms_step = e0.elapsed_time(e1) / max(1, args.steps)
 
-        # ---- dominant kernel: the expert FFN alone, back to back, one launch per set
-        fg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(fg, stream=stream):
-            for i in range(nset):
-                plan.ffn(i)
-        reps = max(1, args.steps // nset)
-        for _ in range(2):
-            fg.replay()
-        torch.cuda.synchronize(dev)
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        for _ in range(reps):
-            fg.replay()
-        f1.record(stream)
-        torch.cuda.synchronize(dev)
-        ffn_ms = f0.elapsed_time(f1) / (reps * nset)
+        # ---- the expert-FFN stage alone, and (decode) the one-launch layer kernel alone
+        ffn_ms = time_graph(plan.ffn)
+        layer_ms = time_graph(plan.layer) if fused and not args.ffn_only else None
 
     # distinct experts per launch (decode bytes) from each set's routing
     distinct = [int(st["active"][0].item()) for st in plan.sets]
     mean_distinct = sum(distinct) / len(distinct)
     bpe = sp.weight_bytes_per_expert()
     decode = sp.T <= 16
+    ffn_stage = None
     if decode:
         alg = mean_distinct * bpe
         achieved = alg / (ffn_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(sp.name, "decode"),
-                "kernel": "ffn_decode_kernel (fused gate_up+SwiGLU+down GEMV)",
-                "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(ffn_ms * 1e3, 3),
-                "distinct_experts_per_launch": mean_distinct}
+        ffn_stage = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(sp.name, "decode"),
+                     "kernel": "ffn_decode_kernel (expert-FFN stage: gate_up+SwiGLU+down GEMV)",
+                     "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(ffn_ms * 1e3, 3),
+                     "distinct_experts_per_launch": mean_distinct}
+        roof = ffn_stage
+        if layer_ms is not None:
+            alg_l = alg + sp.E * sp.H * 2          # plus the bf16 router weights
+            ach_l = alg_l / (layer_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach_l, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach_l / HBM_PEAK_GBS, 4), "traffic": stored_traffic(sp.name, "layer"),
+                    "kernel": "ffn_decode_kernel LAYER (one launch: router, top-k, grouping, expert FFN, combine)",
+                    "algorithmic_bytes_per_launch": int(alg_l), "avg_launch_us": round(layer_ms * 1e3, 3),
+                    "distinct_experts_per_launch": mean_distinct}
     else:
         flops = 2.0 * sp.T * sp.k * 3 * sp.H * sp.I
         achieved = flops / (ffn_ms * 1e-3) / 1e12
@@ -304,10 +357,13 @@ def main():
         "config": {"workload": sp.name, "T": sp.T, "H": sp.H, "E": sp.E, "top_k": sp.k, "I": sp.I,
                    "weight_format": f"int{sp.bits} g128" + (" sym" if sp.bits == 4 else " + zero-point"),
                    "weight_sets_cycled": nset, "launch": "hip graph per step" if use_graph else "eager",
+                   "step": "moe_layer (one launch)" if fused else "stage calls",
                    "wall_s_timed": round(wall, 4)},
         "roofline": roof,
         "cpu_baseline": cpu_res,
     }
+    if ffn_stage is not None and layer_ms is not None:
+        line["ffn_stage"] = ffn_stage
     print(json.dumps(line), flush=True)
 
 

@@ -19,7 +19,7 @@ from typing import Dict, Optional
 import torch
 
 __all__ = [
-    "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "combine", "unpack_codes",
+    "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "layer", "combine", "unpack_codes",
     "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH",
 ]
 
@@ -41,6 +41,9 @@ _SIGS = {
     "moe_expert_ffn_w4a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 5 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 7 + [_vp, _c_size, _vp]),
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_layer_workspace_size": (_c_size, [_c_int] * 5),
+    "moe_layer_w4a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp] * 3 + [_vp, _c_size, _vp]),
+    "moe_layer_w2a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_unpack_codes": (_c_int, [_vp, _c_int, _c_i64, _vp, _vp]),
     "moe_dequant_bf16": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
 }
@@ -208,6 +211,31 @@ def combine(y_perm: torch.Tensor, row_pos: torch.Tensor, gates: torch.Tensor) ->
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _check(lib().moe_combine(_p(y_perm), _p(row_pos), _p(gates), T, k, H, _p(y), _stream(dev)), "moe_combine")
     return y
+
+
+def layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor], weights: Dict[str, torch.Tensor],
+          k: int, bits: int, I: int, ws: Optional[Workspaces] = None, want_routing: bool = False):
+    """The whole decode layer (T <= 16) in one library call; returns y (and ids, gates)."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = w_router.shape[0]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if want_routing else None
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev) if want_routing else None
+    L = lib()
+    w = (ws or Workspaces(dev)).get("layer", L.moe_layer_workspace_size(T, k, E, H, I))
+    head = (_p(x), _p(w_router), _p(logit_bias), T, H, E, k, I)
+    tail = (_p(y), _p(ids), _p(gates), _p(w), w.numel(), _stream(dev))
+    if bits == 4:
+        s = L.moe_layer_w4a16(*head, _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights["w2_codes"]),
+                              _p(weights["w2_scales"]), *tail)
+    elif bits == 2:
+        s = L.moe_layer_w2a16(*head, _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights["w13_zeros"]),
+                              _p(weights["w2_codes"]), _p(weights["w2_scales"]), _p(weights["w2_zeros"]), *tail)
+    else:
+        raise MoEError("bits must be 2 or 4")
+    _check(s, f"moe_layer_w{bits}a16")
+    return (y, ids, gates) if want_routing else y
 
 
 def unpack_codes(words: torch.Tensor, bits: int) -> torch.Tensor:

@@ -243,6 +243,63 @@ moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets
                     w13_scales, w13_zeros, w2_codes, w2_scales, w2_zeros, y_perm, workspace, workspace_bytes, stream);
 }
 
+size_t moe_layer_workspace_size(int T, int k, int E, int H, int I) {
+  if (T < 1 || k < 1 || E < 1 || H < 1 || I < 1) return 0;
+  return round_up(layer_workspace_bytes(T, k, E, H, I), 256);
+}
+
+static moe_status layer(const char *name, int bits, const uint16_t *x, const uint16_t *w_router,
+                        const float *logit_bias, int T, int H, int E, int k, int I, const uint32_t *w13_codes,
+                        const uint16_t *w13_scales, const uint8_t *w13_zeros, const uint32_t *w2_codes,
+                        const uint16_t *w2_scales, const uint8_t *w2_zeros, uint16_t *y, int32_t *topk_ids,
+                        float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status s = check_common_moe(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
+  if (T == 0) return MOE_OK;
+  if (!layer_shape_ok(T, k, E, H, I, bits))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "%s: one-launch layer needs 1 <= T <= %d and a decode-path shape (T=%d, k=%d, E=%d, H=%d, I=%d); "
+                "call the stages instead",
+                name, kDecodeMaxT, T, k, E, H, I);
+  if (!x || !w_router || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !y || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+  if (bits == 2 && (!w13_zeros || !w2_zeros)) return fail(MOE_ERR_INVALID_ARG, "%s: zero-points are required", name);
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16))
+    return fail(MOE_ERR_MISALIGNED, "%s: x, w_router and code arrays need 16-byte alignment", name);
+  if (!aligned(w13_scales, 2) || !aligned(w2_scales, 2) || !aligned(y, 4) || (topk_ids && !aligned(topk_ids, 4)) ||
+      (topk_weights && !aligned(topk_weights, 4)) || (logit_bias && !aligned(logit_bias, 4)))
+    return fail(MOE_ERR_MISALIGNED, "%s: array alignment", name);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
+  const size_t need = moe_layer_workspace_size(T, k, E, H, I);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", name, workspace_bytes, need);
+  DeviceInfo dev;
+  hipError_t he = current_device_info(&dev);
+  if (he != hipSuccess) return from_hip(he, name);
+  FfnArgs a{x, nullptr, nullptr, nullptr, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
+            w2_codes, w2_scales, w2_zeros, nullptr, workspace};
+  LayerArgs l{w_router, logit_bias, y, topk_ids, topk_weights, nullptr};
+  return from_hip(launch_layer_decode(a, l, dev, (hipStream_t)stream), name);
+}
+
+moe_status moe_layer_w4a16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,
+                           int k, int I, const uint32_t *w13_codes, const uint16_t *w13_scales,
+                           const uint32_t *w2_codes, const uint16_t *w2_scales, uint16_t *y, int32_t *topk_ids,
+                           float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+  return layer("moe_layer_w4a16", 4, x, w_router, logit_bias, T, H, E, k, I, w13_codes, w13_scales, nullptr,
+               w2_codes, w2_scales, nullptr, y, topk_ids, topk_weights, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_layer_w2a16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,
+                           int k, int I, const uint32_t *w13_codes, const uint16_t *w13_scales,
+                           const uint8_t *w13_zeros, const uint32_t *w2_codes, const uint16_t *w2_scales,
+                           const uint8_t *w2_zeros, uint16_t *y, int32_t *topk_ids, float *topk_weights,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return layer("moe_layer_w2a16", 2, x, w_router, logit_bias, T, H, E, k, I, w13_codes, w13_scales, w13_zeros,
+               w2_codes, w2_scales, w2_zeros, y, topk_ids, topk_weights, workspace, workspace_bytes, stream);
+}
+
 moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const float *topk_weights, int T, int k, int H,
                        uint16_t *y, void *stream) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);

@@ -21,9 +21,12 @@ constexpr int kGroup = 128;  // quantisation group along K
 //   route workspace:
 //   [32]         selector blocks finished (several selectors grouping rows)
 //   expert-FFN workspace:
-//   [64 ..]      per-active-expert counters, kCtrStride apart
+//   [32]         fused decode layer: combining blocks finished
+//   [64 ..]      per-active-expert counters, kCtrStride apart, then the fused
+//                layer's "past routing" counters
 constexpr int kCtlError = 2;
 constexpr int kCtlRouteSel = 32;
+constexpr int kCtlLayerDone = 32;
 constexpr int kCtlCounters = 64;
 constexpr int kCtrStride = 32;   // ints between counters: one 128-byte line each
 constexpr int kCtlWords = 1024;  // minimum control block: 4 KiB

@@ -43,6 +43,7 @@
 
 #include "common.cuh"
 #include "internal.h"
+#include "route_dev.cuh"
 
 namespace bqmoe {
 namespace {
@@ -69,12 +70,29 @@ struct DecodeParams {
   uint32_t *hbuf;  // [T*k, I] words: kHReady | bf16 bits once written, 0 before
   int *ctl;
   int max_spins;
+  // fused decode layer only
+  const uint16_t *w_router;
+  const float *bias;
+  uint64_t *tl;         // [T, E] tagged logit words
+  uint64_t *rec;        // [T * k] routing record: kRecTag | id << 32 | gate bits
+  uint32_t *ybuf;       // [T*k, H] words: kHReady | bf16 y_perm value once written, 0 before
+  uint16_t *y;          // [T, H] bf16 out
+  int32_t *ids_out;     // [T, k] or null
+  float *gates_out;     // [T, k] or null
+  float *logits_out;    // [T, E] or null
   uint32_t magic;  // 0x43434343 (the bf16 high byte of 128); an argument so that it sits in an SGPR
 };
 
 // Per active slot a: finished phase-2 items, on its own 128-byte line.
 __device__ __forceinline__ int *done2(int *ctl, int a) { return ctl + kCtlCounters + a * kCtrStride; }
+// Fused layer: blocks past their routing step, spread over kRoutedN lines
+// after the Amax slot counters (block b counts on line b % kRoutedN).
+constexpr int kRoutedN = 16;
+__device__ __forceinline__ int *routed_ctr(int *ctl, int amax, int i) {
+  return ctl + kCtlCounters + (amax + i) * kCtrStride;
+}
 constexpr uint32_t kHReady = 1u << 16;  // tag of a written h word
+constexpr uint64_t kRecTag = 1ull << 63;  // tag of a written routing record word
 
 // ---------------------------------------------------------------- operands
 // One chunk of natural-order bf16 activations (d: pairs (x0,x1), (x2,x3), ...)
@@ -383,7 +401,64 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v))
 // FAST: every wave's phase-1 group range and the phase-2 K split into full
 // chunks of kChunkG groups (H % 4096 == 0 and I % 1024 == 0); the first chunk
 // of weights is then requested before the activations are staged.
-template <int BITS, bool ONE, bool FAST>
+// The grouping the fused layer's items need, by one wave: for the rows r < n
+// (expert ids[r] in LDS, all valid) the sorted position pos(r) =
+// #{q : (ids[q], q) < (ids[r], r)}, sorted[pos(r)] = r and rowpos[r] = pos(r);
+// for every expert e with rows, in ascending order (slot a = number of such
+// experts below e): act[1 + a] = e, off[e] = its first sorted position and
+// off[e + 1] = one past its last (off is written for those entries only);
+// act[0] = number of experts with rows.  The same order as moe_permute.
+// Every lane reads the ids with same-address LDS loads (one broadcast each);
+// head[n] is LDS scratch.
+__device__ void layer_group_rows(const int32_t *ids, int n, int32_t *off, int32_t *sorted, int32_t *rowpos,
+                                 int32_t *act, int32_t *head) {
+  const int lane = lane_id();
+#pragma unroll 1
+  for (int r = lane; r < n; r += kWave) {
+    const int kr = ids[r];
+    int less = 0, eqb = 0, cnt = 0;
+#pragma unroll 4
+    for (int q = 0; q < n; ++q) {
+      const int kq = ids[q];
+      less += kq < kr;
+      eqb += (kq == kr) & (q < r);
+      cnt += kq == kr;
+    }
+    const int pos = less + eqb;
+    sorted[pos] = r;
+    rowpos[r] = pos;
+    head[r] = eqb == 0;
+    if (eqb == 0) {
+      off[kr] = less;
+      off[kr + 1] = less + cnt;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  int n_act = 0;
+#pragma unroll 1
+  for (int r = lane; r < n; r += kWave) {
+    const int kr = ids[r];
+    int slot = 0;
+    n_act = 0;
+#pragma unroll 4
+    for (int q = 0; q < n; ++q) {
+      const int h = head[q];
+      slot += h & (ids[q] < kr);
+      n_act += h;
+    }
+    if (head[r]) act[1 + slot] = kr;
+  }
+  if (lane == 0) act[0] = n_act;
+}
+
+// LAYER: the whole decode layer in one launch.  Before its items every block
+// (a) computes router logits, one wave per expert, stored as tagged words;
+// (b) block t < T runs token t's top-k (the same functions as the router
+// kernels, so the same bits) and publishes ids and gates as tagged words;
+// (c) every block reads those T*k words and groups the rows by expert itself,
+// keeping the result in LDS.  After its items, block b < H/128 combines
+// columns [128 b, 128 b + 128) of y from the tagged y_perm words.
+template <int BITS, bool ONE, bool FAST, bool LAYER>
 __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int RM = ONE ? 1 : kRMax;
@@ -395,25 +470,99 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int m = lane % 16, lsub = lane / 16;
   const int nrows = p.T * p.k;
-  // With one token every active slot holds one of its k distinct experts, so
-  // the item partition uses Amax (= k) without first reading the count.
-  const int A = ONE ? p.Amax : min(max(sload(p.active), 0), p.Amax);
   const int per1 = p.I / kRows1, per2 = p.H / kRows2;
-  const int n1 = A * per1, n2 = A * per2;
   const int G1 = p.H / kGroup, G2 = p.I / kGroup;
-  const int Gw1 = (G1 + 3) / 4;  // phase-1 groups per wave
-
   const int pitch1 = p.H * 2 + 16, pitch2 = p.I * 2 + 16;
   const int pmax = pitch1 > pitch2 ? pitch1 : pitch2;
   uint8_t *act = lds;
   float *Xs = (float *)(lds + RM * pmax);
   float *red = Xs + 16 * (G1 > G2 ? G1 : G2);
+  // fused layer: routing results in LDS after the FFN's own arrays
+  const int n_act_slots = 1 + min(p.E, nrows);
+  int32_t *s_ids = (int32_t *)(red + kRedFloats);
+  float *s_gates = (float *)(s_ids + nrows);
+  int32_t *s_off = (int32_t *)(s_gates + nrows);  // [E + 1]
+  int32_t *s_act = s_off + p.E + 1;               // [1 + min(E, T*k)]
+  int32_t *s_sorted = s_act + n_act_slots;
+  int32_t *s_rowpos = s_sorted + nrows;
+  int32_t *s_head = s_rowpos + nrows;
+  if constexpr (LAYER) {
+    // (a) router logits: wave w of block b takes experts 4 b + w, 4 (b + grid) + w, ...
+    const int L = p.H / 64;
+    for (int e = blockIdx.x * 4 + wv; e < p.E; e += gridDim.x * 4) {
+      if (L % 8 == 0)
+        router_logits_wave<8, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
+      else if (L % 4 == 0)
+        router_logits_wave<4, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
+      else
+        router_logits_wave<2, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
+    }
+    // (b) selectors: wave 0 of block t runs token t's top-k (reading and then
+    // clearing its logits) and publishes the ids and gates as one tagged word
+    // each.  Publishing k words instead of having every block read all E
+    // logits keeps the many readers of (c) off a few hot memory lines.
+    if (wv == 0)
+      for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
+        const TaggedLogits ld{p.tl + (size_t)t * p.E, p.E, p.max_spins, p.ctl, true,
+                              p.logits_out ? p.logits_out + (size_t)t * p.E : nullptr};
+        int32_t *ids = s_ids + t * p.k;
+        float *g = s_gates + t * p.k;
+        topk_softmax_any(ld, p.E, p.k, ids, g);
+        __builtin_amdgcn_wave_barrier();
+        if (lane < p.k) {
+          const uint64_t w = kRecTag | ((uint64_t)(uint32_t)ids[lane] << 32) | __float_as_uint(g[lane]);
+          __hip_atomic_store(p.rec + t * p.k + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (p.ids_out) p.ids_out[t * p.k + lane] = ids[lane];
+          if (p.gates_out) p.gates_out[t * p.k + lane] = g[lane];
+        }
+      }
+    // (c) every block reads the record (backing off between reads), then wave 0 groups the rows
+    {
+      bool ok = true;
+      for (int r = threadIdx.x; r < nrows; r += 256) {
+        uint64_t w = 0;
+        for (int spins = 0;; ++spins) {
+          w = __hip_atomic_load(p.rec + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (w & kRecTag) break;
+          if (spins >= p.max_spins) {
+            ok = false;
+            break;
+          }
+          const int nz = min(1 << min(spins, 4), 8);
+          for (int z = 0; z < nz; ++z) __builtin_amdgcn_s_sleep(2);
+        }
+        s_ids[r] = (int32_t)((w >> 32) & 0x7FFFFFFFu);
+        s_gates[r] = __uint_as_float((uint32_t)w);
+      }
+      if (!ok) atomicOr(&p.ctl[kCtlError], 1);
+    }
+    lds_barrier();
+    if (wv == 0) layer_group_rows(s_ids, nrows, s_off, s_sorted, s_rowpos, s_act, s_head);
+    lds_barrier();
+    if (threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
+  }
+  // With one token every active slot holds one of its k distinct experts, so
+  // the item partition uses Amax (= k) without first reading the count.
+  const int A = ONE ? p.Amax : LAYER ? min(max(s_act[0], 0), p.Amax) : min(max(sload(p.active), 0), p.Amax);
+  const int n1 = A * per1, n2 = A * per2;
+  const int Gw1 = (G1 + 3) / 4;  // phase-1 groups per wave
+  auto get_meta = [&](int a) -> Meta {
+    if constexpr (LAYER) {
+      Meta r;
+      r.e = min(max(s_act[1 + a], 0), p.E - 1);
+      r.o0 = min(max(s_off[r.e], 0), nrows);
+      r.o1 = min(max(s_off[r.e + 1], r.o0), nrows);
+      return r;
+    } else {
+      return meta<ONE>(p, a, nrows);
+    }
+  };
 
   for (int item = blockIdx.x; item < n1 + n2; item += gridDim.x) {
     if (item < n1) {
       // ============================================================ phase 1
       const int a = item / per1, i0 = (item - a * per1) * kRows1;
-      const Meta md = meta<ONE>(p, a, nrows);
+      const Meta md = get_meta(a);
       const int g0 = wv * Gw1, ng = max(min(Gw1, G1 - g0), 0);
       const size_t erows = (size_t)md.e * 2 * p.I;  // first row of the expert
       const ExpertW xw = {(const uint8_t *)p.w13c + erows * (G1 * GB), (const uint8_t *)p.w13s + erows * (G1 * 2),
@@ -422,7 +571,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const int nch = ng / kChunkG;
       // activation row of sorted position q
       auto xrow = [&](int q) -> const uint16_t * {
-        const int t = ONE ? 0 : min(max(sload(p.sorted_rows + q), 0) / p.k, p.T - 1);
+        const int t = ONE ? 0 : min(max(LAYER ? s_sorted[q] : sload(p.sorted_rows + q), 0) / p.k, p.T - 1);
         return p.x + (size_t)t * p.H;
       };
       PreAct pa;
@@ -485,7 +634,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       // ============================================================ phase 2
       const int it = item - n1;
       const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 32;
-      const Meta md = meta<ONE>(p, a, nrows);
+      const Meta md = get_meta(a);
       const size_t erows = (size_t)md.e * p.H;
       const ExpertW xw = {(const uint8_t *)p.w2c + erows * (G2 * GB), (const uint8_t *)p.w2s + erows * (G2 * 2),
                           p.w2z + erows * G2};
@@ -521,14 +670,21 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          uint16_t *yrow = p.y_perm + (size_t)rb * p.H + n0 + 16 * s2 + m;
+          const size_t yo = (size_t)rb * p.H + n0 + 16 * s2 + m;
+          auto put = [&](size_t o, float v) {
+            if constexpr (LAYER)
+              __hip_atomic_store(p.ybuf + o, kHReady | (uint32_t)f32_to_bf16(v), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            else
+              p.y_perm[o] = f32_to_bf16(v);
+          };
           if (ONE) {
-            if (lsub == 0) *yrow = f32_to_bf16(ty[s2][0]);
+            if (lsub == 0) put(yo, ty[s2][0]);
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int mm = 4 * lsub + i;
-              if (mm < R) yrow[(size_t)mm * p.H] = f32_to_bf16(ty[s2][i]);
+              if (mm < R) put(yo + (size_t)mm * p.H, ty[s2][i]);
             }
           }
         }
@@ -549,16 +705,99 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       lds_barrier();  // the flag is read before the next item reuses LDS
     }
   }
+  if constexpr (LAYER) {
+    if ((int)blockIdx.x < per2) {
+      // y[t, c] = sum over j ascending of g[t, j] * y_perm[row_pos[t k + j], c] in float32,
+      // rounded once to bf16; each y_perm word is cleared once read.
+      // The words of one token are read kCombB at a time with independent
+      // loads (one round trip per batch), re-read until all carry the tag.
+      constexpr int kCombB = 8;
+      const int c = blockIdx.x * kRows2 + threadIdx.x % kRows2;
+      bool ok = true;
+      for (int t = threadIdx.x / kRows2; t < p.T; t += 256 / kRows2) {
+        float acc = 0.f;
+        for (int j0 = 0; j0 < p.k; j0 += kCombB) {
+          uint32_t *wp[kCombB];
+          uint32_t w[kCombB];
+#pragma unroll
+          for (int b = 0; b < kCombB; ++b)
+            wp[b] = p.ybuf + (size_t)s_rowpos[t * p.k + min(j0 + b, p.k - 1)] * p.H + c;
+          for (int spins = 0;; ++spins) {
+            uint32_t all = kHReady;
+#pragma unroll
+            for (int b = 0; b < kCombB; ++b) {
+              w[b] = __hip_atomic_load(wp[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              all &= w[b];
+            }
+            if (all) break;
+            if (spins >= p.max_spins) {
+              ok = false;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+#pragma unroll
+          for (int b = 0; b < kCombB; ++b) {
+            if (j0 + b < p.k) {
+              __hip_atomic_store(wp[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              acc = __builtin_fmaf(s_gates[t * p.k + j0 + b], bf16_to_f32(w[b] & 0xFFFFu), acc);
+            }
+          }
+        }
+        p.y[(size_t)t * p.H + c] = f32_to_bf16(acc);
+      }
+      if (!ok) atomicOr(&p.ctl[kCtlError], 1);
+      // The last combining block clears the routing record once every block
+      // has counted itself past its routing step, and re-zeroes the counters.
+      int *flag = (int *)red;
+      lds_barrier();
+      if (threadIdx.x == 0) *flag = atomicAdd(&p.ctl[kCtlLayerDone], 1) == per2 - 1;
+      lds_barrier();
+      if (*flag) {
+        if (wv == 0) {
+          for (int spins = 0;; ++spins) {
+            const int c = lane < kRoutedN ? __hip_atomic_load(routed_ctr(p.ctl, p.Amax, lane), __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0;
+            if (__builtin_amdgcn_readfirstlane((int)group_sum((float)c, kRoutedN)) >= (int)gridDim.x) break;
+            if (spins >= p.max_spins) {
+              if (lane == 0) atomicOr(&p.ctl[kCtlError], 1);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        lds_barrier();
+        for (int i = threadIdx.x; i < nrows; i += 256)
+          __hip_atomic_store(p.rec + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x < kRoutedN)
+          __hip_atomic_store(routed_ctr(p.ctl, p.Amax, threadIdx.x), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(&p.ctl[kCtlLayerDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
 }
 
-template <int BITS, bool ONE>
+template <int BITS, bool ONE, bool LAYER>
 const void *decode_fn_fast(bool fast) {
-  return fast ? (const void *)ffn_decode_kernel<BITS, ONE, true> : (const void *)ffn_decode_kernel<BITS, ONE, false>;
+  return fast ? (const void *)ffn_decode_kernel<BITS, ONE, true, LAYER>
+              : (const void *)ffn_decode_kernel<BITS, ONE, false, LAYER>;
 }
 
-const void *decode_kernel_fn(int bits, bool one, bool fast) {
-  if (bits == 4) return one ? decode_fn_fast<4, true>(fast) : decode_fn_fast<4, false>(fast);
-  return one ? decode_fn_fast<2, true>(fast) : decode_fn_fast<2, false>(fast);
+template <bool LAYER>
+const void *decode_fn_layer(int bits, bool one, bool fast) {
+  if (bits == 4) return one ? decode_fn_fast<4, true, LAYER>(fast) : decode_fn_fast<4, false, LAYER>(fast);
+  return one ? decode_fn_fast<2, true, LAYER>(fast) : decode_fn_fast<2, false, LAYER>(fast);
+}
+
+const void *decode_kernel_fn(int bits, bool one, bool fast, bool layer) {
+  return layer ? decode_fn_layer<true>(bits, one, fast) : decode_fn_layer<false>(bits, one, fast);
+}
+
+// LDS of the fused layer's routing results (after the FFN's own arrays).
+size_t layer_lds_bytes(int T, int k, int E) {
+  const long n = (long)T * k;
+  return (size_t)(5 * n + (long)E + 2 + (E < n ? E : n)) * 4;
 }
 
 size_t decode_lds_bytes(int H, int I, bool one) {
@@ -596,13 +835,13 @@ bool decode_layout_ok(int H, int I, int bits) {
 
 size_t ffn_ctl_bytes(int T, int k, int E) {
   const long amax = E < (long)T * k ? E : (long)T * k;
-  size_t b = (size_t)(kCtlCounters + amax * kCtrStride) * 4;
+  size_t b = (size_t)(kCtlCounters + (amax + kRoutedN) * kCtrStride) * 4;
   if (b < kCtlBytes) b = kCtlBytes;
   return (b + 255) / 256 * 256;
 }
 
-hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st) {
-  DecodeParams p;
+static void fill_params(DecodeParams &p, const FfnArgs &a, void *ws) {
+  p = DecodeParams{};
   p.x = a.x;
   p.offsets = a.offsets;
   p.sorted_rows = a.sorted_rows;
@@ -620,14 +859,17 @@ hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_
   p.w2s = a.w2_scales;
   p.w2z = a.w2_zeros;
   p.y_perm = a.y_perm;
-  p.ctl = (int *)a.ws;
-  p.hbuf = (uint32_t *)((char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E));
+  p.ctl = (int *)ws;
+  p.hbuf = (uint32_t *)((char *)ws + ffn_ctl_bytes(a.T, a.k, a.E));
   p.max_spins = 1 << 22;
   p.magic = kMagic43;
+}
+
+static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, const DeviceInfo &dev, hipStream_t st) {
   const bool one = a.T == 1;
   const bool fast = (a.H / kGroup) % (4 * kChunkG) == 0 && (a.I / kGroup) % kChunkG == 0;
-  const void *fn = decode_kernel_fn(a.bits, one, fast);
-  const size_t lds = decode_lds_bytes(a.H, a.I, one);
+  const void *fn = decode_kernel_fn(a.bits, one, fast, layer);
+  const size_t lds = decode_lds_bytes(a.H, a.I, one) + (layer ? layer_lds_bytes(a.T, a.k, a.E) : 0);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long blocks = (long)p.Amax * (a.I / kRows1 + a.H / kRows2);
@@ -636,6 +878,42 @@ hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_
   if (blocks < 1) blocks = 1;
   void *args[] = {&p};
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, lds, st);
+}
+
+hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st) {
+  DecodeParams p;
+  fill_params(p, a, a.ws);
+  return launch_decode(p, a, false, dev, st);
+}
+
+// Fused layer workspace: control block, tagged h, tagged logits, tagged y_perm.
+static size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+size_t layer_workspace_bytes(int T, int k, int E, int H, int I) {
+  const size_t n = (size_t)T * k;
+  return ffn_ctl_bytes(T, k, E) + al256(n * I * 4) + al256((size_t)T * E * 8) + al256(n * H * 4) + al256(n * 8);
+}
+
+bool layer_shape_ok(int T, int k, int E, int H, int I, int bits) {
+  return T >= 1 && T <= kDecodeMaxT && decode_layout_ok(H, I, bits) &&
+         decode_lds_bytes(H, I, T == 1) + layer_lds_bytes(T, k, E) <= 64 * 1024;
+}
+
+hipError_t launch_layer_decode(const FfnArgs &a, const LayerArgs &l, const DeviceInfo &dev, hipStream_t st) {
+  DecodeParams p;
+  fill_params(p, a, a.ws);
+  const size_t n = (size_t)a.T * a.k;
+  char *base = (char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E);
+  p.hbuf = (uint32_t *)base;
+  p.tl = (uint64_t *)(base + al256(n * a.I * 4));
+  p.ybuf = (uint32_t *)(base + al256(n * a.I * 4) + al256((size_t)a.T * a.E * 8));
+  p.rec = (uint64_t *)((char *)p.ybuf + al256(n * a.H * 4));
+  p.w_router = l.w_router;
+  p.bias = l.bias;
+  p.y = l.y;
+  p.ids_out = l.ids;
+  p.gates_out = l.gates;
+  p.logits_out = l.logits;
+  return launch_decode(p, a, true, dev, st);
 }
 
 }  // namespace bqmoe

@@ -55,6 +55,19 @@ struct FfnArgs {
   void *ws;
 };
 hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
+
+// Fused decode layer (ffn_decode.hip): router, grouping, expert FFN and combine in one launch.
+struct LayerArgs {
+  const uint16_t *w_router;
+  const float *bias;
+  uint16_t *y;
+  int32_t *ids;    // optional outputs
+  float *gates;
+  float *logits;
+};
+bool layer_shape_ok(int T, int k, int E, int H, int I, int bits);
+size_t layer_workspace_bytes(int T, int k, int E, int H, int I);
+hipError_t launch_layer_decode(const FfnArgs &a, const LayerArgs &l, const DeviceInfo &dev, hipStream_t st);
 hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
 
 // combine.hip

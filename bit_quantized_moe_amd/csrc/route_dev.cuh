@@ -1,0 +1,355 @@
+// Device-side pieces of the router shared by the router kernels and the fused
+// decode-layer kernel: the fixed-order logit of one expert computed by one
+// wave, the top-k + softmax of one token by one wave, and the stable grouping
+// of routed rows by expert by one wave.  See route.hip for the summation order.
+#pragma once
+
+#include <math.h>
+
+#include "common.cuh"
+
+namespace bqmoe {
+namespace {
+
+// ------------------------------------------------------------ top-k of one token
+// Selection order: logit descending, then expert index ascending.  A logit
+// becomes an order-preserving uint32 (with -0 folded into +0, so equal floats
+// give equal keys) and the pair (key, ~e) is compared as one 64-bit key, so a
+// plain maximum over the wave picks the next slot.
+__device__ __forceinline__ uint32_t ord_key(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ void key_max(uint32_t &hi, uint32_t &lo, uint32_t ohi, uint32_t olo) {
+  const bool take = (ohi > hi) || (ohi == hi && olo > lo);
+  hi = take ? ohi : hi;
+  lo = take ? olo : lo;
+}
+#define BQ_DPP_U32(v, ctrl) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), 0xF, 0xF, false))
+// Maximum (hi, lo) over the 64 lanes, in every lane.
+__device__ __forceinline__ void wave_key_max(uint32_t &hi, uint32_t &lo) {
+  key_max(hi, lo, BQ_DPP_U32(hi, 0xB1), BQ_DPP_U32(lo, 0xB1));
+  key_max(hi, lo, BQ_DPP_U32(hi, 0x4E), BQ_DPP_U32(lo, 0x4E));
+  key_max(hi, lo, BQ_DPP_U32(hi, 0x141), BQ_DPP_U32(lo, 0x141));
+  key_max(hi, lo, BQ_DPP_U32(hi, 0x140), BQ_DPP_U32(lo, 0x140));
+  key_max(hi, lo, xor16_lanes(hi), xor16_lanes(lo));
+  const uint32_t h0 = __builtin_amdgcn_readlane((int)hi, 0), l0 = __builtin_amdgcn_readlane((int)lo, 0);
+  const uint32_t h1 = __builtin_amdgcn_readlane((int)hi, 32), l1 = __builtin_amdgcn_readlane((int)lo, 32);
+  hi = h0;
+  lo = l0;
+  key_max(hi, lo, h1, l1);
+}
+
+// One wave selects the k largest logits and writes ids and softmax gates.
+// NV = values per lane (E <= 64 * NV); load(v) fills v[j] with the logit of
+// expert lane + 64 j (any value where that index is >= E).
+// PUBLISH: ids are stored with device-coherent stores (read back by another
+// block).  key_lds, when given, receives a copy of the ids.
+template <int NV, bool PUBLISH, typename Load>
+__device__ void topk_softmax_wave(Load load, int E, int k, int32_t *ids_out, float *g_out, int *key_lds) {
+  const int lane = lane_id();
+  float v[NV];
+  load(v);
+  uint32_t key[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) key[j] = (lane + kWave * j < E) ? ord_key(v[j]) : 0u;  // 0: never selected (k <= E)
+  uint32_t used = 0, my_hi = 0;
+  int my_e = 0;
+  for (int slot = 0; slot < k; ++slot) {
+    uint32_t hi = 0, lo = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = lane + kWave * j;
+      if (e < E && !((used >> j) & 1u)) key_max(hi, lo, key[j], ~(uint32_t)e);
+    }
+    wave_key_max(hi, lo);
+    const int be = (int)~lo;
+    if ((be % kWave) == lane) used |= 1u << (be / kWave);
+    if (lane == slot) {
+      my_e = be;
+      my_hi = hi;
+    }
+  }
+  const float mine = key_value(my_hi);
+  const float m = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mine)));
+  const float ex = (lane < k) ? expf(mine - m) : 0.f;
+  const float sum = group_sum(ex, kWave);
+  if (lane < k) {
+    if constexpr (PUBLISH)
+      __hip_atomic_store(ids_out + lane, my_e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      ids_out[lane] = my_e;
+    g_out[lane] = ex / sum;
+    if (key_lds) key_lds[lane] = my_e;
+  }
+}
+
+template <bool PUBLISH = false, typename Load>
+__device__ __forceinline__ void topk_softmax_any(Load load, int E, int k, int32_t *ids_out, float *g_out,
+                                                 int *key_lds = nullptr) {
+  if (E <= 64)
+    topk_softmax_wave<1, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
+  else if (E <= 128)
+    topk_softmax_wave<2, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
+  else if (E <= 256)
+    topk_softmax_wave<4, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
+  else if (E <= 512)
+    topk_softmax_wave<8, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
+  else
+    topk_softmax_wave<16, PUBLISH>(load, E, k, ids_out, g_out, key_lds);
+}
+
+// ------------------------------------------------------------ grouping by expert
+// The stable grouping of n rows by expert (the result of moe_permute), done by
+// one wave in LDS: a histogram, one exclusive scan for the offsets and the
+// active list, then placement of the rows 64 at a time in row order.  Within a
+// batch of 64, lanes with the same key find each other by bit-plane ballots,
+// so a lane's rank among them is the number of lower lanes with its key.
+// key[r] is the expert of row r, or E for a dropped row; cur holds E ints.
+constexpr int kFusedRows = 256;  // largest T*k grouped inside the router launch
+
+__device__ int wave_exclusive_scan(int v, int *total) {
+  const int lane = lane_id();
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  *total = __shfl(inc, kWave - 1, kWave);
+  return inc - v;
+}
+
+__device__ void wave_group_rows(const int *key, int n, int E, int *cur, int32_t *offsets, int32_t *sorted_rows,
+                                int32_t *row_pos, int32_t *active, int n_active_slots) {
+  const int lane = lane_id();
+  for (int e = lane; e < E; e += kWave) cur[e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int r = lane; r < n; r += kWave) {
+    const int kk = key[r];
+    if (kk < E) atomicAdd(&cur[kk], 1);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane owns the experts [e0, e1)
+  const int seg = (E + kWave - 1) / kWave;
+  const int e0 = min(E, lane * seg), e1 = min(E, e0 + seg);
+  int rows = 0, acts = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = cur[e];
+    rows += c;
+    acts += c > 0;
+  }
+  int n_valid = 0, n_act = 0;
+  int base = wave_exclusive_scan(rows, &n_valid);
+  int abase = wave_exclusive_scan(acts, &n_act);
+  __builtin_amdgcn_wave_barrier();
+  for (int e = e0; e < e1; ++e) {
+    const int c = cur[e];
+    offsets[e] = base;
+    cur[e] = base;
+    if (c > 0) active[1 + abase++] = e;
+    base += c;
+  }
+  if (lane == 0) {
+    offsets[E] = n_valid;
+    active[0] = n_act;
+  }
+  for (int i = 1 + n_act + lane; i < n_active_slots; i += kWave) active[i] = -1;
+  __builtin_amdgcn_wave_barrier();
+  int nbits = 1;
+  while ((1 << nbits) < E + 2) ++nbits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int rb = 0; rb < n; rb += kWave) {
+    const int r = rb + lane;
+    const int kk = (r < n) ? key[r] : E + 1;  // E + 1: lanes past the last row
+    uint64_t peers = __ballot(1);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot((kk >> b) & 1);
+      peers &= ((kk >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    if (kk < E) {
+      const int pos = cur[kk] + rank;
+      sorted_rows[pos] = r;
+      row_pos[r] = pos;
+    } else if (kk == E) {
+      row_pos[r] = -1;
+    }
+    // every lane has read its cursor before the first lane of each key moves it
+    __builtin_amdgcn_wave_barrier();
+    if (rank == 0 && kk < E) cur[kk] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The same grouping for n <= 64 rows, in registers: lane r holds row r's key
+// (E for a dropped row, E + 1 past the last row) and every count is a loop
+// over the n keys read back one lane at a time.
+__device__ void wave_group_rows_small(int kr, int n, int E, int32_t *offsets, int32_t *sorted_rows, int32_t *row_pos,
+                                      int32_t *active, int n_active_slots) {
+  const int lane = lane_id();
+  int pos = 0;
+  bool first = true;  // no lower row has this key
+  for (int q = 0; q < n; ++q) {
+    const int kq = __builtin_amdgcn_readlane(kr, q);
+    pos += (kq < kr) || (kq == kr && q < lane);
+    first = first && !(kq == kr && q < lane);
+  }
+  if (lane < n) {
+    if (kr < E) {
+      sorted_rows[pos] = lane;
+      row_pos[lane] = pos;
+    } else {
+      row_pos[lane] = -1;
+    }
+  }
+  // heads: the first row of every expert that has rows
+  const uint64_t heads = __ballot(lane < n && kr < E && first);
+  const int n_act = __popcll(heads);
+  for (int e = lane; e <= E; e += kWave) {
+    int below = 0, act_below = 0, here = 0;
+    for (int q = 0; q < n; ++q) {
+      const int kq = __builtin_amdgcn_readlane(kr, q);
+      below += kq < e;
+      act_below += ((heads >> q) & 1ull) && kq < e;
+      here += kq == e;
+    }
+    offsets[e] = below;
+    if (e < E && here > 0) active[1 + act_below] = e;
+  }
+  for (int i = 1 + n_act + lane; i < n_active_slots; i += kWave) active[i] = -1;
+  if (lane == 0) active[0] = n_act;
+}
+
+constexpr int kTB = 4;  // tokens whose activation slices are loaded together
+constexpr uint64_t kLogitTag = 1ull << 32;
+
+// VEC bf16 elements per load: 8 (16 B), 4 (8 B) or 2 (4 B); kept packed.
+template <int VEC>
+struct Vec {
+  uint32_t u[VEC / 2];
+};
+template <int VEC>
+__device__ __forceinline__ Vec<VEC> load_vec(const uint16_t *p) {
+  Vec<VEC> r;
+  if constexpr (VEC == 8) {
+    const u32x4 v = *(const u32x4 *)p;
+    r.u[0] = v[0], r.u[1] = v[1], r.u[2] = v[2], r.u[3] = v[3];
+  } else if constexpr (VEC == 4) {
+    const u32x2 v = *(const u32x2 *)p;
+    r.u[0] = v[0], r.u[1] = v[1];
+  } else {
+    r.u[0] = *(const uint32_t *)p;
+  }
+  return r;
+}
+// acc += x . w over the VEC elements, ascending (bf16 x bf16 is exact in fp32,
+// so each fma adds the exact product)
+template <int VEC>
+__device__ __forceinline__ float fma_vec(const Vec<VEC> &xv, const Vec<VEC> &wv, float acc) {
+#pragma unroll
+  for (int q = 0; q < VEC / 2; ++q) {
+    acc = __builtin_fmaf(bf16lo(xv.u[q]), bf16lo(wv.u[q]), acc);
+    acc = __builtin_fmaf(bf16hi(xv.u[q]), bf16hi(wv.u[q]), acc);
+  }
+  return acc;
+}
+
+// One wave computes the logits of expert e for tokens 0..T-1 (lane s sums
+// slice s of H/64 elements in ascending h, then the 64 slice sums are combined
+// as a balanced pairwise tree, then the bias is added) and stores each as a
+// tagged 64-bit word tl[t * E + e] with a device-coherent store.  TB tokens'
+// activation slices are loaded together (register cost ~ 16 * VEC * TB / 8).
+template <int VEC, int TB = kTB>
+__device__ __forceinline__ void router_logits_wave(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                                                   const float *bias, int T, int H, int E, int e, uint64_t *tl) {
+  constexpr int NVC = 64 / VEC;  // loads per 64-element chunk of a slice
+  const int lane = lane_id();
+  const int L = H / 64;
+  const uint16_t *wrow = w + (size_t)e * H + (size_t)lane * L;
+  const float b = bias ? bias[e] : 0.f;
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    float acc[TB];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) acc[tt] = 0.f;
+    const int ntt = min(TB, T - t0);
+    for (int c0 = 0; c0 < L; c0 += 64) {
+      const int nv = min(64, L - c0) / VEC;
+      // this chunk of the weight slice and of up to TB tokens' activation slices
+      Vec<VEC> wv[NVC], xv[TB][NVC];
+#pragma unroll
+      for (int q = 0; q < NVC; ++q)
+        if (q < nv) wv[q] = load_vec<VEC>(wrow + c0 + q * VEC);
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt)
+        if (tt < ntt) {
+          const uint16_t *xr = x + (size_t)(t0 + tt) * H + (size_t)lane * L + c0;
+#pragma unroll
+          for (int q = 0; q < NVC; ++q)
+            if (q < nv) xv[tt][q] = load_vec<VEC>(xr + q * VEC);
+        }
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt)
+        if (tt < ntt) {
+#pragma unroll
+          for (int q = 0; q < NVC; ++q)
+            if (q < nv) acc[tt] = fma_vec<VEC>(xv[tt][q], wv[q], acc[tt]);
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      const float sum = group_sum(acc[tt], kWave);  // pairwise tree over the 64 slice sums
+      if (lane == 0 && t0 + tt < T)
+        __hip_atomic_store(tl + (size_t)(t0 + tt) * E + e, kLogitTag | __float_as_uint(sum + b), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Loader (for topk_softmax_any) of one token's E tagged logit words: reads
+// them with device-coherent loads until every word carries the tag, then, if
+// clear, zeroes them; out (if not null) receives the float values.  A wait
+// longer than max_spins sets the error flag in ctl and goes on.
+struct TaggedLogits {
+  uint64_t *row;
+  int E, max_spins;
+  int *ctl;
+  bool clear;
+  float *out;
+  template <typename V>
+  __device__ __forceinline__ void operator()(V &v) const {
+    constexpr int NV = sizeof(v) / sizeof(v[0]);
+    const int lane = lane_id();
+    uint64_t wv[NV];
+    for (int spins = 0;; ++spins) {
+      bool ready = true;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int ee = lane + kWave * j;
+        wv[j] = ee < E ? __hip_atomic_load(row + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kLogitTag;
+        ready = ready && (wv[j] & kLogitTag);
+      }
+      if (__ballot(!ready) == 0) break;
+      if (spins >= max_spins) {
+        if (lane == 0) atomicOr(&ctl[kCtlError], 1);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int ee = lane + kWave * j;
+      v[j] = __uint_as_float((uint32_t)wv[j]);
+      if (ee < E) {
+        if (clear) __hip_atomic_store(row + ee, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (out) out[ee] = v[j];
+      }
+    }
+  }
+};
+
+}  // namespace
+}  // namespace bqmoe

@@ -282,6 +282,43 @@ def test_layer_deterministic_and_workspace_left_zero(T):
 
 
 @pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("shape", ["tiny", "mid", "full"])
+def test_layer_fused_matches_stages(bits, shape):
+    """moe_layer_* (one launch) gives the stage calls' y, ids and gates bit for bit, and the oracle's y."""
+    dims = dict(tiny=dict(H=256, I=128, E=8, k=2), mid=dict(H=1024, I=256, E=32, k=4),
+                full=dict(H=4096, I=1024, E=256, k=8))[shape]
+    ws = bq.Workspaces("cuda")
+    Ts = (1, 2, 5, 16) if shape != "full" else (1, 16)
+    for T in Ts:
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, bits=bits, scale_sigma=0.02 if bits == 4 else 0.05,
+                           seed=2000 + T + bits, **dims)
+        inp = workload.make_layer_inputs(sp)
+        wd = weights_to_dev(inp.weights)
+        bias = to_dev(inp.logit_bias) if inp.logit_bias is not None else None
+        for rep in range(2):                                        # the workspace is reused
+            y, ids, gates = bq.layer(to_dev(inp.x), to_dev(inp.w_router), bias, wd, sp.k, sp.bits, sp.I, ws=ws,
+                                     want_routing=True)
+            st = bq.moe_layer(to_dev(inp.x), to_dev(inp.w_router), bias, wd, sp.k, sp.bits, sp.I, ws=ws)
+            assert torch.equal(ids, st["ids"]), (T, rep)
+            assert torch.equal(gates.view(torch.int32), st["gates"].view(torch.int32)), (T, rep)
+            assert torch.equal(y.view(torch.int16), st["y"].view(torch.int16)), (T, rep)
+        say(f"    fused layer T={T}: bit-exact with the stages")
+        if shape != "full" or T == 1:                               # the stages are checked at full size elsewhere
+            ref = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, sp.bits, sp.I)
+            assert oracle.rel_fro(bf16_np_to_f32(to_np(y)), ref["y"]) <= TOL
+    torch.cuda.synchronize()
+    for name, buf in ws._bufs.items():
+        assert int(buf.view(torch.int32).abs().sum()) == 0, name
+
+
+def test_layer_fused_rejects_large_batches():
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=17)
+    inp = workload.make_layer_inputs(sp)
+    with pytest.raises(bq.MoEError, match="stages"):
+        bq.layer(to_dev(inp.x), to_dev(inp.w_router), None, weights_to_dev(inp.weights), sp.k, sp.bits, sp.I)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
 def test_layer_one_workspace_across_paths(bits):
     """Decode and grouped-GEMM calls alternate on one set of workspaces: no call sees another's h."""
     ws = bq.Workspaces("cuda")
