@@ -287,27 +287,42 @@ def main():
                 plan.layer(i)
         torch.cuda.synchronize(dev)
 
+        # Steps run back to back as in a model's forward pass: one graph holds
+        # one step per weight set (set i on step i), and single-step graphs
+        # make up a remainder, so exactly K steps are timed.
         use_graph = not args.eager
         graphs = []
+        g_all = None
         if use_graph:
             for i in range(nset):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
                     plan.step(i)
                 graphs.append(g)
+            g_all = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_all, stream=stream):
+                for i in range(nset):
+                    plan.step(i)
             torch.cuda.synchronize(dev)
-        run = (lambda i: graphs[i % nset].replay()) if use_graph else (lambda i: plan.step(i % nset))
+
+        def run_steps(n):
+            if use_graph:
+                for _ in range(n // nset):
+                    g_all.replay()
+                for i in range(n % nset):
+                    graphs[i].replay()
+            else:
+                for i in range(n):
+                    plan.step(i % nset)
 
         # ---- whole-layer steps
-        for i in range(args.warmup):
-            run(i)
+        run_steps(args.warmup)
         torch.cuda.synchronize(dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0 = time.perf_counter()
         e0.record(stream)
         if not args.ffn_only:
-            for i in range(args.steps):
-                run(i)
+            run_steps(args.steps)
         e1.record(stream)
         torch.cuda.synchronize(dev)
         wall = time.perf_counter() - c0
@@ -356,7 +371,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": sp.name, "T": sp.T, "H": sp.H, "E": sp.E, "top_k": sp.k, "I": sp.I,
                    "weight_format": f"int{sp.bits} g128" + (" sym" if sp.bits == 4 else " + zero-point"),
-                   "weight_sets_cycled": nset, "launch": "hip graph per step" if use_graph else "eager",
+                   "weight_sets_cycled": nset, "launch": f"hip graph of {nset} steps (one per weight set)" if use_graph else "eager",
                    "step": "moe_layer (one launch)" if fused else "stage calls",
                    "wall_s_timed": round(wall, 4)},
         "roofline": roof,

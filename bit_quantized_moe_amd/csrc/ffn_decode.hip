@@ -74,7 +74,7 @@ struct DecodeParams {
   const uint16_t *w_router;
   const float *bias;
   uint64_t *tl;         // [T, E] tagged logit words
-  uint64_t *rec;        // [T * k] routing record: kRecTag | id << 32 | gate bits
+  uint64_t *rec;        // [T * k] routing record in sorted order: kRecTag | row << 48 | id << 32 | gate bits
   uint32_t *ybuf;       // [T*k, H] words: kHReady | bf16 y_perm value once written, 0 before
   uint16_t *y;          // [T, H] bf16 out
   int32_t *ids_out;     // [T, k] or null
@@ -85,7 +85,7 @@ struct DecodeParams {
 
 // Per active slot a: finished phase-2 items, on its own 128-byte line.
 __device__ __forceinline__ int *done2(int *ctl, int a) { return ctl + kCtlCounters + a * kCtrStride; }
-// Fused layer: blocks past their routing step, spread over kRoutedN lines
+// Fused layer: blocks done with their items (so with the routing record), spread over kRoutedN lines
 // after the Amax slot counters (block b counts on line b % kRoutedN).
 constexpr int kRoutedN = 16;
 __device__ __forceinline__ int *routed_ctr(int *ctl, int amax, int i) {
@@ -401,62 +401,141 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v))
 // FAST: every wave's phase-1 group range and the phase-2 K split into full
 // chunks of kChunkG groups (H % 4096 == 0 and I % 1024 == 0); the first chunk
 // of weights is then requested before the activations are staged.
-// The grouping the fused layer's items need, by one wave: for the rows r < n
-// (expert ids[r] in LDS, all valid) the sorted position pos(r) =
-// #{q : (ids[q], q) < (ids[r], r)}, sorted[pos(r)] = r and rowpos[r] = pos(r);
-// for every expert e with rows, in ascending order (slot a = number of such
-// experts below e): act[1 + a] = e, off[e] = its first sorted position and
-// off[e + 1] = one past its last (off is written for those entries only);
-// act[0] = number of experts with rows.  The same order as moe_permute.
-// Every lane reads the ids with same-address LDS loads (one broadcast each);
-// head[n] is LDS scratch.
-__device__ void layer_group_rows(const int32_t *ids, int n, int32_t *off, int32_t *sorted, int32_t *rowpos,
-                                 int32_t *act, int32_t *head) {
+// Fused layer routing record.  The selector block ranks the T*k rows by
+// (expert, row) - the order of moe_permute - and stores, at each sorted
+// position i, one tagged word: kRecTag | row << 48 | expert << 32 | gate bits.
+// Every block then derives its grouping from the words alone.
+constexpr int kRecRowBits = 15;  // rows < 2^15
+constexpr int kRecIdBits = 16;   // experts < 2^16
+
+// Sorted position of the rows r = lane + 64 c (c < NC, r < n) among the rows
+// q < n by (ids[q], q), from bit-plane ballots: walking the id bits from the
+// top, the lanes that agree with r on the bits so far and have a 0 where r has
+// a 1 are below r.  Rows of an earlier chunk, or a lower lane, with r's id
+// are below it too.  nbits covers every id.
+template <int NC>
+__device__ __forceinline__ void wave_rank_rows(const int (&id)[NC], int n, int nbits, int (&pos)[NC]) {
   const int lane = lane_id();
-#pragma unroll 1
-  for (int r = lane; r < n; r += kWave) {
-    const int kr = ids[r];
-    int less = 0, eqb = 0, cnt = 0;
-#pragma unroll 4
-    for (int q = 0; q < n; ++q) {
-      const int kq = ids[q];
-      less += kq < kr;
-      eqb += (kq == kr) & (q < r);
-      cnt += kq == kr;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) pos[c] = 0;
+#pragma unroll
+  for (int d = 0; d < NC; ++d) {
+    if (kWave * d >= n) break;
+    const uint64_t vm = __ballot(lane + kWave * d < n);
+    uint64_t eq[NC];
+    int less[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      eq[c] = vm;
+      less[c] = 0;
     }
-    const int pos = less + eqb;
-    sorted[pos] = r;
-    rowpos[r] = pos;
-    head[r] = eqb == 0;
-    if (eqb == 0) {
-      off[kr] = less;
-      off[kr + 1] = less + cnt;
+    for (int b = nbits - 1; b >= 0; --b) {
+      const uint64_t m = __ballot((id[d] >> b) & 1) & vm;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if ((id[c] >> b) & 1) {
+          less[c] += __popcll(eq[c] & ~m);
+          eq[c] &= m;
+        } else {
+          eq[c] &= ~m;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) pos[c] += less[c] + (d < c ? __popcll(eq[c]) : d == c ? __popcll(eq[c] & below) : 0);
+  }
+}
+
+// Selector wave: ranks the n rows (ids and gates in LDS) and stores the record.
+// NC = 0: n <= 16, ranked by comparing each row's (id, row) key with every
+// other row's, fetched with independent readlanes (a short dependence chain).
+template <int NC>
+__device__ void publish_sorted_record(const int32_t *ids, const float *gates, int n, int E, uint64_t *rec) {
+  const int lane = lane_id();
+  constexpr int NR = NC > 0 ? NC : 1;
+  int id[NR], pos[NR];
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    const int r = lane + kWave * c;
+    id[c] = r < n ? ids[r] : 0;
+  }
+  if constexpr (NC == 0) {
+    const int key = (id[0] << 4) | lane;
+    pos[0] = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (q < n) pos[0] += __builtin_amdgcn_readlane(key, q) < key;
+  } else {
+    wave_rank_rows<NC>(id, n, 32 - __clz(max(E - 1, 0)), pos);
+  }
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    const int r = lane + kWave * c;
+    if (r < n) {
+      const uint64_t w = kRecTag | ((uint64_t)r << 48) | ((uint64_t)(uint32_t)id[c] << 32) | __float_as_uint(gates[r]);
+      __hip_atomic_store(rec + pos[c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  int n_act = 0;
-#pragma unroll 1
-  for (int r = lane; r < n; r += kWave) {
-    const int kr = ids[r];
-    int slot = 0;
-    n_act = 0;
-#pragma unroll 4
-    for (int q = 0; q < n; ++q) {
-      const int h = head[q];
-      slot += h & (ids[q] < kr);
-      n_act += h;
+}
+
+// Every block, one wave: reads the n record words (re-reading, with a short
+// back-off, until all carry the tag) and fills, for sorted position i, row
+// sorted[i] (rowpos[sorted[i]] = i, gates[sorted[i]] = its gate) and, for the
+// a-th expert with rows (ascending), act[1 + a] = expert and start[a] = its
+// first sorted position; act[0] = number of such experts, start[act[0]] = n.
+// Returns false if a wait ran out (the values are then clamped, not exact).
+__device__ bool read_sorted_record(const uint64_t *rec, int n, int E, int max_spins, int32_t *sorted,
+                                   int32_t *rowpos, float *gates, int32_t *act, int32_t *start) {
+  const int lane = lane_id();
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  bool ok = true;
+  int base = 0, prev_last = -1;
+  for (int c0 = 0; c0 < n; c0 += kWave) {
+    const int i = c0 + lane;
+    uint64_t w = kRecTag;
+    for (int spins = 0;; ++spins) {
+      if (i < n) w = __hip_atomic_load(rec + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__ballot(!(w & kRecTag)) == 0) break;
+      if (spins >= max_spins) {
+        ok = false;
+        break;
+      }
+      const int nz = min(1 << min(spins, 2), 4);
+      for (int z = 0; z < nz; ++z) __builtin_amdgcn_s_sleep(2);
     }
-    if (head[r]) act[1 + slot] = kr;
+    const int row = min((int)((w >> 48) & ((1u << kRecRowBits) - 1)), n - 1);
+    const int e = min((int)((w >> 32) & ((1u << kRecIdBits) - 1)), E - 1);
+    int prev = __shfl_up(e, 1, kWave);
+    if (lane == 0) prev = prev_last;
+    const bool head = i < n && e != prev;
+    const uint64_t hm = __ballot(head);
+    if (i < n) {
+      sorted[i] = row;
+      rowpos[row] = i;
+      gates[row] = __uint_as_float((uint32_t)w);
+    }
+    if (head) {
+      const int slot = base + __popcll(hm & below);
+      act[1 + slot] = e;
+      start[slot] = i;
+    }
+    base += __popcll(hm);
+    prev_last = __shfl(e, kWave - 1, kWave);
   }
-  if (lane == 0) act[0] = n_act;
+  if (lane == 0) {
+    act[0] = base;
+    start[base] = n;
+  }
+  return ok;
 }
 
 // LAYER: the whole decode layer in one launch.  Before its items every block
 // (a) computes router logits, one wave per expert, stored as tagged words;
-// (b) block t < T runs token t's top-k (the same functions as the router
-// kernels, so the same bits) and publishes ids and gates as tagged words;
-// (c) every block reads those T*k words and groups the rows by expert itself,
-// keeping the result in LDS.  After its items, block b < H/128 combines
+// (b) block 0 runs every token's top-k (the same functions as the router
+// kernels, so the same bits), ranks the T*k rows by (expert, row) and
+// publishes them in that order as tagged words; (c) every block reads those
+// words and derives the grouping in LDS.  After its items, block b < H/128 combines
 // columns [128 b, 128 b + 128) of y from the tagged y_perm words.
 template <int BITS, bool ONE, bool FAST, bool LAYER>
 __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
@@ -478,14 +557,12 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   float *Xs = (float *)(lds + RM * pmax);
   float *red = Xs + 16 * (G1 > G2 ? G1 : G2);
   // fused layer: routing results in LDS after the FFN's own arrays
-  const int n_act_slots = 1 + min(p.E, nrows);
-  int32_t *s_ids = (int32_t *)(red + kRedFloats);
-  float *s_gates = (float *)(s_ids + nrows);
-  int32_t *s_off = (int32_t *)(s_gates + nrows);  // [E + 1]
-  int32_t *s_act = s_off + p.E + 1;               // [1 + min(E, T*k)]
-  int32_t *s_sorted = s_act + n_act_slots;
+  int32_t *s_ids = (int32_t *)(red + kRedFloats);  // [T*k] selector block only
+  float *s_gates = (float *)(s_ids + nrows);       // [T*k] gate of flat row r
+  int32_t *s_sorted = (int32_t *)(s_gates + nrows);
   int32_t *s_rowpos = s_sorted + nrows;
-  int32_t *s_head = s_rowpos + nrows;
+  int32_t *s_act = s_rowpos + nrows;  // [1 + T*k]
+  int32_t *s_start = s_act + nrows + 1;  // [1 + T*k]
   if constexpr (LAYER) {
     // (a) router logits: wave w of block b takes experts 4 b + w, 4 (b + grid) + w, ...
     const int L = p.H / 64;
@@ -497,12 +574,12 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       else
         router_logits_wave<2, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
     }
-    // (b) selectors: wave 0 of block t runs token t's top-k (reading and then
-    // clearing its logits) and publishes the ids and gates as one tagged word
-    // each.  Publishing k words instead of having every block read all E
-    // logits keeps the many readers of (c) off a few hot memory lines.
-    if (wv == 0)
-      for (int t = blockIdx.x; t < p.T; t += gridDim.x) {
+    // (b) block 0 selects: wave w runs the top-k of tokens w, w + 4, ...
+    // (reading and then clearing their logits), then wave 0 ranks all T*k
+    // rows and publishes them in sorted order.  One block doing the whole
+    // selection lets every other block read a single ready-made record.
+    if (blockIdx.x == 0) {
+      for (int t = wv; t < p.T; t += 4) {
         const TaggedLogits ld{p.tl + (size_t)t * p.E, p.E, p.max_spins, p.ctl, true,
                               p.logits_out ? p.logits_out + (size_t)t * p.E : nullptr};
         int32_t *ids = s_ids + t * p.k;
@@ -510,36 +587,28 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         topk_softmax_any(ld, p.E, p.k, ids, g);
         __builtin_amdgcn_wave_barrier();
         if (lane < p.k) {
-          const uint64_t w = kRecTag | ((uint64_t)(uint32_t)ids[lane] << 32) | __float_as_uint(g[lane]);
-          __hip_atomic_store(p.rec + t * p.k + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (p.ids_out) p.ids_out[t * p.k + lane] = ids[lane];
           if (p.gates_out) p.gates_out[t * p.k + lane] = g[lane];
         }
       }
-    // (c) every block reads the record (backing off between reads), then wave 0 groups the rows
-    {
-      bool ok = true;
-      for (int r = threadIdx.x; r < nrows; r += 256) {
-        uint64_t w = 0;
-        for (int spins = 0;; ++spins) {
-          w = __hip_atomic_load(p.rec + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (w & kRecTag) break;
-          if (spins >= p.max_spins) {
-            ok = false;
-            break;
-          }
-          const int nz = min(1 << min(spins, 4), 8);
-          for (int z = 0; z < nz; ++z) __builtin_amdgcn_s_sleep(2);
-        }
-        s_ids[r] = (int32_t)((w >> 32) & 0x7FFFFFFFu);
-        s_gates[r] = __uint_as_float((uint32_t)w);
+      lds_barrier();
+      if (wv == 0) {
+        if (nrows <= 16)
+          publish_sorted_record<0>(s_ids, s_gates, nrows, p.E, p.rec);
+        else if (nrows <= kWave)
+          publish_sorted_record<1>(s_ids, s_gates, nrows, p.E, p.rec);
+        else if (nrows <= 2 * kWave)
+          publish_sorted_record<2>(s_ids, s_gates, nrows, p.E, p.rec);
+        else
+          publish_sorted_record<4>(s_ids, s_gates, nrows, p.E, p.rec);
       }
-      if (!ok) atomicOr(&p.ctl[kCtlError], 1);
     }
+    // (c) every block reads the record and derives its grouping
+    if (wv == 0 &&
+        !read_sorted_record(p.rec, nrows, p.E, p.max_spins, s_sorted, s_rowpos, s_gates, s_act, s_start) &&
+        lane == 0)
+      atomicOr(&p.ctl[kCtlError], 1);
     lds_barrier();
-    if (wv == 0) layer_group_rows(s_ids, nrows, s_off, s_sorted, s_rowpos, s_act, s_head);
-    lds_barrier();
-    if (threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
   }
   // With one token every active slot holds one of its k distinct experts, so
   // the item partition uses Amax (= k) without first reading the count.
@@ -550,8 +619,8 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
     if constexpr (LAYER) {
       Meta r;
       r.e = min(max(s_act[1 + a], 0), p.E - 1);
-      r.o0 = min(max(s_off[r.e], 0), nrows);
-      r.o1 = min(max(s_off[r.e + 1], r.o0), nrows);
+      r.o0 = min(max(s_start[a], 0), nrows);
+      r.o1 = min(max(s_start[a + 1], r.o0), nrows);
       return r;
     } else {
       return meta<ONE>(p, a, nrows);
@@ -706,6 +775,9 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
     }
   }
   if constexpr (LAYER) {
+    // Counted after the items (not right after reading the record): the
+    // atomic's completion would otherwise hold up the first item's loads.
+    if (threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
     if ((int)blockIdx.x < per2) {
       // y[t, c] = sum over j ascending of g[t, j] * y_perm[row_pos[t k + j], c] in float32,
       // rounded once to bf16; each y_perm word is cleared once read.
@@ -721,7 +793,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
           uint32_t w[kCombB];
 #pragma unroll
           for (int b = 0; b < kCombB; ++b)
-            wp[b] = p.ybuf + (size_t)s_rowpos[t * p.k + min(j0 + b, p.k - 1)] * p.H + c;
+            wp[b] = p.ybuf + (size_t)min(max(s_rowpos[t * p.k + min(j0 + b, p.k - 1)], 0), nrows - 1) * p.H + c;
           for (int spins = 0;; ++spins) {
             uint32_t all = kHReady;
 #pragma unroll
@@ -748,7 +820,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       }
       if (!ok) atomicOr(&p.ctl[kCtlError], 1);
       // The last combining block clears the routing record once every block
-      // has counted itself past its routing step, and re-zeroes the counters.
+      // has counted itself done with it, and re-zeroes the counters.
       int *flag = (int *)red;
       lds_barrier();
       if (threadIdx.x == 0) *flag = atomicAdd(&p.ctl[kCtlLayerDone], 1) == per2 - 1;
@@ -796,8 +868,9 @@ const void *decode_kernel_fn(int bits, bool one, bool fast, bool layer) {
 
 // LDS of the fused layer's routing results (after the FFN's own arrays).
 size_t layer_lds_bytes(int T, int k, int E) {
+  (void)E;
   const long n = (long)T * k;
-  return (size_t)(5 * n + (long)E + 2 + (E < n ? E : n)) * 4;
+  return (size_t)(6 * n + 2) * 4;
 }
 
 size_t decode_lds_bytes(int H, int I, bool one) {
@@ -894,7 +967,7 @@ size_t layer_workspace_bytes(int T, int k, int E, int H, int I) {
 }
 
 bool layer_shape_ok(int T, int k, int E, int H, int I, int bits) {
-  return T >= 1 && T <= kDecodeMaxT && decode_layout_ok(H, I, bits) &&
+  return T >= 1 && T <= kDecodeMaxT && (long)T * k <= 4 * kWave && E <= (1 << kRecIdBits) && decode_layout_ok(H, I, bits) &&
          decode_lds_bytes(H, I, T == 1) + layer_lds_bytes(T, k, E) <= 64 * 1024;
 }
 

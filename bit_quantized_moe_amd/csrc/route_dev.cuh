@@ -13,9 +13,10 @@ namespace {
 
 // ------------------------------------------------------------ top-k of one token
 // Selection order: logit descending, then expert index ascending.  A logit
-// becomes an order-preserving uint32 (with -0 folded into +0, so equal floats
-// give equal keys) and the pair (key, ~e) is compared as one 64-bit key, so a
-// plain maximum over the wave picks the next slot.
+// becomes an order-preserving uint32 key (with -0 folded into +0, so equal
+// floats give equal keys; every finite logit gives a key above 0).  Each
+// slot takes the wave maximum of the keys, then the lowest expert index that
+// holds it (from one ballot per value a lane holds), and zeroes that key.
 __device__ __forceinline__ uint32_t ord_key(float v) {
   const uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -23,24 +24,17 @@ __device__ __forceinline__ uint32_t ord_key(float v) {
 __device__ __forceinline__ float key_value(uint32_t u) {
   return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
-__device__ __forceinline__ void key_max(uint32_t &hi, uint32_t &lo, uint32_t ohi, uint32_t olo) {
-  const bool take = (ohi > hi) || (ohi == hi && olo > lo);
-  hi = take ? ohi : hi;
-  lo = take ? olo : lo;
-}
 #define BQ_DPP_U32(v, ctrl) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), 0xF, 0xF, false))
-// Maximum (hi, lo) over the 64 lanes, in every lane.
-__device__ __forceinline__ void wave_key_max(uint32_t &hi, uint32_t &lo) {
-  key_max(hi, lo, BQ_DPP_U32(hi, 0xB1), BQ_DPP_U32(lo, 0xB1));
-  key_max(hi, lo, BQ_DPP_U32(hi, 0x4E), BQ_DPP_U32(lo, 0x4E));
-  key_max(hi, lo, BQ_DPP_U32(hi, 0x141), BQ_DPP_U32(lo, 0x141));
-  key_max(hi, lo, BQ_DPP_U32(hi, 0x140), BQ_DPP_U32(lo, 0x140));
-  key_max(hi, lo, xor16_lanes(hi), xor16_lanes(lo));
-  const uint32_t h0 = __builtin_amdgcn_readlane((int)hi, 0), l0 = __builtin_amdgcn_readlane((int)lo, 0);
-  const uint32_t h1 = __builtin_amdgcn_readlane((int)hi, 32), l1 = __builtin_amdgcn_readlane((int)lo, 32);
-  hi = h0;
-  lo = l0;
-  key_max(hi, lo, h1, l1);
+// Maximum over the 64 lanes (wave-uniform): four in-row DPP steps, then the
+// four row maxima from readlanes.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, BQ_DPP_U32(v, 0xB1));   // quad_perm [1,0,3,2]
+  v = max(v, BQ_DPP_U32(v, 0x4E));   // quad_perm [2,3,0,1]
+  v = max(v, BQ_DPP_U32(v, 0x141));  // row_half_mirror
+  v = max(v, BQ_DPP_U32(v, 0x140));  // row_mirror
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 // One wave selects the k largest logits and writes ids and softmax gates.
@@ -56,24 +50,30 @@ __device__ void topk_softmax_wave(Load load, int E, int k, int32_t *ids_out, flo
   uint32_t key[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) key[j] = (lane + kWave * j < E) ? ord_key(v[j]) : 0u;  // 0: never selected (k <= E)
-  uint32_t used = 0, my_hi = 0;
+  uint32_t my_key = 0;
   int my_e = 0;
   for (int slot = 0; slot < k; ++slot) {
-    uint32_t hi = 0, lo = 0;
+    uint32_t mx = key[0];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int e = lane + kWave * j;
-      if (e < E && !((used >> j) & 1u)) key_max(hi, lo, key[j], ~(uint32_t)e);
+    for (int j = 1; j < NV; ++j) mx = max(mx, key[j]);
+    mx = wave_max_u32(mx);
+    // lowest expert index with the maximum: the first j whose ballot is not
+    // empty, at its lowest lane
+    int be = 0;
+#pragma unroll
+    for (int j = NV - 1; j >= 0; --j) {
+      const uint64_t b = __ballot(key[j] == mx);
+      if (b) be = kWave * j + (__ffsll((unsigned long long)b) - 1);
     }
-    wave_key_max(hi, lo);
-    const int be = (int)~lo;
-    if ((be % kWave) == lane) used |= 1u << (be / kWave);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (lane + kWave * j == be) key[j] = 0u;
     if (lane == slot) {
       my_e = be;
-      my_hi = hi;
+      my_key = mx;
     }
   }
-  const float mine = key_value(my_hi);
+  const float mine = key_value(my_key);
   const float m = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mine)));
   const float ex = (lane < k) ? expf(mine - m) : 0.f;
   const float sum = group_sum(ex, kWave);
