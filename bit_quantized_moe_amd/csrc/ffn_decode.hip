@@ -49,7 +49,8 @@ namespace bqmoe {
 namespace {
 
 constexpr int kRows1 = 16;   // gate/up row pairs per phase-1 item
-constexpr int kRows2 = 128;  // down rows per phase-2 item (two sets of 16 per wave)
+constexpr int kRows2 = 128;  // down rows per phase-2 item (kSets2 sets of 16 per wave)
+constexpr int kSets2 = kRows2 / 64;
 constexpr int kChunkG = 8;   // K groups whose loads a wave keeps in flight together
 constexpr int kRMax = 4;     // routed rows staged per pass when T > 1
 constexpr int kRedFloats = 4 * 2 * 16 * 16;  // phase-1 cross-wave partials
@@ -461,11 +462,11 @@ __device__ void publish_sorted_record(const int32_t *ids, const float *gates, in
     id[c] = r < n ? ids[r] : 0;
   }
   if constexpr (NC == 0) {
-    const int key = (id[0] << 4) | lane;
+    // lanes past n get the largest key, so they are never counted as lower
+    const int key = lane < n ? (id[0] << 4) | lane : 0x7fffffff;
     pos[0] = 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (q < n) pos[0] += __builtin_amdgcn_readlane(key, q) < key;
+    for (int q = 0; q < 16; ++q) pos[0] += __builtin_amdgcn_readlane(key, q) < key;
   } else {
     wave_rank_rows<NC>(id, n, 32 - __clz(max(E - 1, 0)), pos);
   }
@@ -556,8 +557,12 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   uint8_t *act = lds;
   float *Xs = (float *)(lds + RM * pmax);
   float *red = Xs + 16 * (G1 > G2 ? G1 : G2);
-  // fused layer: routing results in LDS after the FFN's own arrays
-  int32_t *s_ids = (int32_t *)(red + kRedFloats);  // [T*k] selector block only
+  // fused layer: routing results in LDS after the FFN's own arrays, or after
+  // the router's rows where those are larger (they share the start of LDS)
+  const size_t ffn_bytes = (size_t)((uint8_t *)(red + kRedFloats) - lds);
+  const bool lds_router = LAYER && router_lds_ok(p.H);
+  const size_t rbytes = lds_router ? router_lds_bytes(p.H) : 0;
+  int32_t *s_ids = (int32_t *)(lds + (ffn_bytes > rbytes ? ffn_bytes : rbytes));  // [T*k] selector block only
   float *s_gates = (float *)(s_ids + nrows);       // [T*k] gate of flat row r
   int32_t *s_sorted = (int32_t *)(s_gates + nrows);
   int32_t *s_rowpos = s_sorted + nrows;
@@ -565,14 +570,47 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   int32_t *s_start = s_act + nrows + 1;  // [1 + T*k]
   if constexpr (LAYER) {
     // (a) router logits: wave w of block b takes experts 4 b + w, 4 (b + grid) + w, ...
-    const int L = p.H / 64;
-    for (int e = blockIdx.x * 4 + wv; e < p.E; e += gridDim.x * 4) {
-      if (L % 8 == 0)
-        router_logits_wave<8, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
-      else if (L % 4 == 0)
-        router_logits_wave<4, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
-      else
-        router_logits_wave<2, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
+    if (lds_router && p.E <= 2 * (int)gridDim.x) {
+      // block b takes experts 2 b + pair (waves 2 pair, 2 pair + 1): both waves
+      // load half of the weight row each and the block each token's
+      // activations, with coalesced loads, re-laid in LDS by slice; the
+      // pair's first wave runs the dot
+      if ((int)blockIdx.x * 2 < p.E) {
+        const int sw64 = 64 * router_slice_words(p.H);
+        const int pair = wv >> 1, half = wv & 1, nch = p.H / 8;
+        uint32_t *xl = (uint32_t *)lds;
+        uint32_t *wl = xl + sw64 * (1 + pair);
+        const int e = blockIdx.x * 2 + pair;
+        const bool has = e < p.E;
+        // the weight half-row and token 0's activations in one batch of loads
+        // (a wave without an expert loads its pair's row, unused)
+        rows_to_slices<4, 2>(p.w_router + (size_t)min(e, p.E - 1) * p.H, wl, half * (nch / 2),
+                             (half + 1) * (nch / 2), lane, kWave, p.x, xl, 0, nch, threadIdx.x, 256, p.H);
+        const float b = has && p.bias ? p.bias[e] : 0.f;
+        for (int t = 0; t < p.T; ++t) {
+          if (t > 0) {
+            lds_barrier();  // every wave is done with the previous token
+            row_to_slices<2>(p.x + (size_t)t * p.H, p.H, xl, 0, nch, threadIdx.x, 256);
+          }
+          lds_barrier();
+          if (has && half == 0) {
+            const float v = router_dot_slices(xl, wl, p.H, b);
+            if (lane == 0)
+              __hip_atomic_store(p.tl + (size_t)t * p.E + e, kLogitTag | __float_as_uint(v), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    } else {
+      const int L = p.H / 64;
+      for (int e = blockIdx.x * 4 + wv; e < p.E; e += gridDim.x * 4) {
+        if (L % 8 == 0)
+          router_logits_wave<8, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
+        else if (L % 4 == 0)
+          router_logits_wave<4, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
+        else
+          router_logits_wave<2, 1>(p.x, p.w_router, p.bias, p.T, p.H, p.E, e, p.tl);
+      }
     }
     // (b) block 0 selects: wave w runs the top-k of tokens w, w + 4, ...
     // (reading and then clearing their logits), then wave 0 ranks all T*k
@@ -702,17 +740,19 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
     } else {
       // ============================================================ phase 2
       const int it = item - n1;
-      const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 32;
+      const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 16 * kSets2;
       const Meta md = get_meta(a);
       const size_t erows = (size_t)md.e * p.H;
       const ExpertW xw = {(const uint8_t *)p.w2c + erows * (G2 * GB), (const uint8_t *)p.w2s + erows * (G2 * 2),
                           p.w2z + erows * G2};
-      const Off o2[2] = {row_off(n0 + m, G2, 0, GB, lsub), row_off(n0 + 16 + m, G2, 0, GB, lsub)};
+      Off o2[kSets2];
+#pragma unroll
+      for (int s2 = 0; s2 < kSets2; ++s2) o2[s2] = row_off(n0 + 16 * s2 + m, G2, 0, GB, lsub);
       const int nch = G2 / kChunkG;
-      Chunk<BITS> wd[2];
+      Chunk<BITS> wd[kSets2];
       if constexpr (FAST) {
-        load_chunk<BITS>(xw, o2[0], wd[0]);
-        load_chunk<BITS>(xw, o2[1], wd[1]);
+#pragma unroll
+        for (int s2 = 0; s2 < kSets2; ++s2) load_chunk<BITS>(xw, o2[s2], wd[s2]);
       }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
@@ -721,24 +761,26 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         const int arow = ONE ? 0 : min(m, R - 1);
         const uint8_t *ap = act + arow * pitch2 + lsub * 64;
         const float *xs = Xs + (ONE ? 0 : 4 * lsub);
-        f32x4 ty[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 ty[kSets2];
+#pragma unroll
+        for (int s2 = 0; s2 < kSets2; ++s2) ty[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (FAST) {
           for (int ch = 0; ch < nch; ++ch) {
             if (ch > 0) {
-              load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wd[0]);
-              load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wd[1]);
+#pragma unroll
+              for (int s2 = 0; s2 < kSets2; ++s2) load_chunk<BITS>(xw, add_groups(o2[s2], ch * kChunkG, GB), wd[s2]);
             }
-            chunk_gemv<BITS, ONE, 2>(wd, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, ty);
+            chunk_gemv<BITS, ONE, kSets2>(wd, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, ty);
           }
           if (nch > 1 && rb + RM < md.o1) {
-            load_chunk<BITS>(xw, o2[0], wd[0]);
-            load_chunk<BITS>(xw, o2[1], wd[1]);
+#pragma unroll
+            for (int s2 = 0; s2 < kSets2; ++s2) load_chunk<BITS>(xw, o2[s2], wd[s2]);
           }
         } else {
-          groups_gemv_slow<BITS, ONE, 2>(xw, o2, G2, ap, xs, magic, ty);
+          groups_gemv_slow<BITS, ONE, kSets2>(xw, o2, G2, ap, xs, magic, ty);
         }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
+        for (int s2 = 0; s2 < kSets2; ++s2) {
           const size_t yo = (size_t)rb * p.H + n0 + 16 * s2 + m;
           auto put = [&](size_t o, float v) {
             if constexpr (LAYER)
@@ -878,6 +920,14 @@ size_t decode_lds_bytes(int H, int I, bool one) {
   return (size_t)(one ? 1 : kRMax) * (kmax * 2 + 16) + 16 * (kmax / kGroup) * 4 + kRedFloats * 4;
 }
 
+// Fused layer: the router rows (shared start of LDS) or the FFN arrays,
+// whichever is larger, then the routing results.
+size_t layer_lds_total(int T, int k, int E, int H, int I) {
+  const size_t f = decode_lds_bytes(H, I, T == 1);
+  const size_t r = router_lds_ok(H) ? router_lds_bytes(H) : 0;
+  return (f > r ? f : r) + layer_lds_bytes(T, k, E);
+}
+
 // Co-resident blocks per CU of one decode instantiation (cached per device, kernel and LDS size).
 int resident_blocks_per_cu(const void *fn, int device, size_t lds) {
   static std::mutex mu;
@@ -942,7 +992,7 @@ static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, c
   const bool one = a.T == 1;
   const bool fast = (a.H / kGroup) % (4 * kChunkG) == 0 && (a.I / kGroup) % kChunkG == 0;
   const void *fn = decode_kernel_fn(a.bits, one, fast, layer);
-  const size_t lds = decode_lds_bytes(a.H, a.I, one) + (layer ? layer_lds_bytes(a.T, a.k, a.E) : 0);
+  const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I) : decode_lds_bytes(a.H, a.I, one);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long blocks = (long)p.Amax * (a.I / kRows1 + a.H / kRows2);
@@ -968,7 +1018,7 @@ size_t layer_workspace_bytes(int T, int k, int E, int H, int I) {
 
 bool layer_shape_ok(int T, int k, int E, int H, int I, int bits) {
   return T >= 1 && T <= kDecodeMaxT && (long)T * k <= 4 * kWave && E <= (1 << kRecIdBits) && decode_layout_ok(H, I, bits) &&
-         decode_lds_bytes(H, I, T == 1) + layer_lds_bytes(T, k, E) <= 64 * 1024;
+         layer_lds_total(T, k, E, H, I) <= 64 * 1024;
 }
 
 hipError_t launch_layer_decode(const FfnArgs &a, const LayerArgs &l, const DeviceInfo &dev, hipStream_t st) {

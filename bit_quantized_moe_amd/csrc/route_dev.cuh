@@ -263,9 +263,12 @@ __device__ __forceinline__ float fma_vec(const Vec<VEC> &xv, const Vec<VEC> &wv,
 // as a balanced pairwise tree, then the bias is added) and stores each as a
 // tagged 64-bit word tl[t * E + e] with a device-coherent store.  TB tokens'
 // activation slices are loaded together (register cost ~ 16 * VEC * TB / 8).
-template <int VEC, int TB = kTB>
-__device__ __forceinline__ void router_logits_wave(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-                                                   const float *bias, int T, int H, int E, int e, uint64_t *tl) {
+// FULL: every slice is a whole number of 64-element chunks, so the chunk
+// loop needs no guards (straight-line code; branches are costly here).
+template <int VEC, int TB, bool FULL>
+__device__ __forceinline__ void router_logits_wave_impl(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ w, const float *bias, int T,
+                                                        int H, int E, int e, uint64_t *tl) {
   constexpr int NVC = 64 / VEC;  // loads per 64-element chunk of a slice
   const int lane = lane_id();
   const int L = H / 64;
@@ -277,26 +280,26 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t *__restrict__ 
     for (int tt = 0; tt < TB; ++tt) acc[tt] = 0.f;
     const int ntt = min(TB, T - t0);
     for (int c0 = 0; c0 < L; c0 += 64) {
-      const int nv = min(64, L - c0) / VEC;
+      const int nv = FULL ? NVC : min(64, L - c0) / VEC;
       // this chunk of the weight slice and of up to TB tokens' activation slices
       Vec<VEC> wv[NVC], xv[TB][NVC];
 #pragma unroll
       for (int q = 0; q < NVC; ++q)
-        if (q < nv) wv[q] = load_vec<VEC>(wrow + c0 + q * VEC);
+        if (FULL || q < nv) wv[q] = load_vec<VEC>(wrow + c0 + q * VEC);
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt)
-        if (tt < ntt) {
+        if (TB == 1 || tt < ntt) {
           const uint16_t *xr = x + (size_t)(t0 + tt) * H + (size_t)lane * L + c0;
 #pragma unroll
           for (int q = 0; q < NVC; ++q)
-            if (q < nv) xv[tt][q] = load_vec<VEC>(xr + q * VEC);
+            if (FULL || q < nv) xv[tt][q] = load_vec<VEC>(xr + q * VEC);
         }
 #pragma unroll
       for (int tt = 0; tt < TB; ++tt)
-        if (tt < ntt) {
+        if (TB == 1 || tt < ntt) {
 #pragma unroll
           for (int q = 0; q < NVC; ++q)
-            if (q < nv) acc[tt] = fma_vec<VEC>(xv[tt][q], wv[q], acc[tt]);
+            if (FULL || q < nv) acc[tt] = fma_vec<VEC>(xv[tt][q], wv[q], acc[tt]);
         }
     }
 #pragma unroll
@@ -307,6 +310,93 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t *__restrict__ 
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+template <int VEC, int TB = kTB>
+__device__ __forceinline__ void router_logits_wave(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                                                   const float *bias, int T, int H, int E, int e, uint64_t *tl) {
+  if ((H / 64) % 64 == 0)
+    router_logits_wave_impl<VEC, TB, true>(x, w, bias, T, H, E, e, tl);
+  else
+    router_logits_wave_impl<VEC, TB, false>(x, w, bias, T, H, E, e, tl);
+}
+
+// Router logits from LDS, for H a power of two from 512 to 4096 (slices of
+// L = H/64 elements, a multiple of 8).  A slice occupies L/2 words plus 4 of padding, so every
+// 16-byte chunk of a row lands 16-byte aligned and lane s reads its slice with
+// 16-byte LDS loads.  The global reads are then fully coalesced (one 1 KB
+// stretch per load instruction), where slice-per-lane global loads touch 64
+// lines per instruction and take several times longer.
+__device__ __forceinline__ int router_slice_words(int H) { return H / 128 + 4; }
+__host__ __device__ __forceinline__ size_t router_lds_row_bytes(int H) { return (size_t)64 * (H / 128 + 4) * 4; }
+// The fused layer's LDS router: the activation row plus two weight rows (a
+// block takes two experts; two waves load each row, one wave runs its dot).
+__host__ __device__ __forceinline__ bool router_lds_ok(int H) {
+  return H >= 512 && H <= 4096 && (H & (H - 1)) == 0;
+}
+__host__ __device__ __forceinline__ size_t router_lds_bytes(int H) { return 3 * router_lds_row_bytes(H); }
+
+// Chunks [c0, c1) (8 elements each) of a bf16 row of H elements into dst in
+// the padded slice layout; thread t of nthreads loads chunks c0 + t + q * nthreads.
+template <int PER>
+__device__ __forceinline__ void row_to_slices(const uint16_t *__restrict__ row, int H, uint32_t *dst, int c0, int c1,
+                                              int t, int nthreads) {
+  const int sw = router_slice_words(H);
+  const int sh = __builtin_ctz(H / 512);  // 16-byte chunks per slice = 1 << sh
+  u32x4 a[PER];
+  // every load is issued (threads past c1 re-read the last chunk), so they
+  // are all in flight together; only the stores are guarded
+#pragma unroll
+  for (int q = 0; q < PER; ++q) a[q] = ((const u32x4 *)row)[min(c0 + t + q * nthreads, c1 - 1)];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = c0 + t + q * nthreads;
+    if (c < c1) *(u32x4 *)&dst[(c >> sh) * sw + (c & ((1 << sh) - 1)) * 4] = a[q];
+  }
+}
+
+// Two rows at once (chunk ranges of each, as above), so that both sets of
+// loads are in flight together.
+template <int PA, int PB>
+__device__ __forceinline__ void rows_to_slices(const uint16_t *__restrict__ ra, uint32_t *da, int a0, int a1, int ta,
+                                               int na, const uint16_t *__restrict__ rb, uint32_t *db, int b0, int b1,
+                                               int tb, int nb, int H) {
+  const int sw = router_slice_words(H);
+  const int sh = __builtin_ctz(H / 512);
+  u32x4 a[PA], b[PB];
+#pragma unroll
+  for (int q = 0; q < PA; ++q) a[q] = ((const u32x4 *)ra)[min(a0 + ta + q * na, a1 - 1)];
+#pragma unroll
+  for (int q = 0; q < PB; ++q) b[q] = ((const u32x4 *)rb)[min(b0 + tb + q * nb, b1 - 1)];
+#pragma unroll
+  for (int q = 0; q < PA; ++q) {
+    const int c = a0 + ta + q * na;
+    if (c < a1) *(u32x4 *)&da[(c >> sh) * sw + (c & ((1 << sh) - 1)) * 4] = a[q];
+  }
+#pragma unroll
+  for (int q = 0; q < PB; ++q) {
+    const int c = b0 + tb + q * nb;
+    if (c < b1) *(u32x4 *)&db[(c >> sh) * sw + (c & ((1 << sh) - 1)) * 4] = b[q];
+  }
+}
+
+// Lane s chains slice s of x . w (both in the padded layout) in ascending h,
+// then the 64 slice sums are combined by the pairwise tree and the bias added.
+__device__ __forceinline__ float router_dot_slices(const uint32_t *xs, const uint32_t *ws, int H, float b) {
+  const int lane = lane_id();
+  const int sw = router_slice_words(H);
+  const uint32_t *xp = xs + lane * sw, *wp = ws + lane * sw;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < H / 128; j += 4) {
+    const u32x4 xx = *(const u32x4 *)(xp + j), ww = *(const u32x4 *)(wp + j);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      acc = __builtin_fmaf(bf16lo(xx[r]), bf16lo(ww[r]), acc);
+      acc = __builtin_fmaf(bf16hi(xx[r]), bf16hi(ww[r]), acc);
+    }
+  }
+  return group_sum(acc, kWave) + b;
 }
 
 // Loader (for topk_softmax_any) of one token's E tagged logit words: reads
@@ -328,8 +418,10 @@ struct TaggedLogits {
       bool ready = true;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
+        // lanes past E re-read the last word (no branch around the load)
         const int ee = lane + kWave * j;
-        wv[j] = ee < E ? __hip_atomic_load(row + ee, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kLogitTag;
+        const uint64_t got = __hip_atomic_load(row + min(ee, E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wv[j] = ee < E ? got : kLogitTag;
         ready = ready && (wv[j] & kLogitTag);
       }
       if (__ballot(!ready) == 0) break;
@@ -340,14 +432,17 @@ struct TaggedLogits {
       __builtin_amdgcn_s_sleep(1);
     }
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int ee = lane + kWave * j;
-      v[j] = __uint_as_float((uint32_t)wv[j]);
-      if (ee < E) {
-        if (clear) __hip_atomic_store(row + ee, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (out) out[ee] = v[j];
-      }
-    }
+    for (int j = 0; j < NV; ++j) v[j] = __uint_as_float((uint32_t)wv[j]);
+    // every word has been read: clear them (lanes past E clear the last word again)
+    if (clear)
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        __hip_atomic_store(row + min(lane + kWave * j, E - 1), (uint64_t)0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (out)
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        if (lane + kWave * j < E) out[lane + kWave * j] = v[j];
   }
 };
 
