@@ -232,6 +232,154 @@ __global__ void __launch_bounds__(256) route_tiled_kernel(const uint16_t *__rest
   }
 }
 
+// ------------------------------------------------------------ large T, H % 2048 == 0
+// 16 tokens x 256 experts per pass with 512 threads (two waves per SIMD):
+// thread (ty, tx) of wave w owns tokens 4 (w % 4) .. +3 and experts
+// c0 + 128 (w / 4) + 2 tx, +1.  32-h chunks of x and w are converted to
+// float32 into LDS once per block; the next chunk is fetched into registers
+// while the current one is consumed; each h's operands are read from LDS one
+// step ahead of their use.  A slice ends on a chunk boundary (L % 32 == 0), so
+// the carry merge is a uniform switch outside the unrolled h loop.
+constexpr int kHC = 32;  // h per LDS chunk
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int LEV, int N>
+__device__ __forceinline__ void carry_merge(float (&lvl)[6][N], float (&acc)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float v = acc[i];
+#pragma unroll
+    for (int q = 0; q < LEV; ++q) v = lvl[q][i] + v;  // left subtree + right subtree
+    if constexpr (LEV < 6) {
+      lvl[LEV][i] = v;
+      acc[i] = 0.f;
+    } else {
+      acc[i] = v;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(512) route_tiled2_kernel(const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ w, const float *bias,
+                                                           int T, int H, int E, int k, int32_t *ids, float *gates,
+                                                           float *lg_out) {
+  __shared__ __attribute__((aligned(16))) float xs[kHC][kTileT];
+  __shared__ __attribute__((aligned(16))) float wsm[kHC][256];
+  extern __shared__ __attribute__((aligned(16))) float lgs[];  // [kTileT][E]
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, tx = tid % kWave;
+  const int tq = wave % 4, eh = wave / 4;  // token quad, expert half
+  const int t_base = blockIdx.x * kTileT;
+  const int cps = H / 64 / kHC;  // chunks per slice
+  const int nch = H / kHC;
+  // staging: thread tid converts 16 h of expert row c0 + tid / 2; threads
+  // < 64 one 8-h piece of token tid / 4
+  const int xt = t_base + (tid >> 2);
+  const bool xvalid = tid < 64 && xt < T;
+  const u32x4 *xrow = (const u32x4 *)(x + (size_t)min(xt, T - 1) * H) + (tid & 3);
+  const int we = tid >> 1, wh = tid & 1;
+
+  for (int c0 = 0; c0 < E; c0 += 256) {
+    const bool wvalid = c0 + we < E;
+    const u32x4 *wrow = (const u32x4 *)(w + (size_t)min(c0 + we, E - 1) * H) + 2 * wh;
+    u32x4 pw[2], px = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) pw[q] = wrow[q];
+    if (tid < 64) px = xrow[0];
+    float acc[8], lvl[6][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    int s = 0;
+    const float *xsp = &xs[0][4 * tq];
+    const float *wsp = &wsm[0][128 * eh + 2 * tx];
+    for (int ch = 0; ch < nch; ++ch) {
+      __syncthreads();  // the previous chunk has been consumed
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = wh * 16 + q * 8 + 2 * r;
+          wsm[h][we] = wvalid ? bf16lo(pw[q][r]) : 0.f;
+          wsm[h + 1][we] = wvalid ? bf16hi(pw[q][r]) : 0.f;
+        }
+      if (tid < 64)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          xs[(tid & 3) * 8 + 2 * r][tid >> 2] = xvalid ? bf16lo(px[r]) : 0.f;
+          xs[(tid & 3) * 8 + 2 * r + 1][tid >> 2] = xvalid ? bf16hi(px[r]) : 0.f;
+        }
+      __syncthreads();
+      if (ch + 1 < nch) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) pw[q] = wrow[(ch + 1) * 4 + q];
+        if (tid < 64) px = xrow[(ch + 1) * 4];
+      }
+      f32x4 xv = *(const f32x4 *)xsp;
+      f32x2 wv = *(const f32x2 *)wsp;
+#pragma unroll
+      for (int i = 0; i < kHC; ++i) {
+        f32x4 xn;
+        f32x2 wn;
+        if (i + 1 < kHC) {
+          xn = *(const f32x4 *)(xsp + (i + 1) * kTileT);
+          wn = *(const f32x2 *)(wsp + (i + 1) * 256);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) acc[a * 2 + b] = __builtin_fmaf(xv[a], wv[b], acc[a * 2 + b]);
+        if (i + 1 < kHC) {
+          xv = xn;
+          wv = wn;
+        }
+      }
+      if ((ch + 1) % cps == 0) {
+        // slice s is complete: lev = trailing one bits of s = left siblings waiting
+        switch (__builtin_ctz(~(unsigned)s)) {
+          case 0: carry_merge<0>(lvl, acc); break;
+          case 1: carry_merge<1>(lvl, acc); break;
+          case 2: carry_merge<2>(lvl, acc); break;
+          case 3: carry_merge<3>(lvl, acc); break;
+          case 4: carry_merge<4>(lvl, acc); break;
+          case 5: carry_merge<5>(lvl, acc); break;
+          default: carry_merge<6>(lvl, acc); break;  // after slice 63
+        }
+        ++s;
+      }
+    }
+    // acc holds the tree value of every output
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int e = c0 + 128 * eh + 2 * tx + b;
+        if (e < E) {
+          const float lv = acc[a * 2 + b] + (bias ? bias[e] : 0.f);
+          lgs[(4 * tq + a) * E + e] = lv;
+          const int tg = t_base + 4 * tq + a;
+          if (lg_out && tg < T) lg_out[(size_t)tg * E + e] = lv;
+        }
+      }
+  }
+  __syncthreads();
+  for (int t = wave; t < kTileT; t += 8) {
+    const int tg = t_base + t;
+    if (tg < T) {
+      const float *row = lgs + t * E;
+      topk_softmax_any(
+          [&](auto &v) {
+            constexpr int NV = sizeof(v) / sizeof(v[0]);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+              const int ee = lane_id() + kWave * j;
+              v[j] = ee < E ? row[ee] : 0.f;
+            }
+          },
+          E, k, ids + (size_t)tg * k, gates + (size_t)tg * k);
+    }
+  }
+}
+
 }  // namespace
 
 size_t route_workspace_bytes(int T, int E) {
@@ -278,8 +426,12 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *w_router, const float
     launch_route_small<false>(x, w_router, bias, T, H, E, k, ids, gates, logits, ws, GroupOut{}, st);
   } else {
     dim3 grid((T + kTileT - 1) / kTileT), block(256);
-    route_tiled_kernel<<<grid, block, (size_t)kTileT * E * sizeof(float), st>>>(x, w_router, bias, T, H, E, k, ids,
-                                                                                 gates, logits);
+    if (H % (64 * kHC) == 0)
+      route_tiled2_kernel<<<grid, dim3(512), (size_t)kTileT * E * sizeof(float), st>>>(x, w_router, bias, T, H, E, k,
+                                                                                        ids, gates, logits);
+    else
+      route_tiled_kernel<<<grid, block, (size_t)kTileT * E * sizeof(float), st>>>(x, w_router, bias, T, H, E, k, ids,
+                                                                                   gates, logits);
   }
   return hipGetLastError();
 }
