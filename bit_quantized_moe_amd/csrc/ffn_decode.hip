@@ -49,8 +49,7 @@ namespace bqmoe {
 namespace {
 
 constexpr int kRows1 = 16;   // gate/up row pairs per phase-1 item
-constexpr int kRows2 = 128;  // down rows per phase-2 item (kSets2 sets of 16 per wave)
-constexpr int kSets2 = kRows2 / 64;
+constexpr int kRows2 = 128;  // down rows per phase-2 item (two sets of 16 per wave)
 constexpr int kChunkG = 8;   // K groups whose loads a wave keeps in flight together
 constexpr int kRMax = 4;     // routed rows staged per pass when T > 1
 constexpr int kRedFloats = 4 * 2 * 16 * 16;  // phase-1 cross-wave partials
@@ -740,19 +739,17 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
     } else {
       // ============================================================ phase 2
       const int it = item - n1;
-      const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 16 * kSets2;
+      const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 32;
       const Meta md = get_meta(a);
       const size_t erows = (size_t)md.e * p.H;
       const ExpertW xw = {(const uint8_t *)p.w2c + erows * (G2 * GB), (const uint8_t *)p.w2s + erows * (G2 * 2),
                           p.w2z + erows * G2};
-      Off o2[kSets2];
-#pragma unroll
-      for (int s2 = 0; s2 < kSets2; ++s2) o2[s2] = row_off(n0 + 16 * s2 + m, G2, 0, GB, lsub);
+      const Off o2[2] = {row_off(n0 + m, G2, 0, GB, lsub), row_off(n0 + 16 + m, G2, 0, GB, lsub)};
       const int nch = G2 / kChunkG;
-      Chunk<BITS> wd[kSets2];
+      Chunk<BITS> wd[2];
       if constexpr (FAST) {
-#pragma unroll
-        for (int s2 = 0; s2 < kSets2; ++s2) load_chunk<BITS>(xw, o2[s2], wd[s2]);
+        load_chunk<BITS>(xw, o2[0], wd[0]);
+        load_chunk<BITS>(xw, o2[1], wd[1]);
       }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
@@ -761,26 +758,24 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         const int arow = ONE ? 0 : min(m, R - 1);
         const uint8_t *ap = act + arow * pitch2 + lsub * 64;
         const float *xs = Xs + (ONE ? 0 : 4 * lsub);
-        f32x4 ty[kSets2];
-#pragma unroll
-        for (int s2 = 0; s2 < kSets2; ++s2) ty[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 ty[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if constexpr (FAST) {
           for (int ch = 0; ch < nch; ++ch) {
             if (ch > 0) {
-#pragma unroll
-              for (int s2 = 0; s2 < kSets2; ++s2) load_chunk<BITS>(xw, add_groups(o2[s2], ch * kChunkG, GB), wd[s2]);
+              load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wd[0]);
+              load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wd[1]);
             }
-            chunk_gemv<BITS, ONE, kSets2>(wd, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, ty);
+            chunk_gemv<BITS, ONE, 2>(wd, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, ty);
           }
           if (nch > 1 && rb + RM < md.o1) {
-#pragma unroll
-            for (int s2 = 0; s2 < kSets2; ++s2) load_chunk<BITS>(xw, o2[s2], wd[s2]);
+            load_chunk<BITS>(xw, o2[0], wd[0]);
+            load_chunk<BITS>(xw, o2[1], wd[1]);
           }
         } else {
-          groups_gemv_slow<BITS, ONE, kSets2>(xw, o2, G2, ap, xs, magic, ty);
+          groups_gemv_slow<BITS, ONE, 2>(xw, o2, G2, ap, xs, magic, ty);
         }
 #pragma unroll
-        for (int s2 = 0; s2 < kSets2; ++s2) {
+        for (int s2 = 0; s2 < 2; ++s2) {
           const size_t yo = (size_t)rb * p.H + n0 + 16 * s2 + m;
           auto put = [&](size_t o, float v) {
             if constexpr (LAYER)
