@@ -139,13 +139,25 @@ __device__ __forceinline__ void store_act_chunk(uint8_t *row, int q, const uint3
   for (int t = 0; t < kChunkE<BITS> / 2; t += 4) *(u32x4 *)(dst + t) = u32x4{o[t], o[t + 1], o[t + 2], o[t + 3]};
 }
 
+// Through a buffer resource of the row (32-bit offsets), so that no 64-bit
+// addresses stay live across the weight loads that follow.
 template <int BITS, int NPRE>
 __device__ __forceinline__ void pre_load(const uint16_t *src0, int K, PreAct &pa) {
   const int nch = K / kChunkE<BITS>;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src0, (short)0, K * 2, 0x00020000);
 #pragma unroll
   for (int i = 0; i < NPRE; ++i) {
     const int q = threadIdx.x + 256 * i;
-    if (q < nch) load_act_chunk<BITS>(src0, q, pa.d + 4 * i);
+    if (q < nch) {
+#pragma unroll
+      for (int t = 0; t < kChunkE<BITS> / 2; t += 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(q * kChunkE<BITS> * 2 + t * 4), 0, 0);
+        pa.d[4 * i + t] = v[0];
+        pa.d[4 * i + t + 1] = v[1];
+        pa.d[4 * i + t + 2] = v[2];
+        pa.d[4 * i + t + 3] = v[3];
+      }
+    }
   }
 }
 
@@ -241,6 +253,58 @@ __device__ __forceinline__ bool stage_h_rows(uint8_t *act, float *Xs, const uint
   }
   stage_group_sums<BITS>(act, Xs, R, I);
   return ok;
+}
+
+// One-token phase 2, pipelined per K group: wave w stages the h groups
+// g = w + 4 j as their words arrive (polling between its MFMA groups), and
+// every wave runs the groups in K order as each one is staged; a staged group
+// is announced by an LDS flag.  A wave has at most kHPend such groups.
+constexpr int kHPend = 4;
+
+// Operand-order slot of element i of an activation chunk (inverse of the
+// pair order of the unpacked codes, see order_pairs).
+template <int BITS>
+__device__ __forceinline__ int chunk_slot(int i) {
+  return BITS == 4 ? (i >> 1) + 4 * (i & 1) : (i >> 2) + 4 * (i & 3);
+}
+
+// One polling round for the wave's lowest pending group (bit j of pend: group
+// wv + 4 j): every lane reads two of its h words.  Once all carry kHReady the
+// group goes to act in operand order, its sum (the arithmetic of
+// stage_group_sums) to the 16 rows of Xs, and gflag[g] is set.  Returns the
+// groups still pending.
+template <int BITS>
+__device__ uint32_t service_h(uint32_t pend, const uint32_t *h, uint8_t *act, float *Xs, int *gflag, int wv) {
+  constexpr int CE = kChunkE<BITS>;
+  const int lane = lane_id();
+  const int j = __builtin_ctz(pend);
+  const int g = wv + 4 * j;
+  const uint32_t *src = h + g * kGroup + 2 * lane;
+  const uint32_t w0 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t w1 = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__ballot(!(w0 & w1 & kHReady))) return pend;
+  const int e = g * kGroup + 2 * lane;  // element of the row (even)
+  uint16_t *row = (uint16_t *)act;
+  row[(e / CE) * CE + chunk_slot<BITS>(e % CE)] = (uint16_t)(w0 & 0xFFFFu);
+  row[(e / CE) * CE + chunk_slot<BITS>(e % CE + 1)] = (uint16_t)(w1 & 0xFFFFu);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  float sum = 0.f;
+  if (lane < 8) {
+    const u32x4 *pp = (const u32x4 *)(act + (g * kGroup + lane * 16) * 2);
+    const u32x4 v0 = pp[0], v1 = pp[1];
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      sum = dot2_bf16(v0[z], 0x3F803F80u, sum);
+      sum = dot2_bf16(v1[z], 0x3F803F80u, sum);
+    }
+  }
+  sum = group_sum(sum, 8);
+  const float v = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sum)));
+  if (lane < 16) Xs[g * 16 + lane] = v;
+  if (lane == 0) __hip_atomic_store(gflag + g, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return pend & ~(1u << j);
 }
 
 // ---------------------------------------------------------------- weights
@@ -751,7 +815,66 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         load_chunk<BITS>(xw, o2[0], wd[0]);
         load_chunk<BITS>(xw, o2[1], wd[1]);
       }
-      for (int rb = md.o0; rb < md.o1; rb += RM) {
+      // One token with full chunks (the host keeps I / 128 <= 4 kHPend for
+      // it): the per-group pipeline.
+      constexpr bool kPipe = ONE && FAST;
+      if constexpr (kPipe) {
+        int *gflag = (int *)red + 64;
+        if (threadIdx.x < G2) gflag[threadIdx.x] = 0;
+        lds_barrier();
+        const uint32_t *h = p.hbuf + (size_t)md.o0 * p.I;
+        uint32_t pend = (1u << ((G2 - wv + 3) / 4)) - 1u;
+        pend = service_h<BITS>(pend, h, act, Xs, gflag, wv);
+        const uint8_t *ap = act + lsub * 64;
+        f32x4 ty[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        bool ok = true;
+        for (int ch = 0; ch < nch; ++ch) {
+          if (ch > 0) {
+            load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wd[0]);
+            load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wd[1]);
+          }
+#pragma unroll
+          for (int c = 0; c < kChunkG; ++c) {
+            const int g = ch * kChunkG + c;
+            for (int spins = 0;; ++spins) {
+              if (__hip_atomic_load(gflag + g, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+              if (spins >= p.max_spins) {
+                ok = false;
+                break;
+              }
+              if (pend)
+                pend = service_h<BITS>(pend, h, act, Xs, gflag, wv);
+              else
+                __builtin_amdgcn_s_sleep(1);
+            }
+            Word<BITS> w2[2];
+            f32x4 cg[2];
+            w2[0] = wd[0].w[c];
+            w2[1] = wd[1].w[c];
+            group_mfma<BITS, 2>(w2, ap + g * (kGroup * 2), magic, cg);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+              const float sc = bf16_to_f32((wd[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
+              const float zo = zero_off<BITS>((wd[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
+              group_acc<ONE>(cg[r], sc, zo, Xs + g * 16, ty[r]);
+            }
+          }
+        }
+        if (!ok && threadIdx.x % kWave == 0) atomicOr(&p.ctl[kCtlError], 1);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const size_t yo = (size_t)md.o0 * p.H + n0 + 16 * s2 + m;
+          if (lsub == 0) {
+            if constexpr (LAYER)
+              __hip_atomic_store(p.ybuf + yo, kHReady | (uint32_t)f32_to_bf16(ty[s2][0]), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            else
+              p.y_perm[yo] = f32_to_bf16(ty[s2][0]);
+          }
+        }
+        lds_barrier();  // LDS is rewritten by the next item
+      }
+      for (int rb = md.o0; rb < (kPipe ? md.o0 : md.o1); rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
         if (!stage_h_rows<BITS>(act, Xs, p.hbuf + (size_t)rb * p.I, R, p.I, p.max_spins))
           atomicOr(&p.ctl[kCtlError], 1);
@@ -985,7 +1108,9 @@ static void fill_params(DecodeParams &p, const FfnArgs &a, void *ws) {
 
 static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, const DeviceInfo &dev, hipStream_t st) {
   const bool one = a.T == 1;
-  const bool fast = (a.H / kGroup) % (4 * kChunkG) == 0 && (a.I / kGroup) % kChunkG == 0;
+  // full chunks; with one token also few enough h groups for the phase-2 pipeline
+  const bool fast = (a.H / kGroup) % (4 * kChunkG) == 0 && (a.I / kGroup) % kChunkG == 0 &&
+                    (!one || a.I / kGroup <= 4 * kHPend);
   const void *fn = decode_kernel_fn(a.bits, one, fast, layer);
   const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I) : decode_lds_bytes(a.H, a.I, one);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
