@@ -728,6 +728,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
     }
   };
 
+  bool routed = false;  // fused layer: this block has counted itself done with the record
   for (int item = blockIdx.x; item < n1 + n2; item += gridDim.x) {
     if (item < n1) {
       // ============================================================ phase 1
@@ -919,6 +920,13 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         }
         lds_barrier();  // LDS is rewritten by the next pass
       }
+      // Fused layer: a phase-2 block counts itself done with the routing
+      // record once its y is stored (ahead of the done counter below, whose
+      // round trip would otherwise delay the last combiner's clean-up).
+      if (LAYER && !routed) {
+        if (threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
+        routed = true;
+      }
       // The last phase-2 item of the expert clears the expert's h words and
       // its done counter: every phase-2 item has read h by then.
       int *flag = (int *)red;
@@ -937,7 +945,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   if constexpr (LAYER) {
     // Counted after the items (not right after reading the record): the
     // atomic's completion would otherwise hold up the first item's loads.
-    if (threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
+    if (!routed && threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
     if ((int)blockIdx.x < per2) {
       // y[t, c] = sum over j ascending of g[t, j] * y_perm[row_pos[t k + j], c] in float32,
       // rounded once to bf16; each y_perm word is cleared once read.
