@@ -594,8 +594,10 @@ __device__ bool read_sorted_record(const uint64_t *rec, int n, int E, int max_sp
   return ok;
 }
 
-// LAYER: the whole decode layer in one launch.  Before its items every block
-// (a) computes router logits, one wave per expert, stored as tagged words;
+// LAYER: the whole decode layer in one launch.  Before its items (a) the
+// first blocks compute the router logits (two experts per block, staged in
+// LDS by slice, or one wave per expert where H does not suit), stored as
+// tagged words;
 // (b) block 0 runs every token's top-k (the same functions as the router
 // kernels, so the same bits), ranks the T*k rows by (expert, row) and
 // publishes them in that order as tagged words; (c) every block reads those

@@ -204,11 +204,11 @@ moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const flo
  * moe_layer_w4a16 / moe_layer_w2a16: the whole layer of a small batch in one
  * launch: y = moe_combine(expert FFN(moe_route_permute(x))), with the same
  * bits as those calls made one after another (router order, ties, gates,
- * grouping, FFN arithmetic and combine order are shared).  Every block of the
- * launch first computes router logits (one wave per expert), then runs the
- * top-k of every token and the grouping itself, streams its share of the
- * selected experts' weights, and finally some blocks combine y.  This removes
- * the launches and hand-offs between the stages on the decode path.
+ * grouping, FFN arithmetic and combine order are shared).  The blocks of the
+ * launch first compute the router logits, one block runs every token's top-k
+ * and publishes the rows grouped by expert, every block streams its share of
+ * the selected experts' weights, and finally some blocks combine y.  This
+ * removes the launches and hand-offs between the stages on the decode path.
  *
  *   x, w_router, logit_bias, T, H, E, k   as for moe_route
  *   I, w13_*, w2_*                        as for moe_expert_ffn_w4a16 / _w2a16
@@ -216,9 +216,10 @@ moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const flo
  *   topk_ids      [T, k] int32 out, or NULL;  topk_weights [T, k] float32 out, or NULL
  *   workspace     moe_layer_workspace_size(T, k, E, H, I) bytes, all-zero
  *                 before the first call, left all-zero by every call
- * Requirements: those of the stages, plus 1 <= T <= 16 and a shape the decode
- * path supports (I % 16 == 0, and its LDS fits); otherwise the call returns
- * MOE_ERR_UNSUPPORTED_SHAPE and the stage calls are the way to run the layer.
+ * Requirements: those of the stages, plus 1 <= T <= 16, T*k <= 256,
+ * E <= 65536 and a shape the decode path supports (I % 16 == 0, and its LDS
+ * fits); otherwise the call returns MOE_ERR_UNSUPPORTED_SHAPE and the stage
+ * calls are the way to run the layer.
  */
 size_t moe_layer_workspace_size(int T, int k, int E, int H, int I);
 moe_status moe_layer_w4a16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
