@@ -336,7 +336,7 @@ def main():
     distinct = [int(st["active"][0].item()) for st in plan.sets]
     mean_distinct = sum(distinct) / len(distinct)
     bpe = sp.weight_bytes_per_expert()
-    decode = sp.T <= 16
+    decode = sp.T <= 512 and sp.T * sp.k <= 6 * sp.E   # the library's decode-path dispatch (HBM-bound)
     ffn_stage = None
     if decode:
         alg = mean_distinct * bpe

@@ -74,7 +74,7 @@ size_t ffn_workspace_bytes(int T, int k, int E, int H, int I) {
   (void)E;
   (void)H;
   // h: 32-bit tagged words on the decode path, bf16 on the grouped-GEMM path
-  const size_t h_elem = T <= kDecodeMaxT ? sizeof(uint32_t) : sizeof(uint16_t);
+  const size_t h_elem = decode_path(T, k, E) ? sizeof(uint32_t) : sizeof(uint16_t);
   return round_up(ffn_ctl_bytes(T, k, E) + (size_t)T * k * I * h_elem, 256);
 }
 
@@ -218,7 +218,7 @@ static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, cons
   if (he != hipSuccess) return from_hip(he, name);
   FfnArgs a{x, expert_offsets, sorted_rows, active, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
             w2_codes, w2_scales, w2_zeros, y_perm, workspace};
-  if (T <= kDecodeMaxT && decode_layout_ok(H, I, bits))
+  if (decode_path(T, k, E) && decode_layout_ok(H, I, bits))
     return from_hip(launch_ffn_decode(a, dev, (hipStream_t)stream), name);
   // the grouped GEMMs address x and one expert's codes with 32-bit byte offsets
   if ((long long)T * H > (1LL << 30) || (long long)I * H > (1LL << 30))
@@ -261,7 +261,7 @@ static moe_status layer(const char *name, int bits, const uint16_t *x, const uin
     return fail(MOE_ERR_UNSUPPORTED_SHAPE,
                 "%s: one-launch layer needs 1 <= T <= %d and a decode-path shape (T=%d, k=%d, E=%d, H=%d, I=%d); "
                 "call the stages instead",
-                name, kDecodeMaxT, T, k, E, H, I);
+                name, kLayerMaxT, T, k, E, H, I);
   if (!x || !w_router || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !y || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
   if (bits == 2 && (!w13_zeros || !w2_zeros)) return fail(MOE_ERR_INVALID_ARG, "%s: zero-points are required", name);

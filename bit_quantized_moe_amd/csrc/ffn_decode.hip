@@ -1147,7 +1147,7 @@ size_t layer_workspace_bytes(int T, int k, int E, int H, int I) {
 }
 
 bool layer_shape_ok(int T, int k, int E, int H, int I, int bits) {
-  return T >= 1 && T <= kDecodeMaxT && (long)T * k <= 4 * kWave && E <= (1 << kRecIdBits) && decode_layout_ok(H, I, bits) &&
+  return T >= 1 && T <= kLayerMaxT && (long)T * k <= 4 * kWave && E <= (1 << kRecIdBits) && decode_layout_ok(H, I, bits) &&
          layer_lds_total(T, k, E, H, I) <= 64 * 1024;
 }
 

@@ -1,4 +1,4 @@
-// Prefill-path expert FFN (T > 16 tokens): two grouped GEMMs on bf16 MFMA.
+// Grouped-GEMM expert FFN (many rows per expert, e.g. prefill): two grouped GEMMs on bf16 MFMA.
 //
 //   G1: h[p, i] = silu(x_t . W13[e, i]) * (x_t . W13[e, I + i])   -> bf16 workspace
 //   G2: y_perm[p, n] = h[p] . W2[e, n]                            -> bf16

@@ -17,7 +17,7 @@ struct DeviceInfo {
 hipError_t current_device_info(DeviceInfo *out);
 
 // route.hip
-constexpr int kRouteSmallT = 32;  // T at or below: split-expert kernel + last-block top-k
+constexpr int kRouteSmallT = 256;  // T at or below: one block per expert (tagged logits) + selector blocks (measured faster than the token-tiled kernel up to T = 256 at H = 4096, E = 256)
 size_t route_workspace_bytes(int T, int E);
 hipError_t launch_route(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
                         int k, int32_t *ids, float *gates, float *logits, void *ws, hipStream_t st);
@@ -34,7 +34,17 @@ hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *offs
                           int32_t *row_pos, int32_t *active, void *ws, hipStream_t st);
 
 // ffn_decode.hip / ffn_prefill.hip
-constexpr int kDecodeMaxT = 16;  // T at or below uses the fused decode GEMV
+// Expert FFN dispatch: the decode path (weights streamed once per expert,
+// rows in passes of four) while the rows per expert stay few, the grouped
+// MFMA GEMMs above.  Measured at H = 4096, I = 1024, E = 256, top-8 (INT4):
+// the decode path is faster up to T = 192 (6 rows per expert when every
+// expert is active) and even at T = 256.
+constexpr int kDecodeMaxT = 512;       // never the decode path above this T
+constexpr int kDecodeRowsPerExpert = 6;
+inline bool decode_path(int T, int k, int E) {
+  return T <= kDecodeMaxT && (long)T * k <= (long)kDecodeRowsPerExpert * E;
+}
+constexpr int kLayerMaxT = 16;  // the one-launch decode layer
 size_t ffn_workspace_bytes(int T, int k, int E, int H, int I);
 size_t ffn_ctl_bytes(int T, int k, int E);  // control block at the start of the FFN workspace (x256)
 bool decode_layout_ok(int H, int I, int bits);

@@ -124,8 +124,8 @@ moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E,
 
 /* ---------------------------------------------------------------- route + permutation
  * moe_route_permute: moe_route, then moe_permute on its topk_ids, with the
- * outputs of both bit for bit (same arguments, same meaning).  For T <= 32
- * and T*k <= 256 both steps run in one launch: the block that finishes the
+ * outputs of both bit for bit (same arguments, same meaning).  For
+ * T*k <= 256 both steps run in one launch: the block that finishes the
  * top-k last groups the rows by expert in LDS, which saves a launch on the
  * decode path.  Other shapes run the two launches in order.  topk_ids are
  * always valid expert ids here, so row_pos has no -1 entries.
@@ -149,10 +149,11 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  *     y_perm[p] = W2_e h                down, H outputs, stored as bf16
  * with W = q * s dequantised from INT4 symmetric group-128 codes.  The dot
  * products accumulate in float32; h is rounded to bf16 before the down
- * projection.  T <= 16 uses the decode path (one fused GEMV kernel streaming
- * each selected expert's packed weights once); larger T uses grouped
- * bf16-MFMA GEMMs.  The permutation arrays must come from moe_permute with
- * the same T, k, E.
+ * projection.  While T <= 512 and T*k <= 6*E (at most about six rows per
+ * expert) the call uses the decode path (one fused GEMV kernel streaming each
+ * selected expert's packed weights once, rows in passes of four); otherwise
+ * grouped bf16-MFMA GEMMs.  The permutation arrays must come from moe_permute
+ * with the same T, k, E.
  *
  *   x           [T, H] bf16, 16-byte aligned
  *   w13_codes   [E, 2I, H/8]  uint32, 16-byte aligned
@@ -165,7 +166,7 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  *               leaves all of it zero again (the decode path tells written
  *               intermediate values from unwritten ones by a nonzero tag)
  * Requirements: H % 128 == 0, I % 128 == 0, 1 <= E <= 1024, 1 <= k <= 32;
- * for T > 16 also T*H <= 2^30 and I*H <= 2^30 (32-bit offsets in the GEMMs).
+ * on the grouped-GEMM path also T*H <= 2^30 and I*H <= 2^30 (32-bit offsets).
  */
 size_t moe_expert_ffn_workspace_size(int T, int k, int E, int H, int I);
 moe_status moe_expert_ffn_w4a16(const uint16_t *x, const int32_t *expert_offsets,

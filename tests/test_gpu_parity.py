@@ -367,7 +367,8 @@ def test_layer_decode_full_size(name):
     _full_decode(name, n_sets=2 if "t1_" in name else 1)
 
 
-@pytest.mark.parametrize("name", ["prefill_t4096_h4096_e256_k8_i1024_int4", "prefill_t8192_h4096_e256_k8_i1024_int2"])
+@pytest.mark.parametrize("name", ["prefill_t4096_h4096_e256_k8_i1024_int4", "prefill_t8192_h4096_e256_k8_i1024_int2",
+                                  "mid_t64_h4096_e256_k8_i1024_int4"])
 def test_layer_prefill_full_size_sampled(name):
     sp = workload.spec(name)
     inp = workload.make_layer_inputs(sp)

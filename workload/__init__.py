@@ -99,6 +99,9 @@ SPECS: Dict[str, Spec] = {
         Spec("prefill_t8192_h4096_e256_k8_i1024_int2", T=8192, H=4096, E=256, k=8, I=1024, bits=2,
              seed=1005, zipf_s=1.1, scale_sigma=0.05,
              note="2-bit experts, prefill chunk with Zipf(1.1) log-prior"),
+        Spec("mid_t64_h4096_e256_k8_i1024_int4", T=64, H=4096, E=256, k=8, I=1024, bits=4,
+             seed=1006, router_law="uniform", x_law="ar1_streams", streams=16, n_sets=2,
+             note="middle batch: 16 streams x 4 draft tokens (higher-concurrency verify), decode path"),
     ]
 }
 
