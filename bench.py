@@ -2,6 +2,7 @@
 """Throughput of the routed-expert MoE layer with low-bit experts on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu-baseline]
+                    [--experts arrays|table|host]
 
 A step is one pass of the whole layer over one batch of synthetic input
 already resident in HBM, through the C ABI: for T <= 4 one moe_layer_w4a16 /
@@ -11,7 +12,9 @@ moe_expert_ffn_w4a16/_w2a16 and moe_combine.  Decode workloads cycle through
 their distinct weight sets (and activations) step by step, so the expert bytes
 a step touches come from HBM rather than the 256 MB Infinity Cache.  By
 default each step is replayed from a HIP graph (--eager launches the calls one
-by one instead).
+by one instead).  --experts table runs the expert FFN through the address-table
+entry points with the experts in HBM, --experts host with every expert in
+pinned host memory read in place over PCIe (both as stage calls).
 
 Printed: one JSON line with tokens/s over the timed steps, the roofline of
 the dominant kernel (decode: the one-launch layer kernel, HBM-bound on the
@@ -37,6 +40,7 @@ METRIC = "MoE-layer tokens/s; decode HBM GB/s % peak; prefill MFMA % peak (1 GPU
 DEFAULT_WORKLOAD = "decode_t1_h4096_e256_k8_i1024_int4"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 16 lanes x 32 GT/s x 128/130 / 8
 FUSED_MAX_T = 4  # decode batches up to this size run as one moe_layer launch; larger ones as the stages
 
 
@@ -51,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--ffn-only", action="store_true", help="time only the expert-FFN stage launches (for profiling)")
     ap.add_argument("--stages", action="store_true", help="decode: run the stage calls instead of the one-launch layer")
+    ap.add_argument("--experts", choices=("arrays", "table", "host"), default="arrays",
+                    help="expert weights as stacked arrays, through an address table (HBM), or in pinned host memory")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (to scale the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
@@ -128,7 +134,7 @@ def finish_cpu_baseline(proc):
 class Plan:
     """Device buffers and pre-bound C-ABI calls for one workload."""
 
-    def __init__(self, sp, dev, fused=False):
+    def __init__(self, sp, dev, fused=False, experts="arrays"):
         import numpy as np
         import torch
 
@@ -137,6 +143,7 @@ class Plan:
 
         self.sp, self.dev, self.L = sp, dev, bq.lib()
         self.fused = fused
+        self.experts = experts
         T, H, E, k, I = sp.T, sp.H, sp.E, sp.k, sp.I
         n = T * k
 
@@ -153,11 +160,20 @@ class Plan:
         self.bias = up(bias) if bias is not None else None
         self.sets = []
         t0 = time.time()
-        for s in range(sp.n_sets):
+        # host memory is not cached by the GPU, so two sets are enough there
+        self.n_sets = min(sp.n_sets, 2) if experts == "host" else sp.n_sets
+        for s in range(self.n_sets):
             w = workload.make_weight_set(sp, s)
-            dw = {kk: up(v) for kk, v in w.items()}
+            if experts == "host":   # every expert's blocks in pinned host memory
+                as_torch = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16}
+                dw = {kk: torch.from_numpy(np.ascontiguousarray(v).view(as_torch.get(v.dtype, v.dtype))).pin_memory()
+                      for kk, v in w.items()}
+            else:
+                dw = {kk: up(v) for kk, v in w.items()}
             del w
             st = dict(w=dw, x=up(workload.make_x(sp, s)))
+            if experts != "arrays":
+                st["table"] = bq.expert_table(dw, sp.bits, device=dev)
             st["ids"] = torch.empty((T, k), dtype=torch.int32, device=dev)
             st["gates"] = torch.empty((T, k), dtype=torch.float32, device=dev)
             st["offsets"] = torch.empty(E + 1, dtype=torch.int32, device=dev)
@@ -165,7 +181,7 @@ class Plan:
             st["row_pos"] = torch.empty(n, dtype=torch.int32, device=dev)
             st["active"] = torch.empty(1 + min(E, n), dtype=torch.int32, device=dev)
             self.sets.append(st)
-        print(f"[bench] {sp.n_sets} weight set(s) generated and uploaded in {time.time() - t0:.1f} s", flush=True)
+        print(f"[bench] {self.n_sets} weight set(s) generated and uploaded in {time.time() - t0:.1f} s", flush=True)
         self.y_perm = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.ws_route = torch.zeros(self.L.moe_route_permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
@@ -193,7 +209,11 @@ class Plan:
         w = st["w"]
         common = (st["x"].data_ptr(), st["offsets"].data_ptr(), st["sorted_rows"].data_ptr(), st["active"].data_ptr(),
                   sp.T, sp.k, sp.E, sp.H, sp.I)
-        if sp.bits == 4:
+        if self.experts != "arrays":
+            fn = L.moe_expert_ffn_w4a16_table if sp.bits == 4 else L.moe_expert_ffn_w2a16_table
+            s = fn(*common, st["table"].data_ptr(), self.y_perm.data_ptr(), self.ws_ffn.data_ptr(),
+                   self.ws_ffn.numel(), stream)
+        elif sp.bits == 4:
             s = L.moe_expert_ffn_w4a16(*common, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
                                        w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(), self.y_perm.data_ptr(),
                                        self.ws_ffn.data_ptr(), self.ws_ffn.numel(), stream)
@@ -239,6 +259,21 @@ class Plan:
             self.stages(i)
 
 
+def host_copy_rate(torch, dev):
+    """GB/s of a plain pinned-host to device copy of 256 MiB (the link as torch drives it)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(4):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize(dev)
+    return 4 * COPY_BYTES / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -257,9 +292,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sp = workload.spec(args.workload)
-    fused = sp.T <= FUSED_MAX_T and not args.stages
-    plan = Plan(sp, dev, fused=fused)
-    nset = sp.n_sets
+    fused = sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays"
+    plan = Plan(sp, dev, fused=fused, experts=args.experts)
+    nset = plan.n_sets
     stream = torch.cuda.Stream(dev)
 
     def time_graph(fn):
@@ -338,11 +373,21 @@ def main():
     bpe = sp.weight_bytes_per_expert()
     decode = sp.T <= 512 and sp.T * sp.k <= 6 * sp.E   # the library's decode-path dispatch (HBM-bound)
     ffn_stage = None
-    if decode:
+    if decode and args.experts == "host":
+        alg = mean_distinct * bpe
+        achieved = alg / (ffn_ms * 1e-3) / 1e9
+        roof = {"bound": "pcie", "achieved": round(achieved, 1), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None,
+                "kernel": "ffn_decode_kernel (address table, experts read in place from pinned host memory)",
+                "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(ffn_ms * 1e3, 3),
+                "distinct_experts_per_launch": mean_distinct,
+                "host_to_device_copy_GBs": round(host_copy_rate(torch, dev), 1)}
+    elif decode:
         alg = mean_distinct * bpe
         achieved = alg / (ffn_ms * 1e-3) / 1e9
         ffn_stage = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(sp.name, "decode"),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(sp.name, "decode") if args.experts == "arrays" else None,
                      "kernel": "ffn_decode_kernel (expert-FFN stage: gate_up+SwiGLU+down GEMV)",
                      "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(ffn_ms * 1e3, 3),
                      "distinct_experts_per_launch": mean_distinct}
@@ -359,7 +404,7 @@ def main():
         flops = 2.0 * sp.T * sp.k * 3 * sp.H * sp.I
         achieved = flops / (ffn_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(sp.name, "prefill"),
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(sp.name, "prefill") if args.experts == "arrays" else None,
                 "kernel": "expert FFN call (ffn_gemm_kernel gate_up+SwiGLU, then down)",
                 "algorithmic_flops_per_launch": flops, "avg_launch_us": round(ffn_ms * 1e3, 3)}
 
@@ -371,7 +416,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": sp.name, "T": sp.T, "H": sp.H, "E": sp.E, "top_k": sp.k, "I": sp.I,
                    "weight_format": f"int{sp.bits} g128" + (" sym" if sp.bits == 4 else " + zero-point"),
-                   "weight_sets_cycled": nset, "launch": f"hip graph of {nset} steps (one per weight set)" if use_graph else "eager",
+                   "weight_sets_cycled": nset, "experts": args.experts, "launch": f"hip graph of {nset} steps (one per weight set)" if use_graph else "eager",
                    "step": "moe_layer (one launch)" if fused else "stage calls",
                    "wall_s_timed": round(wall, 4)},
         "roofline": roof,

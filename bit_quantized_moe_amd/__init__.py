@@ -19,7 +19,8 @@ from typing import Dict, Optional
 import torch
 
 __all__ = [
-    "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "layer", "combine", "unpack_codes",
+    "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "expert_table", "expert_ffn_table",
+    "layer", "combine", "unpack_codes",
     "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH",
 ]
 
@@ -40,6 +41,9 @@ _SIGS = {
     "moe_expert_ffn_workspace_size": (_c_size, [_c_int] * 5),
     "moe_expert_ffn_w4a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 5 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 7 + [_vp, _c_size, _vp]),
+    "moe_expert_ffn_w4a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
+    "moe_expert_ffn_w2a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
+    "moe_device_address": (_c_int, [_vp, ctypes.POINTER(ctypes.c_uint64)]),
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_layer_workspace_size": (_c_size, [_c_int] * 5),
     "moe_layer_w4a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp] * 3 + [_vp, _c_size, _vp]),
@@ -200,6 +204,74 @@ def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: D
         _check(s, "moe_expert_ffn_w2a16")
     else:
         raise MoEError("bits must be 2 or 4")
+    return y_perm
+
+
+_TABLE_FIELDS = ("w13_codes", "w13_scales", "w13_zeros", "w2_codes", "w2_scales", "w2_zeros")
+
+
+def expert_table(experts, bits: int, device=None) -> torch.Tensor:
+    """Per-expert address table [E, 6] int64 for ``expert_ffn_table``.
+
+    ``experts`` is a list with one dict per expert (the keys of the stacked
+    weights, each tensor that expert's own contiguous block, in device memory
+    or in pinned host memory), or one stacked weights dict, whose [e] slices
+    are used.  Addresses go through ``moe_device_address``, which rejects
+    memory the kernels cannot read.  The table does not keep the expert
+    tensors alive.  ``device`` is where the table itself lives: a CUDA device
+    (default: the current one) or "pinned" for pinned host memory.
+    """
+    if isinstance(experts, dict):
+        E = experts["w13_codes"].shape[0]
+        experts = [{n: t[e] for n, t in experts.items()} for e in range(E)]
+    L = lib()
+    rows = []
+    for e, w in enumerate(experts):
+        row = []
+        for n in _TABLE_FIELDS:
+            t = w.get(n)
+            if t is None or (bits == 4 and n.endswith("zeros")):
+                row.append(0)
+                continue
+            if not t.is_contiguous():
+                raise MoEError(f"expert_table: expert {e} {n} is not contiguous")
+            a = ctypes.c_uint64(0)
+            _check(L.moe_device_address(ctypes.c_void_p(t.data_ptr()), ctypes.byref(a)),
+                   f"moe_device_address (expert {e} {n})")
+            row.append(a.value)
+        rows.append(row)
+    tab = torch.tensor(rows, dtype=torch.int64).view(-1, len(_TABLE_FIELDS))
+    if device == "pinned":
+        return tab.pin_memory()
+    return tab.to(torch.device("cuda", torch.cuda.current_device()) if device is None else device)
+
+
+def expert_ffn_table(x: torch.Tensor, offsets, sorted_rows, active, k: int, table: torch.Tensor, bits: int, I: int,
+                     ws: Optional[Workspaces] = None, y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``expert_ffn`` with the expert weights found through an address table."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = offsets.numel() - 1
+    if table.dtype != torch.int64 or tuple(table.shape) != (E, len(_TABLE_FIELDS)):
+        raise MoEError(f"expert_ffn_table: table must be int64 [{E}, {len(_TABLE_FIELDS)}]")
+    if not (table.is_cuda or table.is_pinned()):
+        raise MoEError("expert_ffn_table: the table must be in device or pinned host memory")
+    if y_perm is None:
+        y_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    L = lib()
+    nbytes = L.moe_expert_ffn_workspace_size(T, k, E, H, I)
+    w = (ws or Workspaces(dev)).get("ffn", nbytes)
+    if bits not in (2, 4):
+        raise MoEError("bits must be 2 or 4")
+    tab_ptr = _p(table)
+    if not table.is_cuda:
+        a = ctypes.c_uint64(0)
+        _check(L.moe_device_address(ctypes.c_void_p(tab_ptr), ctypes.byref(a)), "moe_device_address (table)")
+        tab_ptr = a.value
+    name = "moe_expert_ffn_w4a16_table" if bits == 4 else "moe_expert_ffn_w2a16_table"
+    s = getattr(L, name)(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I, tab_ptr, _p(y_perm),
+                         _p(w), w.numel(), _stream(dev))
+    _check(s, name)
     return y_perm
 
 

@@ -195,18 +195,24 @@ static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, cons
                              const int32_t *sorted_rows, const int32_t *active, int T, int k, int E, int H, int I,
                              const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
                              const uint32_t *w2_codes, const uint16_t *w2_scales, const uint8_t *w2_zeros,
-                             uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream) {
+                             uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream,
+                             const uint64_t *table = nullptr) {
   moe_status s = check_common_moe(T, H, E, k);
   if (s != MOE_OK) return s;
   if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
-  if (!x || !expert_offsets || !sorted_rows || !active || !w13_codes || !w13_scales || !w2_codes || !w2_scales ||
-      !y_perm || !workspace)
+  if (!x || !expert_offsets || !sorted_rows || !active || !y_perm || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
-  if (bits == 2 && (!w13_zeros || !w2_zeros)) return fail(MOE_ERR_INVALID_ARG, "%s: zero-points are required", name);
-  if (!aligned(x, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16))
-    return fail(MOE_ERR_MISALIGNED, "%s: x and code arrays need 16-byte alignment", name);
-  if (!aligned(w13_scales, 2) || !aligned(w2_scales, 2) || !aligned(y_perm, 4) || !aligned(expert_offsets, 4) ||
-      !aligned(sorted_rows, 4) || !aligned(active, 4))
+  if (table) {
+    if (!aligned(table, 8)) return fail(MOE_ERR_MISALIGNED, "%s: the expert table needs 8-byte alignment", name);
+  } else {
+    if (!w13_codes || !w13_scales || !w2_codes || !w2_scales)
+      return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+    if (bits == 2 && (!w13_zeros || !w2_zeros)) return fail(MOE_ERR_INVALID_ARG, "%s: zero-points are required", name);
+    if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(w13_scales, 2) || !aligned(w2_scales, 2))
+      return fail(MOE_ERR_MISALIGNED, "%s: code arrays need 16-byte and scale arrays 2-byte alignment", name);
+  }
+  if (!aligned(x, 16)) return fail(MOE_ERR_MISALIGNED, "%s: x needs 16-byte alignment", name);
+  if (!aligned(y_perm, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_rows, 4) || !aligned(active, 4))
     return fail(MOE_ERR_MISALIGNED, "%s: array alignment", name);
   if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
   const size_t need = moe_expert_ffn_workspace_size(T, k, E, H, I);
@@ -217,7 +223,7 @@ static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, cons
   hipError_t he = current_device_info(&dev);
   if (he != hipSuccess) return from_hip(he, name);
   FfnArgs a{x, expert_offsets, sorted_rows, active, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
-            w2_codes, w2_scales, w2_zeros, y_perm, workspace};
+            w2_codes, w2_scales, w2_zeros, y_perm, workspace, table};
   if (decode_path(T, k, E) && decode_layout_ok(H, I, bits))
     return from_hip(launch_ffn_decode(a, dev, (hipStream_t)stream), name);
   // the grouped GEMMs address x and one expert's codes with 32-bit byte offsets
@@ -241,6 +247,49 @@ moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets
                                 void *workspace, size_t workspace_bytes, void *stream) {
   return expert_ffn("moe_expert_ffn_w2a16", 2, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
                     w13_scales, w13_zeros, w2_codes, w2_scales, w2_zeros, y_perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_w4a16_table(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                      const int32_t *active, int T, int k, int E, int H, int I,
+                                      const uint64_t *expert_table, uint16_t *y_perm, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (!expert_table) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_w4a16_table: expert_table is NULL");
+  return expert_ffn("moe_expert_ffn_w4a16_table", 4, x, expert_offsets, sorted_rows, active, T, k, E, H, I, nullptr,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, y_perm, workspace, workspace_bytes, stream,
+                    expert_table);
+}
+
+moe_status moe_expert_ffn_w2a16_table(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                      const int32_t *active, int T, int k, int E, int H, int I,
+                                      const uint64_t *expert_table, uint16_t *y_perm, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (!expert_table) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_w2a16_table: expert_table is NULL");
+  return expert_ffn("moe_expert_ffn_w2a16_table", 2, x, expert_offsets, sorted_rows, active, T, k, E, H, I, nullptr,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, y_perm, workspace, workspace_bytes, stream,
+                    expert_table);
+}
+
+moe_status moe_device_address(const void *ptr, uint64_t *out) {
+  if (!ptr || !out) return fail(MOE_ERR_INVALID_ARG, "moe_device_address: NULL argument");
+  hipPointerAttribute_t at{};
+  const hipError_t e = hipPointerGetAttributes(&at, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // an unknown pointer leaves a sticky error code behind
+    return fail(MOE_ERR_INVALID_ARG, "moe_device_address: %p is not memory the HIP runtime knows (%s)", ptr,
+                hipGetErrorString(e));
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *out = (uint64_t)(uintptr_t)ptr;
+    return MOE_OK;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    // The runtime may report the mapping of the allocation's base or of ptr
+    // itself; the offset from the reported host pointer covers both.
+    const char *hp = at.hostPointer ? (const char *)at.hostPointer : (const char *)ptr;
+    *out = (uint64_t)(uintptr_t)((const char *)at.devicePointer + ((const char *)ptr - hp));
+    return MOE_OK;
+  }
+  return fail(MOE_ERR_INVALID_ARG, "moe_device_address: %p is not device-readable (pageable host memory?)", ptr);
 }
 
 size_t moe_layer_workspace_size(int T, int k, int E, int H, int I) {

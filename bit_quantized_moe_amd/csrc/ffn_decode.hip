@@ -66,6 +66,7 @@ struct DecodeParams {
   const uint32_t *w2c;
   const uint16_t *w2s;
   const uint8_t *w2z;
+  const uint64_t *tab;  // per-expert address table (kTabStride entries per expert) or null
   uint16_t *y_perm;
   uint32_t *hbuf;  // [T*k, I] words: kHReady | bf16 bits once written, 0 before
   int *ctl;
@@ -344,6 +345,15 @@ __device__ __forceinline__ Off add_groups(Off o, int dg, int gbytes) {
 struct ExpertW {
   const uint8_t *codes, *scales, *zeros;
 };
+// Expert e's W13 (first = 0) or W2 (first = 3) blocks from the address table
+// (wave-uniform entries, read through the scalar cache).  The table the
+// pages describe lets experts live anywhere the GPU can read, e.g. pinned
+// host memory read in place (page "Qwen3.8-Flash-Next on one 24 GB GPU",
+// "What the patch does").
+__device__ __forceinline__ ExpertW expert_from_table(const uint64_t *tab, int e, int first) {
+  const uint64_t *t = tab + (size_t)e * kTabStride + first;
+  return ExpertW{(const uint8_t *)sload(t), (const uint8_t *)sload(t + 1), (const uint8_t *)sload(t + 2)};
+}
 
 template <int BITS>
 __device__ __forceinline__ void load_chunk(const ExpertW &x, Off o, Chunk<BITS> &ch) {
@@ -603,7 +613,7 @@ __device__ bool read_sorted_record(const uint64_t *rec, int n, int E, int max_sp
 // publishes them in that order as tagged words; (c) every block reads those
 // words and derives the grouping in LDS.  After its items, block b < H/128 combines
 // columns [128 b, 128 b + 128) of y from the tagged y_perm words.
-template <int BITS, bool ONE, bool FAST, bool LAYER>
+template <int BITS, bool ONE, bool FAST, bool LAYER, bool TAB>
 __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int RM = ONE ? 1 : kRMax;
@@ -738,8 +748,9 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const Meta md = get_meta(a);
       const int g0 = wv * Gw1, ng = max(min(Gw1, G1 - g0), 0);
       const size_t erows = (size_t)md.e * 2 * p.I;  // first row of the expert
-      const ExpertW xw = {(const uint8_t *)p.w13c + erows * (G1 * GB), (const uint8_t *)p.w13s + erows * (G1 * 2),
-                          p.w13z + erows * G1};
+      const ExpertW xw = TAB ? expert_from_table(p.tab, md.e, 0)
+                             : ExpertW{(const uint8_t *)p.w13c + erows * (G1 * GB),
+                                         (const uint8_t *)p.w13s + erows * (G1 * 2), p.w13z + erows * G1};
       const Off o2[2] = {row_off(i0 + m, G1, g0, GB, lsub), row_off(p.I + i0 + m, G1, g0, GB, lsub)};
       const int nch = ng / kChunkG;
       // activation row of sorted position q
@@ -809,8 +820,9 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 32;
       const Meta md = get_meta(a);
       const size_t erows = (size_t)md.e * p.H;
-      const ExpertW xw = {(const uint8_t *)p.w2c + erows * (G2 * GB), (const uint8_t *)p.w2s + erows * (G2 * 2),
-                          p.w2z + erows * G2};
+      const ExpertW xw = TAB ? expert_from_table(p.tab, md.e, 3)
+                             : ExpertW{(const uint8_t *)p.w2c + erows * (G2 * GB),
+                                         (const uint8_t *)p.w2s + erows * (G2 * 2), p.w2z + erows * G2};
       const Off o2[2] = {row_off(n0 + m, G2, 0, GB, lsub), row_off(n0 + 16 + m, G2, 0, GB, lsub)};
       const int nch = G2 / kChunkG;
       Chunk<BITS> wd[2];
@@ -1020,20 +1032,23 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   }
 }
 
-template <int BITS, bool ONE, bool LAYER>
+template <int BITS, bool ONE, bool LAYER, bool TAB>
 const void *decode_fn_fast(bool fast) {
-  return fast ? (const void *)ffn_decode_kernel<BITS, ONE, true, LAYER>
-              : (const void *)ffn_decode_kernel<BITS, ONE, false, LAYER>;
+  return fast ? (const void *)ffn_decode_kernel<BITS, ONE, true, LAYER, TAB>
+              : (const void *)ffn_decode_kernel<BITS, ONE, false, LAYER, TAB>;
 }
 
-template <bool LAYER>
+template <bool LAYER, bool TAB>
 const void *decode_fn_layer(int bits, bool one, bool fast) {
-  if (bits == 4) return one ? decode_fn_fast<4, true, LAYER>(fast) : decode_fn_fast<4, false, LAYER>(fast);
-  return one ? decode_fn_fast<2, true, LAYER>(fast) : decode_fn_fast<2, false, LAYER>(fast);
+  if (bits == 4) return one ? decode_fn_fast<4, true, LAYER, TAB>(fast) : decode_fn_fast<4, false, LAYER, TAB>(fast);
+  return one ? decode_fn_fast<2, true, LAYER, TAB>(fast) : decode_fn_fast<2, false, LAYER, TAB>(fast);
 }
 
-const void *decode_kernel_fn(int bits, bool one, bool fast, bool layer) {
-  return layer ? decode_fn_layer<true>(bits, one, fast) : decode_fn_layer<false>(bits, one, fast);
+// The layer kernel reads stacked arrays only; the address-table variant is a
+// separate instantiation so that the array kernels keep their registers.
+const void *decode_kernel_fn(int bits, bool one, bool fast, bool layer, bool tab) {
+  if (layer) return decode_fn_layer<true, false>(bits, one, fast);
+  return tab ? decode_fn_layer<false, true>(bits, one, fast) : decode_fn_layer<false, false>(bits, one, fast);
 }
 
 // LDS of the fused layer's routing results (after the FFN's own arrays).
@@ -1109,6 +1124,7 @@ static void fill_params(DecodeParams &p, const FfnArgs &a, void *ws) {
   p.w2c = a.w2_codes;
   p.w2s = a.w2_scales;
   p.w2z = a.w2_zeros;
+  p.tab = a.tab;
   p.y_perm = a.y_perm;
   p.ctl = (int *)ws;
   p.hbuf = (uint32_t *)((char *)ws + ffn_ctl_bytes(a.T, a.k, a.E));
@@ -1121,7 +1137,7 @@ static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, c
   // full chunks; with one token also few enough h groups for the phase-2 pipeline
   const bool fast = (a.H / kGroup) % (4 * kChunkG) == 0 && (a.I / kGroup) % kChunkG == 0 &&
                     (!one || a.I / kGroup <= 4 * kHPend);
-  const void *fn = decode_kernel_fn(a.bits, one, fast, layer);
+  const void *fn = decode_kernel_fn(a.bits, one, fast, layer, a.tab != nullptr);
   const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I) : decode_lds_bytes(a.H, a.I, one);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;

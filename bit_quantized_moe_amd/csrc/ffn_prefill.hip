@@ -48,6 +48,8 @@ struct GemmParams {
   const uint8_t *zeros;
   uint16_t *out;           // G1: h; G2: y_perm
   int n_rows_w;            // rows of one expert's weight matrix: 2I (G1) or H (G2)
+  const uint64_t *tab;     // per-expert address table or null; this GEMM's entries start at tab_off
+  int tab_off;
   int n_blocks;            // N tiles: I / 64 (G1) or H / BN (G2)
 };
 
@@ -159,12 +161,16 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   }
   const int wpr = p.K * BITS / 32, gpr = p.K / kGroup;  // code words and groups per weight row
   const size_t erow0 = (size_t)e * p.n_rows_w;          // the expert's first weight row
+  const uint64_t *te = p.tab ? p.tab + (size_t)e * kTabStride + p.tab_off : nullptr;
+  const uint32_t *e_codes = te ? (const uint32_t *)sload(te) : p.codes + erow0 * wpr;
+  const uint16_t *e_scales = te ? (const uint16_t *)sload(te + 1) : p.scales + erow0 * gpr;
+  const uint8_t *e_zeros = te ? (const uint8_t *)sload(te + 2) : (BITS == 2 ? p.zeros + erow0 * gpr : p.zeros);
   const __amdgpu_buffer_rsrc_t b_rs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.codes + erow0 * wpr), (short)0, p.n_rows_w * wpr * 4, kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)e_codes, (short)0, p.n_rows_w * wpr * 4, kBufWord3);
   const __amdgpu_buffer_rsrc_t s_rs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(p.scales + erow0 * gpr), (short)0, p.n_rows_w * gpr * 2, kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)e_scales, (short)0, p.n_rows_w * gpr * 2, kBufWord3);
   const __amdgpu_buffer_rsrc_t z_rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(BITS == 2 ? p.zeros + erow0 * gpr : p.zeros), (short)0, BITS == 2 ? p.n_rows_w * gpr : 0, kBufWord3);
+      (void *)e_zeros, (short)0, BITS == 2 ? p.n_rows_w * gpr : 0, kBufWord3);
   const uint32_t b_off = (uint32_t)(wrow * wpr + bh * WPL) * 4u;  // bytes
   const uint32_t s_off = (uint32_t)(wrow * gpr);                  // elements
 
@@ -328,6 +334,8 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   g1.zeros = a.w13_zeros;
   g1.out = hbuf;
   g1.n_rows_w = 2 * a.I;
+  g1.tab = a.tab;
+  g1.tab_off = 0;
 
   GemmParams g2 = g1;
   g2.a_src = hbuf;
@@ -337,6 +345,7 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   g2.zeros = a.w2_zeros;
   g2.out = a.y_perm;
   g2.n_rows_w = a.H;
+  g2.tab_off = 3;
 
   g1.n_blocks = a.I / 64;
   g2.n_blocks = a.H / BN;

@@ -63,7 +63,12 @@ struct FfnArgs {
   const uint8_t *w2_zeros;
   uint16_t *y_perm;
   void *ws;
+  // optional per-expert address table (device memory, kTabStride uint64 per
+  // expert: w13 codes, w13 scales, w13 zeros, w2 codes, w2 scales, w2 zeros,
+  // each the expert's own block); when set the array pointers are unused
+  const uint64_t *tab = nullptr;
 };
+constexpr int kTabStride = 6;
 hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
 
 // Fused decode layer (ffn_decode.hip): router, grouping, expert FFN and combine in one launch.

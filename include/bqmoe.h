@@ -10,6 +10,9 @@
  *   moe_expert_ffn_w4a16 / _w2a16
  *                   per-expert gate_up -> SwiGLU -> down with the expert weights
  *                   dequantised on the fly from packed codes
+ *   moe_expert_ffn_w4a16_table / _w2a16_table
+ *                   the same, each expert's weights located through a
+ *                   per-expert address table
  *   moe_combine     gate-weighted sum of each token's k expert outputs
  *
  * Weight formats.  INT4 symmetric with one bf16 scale per 128 consecutive K
@@ -190,6 +193,49 @@ moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets
                                 const uint8_t *w2_zeros,
                                 uint16_t *y_perm, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/* moe_expert_ffn_w4a16_table / moe_expert_ffn_w2a16_table: the same
+ * computation, with each expert's weights found through a per-expert address
+ * table instead of three stacked arrays per projection, so that every expert
+ * is read where it lives (device memory, or pinned host memory that the device
+ * can address) and moving an expert is a write of its table entry.  Page
+ * "Qwen3.8-Flash-Next on one 24 GB GPU", "What the patch does" (experts read
+ * in place through an int64 address table; placement as a table write).
+ *   expert_table  [E, 6] uint64, device-readable (device or pinned host
+ *                 memory), 8-byte aligned, not modified.  Row e holds the
+ *                 addresses of expert e's own blocks, in this order:
+ *                   0  w13 codes   [2I, H/P] uint32 (P = 8 INT4, 16 2-bit)
+ *                   1  w13 scales  [2I, H/128] bf16
+ *                   2  w13 zeros   [2I, H/128] uint8  (2-bit only, else unused)
+ *                   3  w2 codes    [H, I/P] uint32
+ *                   4  w2 scales   [H, I/128] bf16
+ *                   5  w2 zeros    [H, I/128] uint8   (2-bit only, else unused)
+ *                 i.e. the slices [e] of the stacked arrays above.  Code blocks
+ *                 must be 16-byte aligned and scale blocks 2-byte aligned; each
+ *                 entry must be a valid device-visible address while the call
+ *                 runs (rows of inactive experts are never read).
+ * All other arguments, the requirements, the dispatch and the results are
+ * those of moe_expert_ffn_w4a16 / _w2a16: with the same weights the output is
+ * bit-identical.  A NULL table returns MOE_ERR_INVALID_ARG. */
+moe_status moe_expert_ffn_w4a16_table(const uint16_t *x, const int32_t *expert_offsets,
+                                      const int32_t *sorted_rows, const int32_t *active,
+                                      int T, int k, int E, int H, int I,
+                                      const uint64_t *expert_table,
+                                      uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+moe_status moe_expert_ffn_w2a16_table(const uint16_t *x, const int32_t *expert_offsets,
+                                      const int32_t *sorted_rows, const int32_t *active,
+                                      int T, int k, int E, int H, int I,
+                                      const uint64_t *expert_table,
+                                      uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/* moe_device_address: the address under which the kernels read ptr, for
+ * filling an expert table.  Device (and managed) memory is returned as is;
+ * pinned host memory (hipHostMalloc, torch pin_memory) through the runtime's
+ * device mapping, offset kept.  Pageable host memory and pointers the runtime
+ * does not know return MOE_ERR_INVALID_ARG: the kernels cannot read them. */
+moe_status moe_device_address(const void *ptr, uint64_t *out);
 
 /* ---------------------------------------------------------------- combine
  * moe_combine: y[t] = sum over j = 0..k-1 (ascending) of

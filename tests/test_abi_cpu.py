@@ -119,6 +119,30 @@ def test_ffn_argument_errors():
     assert need >= 4096 + 16 * 8 * 1024 * 2 and need % 256 == 0
 
 
+def _ffn_table(bits=4, T=2, k=2, E=8, H=256, I=128, x=A, tab=A, ws=A, wsb=1 << 24):
+    L = bq.lib()
+    fn = L.moe_expert_ffn_w4a16_table if bits == 4 else L.moe_expert_ffn_w2a16_table
+    return fn(x, A, A, A, T, k, E, H, I, tab, A, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_ffn_table_argument_errors(bits):
+    assert _ffn_table(bits, tab=None) == INVALID
+    assert _ffn_table(bits, tab=A + 4) == MISALIGNED
+    assert _ffn_table(bits, I=100) == SHAPE
+    assert _ffn_table(bits, x=None) == INVALID
+    assert _ffn_table(bits, x=A + 8) == MISALIGNED
+    assert _ffn_table(bits, wsb=100) == WS_SMALL
+    assert _ffn_table(bits, T=0) == OK        # no weight arrays are needed beside the table
+
+
+def test_device_address_argument_errors():
+    L = bq.lib()
+    out = ctypes.c_uint64(0)
+    assert L.moe_device_address(None, ctypes.byref(out)) == INVALID
+    assert L.moe_device_address(A, None) == INVALID
+
+
 def test_combine_unpack_dequant_argument_errors():
     L = bq.lib()
     assert L.moe_combine(A, A, A, 4, 2, 100, A, None) == SHAPE       # H % 8

@@ -1,0 +1,122 @@
+"""GPU: the expert FFN through a per-expert address table.
+
+Each expert's weights sit in an allocation of their own (in device memory or in
+pinned host memory, read in place), found through an int64 table (page
+"Qwen3.8-Flash-Next on one 24 GB GPU", "What the patch does").  With the same
+weights the table entry points must give the stacked-array entry points' y_perm
+bit for bit, on the decode path (one token, a few tokens) and on the grouped
+GEMM path, and the array path is checked against the oracle elsewhere; one
+small case is also checked against the oracle here.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_amd as bq
+import oracle
+import workload
+from gpu_util import bf16_np_to_f32, to_dev, to_np, weights_to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"[gpu-test] start {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+def _scattered_experts(wd, host_every=0):
+    """One allocation per expert and tensor, made in reverse expert order; with
+    host_every = n every n-th expert is copied to pinned host memory instead."""
+    E = wd["w13_codes"].shape[0]
+    experts = [None] * E
+    for e in reversed(range(E)):
+        on_host = host_every and e % host_every == 1
+        experts[e] = {n: (t[e].cpu().pin_memory() if on_host else t[e].clone()) for n, t in wd.items()}
+    return experts
+
+
+def _route(inp, wd):
+    sp = inp.spec
+    bias = to_dev(inp.logit_bias) if inp.logit_bias is not None else None
+    return bq.route_permute(to_dev(inp.x), to_dev(inp.w_router), sp.k, bias)
+
+
+CASES = [  # T, H, I, E, k: one token (full-chunk and ragged-chunk kernels), a few tokens, grouped GEMM
+    (1, 4096, 1024, 16, 4),
+    (1, 256, 128, 8, 2),
+    (5, 512, 256, 16, 4),
+    (16, 4096, 1024, 64, 8),
+    (40, 256, 128, 8, 2),
+    (300, 512, 256, 16, 4),
+]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_I%d_E%d_k%d" % c)
+@pytest.mark.parametrize("where", ["device", "mixed"])
+def test_table_path_matches_arrays(bits, case, where):
+    T, H, I, E, k = case
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, I=I, E=E, k=k, bits=bits,
+                       scale_sigma=0.02 if bits == 4 else 0.05, seed=3100 + T + bits + E)
+    inp = workload.make_layer_inputs(sp)
+    wd = weights_to_dev(inp.weights)
+    r = _route(inp, wd)
+    x = to_dev(inp.x)
+    ref = bq.expert_ffn(x, r["offsets"], r["sorted_rows"], r["active"], k, wd, bits, I)
+    experts = _scattered_experts(wd, host_every=3 if where == "mixed" else 0)
+    table = bq.expert_table(experts, bits, device="pinned" if where == "mixed" else None)
+    ws = bq.Workspaces("cuda")
+    for rep in range(2):
+        got = bq.expert_ffn_table(x, r["offsets"], r["sorted_rows"], r["active"], k, table, bits, I, ws=ws)
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), rep
+    torch.cuda.synchronize()
+    assert int(ws._bufs["ffn"].view(torch.int32).abs().sum()) == 0
+    say(f"    {where} experts, T={T}: table path bit-exact with the arrays")
+    if T == 40 and where == "mixed":
+        yp = oracle.expert_ffn(inp.x, to_np(r["offsets"]), to_np(r["sorted_rows"]), k, inp.weights, bits, I)
+        assert oracle.rel_fro(bf16_np_to_f32(to_np(got)), yp) <= TOL
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_table_of_stacked_arrays_and_a_moved_expert(bits):
+    """The table can point into the stacked arrays; rewriting two rows swaps two
+    experts, which must equal the array path with those experts' weights swapped."""
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=3, H=512, I=256, E=8, k=8, bits=bits,
+                       scale_sigma=0.02 if bits == 4 else 0.05, seed=3300 + bits)
+    inp = workload.make_layer_inputs(sp)
+    wd = weights_to_dev(inp.weights)
+    r = _route(inp, wd)
+    x = to_dev(inp.x)
+    args = (x, r["offsets"], r["sorted_rows"], r["active"], sp.k)
+    table = bq.expert_table(wd, bits)
+    got = bq.expert_ffn_table(*args, table, bits, sp.I)
+    ref = bq.expert_ffn(*args, wd, bits, sp.I)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    perm = torch.arange(sp.E, device="cuda")
+    perm[[2, 5]] = perm[[5, 2]]
+    swapped = bq.expert_ffn_table(*args, table[perm].contiguous(), bits, sp.I)
+    wd_sw = {n: t[perm].contiguous() for n, t in wd.items()}
+    ref_sw = bq.expert_ffn(*args, wd_sw, bits, sp.I)
+    assert torch.equal(swapped.view(torch.int16), ref_sw.view(torch.int16))
+    assert not torch.equal(swapped.view(torch.int16), ref.view(torch.int16))
+
+
+def test_table_rejects_pageable_host_memory_and_bad_tables():
+    w = {"w13_codes": torch.zeros((4, 2), dtype=torch.int32)}          # pageable host memory
+    with pytest.raises(bq.MoEError, match="device-readable|knows"):
+        bq.expert_table([w], 4)
+    x = torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda")
+    z = torch.zeros(9, dtype=torch.int32, device="cuda")
+    with pytest.raises(bq.MoEError, match="int64"):
+        bq.expert_ffn_table(x, z, z[:1], z[:1], 1, torch.zeros((8, 5), dtype=torch.int64, device="cuda"), 4, 128)
