@@ -47,7 +47,7 @@ def main() -> None:
     while True:
         x = xs[calls % len(xs)]
         tok = np.sort(rng.choice(sp.T, n_tok, replace=False)) if n_tok < sp.T else np.arange(sp.T)
-        O.moe_layer_tokens(x, w_r, bias, weights, sp.k, sp.bits, sp.I, tok)
+        O.moe_layer_tokens(x, w_r, bias, weights, sp.k, sp.bits, sp.I, tok, group=sp.group)
         calls += 1
         tokens += len(tok)
         el = time.perf_counter() - t0

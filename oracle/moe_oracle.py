@@ -1,4 +1,4 @@
-"""CPU oracle for the routed-expert MoE layer with low-bit (INT4 / 2-bit) experts.
+"""CPU oracle for the routed-expert MoE layer with low-bit (INT4 / 2-bit / INT8) experts.
 
 TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference that the
 GPU library is checked against.  Only the test suite, the smoke check and the
@@ -13,7 +13,7 @@ O2  top-k experts per token, ties to the lower expert index;
 O3  softmax over the k selected logits (float64, stored as float32);
 O4  stable counting-sort permutation of the T*k (token, slot) rows by expert;
 O5  unpacking of the packed code words;
-O6  dequantisation w = (q - z) * s per 128-wide group;
+O6  dequantisation w = (q - z) * s per K group (128 wide, or 32);
 O7  per-expert FFN: gate_up matmul, SwiGLU, down matmul (float32);
 O8  weighted combine of each token's k expert outputs (float32).
 
@@ -22,7 +22,15 @@ weight-only experts with 16-bit activations (page "Qwen3.8-Flash-Next on 2x RTX
 3090", storage-format table; page "Qwen3.8-Flash-Next on dual RTX 3090: W4A16 +
 FP8 PLE + MTP3", "Composition"), and 2-bit group-128 GPTQ-style experts with 16
 codes per 32-bit word along K (page "Qwen3.8-Flash-Next on one 24 GB GPU",
-"What the patch does" and "Hardware and software requirements").  The pages fix
+"What the patch does" and "Hardware and software requirements").  Two more
+formats take the same path with other group sizes and widths: INT4 symmetric
+with group 32 (the draft-layer experts of page "Qwen3.8-Flash-Next on 2x RTX
+3090", storage-format table, and of page "Qwen3.8-Flash-Next on dual RTX 3090:
+W4A16 + FP8 PLE + MTP3", "Composition"), and INT8 symmetric with codes
+-127..127 and group 128 or 32 (page "Qwen3.8-Flash-Next on one 24 GB GPU",
+"What the patch does": dense projections re-packed to INT8 g128; page
+"Qwen3.8-Flash-Next FP6-INT8", "Precision map" and "Kernel-level
+verification": an int8 g32 tier).  The pages fix
 activations at bf16 with float32 accumulation (page "Qwen3.8-Flash-Next
 FP6-INT8", "Precision map"), so the oracle accumulates in float32.  They keep
 the router in 16-bit precision because near-tied logits flip routing under
@@ -62,11 +70,12 @@ def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
 
     Field i of word kw (bits [b*i, b*i+b), least significant first) holds the
     code for K index P*kw + i, P = 32/b.  INT4 fields store q + 8 (offset
-    binary), so q = field - 8 spans [-8, 7]; 2-bit fields store q in {0..3}
+    binary), so q = field - 8 spans [-8, 7]; INT8 fields store q + 128, so
+    q = field - 128 (the format uses -127..127); 2-bit fields store q in {0..3}
     directly and the zero-point is subtracted at dequantisation.
     """
-    if bits not in (2, 4):
-        raise ValueError("bits must be 2 or 4")
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
     w = np.ascontiguousarray(words, dtype=np.uint32)
     P = 32 // bits
     mask = np.uint32((1 << bits) - 1)
@@ -76,6 +85,8 @@ def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
     q = fields.reshape(w.shape[:-1] + (w.shape[-1] * P,))
     if bits == 4:
         q = q - 8
+    elif bits == 8:
+        q = q - 128
     return q.astype(np.int8)
 
 
@@ -85,7 +96,7 @@ def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
     P = 32 // bits
     if q.shape[-1] % P:
         raise ValueError("K must be a multiple of codes-per-word")
-    u = q + 8 if bits == 4 else q
+    u = q + {4: 8, 8: 128}.get(bits, 0)
     if u.min(initial=0) < 0 or u.max(initial=0) >= (1 << bits):
         raise ValueError("code out of range")
     u = u.astype(np.uint32).reshape(q.shape[:-1] + (q.shape[-1] // P, P))
@@ -95,21 +106,24 @@ def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
     return w
 
 
-def dequantize(words: np.ndarray, scales: np.ndarray, zeros, bits: int) -> np.ndarray:
+def dequantize(words: np.ndarray, scales: np.ndarray, zeros, bits: int, group: int = GROUP) -> np.ndarray:
     """O6: one expert matrix [N, K/P] words -> float32 weights [N, K].
 
-    W[n, k] = (q[n, k] - z[n, k // 128]) * s[n, k // 128], with z = 0 for the
-    symmetric INT4 format.  (q - z) is a small integer and s a bf16 value, so
-    the product is exact in float32.
+    W[n, k] = (q[n, k] - z[n, k // G]) * s[n, k // G] for group size G, with
+    z = 0 for the symmetric INT4 and INT8 formats.  (q - z) is an integer of at
+    most 8 bits and s a bf16 value (8 significant bits), so the product is
+    exact in float32.
     """
     q = unpack_codes(words, bits).astype(np.float32)           # [N, K]
     N, K = q.shape
-    s = bf16_to_f32(scales).reshape(N, K // GROUP)
-    s_full = np.repeat(s, GROUP, axis=1)                        # [N, K]
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    s = bf16_to_f32(scales).reshape(N, K // group)
+    s_full = np.repeat(s, group, axis=1)                        # [N, K]
     if zeros is None:
         z_full = np.zeros_like(q)
     else:
-        z_full = np.repeat(np.asarray(zeros, dtype=np.float32).reshape(N, K // GROUP), GROUP, axis=1)
+        z_full = np.repeat(np.asarray(zeros, dtype=np.float32).reshape(N, K // group), group, axis=1)
     return ((q - z_full) * s_full).astype(np.float32)
 
 
@@ -202,7 +216,7 @@ def silu(a: np.ndarray) -> np.ndarray:
 
 
 def expert_ffn(x, offsets, sorted_rows, k: int, weights: dict, bits: int, I: int,
-               experts=None, dtype=np.float32) -> np.ndarray:
+               experts=None, dtype=np.float32, group: int = GROUP) -> np.ndarray:
     """O7: y_perm [T*k, H]: the expert FFN of every row, in sorted order.
 
     For expert e with rows R = sorted_rows[o_e : o_(e+1)] (tokens R // k):
@@ -225,11 +239,11 @@ def expert_ffn(x, offsets, sorted_rows, k: int, weights: dict, bits: int, I: int
         toks = sorted_rows[o0:o1] // k
         Xe = xf[toks]
         W13 = dequantize(weights["w13_codes"][e], weights["w13_scales"][e],
-                         None if zk13 is None else zk13[e], bits).astype(dtype)
+                         None if zk13 is None else zk13[e], bits, group).astype(dtype)
         A = Xe @ W13.T
         h = silu(A[:, :I]) * A[:, I:]
         W2 = dequantize(weights["w2_codes"][e], weights["w2_scales"][e],
-                        None if zk2 is None else zk2[e], bits).astype(dtype)
+                        None if zk2 is None else zk2[e], bits, group).astype(dtype)
         y[o0:o1] = h @ W2.T
     return y
 
@@ -245,20 +259,21 @@ def combine(y_perm: np.ndarray, row_pos: np.ndarray, gates: np.ndarray) -> np.nd
 
 
 # ---------------------------------------------------------------- whole layer
-def moe_layer(x, w_router, logit_bias, weights, k: int, bits: int, I: int, dtype=np.float32) -> dict:
+def moe_layer(x, w_router, logit_bias, weights, k: int, bits: int, I: int, dtype=np.float32,
+              group: int = GROUP) -> dict:
     """O1..O8 on one batch; returns every intermediate for element-wise checks."""
     E = w_router.shape[0]
     logits = router_logits(x, w_router, logit_bias)
     ids, gates = topk_softmax(logits, k)
     offsets, sorted_rows, row_pos, active = permute(ids, E)
-    y_perm = expert_ffn(x, offsets, sorted_rows, k, weights, bits, I, dtype=dtype)
+    y_perm = expert_ffn(x, offsets, sorted_rows, k, weights, bits, I, dtype=dtype, group=group)
     y = combine(y_perm, row_pos, gates)
     return dict(logits=logits, ids=ids, gates=gates, offsets=offsets, sorted_rows=sorted_rows,
                 row_pos=row_pos, active=active, y_perm=y_perm, y=y)
 
 
 def moe_layer_tokens(x, w_router, logit_bias, weights, k: int, bits: int, I: int, tokens,
-                     dtype=np.float32) -> dict:
+                     dtype=np.float32, group: int = GROUP) -> dict:
     """The layer output for a subset of tokens only (each token is independent).
 
     Used to check full-size runs on sampled tokens: routing of the sampled
@@ -266,7 +281,7 @@ def moe_layer_tokens(x, w_router, logit_bias, weights, k: int, bits: int, I: int
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     xs = np.asarray(x)[tokens]
-    return moe_layer(xs, w_router, logit_bias, weights, k, bits, I, dtype=dtype)
+    return moe_layer(xs, w_router, logit_bias, weights, k, bits, I, dtype=dtype, group=group)
 
 
 def rel_fro(a: np.ndarray, ref: np.ndarray) -> float:

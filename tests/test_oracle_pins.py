@@ -43,11 +43,11 @@ def test_unpack_matches_hand_derived_golden():
         assert got.tolist() == codes, (bits, hex(word))
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 2, 8])
 def test_pack_unpack_exhaustive_every_code_every_field(bits):
     """Every code value in every field position of a word round-trips."""
     P = 32 // bits
-    lo, hi = (-8, 7) if bits == 4 else (0, 3)
+    lo, hi = {4: (-8, 7), 2: (0, 3), 8: (-127, 127)}[bits]
     codes = np.arange(lo, hi + 1)
     rows = []
     for pos in range(P):
@@ -64,10 +64,10 @@ def test_pack_unpack_exhaustive_every_code_every_field(bits):
     for r, word in zip(rows, w[:, 0].tolist()):
         for pos in range(P):
             field = (word >> (bits * pos)) & ((1 << bits) - 1)
-            assert field == (int(r[pos]) + (8 if bits == 4 else 0))
+            assert field == (int(r[pos]) + {4: 8, 2: 0, 8: 128}[bits])
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 2, 8])
 def test_unpack_pack_random_words_roundtrip(bits):
     rng = np.random.default_rng(7)
     w = rng.integers(0, 2**32, size=(5, 9), dtype=np.uint32)
@@ -95,7 +95,7 @@ def test_dequant_golden_values():
     assert W2[0, :4].tolist() == [-4.0, -2.0, 0.0, 2.0]
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 2, 8])
 def test_dequant_unit_scale_zero_point_gives_codes(bits):
     rng = np.random.default_rng(3)
     N, K = 3, 256
@@ -126,6 +126,68 @@ def test_dequant_group_boundaries(bits):
         assert diff.size > 0
         assert set(diff[:, 0].tolist()) == {n}
         assert diff[:, 1].min() >= 128 * g and diff[:, 1].max() < 128 * (g + 1)
+
+
+def test_dequant_golden_values_group32_and_int8():
+    # INT8 word 0x81818181 holds q = 1 in every byte; K = 128 in four groups of
+    # 32 with scales 0.5, 1, 2, 4 -> 32 copies of each scale, in K order
+    words = np.full((1, 32), 0x81818181, dtype=np.uint32)
+    W = oracle.dequantize(words, _bf16([[0.5, 1.0, 2.0, 4.0]]), None, 8, group=32)
+    assert W[0].tolist() == [0.5] * 32 + [1.0] * 32 + [2.0] * 32 + [4.0] * 32
+    # INT4 word 0x0F0F0F0F holds q = 7, -8, 7, -8, ...; group 32, scales 1 and -0.25
+    w4 = np.full((1, 8), 0x0F0F0F0F, dtype=np.uint32)               # K = 64
+    W4 = oracle.dequantize(w4, _bf16([[1.0, -0.25]]), None, 4, group=32)
+    assert W4[0, :4].tolist() == [7.0, -8.0, 7.0, -8.0]
+    assert W4[0, 32:36].tolist() == [-1.75, 2.0, -1.75, 2.0]
+    # INT8 extremes: 0x01 -> -127, 0xFF -> 127
+    W8 = oracle.dequantize(np.full((1, 32), 0xFF01FF01, dtype=np.uint32), _bf16([[0.5]]), None, 8)
+    assert W8[0, :4].tolist() == [-63.5, 63.5, -63.5, 63.5]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dequant_group32_boundaries_and_reduction_to_group128(bits):
+    """With group 32, scale j of a row moves exactly columns [32j, 32j+32); four
+    equal scales per 128 columns give the group-128 result."""
+    rng = np.random.default_rng(21)
+    N, K = 3, 256
+    w = rng.integers(0, 2**32, size=(N, K * bits // 32), dtype=np.uint32)
+    s = _bf16(np.abs(rng.standard_normal((N, K // 32))) + 0.1)
+    base = oracle.dequantize(w, s, None, bits, group=32)
+    for n, j in [(0, 0), (1, 5), (2, 7)]:
+        s2 = s.copy()
+        s2[n, j] = _bf16([[8.0]])[0, 0]
+        diff = np.argwhere(oracle.dequantize(w, s2, None, bits, group=32) != base)
+        assert set(diff[:, 0].tolist()) == {n}
+        assert diff[:, 1].min() >= 32 * j and diff[:, 1].max() < 32 * (j + 1)
+    s128 = _bf16(np.abs(rng.standard_normal((N, K // 128))) + 0.1)
+    assert np.array_equal(oracle.dequantize(w, np.repeat(s128, 4, axis=1), None, bits, group=32),
+                          oracle.dequantize(w, s128, None, bits, group=128))
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_int8_every_code_every_group_position_scale_and_activation_extremes(group):
+    """The pages' int8 battery, applied to the oracle: each code -127..127 at
+    each position of a group, under extreme scales and activations, gives the
+    product code * scale * x exactly (checked in exact rationals)."""
+    from fractions import Fraction
+    scales = [2.0 ** -14, 1.0, 2.0 ** 7]                     # bf16-exact scale extremes
+    acts = [2.0 ** -10, -1.0, 2.0 ** 6]                      # bf16-exact activation extremes
+    codes = np.arange(-127, 128)
+    K = group
+    for pos in range(0, group, 3 if group == 128 else 1):
+        q = np.zeros((codes.size, K), np.int16)
+        q[:, pos] = codes
+        words = oracle.pack_codes(q, 8)
+        for sc in scales:
+            W = oracle.dequantize(words, _bf16(np.full((codes.size, 1), sc)), None, 8, group=group)
+            nz = np.flatnonzero(W.any(axis=0))
+            assert nz.tolist() in ([pos], [])
+            for xv in acts:
+                x = np.zeros(K, np.float32)
+                x[pos] = xv
+                y = W.astype(np.float64) @ x.astype(np.float64)
+                for c, yv in zip(codes[::17], y[::17]):
+                    assert Fraction(float(yv)) == Fraction(int(c)) * Fraction(sc) * Fraction(xv)
 
 
 def test_dequant_exact_against_integer_arithmetic():
@@ -302,19 +364,23 @@ def _tiny(bits=4, **kw):
     sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", **kw)
     if bits == 2:
         sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", bits=2, scale_sigma=0.05, **kw)
+    elif bits == 8:
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", bits=8, scale_sigma=0.0015, **kw)
     return workload.make_layer_inputs(sp)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
-def test_ffn_all_equal_weights_closed_form(bits):
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 128), (4, 32), (8, 128), (8, 32)])
+def test_ffn_all_equal_weights_closed_form(bits, group):
     """Every weight = c: A_n = c*S (S = sum of x), h = silu(cS)*cS, y = I*c*h for all rows."""
-    inp = _tiny(bits)
+    inp = _tiny(bits, group=group)
     sp = inp.spec
     E, H, I = sp.E, sp.H, sp.I
     wt = dict(inp.weights)
     if bits == 4:
         word, c = 0x99999999, 1.0                     # q = 1
         z13 = z2 = None
+    elif bits == 8:
+        word, c = 0x7F7F7F7F, -1.0                    # q = -1
     else:
         word, c = 0xFFFFFFFF, 2.0                     # u = 3, z = 1 -> 2
         wt["w13_zeros"] = np.ones_like(wt["w13_zeros"])
@@ -323,7 +389,7 @@ def test_ffn_all_equal_weights_closed_form(bits):
     wt["w2_codes"] = np.full_like(wt["w2_codes"], word)
     wt["w13_scales"] = _bf16(np.ones(wt["w13_scales"].shape))
     wt["w2_scales"] = _bf16(np.ones(wt["w2_scales"].shape))
-    out = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, wt, sp.k, bits, I)
+    out = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, wt, sp.k, bits, I, group=group)
     xf = oracle.bf16_to_f32(inp.x).astype(np.float64)
     S = c * xf.sum(1)
     hval = S / (1 + np.exp(-S)) * S
@@ -357,6 +423,31 @@ def test_ffn_one_hot_input_reads_one_weight_column():
     assert oracle.rel_fro(y[0], W2 @ h) < 1e-5
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_ffn_one_hot_input_group32_reads_bytes_directly(bits):
+    """Group 32: x = e_j gives A[n] = (field - offset) * s[n, j // 32], read from the bits."""
+    inp = _tiny(bits, group=32)
+    sp = inp.spec
+    I, P = sp.I, 32 // bits
+    e = 5
+    off = np.array([0] * (e + 1) + [1] * (sp.E - e), np.int32)
+    codes = inp.weights["w13_codes"][e]
+    sc = oracle.bf16_to_f32(inp.weights["w13_scales"][e])
+    W2 = oracle.dequantize(inp.weights["w2_codes"][e], inp.weights["w2_scales"][e], None, bits,
+                           group=32).astype(np.float64)
+    for j in (0, 31, 32, 95, 200):
+        x = np.zeros((1, sp.H), np.float32)
+        x[0, j] = 1.0
+        y = oracle.expert_ffn(_bf16(x), off, np.array([0], np.int32), 1, inp.weights, bits, I, experts=[e],
+                              group=32)
+        a = np.empty(2 * I)
+        for n in range(2 * I):
+            u = (int(codes[n, j // P]) >> (bits * (j % P))) & ((1 << bits) - 1)
+            a[n] = (u - (1 << (bits - 1))) * float(sc[n, j // 32])
+        h = a[:I] / (1 + np.exp(-a[:I])) * a[I:]
+        assert oracle.rel_fro(y[0], W2 @ h) < 1e-5
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 def test_dense_equivalence_all_experts_selected(bits):
     """k = E: the routed layer equals sum_e softmax(l)_e FFN_e(x) computed densely."""
@@ -381,13 +472,13 @@ def test_dense_equivalence_all_experts_selected(bits):
     assert oracle.rel_fro(out["y"], y) < 1e-5
 
 
-@pytest.mark.parametrize("bits", [4, 2])
-def test_float32_oracle_close_to_float64(bits):
-    inp = _tiny(bits)
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 128), (4, 32), (8, 128), (8, 32)])
+def test_float32_oracle_close_to_float64(bits, group):
+    inp = _tiny(bits, group=group)
     sp = inp.spec
-    o32 = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, bits, sp.I)
+    o32 = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, bits, sp.I, group=group)
     o64 = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, bits, sp.I,
-                           dtype=np.float64)
+                           dtype=np.float64, group=group)
     assert np.array_equal(o32["ids"], o64["ids"])
     assert oracle.rel_fro(o32["y"], o64["y"]) < 1e-5
 

@@ -29,9 +29,9 @@ def test_shapes_and_determinism(name):
     assert a.w_router.shape == (small.E, small.H)
     w = a.weights
     assert w["w13_codes"].shape == (small.E, 2 * small.I, small.H // P)
-    assert w["w13_scales"].shape == (small.E, 2 * small.I, small.H // 128)
+    assert w["w13_scales"].shape == (small.E, 2 * small.I, small.H // small.group)
     assert w["w2_codes"].shape == (small.E, small.H, small.I // P)
-    assert w["w2_scales"].shape == (small.E, small.H, small.I // 128)
+    assert w["w2_scales"].shape == (small.E, small.H, small.I // small.group)
     if small.bits == 2:
         assert set(np.unique(w["w13_zeros"]).tolist()) <= {1, 2}
     for key in w:
@@ -47,6 +47,16 @@ def test_codes_are_uniform():
     q = oracle.unpack_codes(w, 4)
     hist = np.bincount((q.ravel() + 8).astype(np.int64), minlength=16)
     assert hist.min() > 0.9 * hist.mean() and hist.max() < 1.1 * hist.mean()
+
+
+def test_int8_codes_uniform_over_the_symmetric_range():
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", bits=8, group=32)
+    w = workload.make_weight_set(sp)
+    q = oracle.unpack_codes(w["w13_codes"], 8).astype(np.int64)
+    assert q.min() == -127 and q.max() == 127
+    hist = np.bincount((q.ravel() + 127), minlength=255)
+    assert hist.min() > 0.6 * hist.mean() and hist.max() < 1.4 * hist.mean()
+    assert w["w13_scales"].shape == (8, 256, 256 // 32)
 
 
 def test_verify_streams_share_about_half_their_experts():

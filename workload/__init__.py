@@ -18,14 +18,17 @@ Input formats (all row-major, contiguous):
                                along K (the reduction dimension), least
                                significant field first.  Rows [0, I) are the
                                gate projection, rows [I, 2I) the up projection.
-* ``w13_scales`` [E, 2I, H/128] uint16 bfloat16 bits, one per 128-wide K group.
-* ``w13_zeros``  [E, 2I, H/128] uint8 zero-points (2-bit format only).
-* ``w2_codes``   [E, H, I/P], ``w2_scales`` [E, H, I/128], ``w2_zeros`` likewise
+* ``w13_scales`` [E, 2I, H/G] uint16 bfloat16 bits, one per G-wide K group
+                               (G = 128, or 32 for the group-32 formats).
+* ``w13_zeros``  [E, 2I, H/G]  uint8 zero-points (2-bit format only).
+* ``w2_codes``   [E, H, I/P], ``w2_scales`` [E, H, I/G], ``w2_zeros`` likewise
                  for the down projection.
 
-Codes are drawn as uniformly random 32-bit words: every field of a uniform word
-is uniform over its 2**bits values, so INT4 codes are uniform over the 16
-signed values and 2-bit codes uniform over {0..3}.
+INT4 and 2-bit codes are drawn as uniformly random 32-bit words: every field
+of a uniform word is uniform over its 2**bits values, so INT4 codes are
+uniform over the 16 signed values and 2-bit codes uniform over {0..3}.  INT8
+codes are drawn uniformly from -127..127 (the symmetric range, no -128) and
+stored as the bytes q + 128, four per word, least significant first.
 
 Each tensor gets its own PCG64 stream keyed by (workload seed, tensor tag,
 weight-set index), so any one tensor can be regenerated alone.
@@ -62,6 +65,7 @@ class Spec:
     streams: int = 0               # ar1_streams: number of independent streams
     ar1_alpha: float = 0.85
     scale_sigma: float = 0.02      # scales are |N(0,1)| * scale_sigma
+    group: int = 128               # quantisation group along K (128 or 32)
     n_sets: int = 1                # distinct weight sets cycled by the bench
     note: str = ""
 
@@ -74,7 +78,7 @@ class Spec:
         H, I = self.H, self.I
         n_w = 2 * I * H + H * I                  # weights in gate_up and down
         codes = n_w * self.bits // 8
-        groups = n_w // GROUP
+        groups = n_w // self.group
         zeros = groups if self.bits == 2 else 0
         return codes + 2 * groups + zeros
 
@@ -99,6 +103,18 @@ SPECS: Dict[str, Spec] = {
         Spec("prefill_t8192_h4096_e256_k8_i1024_int2", T=8192, H=4096, E=256, k=8, I=1024, bits=2,
              seed=1005, zipf_s=1.1, scale_sigma=0.05,
              note="2-bit experts, prefill chunk with Zipf(1.1) log-prior"),
+        Spec("decode_t1_h4096_e256_k8_i1024_int4g32", T=1, H=4096, E=256, k=8, I=1024, bits=4, group=32,
+             seed=1007, router_law="uniform", n_sets=8,
+             note="batch-1 decode, INT4 symmetric group-32 experts (the draft-layer format)"),
+        Spec("decode_t1_h4096_e256_k8_i1024_int8", T=1, H=4096, E=256, k=8, I=1024, bits=8,
+             seed=1008, router_law="uniform", scale_sigma=0.0015, n_sets=4,
+             note="batch-1 decode, INT8 symmetric group-128 experts; 4 sets of 3.2 GB cycled"),
+        Spec("decode_t1_h4096_e256_k8_i1024_int8g32", T=1, H=4096, E=256, k=8, I=1024, bits=8, group=32,
+             seed=1009, router_law="uniform", scale_sigma=0.0015, n_sets=4,
+             note="batch-1 decode, INT8 symmetric group-32 experts"),
+        Spec("prefill_t4096_h4096_e256_k8_i1024_int8g32", T=4096, H=4096, E=256, k=8, I=1024, bits=8, group=32,
+             seed=1010, zipf_s=1.1, scale_sigma=0.0015,
+             note="prefill chunk, INT8 group-32 experts, Zipf(1.1) log-prior"),
         Spec("mid_t64_h4096_e256_k8_i1024_int4", T=64, H=4096, E=256, k=8, I=1024, bits=4,
              seed=1006, router_law="uniform", x_law="ar1_streams", streams=16, n_sets=2,
              note="middle batch: 16 streams x 4 draft tokens (higher-concurrency verify), decode path"),
@@ -132,6 +148,12 @@ def _uniform_words(rng: np.random.Generator, shape) -> np.ndarray:
     n64 = (n + 1) // 2
     w = rng.bit_generator.random_raw(n64).view(np.uint32)[:n]
     return np.ascontiguousarray(w.reshape(shape))
+
+
+def _int8_words(rng: np.random.Generator, shape) -> np.ndarray:
+    """Words of four INT8 codes, each uniform over -127..127, stored as q + 128."""
+    u = rng.integers(1, 256, size=tuple(shape[:-1]) + (4 * shape[-1],), dtype=np.uint8)
+    return np.ascontiguousarray(u).view("<u4").astype(np.uint32)
 
 
 def make_x(sp: Spec, set_idx: int = 0) -> np.ndarray:
@@ -180,21 +202,24 @@ def _scales(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
 
 def make_weight_set(sp: Spec, set_idx: int = 0) -> Dict[str, np.ndarray]:
     """One full layer of expert weights in the packed formats described above."""
-    E, H, I, P = sp.E, sp.H, sp.I, sp.codes_per_word
+    E, H, I, P, G = sp.E, sp.H, sp.I, sp.codes_per_word, sp.group
     if H % GROUP or I % GROUP:
-        raise ValueError("H and I must be multiples of the 128-wide group")
+        raise ValueError("H and I must be multiples of 128")
+    if G not in (32, 128) or (G == 32 and sp.bits == 2):
+        raise ValueError("group 128, or 32 for INT4 / INT8")
+    codes = _int8_words if sp.bits == 8 else _uniform_words
     out = {
-        "w13_codes": _uniform_words(_rng(sp.seed, _TAG_W13C, set_idx), (E, 2 * I, H // P)),
-        "w13_scales": _scales(_rng(sp.seed, _TAG_W13S, set_idx), (E, 2 * I, H // GROUP), sp.scale_sigma),
-        "w2_codes": _uniform_words(_rng(sp.seed, _TAG_W2C, set_idx), (E, H, I // P)),
-        "w2_scales": _scales(_rng(sp.seed, _TAG_W2S, set_idx), (E, H, I // GROUP), sp.scale_sigma),
+        "w13_codes": codes(_rng(sp.seed, _TAG_W13C, set_idx), (E, 2 * I, H // P)),
+        "w13_scales": _scales(_rng(sp.seed, _TAG_W13S, set_idx), (E, 2 * I, H // G), sp.scale_sigma),
+        "w2_codes": codes(_rng(sp.seed, _TAG_W2C, set_idx), (E, H, I // P)),
+        "w2_scales": _scales(_rng(sp.seed, _TAG_W2S, set_idx), (E, H, I // G), sp.scale_sigma),
     }
     if sp.bits == 2:
         # integer zero-points drawn uniformly from {1, 2}
         out["w13_zeros"] = _rng(sp.seed, _TAG_W13Z, set_idx).integers(
-            1, 3, size=(E, 2 * I, H // GROUP), dtype=np.uint8)
+            1, 3, size=(E, 2 * I, H // G), dtype=np.uint8)
         out["w2_zeros"] = _rng(sp.seed, _TAG_W2Z, set_idx).integers(
-            1, 3, size=(E, H, I // GROUP), dtype=np.uint8)
+            1, 3, size=(E, H, I // G), dtype=np.uint8)
     return out
 
 
