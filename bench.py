@@ -213,6 +213,11 @@ class Plan:
             fn = L.moe_expert_ffn_w4a16_table if sp.bits == 4 else L.moe_expert_ffn_w2a16_table
             s = fn(*common, st["table"].data_ptr(), self.y_perm.data_ptr(), self.ws_ffn.data_ptr(),
                    self.ws_ffn.numel(), stream)
+        elif sp.bits == 8 or sp.group != 128:
+            s = L.moe_expert_ffn_wna16(*common, sp.bits, sp.group, w["w13_codes"].data_ptr(),
+                                       w["w13_scales"].data_ptr(), None, w["w2_codes"].data_ptr(),
+                                       w["w2_scales"].data_ptr(), None, self.y_perm.data_ptr(),
+                                       self.ws_ffn.data_ptr(), self.ws_ffn.numel(), stream)
         elif sp.bits == 4:
             s = L.moe_expert_ffn_w4a16(*common, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
                                        w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(), self.y_perm.data_ptr(),
@@ -292,7 +297,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sp = workload.spec(args.workload)
-    fused = sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays"
+    if args.experts != "arrays" and (sp.bits == 8 or sp.group != 128):
+        print(json.dumps({"error": "the address-table entry points take INT4 and 2-bit with groups of 128"}))
+        sys.exit(2)
+    # the one-launch layer takes INT4 and 2-bit with groups of 128 from stacked arrays
+    fused = (sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays" and sp.bits in (2, 4)
+             and sp.group == 128)
     plan = Plan(sp, dev, fused=fused, experts=args.experts)
     nset = plan.n_sets
     stream = torch.cuda.Stream(dev)
@@ -415,7 +425,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": sp.name, "T": sp.T, "H": sp.H, "E": sp.E, "top_k": sp.k, "I": sp.I,
-                   "weight_format": f"int{sp.bits} g128" + (" sym" if sp.bits == 4 else " + zero-point"),
+                   "weight_format": f"int{sp.bits} g{sp.group}" + (" + zero-point" if sp.bits == 2 else " sym"),
                    "weight_sets_cycled": nset, "experts": args.experts, "launch": f"hip graph of {nset} steps (one per weight set)" if use_graph else "eager",
                    "step": "moe_layer (one launch)" if fused else "stage calls",
                    "wall_s_timed": round(wall, 4)},

@@ -41,6 +41,7 @@ _SIGS = {
     "moe_expert_ffn_workspace_size": (_c_size, [_c_int] * 5),
     "moe_expert_ffn_w4a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 5 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 7 + [_vp, _c_size, _vp]),
+    "moe_expert_ffn_wna16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 7 + [_vp] * 6 + [_vp, _vp, _c_size, _vp]),
     "moe_expert_ffn_w4a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
     "moe_device_address": (_c_int, [_vp, ctypes.POINTER(ctypes.c_uint64)]),
@@ -50,6 +51,7 @@ _SIGS = {
     "moe_layer_w2a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_unpack_codes": (_c_int, [_vp, _c_int, _c_i64, _vp, _vp]),
     "moe_dequant_bf16": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_dequant_bf16_grouped": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -180,8 +182,12 @@ def route_permute(x: torch.Tensor, w_router: torch.Tensor, k: int, logit_bias: O
 
 
 def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: Dict[str, torch.Tensor], bits: int,
-               I: int, ws: Optional[Workspaces] = None, y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-expert gate_up -> SwiGLU -> down on the sorted rows; bf16 [T*k, H]."""
+               I: int, ws: Optional[Workspaces] = None, y_perm: Optional[torch.Tensor] = None,
+               group: int = 128) -> torch.Tensor:
+    """Per-expert gate_up -> SwiGLU -> down on the sorted rows; bf16 [T*k, H].
+
+    bits 4 or 2 with group 128 call moe_expert_ffn_w4a16 / _w2a16; other
+    formats (INT4 group 32, INT8 group 128 or 32) moe_expert_ffn_wna16."""
     dev = _dev(x)
     T, H = x.shape
     E = offsets.numel() - 1
@@ -191,7 +197,13 @@ def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: D
     nbytes = L.moe_expert_ffn_workspace_size(T, k, E, H, I)
     w = (ws or Workspaces(dev)).get("ffn", nbytes)
     st = _stream(dev)
-    if bits == 4:
+    if bits == 8 or group != 128:
+        s = L.moe_expert_ffn_wna16(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I, bits, group,
+                                   _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights.get("w13_zeros")),
+                                   _p(weights["w2_codes"]), _p(weights["w2_scales"]), _p(weights.get("w2_zeros")),
+                                   _p(y_perm), _p(w), w.numel(), st)
+        _check(s, "moe_expert_ffn_wna16")
+    elif bits == 4:
         s = L.moe_expert_ffn_w4a16(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I,
                                    _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights["w2_codes"]),
                                    _p(weights["w2_scales"]), _p(y_perm), _p(w), w.numel(), st)
@@ -320,22 +332,23 @@ def unpack_codes(words: torch.Tensor, bits: int) -> torch.Tensor:
 
 
 def dequant_bf16(words: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor], bits: int,
-                 N: int, K: int) -> torch.Tensor:
+                 N: int, K: int, group: int = 128) -> torch.Tensor:
     """[N, K] bf16 weights by the grouped-GEMM dequant routine."""
     dev = _dev(words)
     out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    _check(lib().moe_dequant_bf16(_p(words), _p(scales), _p(zeros), bits, N, K, _p(out), _stream(dev)),
-           "moe_dequant_bf16")
+    _check(lib().moe_dequant_bf16_grouped(_p(words), _p(scales), _p(zeros), bits, group, N, K, _p(out),
+                                          _stream(dev)), "moe_dequant_bf16_grouped")
     return out
 
 
 def moe_layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
               weights: Dict[str, torch.Tensor], k: int, bits: int, I: int, ws: Optional[Workspaces] = None,
-              want_logits: bool = False) -> Dict[str, torch.Tensor]:
+              want_logits: bool = False, group: int = 128) -> Dict[str, torch.Tensor]:
     """The whole layer: moe_route_permute, the expert FFN and moe_combine; returns every intermediate."""
     ws = ws or Workspaces(x.device)
     out = route_permute(x, w_router, k, logit_bias, want_logits=want_logits, ws=ws)
-    y_perm = expert_ffn(x, out["offsets"], out["sorted_rows"], out["active"], k, weights, bits, I, ws=ws)
+    y_perm = expert_ffn(x, out["offsets"], out["sorted_rows"], out["active"], k, weights, bits, I, ws=ws,
+                        group=group)
     out["y_perm"] = y_perm
     out["y"] = combine(y_perm, out["row_pos"], out["gates"])
     return out

@@ -196,7 +196,7 @@ static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, cons
                              const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
                              const uint32_t *w2_codes, const uint16_t *w2_scales, const uint8_t *w2_zeros,
                              uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream,
-                             const uint64_t *table = nullptr) {
+                             const uint64_t *table = nullptr, int group = 128) {
   moe_status s = check_common_moe(T, H, E, k);
   if (s != MOE_OK) return s;
   if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
@@ -223,8 +223,8 @@ static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, cons
   hipError_t he = current_device_info(&dev);
   if (he != hipSuccess) return from_hip(he, name);
   FfnArgs a{x, expert_offsets, sorted_rows, active, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
-            w2_codes, w2_scales, w2_zeros, y_perm, workspace, table};
-  if (decode_path(T, k, E) && decode_layout_ok(H, I, bits))
+            w2_codes, w2_scales, w2_zeros, y_perm, workspace, table, group};
+  if (decode_path(T, k, E) && decode_layout_ok(H, I, bits, group))
     return from_hip(launch_ffn_decode(a, dev, (hipStream_t)stream), name);
   // the grouped GEMMs address x and one expert's codes with 32-bit byte offsets
   if ((long long)T * H > (1LL << 30) || (long long)I * H > (1LL << 30))
@@ -247,6 +247,20 @@ moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets
                                 void *workspace, size_t workspace_bytes, void *stream) {
   return expert_ffn("moe_expert_ffn_w2a16", 2, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
                     w13_scales, w13_zeros, w2_codes, w2_scales, w2_zeros, y_perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_wna16(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                const int32_t *active, int T, int k, int E, int H, int I, int bits, int group_size,
+                                const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
+                                const uint32_t *w2_codes, const uint16_t *w2_scales, const uint8_t *w2_zeros,
+                                uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream) {
+  const bool ok = (bits == 4 && (group_size == 128 || group_size == 32)) ||
+                  (bits == 8 && (group_size == 128 || group_size == 32)) || (bits == 2 && group_size == 128);
+  if (!ok)
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wna16: unsupported format: %d bits, group %d", bits, group_size);
+  return expert_ffn("moe_expert_ffn_wna16", bits, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
+                    w13_scales, bits == 2 ? w13_zeros : nullptr, w2_codes, w2_scales, bits == 2 ? w2_zeros : nullptr,
+                    y_perm, workspace, workspace_bytes, stream, nullptr, group_size);
 }
 
 moe_status moe_expert_ffn_w4a16_table(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
@@ -363,7 +377,8 @@ moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const flo
 }
 
 moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, int8_t *out, void *stream) {
-  if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2 or 4 (got %d)", bits);
+  if (bits != 2 && bits != 4 && bits != 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2, 4 or 8 (got %d)", bits);
   if (n_words < 0) return fail(MOE_ERR_INVALID_ARG, "n_words must be >= 0");
   if (n_words > (1LL << 36)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "n_words too large");
   if (!words || !out) return fail(MOE_ERR_INVALID_ARG, "moe_unpack_codes: words and out are required");
@@ -372,9 +387,12 @@ moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, in
   return from_hip(launch_unpack(words, bits, n_words, out, (hipStream_t)stream), "moe_unpack_codes launch");
 }
 
-moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits, int N, int K,
-                            uint16_t *out, void *stream) {
-  if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2 or 4 (got %d)", bits);
+moe_status moe_dequant_bf16_grouped(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
+                                    int group_size, int N, int K, uint16_t *out, void *stream) {
+  if (bits != 2 && bits != 4 && bits != 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2, 4 or 8 (got %d)", bits);
+  if (group_size != 128 && !(group_size == 32 && bits != 2))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "group size 128, or 32 for INT4 / INT8 (got %d)", group_size);
   if (N < 0 || K < 0) return fail(MOE_ERR_INVALID_ARG, "N and K must be >= 0");
   if (K % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K must be a multiple of 128 (got %d)", K);
   if ((long long)N * K > (1LL << 36)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "N*K too large");
@@ -383,8 +401,13 @@ moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const
   if (!aligned(words, 4) || !aligned(scales, 2) || !aligned(out, 4))
     return fail(MOE_ERR_MISALIGNED, "moe_dequant_bf16: array alignment");
   if (N == 0 || K == 0) return MOE_OK;
-  return from_hip(launch_dequant_bf16(words, scales, zeros, bits, N, K, out, (hipStream_t)stream),
+  return from_hip(launch_dequant_bf16(words, scales, zeros, bits, group_size, N, K, out, (hipStream_t)stream),
                   "moe_dequant_bf16 launch");
+}
+
+moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits, int N, int K,
+                            uint16_t *out, void *stream) {
+  return moe_dequant_bf16_grouped(words, scales, zeros, bits, 128, N, K, out, stream);
 }
 
 }  // extern "C"

@@ -81,6 +81,17 @@ __device__ __forceinline__ u32x4 unpack2_pairs(uint32_t w, int half, uint32_t ma
                __builtin_amdgcn_perm(magic, b, kPermB01), __builtin_amdgcn_perm(magic, b, kPermB23)};
 }
 
+// INT8 fields are 8 bits wide, too many for the offset form: each byte u goes
+// through a float conversion, exact for 0..255, whose upper 16 bits are the
+// bf16 value u.  Two words (8 fields) -> four bf16 pairs in K order.
+__device__ __forceinline__ u32x4 unpack8_bf16(uint32_t w0, uint32_t w1) {
+  auto pr = [](uint32_t w, int b) {
+    const float lo = (float)((w >> (8 * b)) & 0xFFu), hi = (float)((w >> (8 * b + 8)) & 0xFFu);
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  };
+  return u32x4{pr(w0, 0), pr(w0, 2), pr(w1, 0), pr(w1, 2)};
+}
+
 // Natural-order bf16 activations d (pairs (x0,x1), (x2,x3), ...) -> the pair
 // order of the unpacked codes: o[i] = (x[ord[2i]], x[ord[2i+1]]).  N elements.
 template <int N>
@@ -107,6 +118,16 @@ __device__ __forceinline__ void dequant8_int4(uint32_t w, float s, float zs, uin
     const float f1 = (float)((hi >> (8 * b)) & 0xFFu);
     out[b] = pack_bf16x2(__builtin_fmaf(f0, s, zs), __builtin_fmaf(f1, s, zs));
   }
+}
+
+// Four 8-bit fields of w (u = q + 128) -> two packed bf16 pairs of (u - 128) * s,
+// in K order (zs = -128 * s).  (u - 128) * s has at most 16 significant bits, so
+// the fma is exact in float32; the conversion to bf16 rounds to nearest even.
+__device__ __forceinline__ void dequant4_int8(uint32_t w, float s, float zs, uint32_t out[2]) {
+  const float f0 = (float)(w & 0xFFu), f1 = (float)((w >> 8) & 0xFFu);
+  const float f2 = (float)((w >> 16) & 0xFFu), f3 = (float)(w >> 24);
+  out[0] = pack_bf16x2(__builtin_fmaf(f0, s, zs), __builtin_fmaf(f1, s, zs));
+  out[1] = pack_bf16x2(__builtin_fmaf(f2, s, zs), __builtin_fmaf(f3, s, zs));
 }
 
 // Sixteen 2-bit fields of w -> eight packed bf16 pairs of (u - z) * s, in K order.

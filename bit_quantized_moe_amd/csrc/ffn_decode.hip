@@ -50,7 +50,6 @@ namespace {
 
 constexpr int kRows1 = 16;   // gate/up row pairs per phase-1 item
 constexpr int kRows2 = 128;  // down rows per phase-2 item (two sets of 16 per wave)
-constexpr int kChunkG = 8;   // K groups whose loads a wave keeps in flight together
 constexpr int kRMax = 4;     // routed rows staged per pass when T > 1
 constexpr int kRedFloats = 4 * 2 * 16 * 16;  // phase-1 cross-wave partials
 
@@ -95,21 +94,39 @@ __device__ __forceinline__ int *routed_ctr(int *ctl, int amax, int i) {
 constexpr uint32_t kHReady = 1u << 16;  // tag of a written h word
 constexpr uint64_t kRecTag = 1ull << 63;  // tag of a written routing record word
 
+// ---------------------------------------------------------------- formats
+// BITS: 4 (INT4, field q + 8), 2 (field u, integer zero-point) or 8 (INT8,
+// field q + 128).  GS: quantisation group along K, 128 or 32.  The kernels
+// walk K in units of 128 (kGroup); a unit holds 128 / GS scales per row.
+template <int GS>
+constexpr int kSPU = kGroup / GS;
+// Units whose weight loads a wave keeps in flight together: 8 of INT4 or
+// 2-bit, 4 of INT8 (the same bytes); half that with groups of 32, whose four
+// scales per unit and transposed slices take registers.
+template <int BITS, int GS>
+constexpr int kCG = (BITS == 8 ? 4 : 8) / (GS == 32 ? 2 : 1);
+
 // ---------------------------------------------------------------- operands
 // One chunk of natural-order bf16 activations (d: pairs (x0,x1), (x2,x3), ...)
-// in the field order of the unpacked codes: INT4 chunks of 8, INT2 chunks of 16.
+// in the field order of the unpacked codes: INT4 chunks of 8, INT2 chunks of
+// 16; INT8 codes unpack in K order, so its chunks (of 8) stay as they are.
 template <int BITS>
 __device__ __forceinline__ void permute_chunk(const uint32_t *d, uint32_t *o) {
-  order_pairs<BITS == 4 ? 8 : 16>(d, o);
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = d[i];
+  } else {
+    order_pairs<BITS == 4 ? 8 : 16>(d, o);
+  }
 }
 
 // ---------------------------------------------------------------- LDS staging
 // Activation row r (K bf16) goes to LDS act + r * (K*2 + 16) in operand order,
-// in chunks of 8 (INT4) or 16 (INT2) elements; its per-group sums go to
+// in chunks of 8 (INT4, INT8) or 16 (INT2) elements; its per-group sums go to
 // Xs[g*16 + m] for the MFMA rows m that read it (row m reads activation row
-// min(m, R-1)).
+// min(m, R-1)), g counting groups of GS.
 template <int BITS>
-constexpr int kChunkE = BITS == 4 ? 8 : 16;
+constexpr int kChunkE = BITS == 2 ? 16 : 8;
 // Chunks of activation row 0 that every thread loads before its weights:
 // chunks t + 256 i, i < NPRE, of thread t (NPRE = 2 covers K = 4096 for INT4).
 // Vector memory loads retire in issue order, so only loads issued before the
@@ -162,17 +179,18 @@ __device__ __forceinline__ void pre_load(const uint16_t *src0, int K, PreAct &pa
   }
 }
 
-// Per-group sums of the staged rows 0..R-1 (8 threads per group, 16 elements
-// each) into Xs; starts and ends with a block barrier.
-template <int BITS>
+// Per-group sums of the staged rows 0..R-1 (GS / 16 threads per group, 16
+// elements each) into Xs; starts and ends with a block barrier.
+template <int GS>
 __device__ __forceinline__ void stage_group_sums(const uint8_t *act, float *Xs, int R, int K) {
+  constexpr int NP = GS / 16;
   const int pitch = K * 2 + 16;
   lds_barrier();
-  const int G = K / kGroup;
+  const int G = K / GS;
   for (int r = 0; r < R; ++r) {
-    for (int t = threadIdx.x; t < G * 8; t += 256) {
-      const int g = t / 8, part = t % 8;
-      const u32x4 *p = (const u32x4 *)(act + r * pitch + (g * kGroup + part * 16) * 2);
+    for (int t = threadIdx.x; t < G * NP; t += 256) {
+      const int g = t / NP, part = t % NP;
+      const u32x4 *p = (const u32x4 *)(act + r * pitch + (g * GS + part * 16) * 2);
       const u32x4 v0 = p[0], v1 = p[1];
       float sum = 0.f;
 #pragma unroll
@@ -180,7 +198,7 @@ __device__ __forceinline__ void stage_group_sums(const uint8_t *act, float *Xs, 
         sum = dot2_bf16(v0[z], 0x3F803F80u, sum);
         sum = dot2_bf16(v1[z], 0x3F803F80u, sum);
       }
-      sum = group_sum(sum, 8);
+      sum = group_sum(sum, NP);
       if (part == 0) {
         if (r == R - 1) {
           for (int m = r; m < 16; ++m) Xs[g * 16 + m] = sum;
@@ -195,7 +213,7 @@ __device__ __forceinline__ void stage_group_sums(const uint8_t *act, float *Xs, 
 
 // Stages activation rows 0..R-1 (src(r): row r's global address); chunks
 // q < q0 of row 0 come from pa (q0 = 256 * NPRE or 0).  Ends with a block barrier.
-template <int BITS, int NPRE, typename Src>
+template <int BITS, int GS, int NPRE, typename Src>
 __device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int R, int K, int q0,
                                            const PreAct *pa) {
   const int pitch = K * 2 + 16;
@@ -215,13 +233,13 @@ __device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int
       store_act_chunk<BITS>(act + r * pitch, q, d);
     }
   }
-  stage_group_sums<BITS>(act, Xs, R, K);
+  stage_group_sums<GS>(act, Xs, R, K);
 }
 
 // Stages h rows 0..R-1 (h0: row 0's words, rows I words apart) once phase 1
 // has written them: each thread reads its chunks with device-coherent loads
 // until every word carries kHReady.  Returns false if a wait timed out.
-template <int BITS>
+template <int BITS, int GS>
 __device__ __forceinline__ bool stage_h_rows(uint8_t *act, float *Xs, const uint32_t *h0, int R, int I,
                                              int max_spins) {
   constexpr int CE = kChunkE<BITS>;
@@ -252,7 +270,7 @@ __device__ __forceinline__ bool stage_h_rows(uint8_t *act, float *Xs, const uint
       store_act_chunk<BITS>(act + r * pitch, q, d);
     }
   }
-  stage_group_sums<BITS>(act, Xs, R, I);
+  stage_group_sums<GS>(act, Xs, R, I);
   return ok;
 }
 
@@ -266,15 +284,15 @@ constexpr int kHPend = 4;
 // pair order of the unpacked codes, see order_pairs).
 template <int BITS>
 __device__ __forceinline__ int chunk_slot(int i) {
-  return BITS == 4 ? (i >> 1) + 4 * (i & 1) : (i >> 2) + 4 * (i & 3);
+  return BITS == 8 ? i : BITS == 4 ? (i >> 1) + 4 * (i & 1) : (i >> 2) + 4 * (i & 3);
 }
 
-// One polling round for the wave's lowest pending group (bit j of pend: group
-// wv + 4 j): every lane reads two of its h words.  Once all carry kHReady the
-// group goes to act in operand order, its sum (the arithmetic of
-// stage_group_sums) to the 16 rows of Xs, and gflag[g] is set.  Returns the
-// groups still pending.
-template <int BITS>
+// One polling round for the wave's lowest pending unit (bit j of pend: unit
+// wv + 4 j of 128 K): every lane reads two of its h words.  Once all carry
+// kHReady the unit goes to act in operand order, its group sums (the
+// arithmetic of stage_group_sums) to the 16 rows of Xs, and gflag[g] is set.
+// Returns the units still pending.
+template <int BITS, int GS>
 __device__ uint32_t service_h(uint32_t pend, const uint32_t *h, uint8_t *act, float *Xs, int *gflag, int wv) {
   constexpr int CE = kChunkE<BITS>;
   const int lane = lane_id();
@@ -301,44 +319,62 @@ __device__ uint32_t service_h(uint32_t pend, const uint32_t *h, uint8_t *act, fl
       sum = dot2_bf16(v1[z], 0x3F803F80u, sum);
     }
   }
-  sum = group_sum(sum, 8);
-  const float v = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sum)));
-  if (lane < 16) Xs[g * 16 + lane] = v;
+  if constexpr (GS == 128) {
+    sum = group_sum(sum, 8);
+    const float v = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sum)));
+    if (lane < 16) Xs[g * 16 + lane] = v;
+  } else {
+    // groups of 32: the sums of lanes 0, 2, 4, 6; lane 16 j + m writes group j, row m
+    sum = group_sum(sum, 2);
+    const int j = lane >> 4;
+    const int src = __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 0);
+    const int s1 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 2);
+    const int s2 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 4);
+    const int s3 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 6);
+    const int v = j == 0 ? src : j == 1 ? s1 : j == 2 ? s2 : s3;
+    Xs[(4 * g + j) * 16 + (lane & 15)] = __builtin_bit_cast(float, v);
+  }
   if (lane == 0) __hip_atomic_store(gflag + g, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   return pend & ~(1u << j);
 }
 
 // ---------------------------------------------------------------- weights
-// A lane reads 32 consecutive K of one weight row per group: a 16-byte (INT4)
-// or 8-byte (INT2) slice at byte lsub * kGroupBytes / 4 of the group.
+// A lane reads 32 consecutive K of one weight row per 128-K unit: a 16-byte
+// (INT4), 8-byte (INT2) or 32-byte (INT8) slice at byte lsub * kGroupBytes / 4
+// of the unit.
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 template <int BITS>
-using Word = typename std::conditional<BITS == 4, u32x4, u32x2>::type;
+using Word = typename std::conditional<BITS == 4, u32x4,
+                                       typename std::conditional<BITS == 2, u32x2, u32x8>::type>::type;
 template <int BITS>
 constexpr int kGroupBytes = kGroup * BITS / 8;
 
-// kChunkG consecutive groups of one row (the lane's slices), their bf16 scales
-// (16 bytes) and, for INT2, their zero-points (8 bytes).
-template <int BITS>
+// kCG consecutive units of one row (the lane's slices), their bf16 scales
+// (kCG * 128 / GS of them, two per word) and, for INT2, their zero-points
+// (8 bytes).
+template <int BITS, int GS>
 struct Chunk {
-  Word<BITS> w[kChunkG];
-  u32x4 s;
+  Word<BITS> w[kCG<BITS, GS>];
+  uint32_t s[kCG<BITS, GS> * kSPU<GS> / 2];
   u32x2 z;
 };
 
-// Offsets (bytes) of a lane's first group in the expert's code, scale and
-// zero-point arrays.
+// Offsets (bytes) of a lane's first unit in the expert's code, scale and
+// zero-point arrays (SPU scales per unit).
 struct Off {
   uint32_t c, s, z;
 };
+template <int SPU>
 __device__ __forceinline__ Off row_off(int row, int G, int g0, int gbytes, int lsub) {
   Off o;
   o.z = (uint32_t)row * G + g0;
-  o.s = 2 * o.z;
+  o.s = 2 * SPU * o.z;
   o.c = o.z * gbytes + lsub * (gbytes / 4);
   return o;
 }
+template <int SPU>
 __device__ __forceinline__ Off add_groups(Off o, int dg, int gbytes) {
-  return Off{o.c + dg * gbytes, o.s + 2 * dg, o.z + dg};
+  return Off{o.c + dg * gbytes, o.s + 2 * SPU * dg, o.z + dg};
 }
 
 // Expert-local arrays (wave-uniform bases).
@@ -355,21 +391,37 @@ __device__ __forceinline__ ExpertW expert_from_table(const uint64_t *tab, int e,
   return ExpertW{(const uint8_t *)sload(t), (const uint8_t *)sload(t + 1), (const uint8_t *)sload(t + 2)};
 }
 
-template <int BITS>
-__device__ __forceinline__ void load_chunk(const ExpertW &x, Off o, Chunk<BITS> &ch) {
+template <int BITS, int GS>
+__device__ __forceinline__ void load_chunk(const ExpertW &x, Off o, Chunk<BITS, GS> &ch) {
+  constexpr int CG = kCG<BITS, GS>;
+  constexpr int NS = CG * kSPU<GS> / 2;  // scale words: 4 (16 bytes), 2 or 8
 #pragma unroll
-  for (int c = 0; c < kChunkG; ++c) ch.w[c] = *(const Word<BITS> *)(x.codes + o.c + c * kGroupBytes<BITS>);
-  ch.s = *(const u32x4 *)(x.scales + o.s);
+  for (int c = 0; c < CG; ++c) ch.w[c] = *(const Word<BITS> *)(x.codes + o.c + c * kGroupBytes<BITS>);
+  if constexpr (NS == 2) {
+    const u32x2 v = *(const u32x2 *)(x.scales + o.s);
+    ch.s[0] = v[0];
+    ch.s[1] = v[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < NS / 4; ++h) {
+      const u32x4 v = *(const u32x4 *)(x.scales + o.s + 16 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ch.s[4 * h + i] = v[i];
+    }
+  }
   if constexpr (BITS == 2) ch.z = *(const u32x2 *)(x.zeros + o.z);
 }
 
-// B operand j (32 K of the lane's slice) of one group.
+// B operand j (8 K per lane) from words of the lane's slice: INT4 word j, INT2
+// half j & 1 of word j / 2, INT8 words 2j and 2j + 1.
 template <int BITS>
 __device__ __forceinline__ bf16x8 b_op(Word<BITS> w, int j, uint32_t magic) {
   if constexpr (BITS == 4)
     return __builtin_bit_cast(bf16x8, unpack4_pairs(w[j], magic));
-  else
+  else if constexpr (BITS == 2)
     return __builtin_bit_cast(bf16x8, unpack2_pairs(w[j / 2], j & 1, magic));
+  else
+    return __builtin_bit_cast(bf16x8, unpack8_bf16(w[2 * j], w[2 * j + 1]));
 }
 
 // C (16 activation rows x 16 weight rows) over one 128-wide group, for NR row
@@ -401,51 +453,126 @@ __device__ __forceinline__ void group_acc(f32x4 cg, float s, float zo, const flo
   }
 }
 
+// The B value of code 0 offset: the unpacked value minus the signed code.
 template <int BITS>
 __device__ __forceinline__ float zero_off(uint32_t z) {
   if constexpr (BITS == 4)
     return 136.f;  // offset-binary code q + 8, plus the 128 of the unpack
+  else if constexpr (BITS == 8)
+    return 128.f;  // offset-binary code q + 128, unpacked as is
   else
     return 128.f + (float)z;
 }
 
-// A full chunk (groups G0 .. G0+kChunkG-1) of NR row sets.  ap: activation
-// bytes of group G0 for the lane; xs: Xs + G0 * 16 (+ 4 * lsub unless ONE).
+// Groups of 32: a lane's slice of a unit is one whole group, but an MFMA sums
+// over the slices of the four lanes 16 r + n.  A 4 x 4 transpose of words
+// across those lanes (two swaps of 32-lane halves, two of 16-lane rows) gives
+// lane 16 r + n, in v[j], the word lane 16 j + n held in v[r]: afterwards MFMA
+// j reads group j only.
+__device__ __forceinline__ void transpose4_rows(uint32_t &v0, uint32_t &v1, uint32_t &v2, uint32_t &v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  v0 = c[0];
+  v1 = c[1];
+  v2 = d[0];
+  v3 = d[1];
+}
+template <int BITS>
+__device__ __forceinline__ void transpose_slices(Word<BITS> &w) {
+  if constexpr (BITS == 4) {
+    uint32_t v0 = w[0], v1 = w[1], v2 = w[2], v3 = w[3];
+    transpose4_rows(v0, v1, v2, v3);
+    w = u32x4{v0, v1, v2, v3};
+  } else {  // INT8: word pairs, transposed as even and odd words
+    uint32_t e0 = w[0], e1 = w[2], e2 = w[4], e3 = w[6], o0 = w[1], o1 = w[3], o2 = w[5], o3 = w[7];
+    transpose4_rows(e0, e1, e2, e3);
+    transpose4_rows(o0, o1, o2, o3);
+    w = u32x8{e0, o0, e1, o1, e2, o2, e3, o3};
+  }
+}
+
+// One 128-K unit with groups of 32, NR row sets: MFMA j covers group j (A from
+// K 32 j + 8 lsub, ap: the unit's activation bytes of the row + 16 lsub), and
+// each group's C is corrected with its own scale.  sc[r]: the unit's four bf16
+// scales of row set r (two words); xs: Xs of the unit's first group.
 template <int BITS, bool ONE, int NR>
-__device__ __forceinline__ void chunk_gemv(const Chunk<BITS> *ch, const uint8_t *ap, const float *xs, uint32_t magic,
-                                           f32x4 *acc) {
+__device__ __forceinline__ void unit32_acc(Word<BITS> *w, const uint8_t *ap, const uint32_t (*sc)[2], const float *xs,
+                                           uint32_t magic, f32x4 *acc) {
 #pragma unroll
-  for (int c = 0; c < kChunkG; ++c) {
-    Word<BITS> w[NR];
-    f32x4 cg[NR];
+  for (int r = 0; r < NR; ++r) transpose_slices<BITS>(w[r]);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) w[r] = ch[r].w[c];
-    group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
+  for (int j = 0; j < 4; ++j) {
+    const bf16x8 a = *(const bf16x8 *)(ap + j * 64);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const float s = bf16_to_f32((ch[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
-      const float zo = zero_off<BITS>((ch[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
-      group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
+      const f32x4 cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b_op<BITS>(w[r], j, magic),
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const float s = bf16_to_f32((sc[r][j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+      group_acc<ONE>(cg, s, zero_off<BITS>(0u), xs + j * 16, acc[r]);
     }
   }
 }
 
-// One group at a time (shapes whose groups do not split into full chunks),
+// A full chunk (units G0 .. G0+kCG-1) of NR row sets.  ap: activation bytes of
+// unit G0 for the lane; xs: Xs of unit G0's first group (+ 4 * lsub unless ONE).
+template <int BITS, int GS, bool ONE, int NR>
+__device__ __forceinline__ void chunk_gemv(Chunk<BITS, GS> *ch, const uint8_t *ap, const float *xs, uint32_t magic,
+                                           f32x4 *acc) {
+#pragma unroll
+  for (int c = 0; c < kCG<BITS, GS>; ++c) {
+    Word<BITS> w[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[r] = ch[r].w[c];
+    if constexpr (GS == 32) {
+      uint32_t sc[NR][2];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        sc[r][0] = ch[r].s[2 * c];
+        sc[r][1] = ch[r].s[2 * c + 1];
+      }
+      unit32_acc<BITS, ONE, NR>(w, ap + c * (kGroup * 2), sc, xs + c * 64, magic, acc);
+    } else {
+      f32x4 cg[NR];
+      group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float s = bf16_to_f32((ch[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
+        const float zo = zero_off<BITS>((ch[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
+        group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
+      }
+    }
+  }
+}
+
+// One unit at a time (shapes whose units do not split into full chunks),
 // NR row sets at offsets o[r].
-template <int BITS, bool ONE, int NR>
+template <int BITS, int GS, bool ONE, int NR>
 __device__ __forceinline__ void groups_gemv_slow(const ExpertW &x, const Off *o, int ng, const uint8_t *ap,
                                                  const float *xs, uint32_t magic, f32x4 *acc) {
   for (int c = 0; c < ng; ++c) {
     Word<BITS> w[NR];
-    f32x4 cg[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[r] = *(const Word<BITS> *)(x.codes + o[r].c + c * kGroupBytes<BITS>);
-    group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
+    if constexpr (GS == 32) {
+      uint32_t sc[NR][2];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const float s = bf16_to_f32(*(const uint16_t *)(x.scales + o[r].s + 2 * c));
-      const float zo = zero_off<BITS>(BITS == 2 ? x.zeros[o[r].z + c] : 0u);
-      group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
+      for (int r = 0; r < NR; ++r) {
+        const u32x2 v = *(const u32x2 *)(x.scales + o[r].s + 8 * c);
+        sc[r][0] = v[0];
+        sc[r][1] = v[1];
+      }
+      unit32_acc<BITS, ONE, NR>(w, ap + c * (kGroup * 2), sc, xs + c * 64, magic, acc);
+    } else {
+      f32x4 cg[NR];
+      group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float s = bf16_to_f32(*(const uint16_t *)(x.scales + o[r].s + 2 * c));
+        const float zo = zero_off<BITS>(BITS == 2 ? x.zeros[o[r].z + c] : 0u);
+        group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
+      }
     }
   }
 }
@@ -472,9 +599,10 @@ __device__ __forceinline__ Meta meta(const DecodeParams &p, int a, int nrows) {
 __device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v)); }
 
 // ONE: T == 1 (every active expert has exactly one routed row, of token 0).
-// FAST: every wave's phase-1 group range and the phase-2 K split into full
-// chunks of kChunkG groups (H % 4096 == 0 and I % 1024 == 0); the first chunk
-// of weights is then requested before the activations are staged.
+// FAST: every wave's phase-1 unit range and the phase-2 K split into full
+// chunks of kCG units (INT4 and 2-bit with groups of 128: H % 4096 == 0 and
+// I % 1024 == 0); the first chunk of weights is then requested before the
+// activations are staged.
 // Fused layer routing record.  The selector block ranks the T*k rows by
 // (expert, row) - the order of moe_permute - and stores, at each sorted
 // position i, one tagged word: kRecTag | row << 48 | expert << 32 | gate bits.
@@ -613,13 +741,17 @@ __device__ bool read_sorted_record(const uint64_t *rec, int n, int E, int max_sp
 // publishes them in that order as tagged words; (c) every block reads those
 // words and derives the grouping in LDS.  After its items, block b < H/128 combines
 // columns [128 b, 128 b + 128) of y from the tagged y_perm words.
-template <int BITS, bool ONE, bool FAST, bool LAYER, bool TAB>
+template <int BITS, int GS, bool ONE, bool FAST, bool LAYER, bool TAB>
 __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int RM = ONE ? 1 : kRMax;
   constexpr int GB = kGroupBytes<BITS>;
+  constexpr int CG = kCG<BITS, GS>, SPU = kSPU<GS>;
+  // a lane's activation bytes within a unit: K 32 lsub (groups of 128) or
+  // 8 lsub, then +32 per MFMA (groups of 32, after the slice transpose)
+  constexpr int LA = GS == 32 ? 16 : 64;
   // activation chunks per thread loaded ahead of the phase-1 weights
-  constexpr int NPRE = (BITS == 4 && ONE) ? 2 : 1;
+  constexpr int NPRE = (BITS != 2 && ONE) ? 2 : 1;
   const uint32_t magic = p.magic;
   const int lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -631,7 +763,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   const int pmax = pitch1 > pitch2 ? pitch1 : pitch2;
   uint8_t *act = lds;
   float *Xs = (float *)(lds + RM * pmax);
-  float *red = Xs + 16 * (G1 > G2 ? G1 : G2);
+  float *red = Xs + 16 * SPU * (G1 > G2 ? G1 : G2);
   // fused layer: routing results in LDS after the FFN's own arrays, or after
   // the router's rows where those are larger (they share the start of LDS)
   const size_t ffn_bytes = (size_t)((uint8_t *)(red + kRedFloats) - lds);
@@ -750,9 +882,9 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const size_t erows = (size_t)md.e * 2 * p.I;  // first row of the expert
       const ExpertW xw = TAB ? expert_from_table(p.tab, md.e, 0)
                              : ExpertW{(const uint8_t *)p.w13c + erows * (G1 * GB),
-                                         (const uint8_t *)p.w13s + erows * (G1 * 2), p.w13z + erows * G1};
-      const Off o2[2] = {row_off(i0 + m, G1, g0, GB, lsub), row_off(p.I + i0 + m, G1, g0, GB, lsub)};
-      const int nch = ng / kChunkG;
+                                         (const uint8_t *)p.w13s + erows * (G1 * 2 * SPU), p.w13z + erows * G1};
+      const Off o2[2] = {row_off<SPU>(i0 + m, G1, g0, GB, lsub), row_off<SPU>(p.I + i0 + m, G1, g0, GB, lsub)};
+      const int nch = ng / CG;
       // activation row of sorted position q
       auto xrow = [&](int q) -> const uint16_t * {
         const int t = ONE ? 0 : min(max(LAYER ? s_sorted[q] : sload(p.sorted_rows + q), 0) / p.k, p.T - 1);
@@ -760,36 +892,36 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       };
       PreAct pa;
       int q0 = 0;
-      Chunk<BITS> wgu[2];
+      Chunk<BITS, GS> wgu[2];
       if constexpr (FAST) {
         if (md.o0 < md.o1) {
           pre_load<BITS, NPRE>(xrow(md.o0), p.H, pa);
           q0 = 256 * NPRE;
         }
-        load_chunk<BITS>(xw, o2[0], wgu[0]);
-        load_chunk<BITS>(xw, o2[1], wgu[1]);
+        load_chunk<BITS, GS>(xw, o2[0], wgu[0]);
+        load_chunk<BITS, GS>(xw, o2[1], wgu[1]);
       }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
-        stage_rows<BITS, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
+        stage_rows<BITS, GS, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
         const int arow = ONE ? 0 : min(m, R - 1);
-        const uint8_t *ap = act + arow * pitch1 + lsub * 64 + g0 * (kGroup * 2);
-        const float *xs = Xs + g0 * 16 + (ONE ? 0 : 4 * lsub);
+        const uint8_t *ap = act + arow * pitch1 + lsub * LA + g0 * (kGroup * 2);
+        const float *xs = Xs + g0 * 16 * SPU + (ONE ? 0 : 4 * lsub);
         f32x4 tgu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if constexpr (FAST) {
           for (int ch = 0; ch < nch; ++ch) {
             if (ch > 0) {
-              load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wgu[0]);
-              load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wgu[1]);
+              load_chunk<BITS, GS>(xw, add_groups<SPU>(o2[0], ch * CG, GB), wgu[0]);
+              load_chunk<BITS, GS>(xw, add_groups<SPU>(o2[1], ch * CG, GB), wgu[1]);
             }
-            chunk_gemv<BITS, ONE, 2>(wgu, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, tgu);
+            chunk_gemv<BITS, GS, ONE, 2>(wgu, ap + ch * CG * (kGroup * 2), xs + ch * CG * 16 * SPU, magic, tgu);
           }
           if (nch > 1 && rb + RM < md.o1) {  // the next pass starts again from the first chunk
-            load_chunk<BITS>(xw, o2[0], wgu[0]);
-            load_chunk<BITS>(xw, o2[1], wgu[1]);
+            load_chunk<BITS, GS>(xw, o2[0], wgu[0]);
+            load_chunk<BITS, GS>(xw, o2[1], wgu[1]);
           }
         } else {
-          groups_gemv_slow<BITS, ONE, 2>(xw, o2, ng, ap, xs, magic, tgu);
+          groups_gemv_slow<BITS, GS, ONE, 2>(xw, o2, ng, ap, xs, magic, tgu);
         }
         const f32x4 tg = tgu[0], tu = tgu[1];
         // cross-wave sum of the 16 x 16 gate / up partials: red[wave][gate|up][row][col]
@@ -822,13 +954,13 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const size_t erows = (size_t)md.e * p.H;
       const ExpertW xw = TAB ? expert_from_table(p.tab, md.e, 3)
                              : ExpertW{(const uint8_t *)p.w2c + erows * (G2 * GB),
-                                         (const uint8_t *)p.w2s + erows * (G2 * 2), p.w2z + erows * G2};
-      const Off o2[2] = {row_off(n0 + m, G2, 0, GB, lsub), row_off(n0 + 16 + m, G2, 0, GB, lsub)};
-      const int nch = G2 / kChunkG;
-      Chunk<BITS> wd[2];
+                                         (const uint8_t *)p.w2s + erows * (G2 * 2 * SPU), p.w2z + erows * G2};
+      const Off o2[2] = {row_off<SPU>(n0 + m, G2, 0, GB, lsub), row_off<SPU>(n0 + 16 + m, G2, 0, GB, lsub)};
+      const int nch = G2 / CG;
+      Chunk<BITS, GS> wd[2];
       if constexpr (FAST) {
-        load_chunk<BITS>(xw, o2[0], wd[0]);
-        load_chunk<BITS>(xw, o2[1], wd[1]);
+        load_chunk<BITS, GS>(xw, o2[0], wd[0]);
+        load_chunk<BITS, GS>(xw, o2[1], wd[1]);
       }
       // One token with full chunks (the host keeps I / 128 <= 4 kHPend for
       // it): the per-group pipeline.
@@ -839,18 +971,18 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         lds_barrier();
         const uint32_t *h = p.hbuf + (size_t)md.o0 * p.I;
         uint32_t pend = (1u << ((G2 - wv + 3) / 4)) - 1u;
-        pend = service_h<BITS>(pend, h, act, Xs, gflag, wv);
-        const uint8_t *ap = act + lsub * 64;
+        pend = service_h<BITS, GS>(pend, h, act, Xs, gflag, wv);
+        const uint8_t *ap = act + lsub * LA;
         f32x4 ty[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         bool ok = true;
         for (int ch = 0; ch < nch; ++ch) {
           if (ch > 0) {
-            load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wd[0]);
-            load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wd[1]);
+            load_chunk<BITS, GS>(xw, add_groups<SPU>(o2[0], ch * CG, GB), wd[0]);
+            load_chunk<BITS, GS>(xw, add_groups<SPU>(o2[1], ch * CG, GB), wd[1]);
           }
 #pragma unroll
-          for (int c = 0; c < kChunkG; ++c) {
-            const int g = ch * kChunkG + c;
+          for (int c = 0; c < CG; ++c) {
+            const int g = ch * CG + c;
             for (int spins = 0;; ++spins) {
               if (__hip_atomic_load(gflag + g, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
               if (spins >= p.max_spins) {
@@ -858,20 +990,25 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
                 break;
               }
               if (pend)
-                pend = service_h<BITS>(pend, h, act, Xs, gflag, wv);
+                pend = service_h<BITS, GS>(pend, h, act, Xs, gflag, wv);
               else
                 __builtin_amdgcn_s_sleep(1);
             }
             Word<BITS> w2[2];
-            f32x4 cg[2];
             w2[0] = wd[0].w[c];
             w2[1] = wd[1].w[c];
-            group_mfma<BITS, 2>(w2, ap + g * (kGroup * 2), magic, cg);
+            if constexpr (GS == 32) {
+              const uint32_t sc[2][2] = {{wd[0].s[2 * c], wd[0].s[2 * c + 1]}, {wd[1].s[2 * c], wd[1].s[2 * c + 1]}};
+              unit32_acc<BITS, ONE, 2>(w2, ap + g * (kGroup * 2), sc, Xs + g * 64, magic, ty);
+            } else {
+              f32x4 cg[2];
+              group_mfma<BITS, 2>(w2, ap + g * (kGroup * 2), magic, cg);
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-              const float sc = bf16_to_f32((wd[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
-              const float zo = zero_off<BITS>((wd[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
-              group_acc<ONE>(cg[r], sc, zo, Xs + g * 16, ty[r]);
+              for (int r = 0; r < 2; ++r) {
+                const float sc = bf16_to_f32((wd[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
+                const float zo = zero_off<BITS>((wd[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
+                group_acc<ONE>(cg[r], sc, zo, Xs + g * 16, ty[r]);
+              }
             }
           }
         }
@@ -891,26 +1028,26 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       }
       for (int rb = md.o0; rb < (kPipe ? md.o0 : md.o1); rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
-        if (!stage_h_rows<BITS>(act, Xs, p.hbuf + (size_t)rb * p.I, R, p.I, p.max_spins))
+        if (!stage_h_rows<BITS, GS>(act, Xs, p.hbuf + (size_t)rb * p.I, R, p.I, p.max_spins))
           atomicOr(&p.ctl[kCtlError], 1);
         const int arow = ONE ? 0 : min(m, R - 1);
-        const uint8_t *ap = act + arow * pitch2 + lsub * 64;
+        const uint8_t *ap = act + arow * pitch2 + lsub * LA;
         const float *xs = Xs + (ONE ? 0 : 4 * lsub);
         f32x4 ty[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if constexpr (FAST) {
           for (int ch = 0; ch < nch; ++ch) {
             if (ch > 0) {
-              load_chunk<BITS>(xw, add_groups(o2[0], ch * kChunkG, GB), wd[0]);
-              load_chunk<BITS>(xw, add_groups(o2[1], ch * kChunkG, GB), wd[1]);
+              load_chunk<BITS, GS>(xw, add_groups<SPU>(o2[0], ch * CG, GB), wd[0]);
+              load_chunk<BITS, GS>(xw, add_groups<SPU>(o2[1], ch * CG, GB), wd[1]);
             }
-            chunk_gemv<BITS, ONE, 2>(wd, ap + ch * kChunkG * (kGroup * 2), xs + ch * kChunkG * 16, magic, ty);
+            chunk_gemv<BITS, GS, ONE, 2>(wd, ap + ch * CG * (kGroup * 2), xs + ch * CG * 16 * SPU, magic, ty);
           }
           if (nch > 1 && rb + RM < md.o1) {
-            load_chunk<BITS>(xw, o2[0], wd[0]);
-            load_chunk<BITS>(xw, o2[1], wd[1]);
+            load_chunk<BITS, GS>(xw, o2[0], wd[0]);
+            load_chunk<BITS, GS>(xw, o2[1], wd[1]);
           }
         } else {
-          groups_gemv_slow<BITS, ONE, 2>(xw, o2, G2, ap, xs, magic, ty);
+          groups_gemv_slow<BITS, GS, ONE, 2>(xw, o2, G2, ap, xs, magic, ty);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -1032,24 +1169,33 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   }
 }
 
-template <int BITS, bool ONE, bool LAYER, bool TAB>
-const void *decode_fn_fast(bool fast) {
-  return fast ? (const void *)ffn_decode_kernel<BITS, ONE, true, LAYER, TAB>
-              : (const void *)ffn_decode_kernel<BITS, ONE, false, LAYER, TAB>;
+template <int BITS, int GS, bool LAYER, bool TAB>
+const void *decode_fn_fast(bool one, bool fast) {
+  if (one)
+    return fast ? (const void *)ffn_decode_kernel<BITS, GS, true, true, LAYER, TAB>
+                : (const void *)ffn_decode_kernel<BITS, GS, true, false, LAYER, TAB>;
+  return fast ? (const void *)ffn_decode_kernel<BITS, GS, false, true, LAYER, TAB>
+              : (const void *)ffn_decode_kernel<BITS, GS, false, false, LAYER, TAB>;
 }
 
 template <bool LAYER, bool TAB>
 const void *decode_fn_layer(int bits, bool one, bool fast) {
-  if (bits == 4) return one ? decode_fn_fast<4, true, LAYER, TAB>(fast) : decode_fn_fast<4, false, LAYER, TAB>(fast);
-  return one ? decode_fn_fast<2, true, LAYER, TAB>(fast) : decode_fn_fast<2, false, LAYER, TAB>(fast);
+  return bits == 4 ? decode_fn_fast<4, 128, LAYER, TAB>(one, fast) : decode_fn_fast<2, 128, LAYER, TAB>(one, fast);
 }
 
 // The layer kernel reads stacked arrays only; the address-table variant is a
-// separate instantiation so that the array kernels keep their registers.
-const void *decode_kernel_fn(int bits, bool one, bool fast, bool layer, bool tab) {
+// separate instantiation so that the array kernels keep their registers.  The
+// group-32 and INT8 formats take the stage call with stacked arrays.
+const void *decode_kernel_fn(int bits, int group, bool one, bool fast, bool layer, bool tab) {
   if (layer) return decode_fn_layer<true, false>(bits, one, fast);
+  if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, false, false>(one, fast)
+                                    : decode_fn_fast<8, 128, false, false>(one, fast);
+  if (group == 32) return decode_fn_fast<4, 32, false, false>(one, fast);
   return tab ? decode_fn_layer<false, true>(bits, one, fast) : decode_fn_layer<false, false>(bits, one, fast);
 }
+
+// Units per chunk of a format (kCG on the host).
+int chunk_units(int bits, int group) { return (bits == 8 ? 4 : 8) / (group == 32 ? 2 : 1); }
 
 // LDS of the fused layer's routing results (after the FFN's own arrays).
 size_t layer_lds_bytes(int T, int k, int E) {
@@ -1058,9 +1204,9 @@ size_t layer_lds_bytes(int T, int k, int E) {
   return (size_t)(6 * n + 2) * 4;
 }
 
-size_t decode_lds_bytes(int H, int I, bool one) {
+size_t decode_lds_bytes(int H, int I, bool one, int group = kGroup) {
   const size_t kmax = H > I ? H : I;
-  return (size_t)(one ? 1 : kRMax) * (kmax * 2 + 16) + 16 * (kmax / kGroup) * 4 + kRedFloats * 4;
+  return (size_t)(one ? 1 : kRMax) * (kmax * 2 + 16) + 16 * (kmax / group) * 4 + kRedFloats * 4;
 }
 
 // Fused layer: the router rows (shared start of LDS) or the FFN arrays,
@@ -1094,9 +1240,9 @@ int resident_blocks_per_cu(const void *fn, int device, size_t lds) {
 
 }  // namespace
 
-bool decode_layout_ok(int H, int I, int bits) {
+bool decode_layout_ok(int H, int I, int bits, int group) {
   (void)bits;
-  return I % kRows1 == 0 && H % kRows2 == 0 && decode_lds_bytes(H, I, false) <= 64 * 1024;
+  return I % kRows1 == 0 && H % kRows2 == 0 && decode_lds_bytes(H, I, false, group) <= 64 * 1024;
 }
 
 size_t ffn_ctl_bytes(int T, int k, int E) {
@@ -1134,11 +1280,12 @@ static void fill_params(DecodeParams &p, const FfnArgs &a, void *ws) {
 
 static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, const DeviceInfo &dev, hipStream_t st) {
   const bool one = a.T == 1;
-  // full chunks; with one token also few enough h groups for the phase-2 pipeline
-  const bool fast = (a.H / kGroup) % (4 * kChunkG) == 0 && (a.I / kGroup) % kChunkG == 0 &&
-                    (!one || a.I / kGroup <= 4 * kHPend);
-  const void *fn = decode_kernel_fn(a.bits, one, fast, layer, a.tab != nullptr);
-  const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I) : decode_lds_bytes(a.H, a.I, one);
+  // full chunks; with one token also few enough h units for the phase-2 pipeline
+  const int cg = chunk_units(a.bits, a.group);
+  const bool fast = (a.H / kGroup) % (4 * cg) == 0 && (a.I / kGroup) % cg == 0 && (!one || a.I / kGroup <= 4 * kHPend);
+  const void *fn = decode_kernel_fn(a.bits, a.group, one, fast, layer, a.tab != nullptr);
+  const size_t lds =
+      layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I) : decode_lds_bytes(a.H, a.I, one, a.group);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long blocks = (long)p.Amax * (a.I / kRows1 + a.H / kRows2);

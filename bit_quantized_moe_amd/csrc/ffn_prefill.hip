@@ -14,7 +14,8 @@
 //    M-tile) is derived on the device from the permutation offsets, so the
 //    host launches an upper bound of M-tile slots and surplus blocks exit;
 //  * A rows (gathered activations for G1, contiguous h rows for G2) and the B
-//    tile, dequantised once per block to bf16 (q - z) * s, go through two LDS
+//    tile, dequantised once per block to bf16 (q - z) * s (INT4, 2-bit or INT8
+//    codes; one scale per 128 or per 32 K), go through two LDS
 //    buffers with an XOR swizzle of 16-byte chunks, so both the staging
 //    writes and the MFMA operand reads are free of bank conflicts;
 //  * 4 waves in a 2 x 2 arrangement each own a 64 x 64 sub-tile computed with
@@ -31,7 +32,7 @@ namespace bqmoe {
 namespace {
 
 constexpr int BM = 128, BN = 128;
-constexpr int BK = 64;                       // K per tile: half a quantisation group
+constexpr int BK = 64;                       // K per tile: half a 128 group, two 32 groups
 constexpr int kRowBytes = BK * 2;            // one LDS row: 64 bf16 = 8 chunks of 16 B
 constexpr int kTileBytes = 128 * kRowBytes;  // 16 KiB per operand tile
 constexpr int kBufWord3 = 0x00020000;        // buffer resource word 3: raw 32-bit access
@@ -109,7 +110,9 @@ template <int N>
 using IntC = std::integral_constant<int, N>;
 
 // S: K tiles held in registers ahead of LDS (K / BK must be a multiple of S).
-template <int BITS, bool GATEUP, int S>
+// GS: quantisation group along K, 128 or 32 (a thread's 32 K of a tile then
+// form one group).
+template <int BITS, int GS, bool GATEUP, int S>
 __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   // two LDS buffers, each an A tile then a B tile (BM and BN rows of BK bf16)
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kTileBytes];
@@ -148,8 +151,8 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   // B staging: thread -> weight row tid / 2 of the tile, code words
   // (tid % 2) * WPL .. + WPL of the K tile, i.e. LDS chunks (tid % 2) * 4 .. + 4.
   // G1 tiles give each wave column 32 gate rows then the 32 matching up rows.
-  constexpr int WPT = BK * BITS / 32;         // code words per tile row: 8 (INT4) or 4 (INT2)
-  constexpr int WPL = WPT / 2;                // words per thread: 4 (INT4) or 2 (INT2)
+  constexpr int WPT = BK * BITS / 32;         // code words per tile row: 8 (INT4), 4 (INT2), 16 (INT8)
+  constexpr int WPL = WPT / 2;                // words per thread: 32 K of one row
   const int br = tid >> 1, bh = tid & 1;
   int wrow;
   if (GATEUP) {
@@ -159,7 +162,7 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   } else {
     wrow = nb * BN + br;
   }
-  const int wpr = p.K * BITS / 32, gpr = p.K / kGroup;  // code words and groups per weight row
+  const int wpr = p.K * BITS / 32, gpr = p.K / GS;     // code words and groups per weight row
   const size_t erow0 = (size_t)e * p.n_rows_w;          // the expert's first weight row
   const uint64_t *te = p.tab ? p.tab + (size_t)e * kTabStride + p.tab_off : nullptr;
   const uint32_t *e_codes = te ? (const uint32_t *)sload(te) : p.codes + erow0 * wpr;
@@ -172,7 +175,8 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t z_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)e_zeros, (short)0, BITS == 2 ? p.n_rows_w * gpr : 0, kBufWord3);
   const uint32_t b_off = (uint32_t)(wrow * wpr + bh * WPL) * 4u;  // bytes
-  const uint32_t s_off = (uint32_t)(wrow * gpr);                  // elements
+  // elements; with GS = 32 the thread's half of a tile is group 2 kt + bh
+  const uint32_t s_off = (uint32_t)(wrow * gpr) + (GS == 32 ? bh : 0);
 
   // ---- pipeline: one barrier per K tile.  While the MFMAs read buffer kt & 1,
   // tile kt + 1 is dequantised into the other buffer and tile kt + 1 + S is
@@ -197,7 +201,14 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
     auto load_tile = [&](int kt, int s) {
   #pragma unroll
       for (int j = 0; j < 4; ++j) a_st[s][j] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[j], kt * (BK * 2), 0);
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 8) {
+  #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off + 16 * h, kt * (WPT * 4), 0);
+  #pragma unroll
+          for (int w = 0; w < 4; ++w) b_st[s][4 * h + w] = v[w];
+        }
+      } else if constexpr (BITS == 4) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off, kt * (WPT * 4), 0);
   #pragma unroll
         for (int w = 0; w < 4; ++w) b_st[s][w] = v[w];
@@ -206,7 +217,7 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
         b_st[s][0] = v[0];
         b_st[s][1] = v[1];
       }
-      sc_st[s] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off * 2u, (kt / 2) * 2, 0);
+      sc_st[s] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off * 2u, GS == 32 ? kt * 4 : (kt / 2) * 2, 0);
       if constexpr (BITS == 2) z_st[s] = __builtin_amdgcn_raw_buffer_load_b8(z_rs, s_off, kt / 2, 0);
     };
     auto store_tile = [&](int s, uint8_t *buf) {
@@ -214,10 +225,16 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) *(u32x4 *)(buf + swz(ar + 32 * j, ac)) = a_st[s][j];
       uint8_t *bb = buf + kTileBytes;
       const float sc = bf16_to_f32(sc_st[s]);
-      const float zs = -((BITS == 4) ? 8.f : (float)z_st[s]) * sc;
+      const float zs = -((BITS == 4) ? 8.f : BITS == 8 ? 128.f : (float)z_st[s]) * sc;
   #pragma unroll
       for (int w = 0; w < WPL; ++w) {
-        if constexpr (BITS == 4) {
+        if constexpr (BITS == 8) {
+          if (w & 1) continue;  // words w, w + 1 fill one 16-byte chunk
+          uint32_t o[4];
+          dequant4_int8(b_st[s][w], sc, zs, o);
+          dequant4_int8(b_st[s][w + 1], sc, zs, o + 2);
+          *(u32x4 *)(bb + swz(br, bh * 4 + w / 2)) = u32x4{o[0], o[1], o[2], o[3]};
+        } else if constexpr (BITS == 4) {
           uint32_t o[4];
           dequant8_int4(b_st[s][w], sc, zs, o);
           *(u32x4 *)(bb + swz(br, bh * 4 + w)) = u32x4{o[0], o[1], o[2], o[3]};
@@ -351,13 +368,20 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   g2.n_blocks = a.H / BN;
   dim3 grid1((unsigned)(slots * g1.n_blocks)), grid2((unsigned)(slots * g2.n_blocks));
   // two register stages: K % 128 == 0 makes K / BK even
-  if (a.bits == 4) {
-    ffn_gemm_kernel<4, true, 2><<<grid1, 256, 0, st>>>(g1);
-    ffn_gemm_kernel<4, false, 2><<<grid2, 256, 0, st>>>(g2);
-  } else {
-    ffn_gemm_kernel<2, true, 2><<<grid1, 256, 0, st>>>(g1);
-    ffn_gemm_kernel<2, false, 2><<<grid2, 256, 0, st>>>(g2);
-  }
+  auto run = [&](auto g1k, auto g2k) {
+    g1k<<<grid1, 256, 0, st>>>(g1);
+    g2k<<<grid2, 256, 0, st>>>(g2);
+  };
+  if (a.bits == 4 && a.group == 128)
+    run(ffn_gemm_kernel<4, 128, true, 2>, ffn_gemm_kernel<4, 128, false, 2>);
+  else if (a.bits == 4)
+    run(ffn_gemm_kernel<4, 32, true, 2>, ffn_gemm_kernel<4, 32, false, 2>);
+  else if (a.bits == 8 && a.group == 128)
+    run(ffn_gemm_kernel<8, 128, true, 2>, ffn_gemm_kernel<8, 128, false, 2>);
+  else if (a.bits == 8)
+    run(ffn_gemm_kernel<8, 32, true, 2>, ffn_gemm_kernel<8, 32, false, 2>);
+  else
+    run(ffn_gemm_kernel<2, 128, true, 2>, ffn_gemm_kernel<2, 128, false, 2>);
   // h is T*k*I bf16 (I % 128 == 0, so a whole number of 16-byte chunks)
   const size_t n16 = (size_t)nrows * a.I * sizeof(uint16_t) / 16;
   const size_t zb = (n16 + 255) / 256;

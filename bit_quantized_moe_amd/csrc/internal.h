@@ -47,7 +47,7 @@ inline bool decode_path(int T, int k, int E) {
 constexpr int kLayerMaxT = 16;  // the one-launch decode layer
 size_t ffn_workspace_bytes(int T, int k, int E, int H, int I);
 size_t ffn_ctl_bytes(int T, int k, int E);  // control block at the start of the FFN workspace (x256)
-bool decode_layout_ok(int H, int I, int bits);
+bool decode_layout_ok(int H, int I, int bits, int group = 128);
 
 struct FfnArgs {
   const uint16_t *x;
@@ -67,6 +67,8 @@ struct FfnArgs {
   // expert: w13 codes, w13 scales, w13 zeros, w2 codes, w2 scales, w2 zeros,
   // each the expert's own block); when set the array pointers are unused
   const uint64_t *tab = nullptr;
+  // quantisation group along K: 128, or 32 for the INT4 / INT8 group-32 formats
+  int group = 128;
 };
 constexpr int kTabStride = 6;
 hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
@@ -92,6 +94,6 @@ hipError_t launch_combine(const uint16_t *y_perm, const int32_t *row_pos, const 
 // unpack.hip
 hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_t *out, hipStream_t st);
 hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
-                               int N, int K, uint16_t *out, hipStream_t st);
+                               int group, int N, int K, uint16_t *out, hipStream_t st);
 
 }  // namespace bqmoe

@@ -1,7 +1,9 @@
 // Diagnostic kernels that expose the two device dequantisation routines:
-//  - moe_unpack_codes: the offset-bf16 unpack of the decode GEMV kernels,
-//    converted back to signed integer codes;
-//  - moe_dequant_bf16: the bf16 (q - z) * s of the grouped-GEMM kernels.
+//  - moe_unpack_codes: the bf16 unpack of the decode GEMV kernels (offset
+//    form for INT4 and 2-bit, a float conversion for INT8), converted back to
+//    signed integer codes;
+//  - moe_dequant_bf16 / _grouped: the bf16 (q - z) * s of the grouped-GEMM
+//    kernels.
 #include "common.cuh"
 #include "internal.h"
 
@@ -16,7 +18,14 @@ __global__ void unpack_kernel(const uint32_t *__restrict__ words, int64_t n_word
   constexpr int P = 32 / BITS;
   int8_t q[P];
   // bf16 pairs (128 + u) in the field order of the unpack, back to field order
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 8) {
+    const u32x4 pr = unpack8_bf16(w, 0u);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      q[2 * p] = (int8_t)((int)bf16lo(pr[p]) - 128);
+      q[2 * p + 1] = (int8_t)((int)bf16hi(pr[p]) - 128);
+    }
+  } else if constexpr (BITS == 4) {
     const u32x4 pr = unpack4_pairs(w, kMagic43);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -38,7 +47,7 @@ __global__ void unpack_kernel(const uint32_t *__restrict__ words, int64_t n_word
   for (int p = 0; p < P; ++p) out[i * P + p] = q[p];
 }
 
-template <int BITS>
+template <int BITS, int GS>
 __global__ void dequant_kernel(const uint32_t *__restrict__ words, const uint16_t *__restrict__ scales,
                                const uint8_t *__restrict__ zeros, int N, int K, uint16_t *__restrict__ out) {
   constexpr int P = 32 / BITS;
@@ -47,12 +56,14 @@ __global__ void dequant_kernel(const uint32_t *__restrict__ words, const uint16_
   if (i >= (int64_t)N * wpr) return;
   const int n = (int)(i / wpr);
   const int kw = (int)(i % wpr);
-  const int g = kw * P / kGroup;
-  const float s = bf16_to_f32(scales[(size_t)n * (K / kGroup) + g]);
-  const float z = (BITS == 4) ? 8.f : (float)zeros[(size_t)n * (K / kGroup) + g];
+  const int g = kw * P / GS;
+  const float s = bf16_to_f32(scales[(size_t)n * (K / GS) + g]);
+  const float z = BITS == 4 ? 8.f : BITS == 8 ? 128.f : (float)zeros[(size_t)n * (K / GS) + g];
   const uint32_t w = words[i];
   uint32_t o[P / 2];
-  if constexpr (BITS == 4)
+  if constexpr (BITS == 8)
+    dequant4_int8(w, s, -z * s, o);
+  else if constexpr (BITS == 4)
     dequant8_int4(w, s, -z * s, o);
   else
     dequant16_int2(w, s, -z * s, o);
@@ -66,7 +77,9 @@ __global__ void dequant_kernel(const uint32_t *__restrict__ words, const uint16_
 hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_t *out, hipStream_t st) {
   const int threads = 256;
   const int64_t blocks = (n_words + threads - 1) / threads;
-  if (bits == 4)
+  if (bits == 8)
+    unpack_kernel<8><<<(unsigned)blocks, threads, 0, st>>>(words, n_words, out);
+  else if (bits == 4)
     unpack_kernel<4><<<(unsigned)blocks, threads, 0, st>>>(words, n_words, out);
   else
     unpack_kernel<2><<<(unsigned)blocks, threads, 0, st>>>(words, n_words, out);
@@ -74,14 +87,20 @@ hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_
 }
 
 hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
-                               int N, int K, uint16_t *out, hipStream_t st) {
+                               int group, int N, int K, uint16_t *out, hipStream_t st) {
   const int threads = 256;
   const int64_t n_words = (int64_t)N * K * bits / 32;
-  const int64_t blocks = (n_words + threads - 1) / threads;
-  if (bits == 4)
-    dequant_kernel<4><<<(unsigned)blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
+  const unsigned blocks = (unsigned)((n_words + threads - 1) / threads);
+  if (bits == 8 && group == 32)
+    dequant_kernel<8, 32><<<blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
+  else if (bits == 8)
+    dequant_kernel<8, 128><<<blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
+  else if (bits == 4 && group == 32)
+    dequant_kernel<4, 32><<<blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
+  else if (bits == 4)
+    dequant_kernel<4, 128><<<blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
   else
-    dequant_kernel<2><<<(unsigned)blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
+    dequant_kernel<2, 128><<<blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
   return hipGetLastError();
 }
 

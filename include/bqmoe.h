@@ -1,6 +1,6 @@
 /*
  * bqmoe.h -- C ABI of the routed-expert mixture-of-experts layer with low-bit
- * (weight-only INT4 / 2-bit) experts, for AMD Instinct MI355X (gfx950).
+ * (weight-only INT4 / 2-bit / INT8) experts, for AMD Instinct MI355X (gfx950).
  *
  * The layer, per batch of T tokens with hidden size H, E experts, top-k routing
  * and expert intermediate size I:
@@ -10,6 +10,9 @@
  *   moe_expert_ffn_w4a16 / _w2a16
  *                   per-expert gate_up -> SwiGLU -> down with the expert weights
  *                   dequantised on the fly from packed codes
+ *   moe_expert_ffn_wna16
+ *                   the same for any supported format: INT4 or INT8 with
+ *                   groups of 128 or 32, 2-bit with groups of 128
  *   moe_expert_ffn_w4a16_table / _w2a16_table
  *                   the same, each expert's weights located through a
  *                   per-expert address table
@@ -24,7 +27,12 @@
  * (bits [b*i, b*i+b), least significant first) holds the code of K index
  * P*kw + i, P = 32/b.  INT4 fields hold q + 8 with q in [-8, 7] and the weight
  * is q*s; 2-bit fields hold u in {0..3} and the weight is (u - z)*s with an
- * integer zero-point z per group.
+ * integer zero-point z per group.  Two more formats share the layout: INT4
+ * symmetric with one scale per 32 K (the draft-layer experts of the same two
+ * pages' format tables), and INT8 symmetric, fields q + 128 with q in
+ * [-127, 127], group 128 or 32 (page "Qwen3.8-Flash-Next on one 24 GB GPU",
+ * "What the patch does": INT8 g128; page "Qwen3.8-Flash-Next FP6-INT8",
+ * "Precision map" and "Kernel-level verification": an int8 g32 tier).
  *
  * Conventions shared by every entry point:
  *  - Every array argument is a DEVICE pointer owned by the caller.  The library
@@ -194,6 +202,30 @@ moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets
                                 uint16_t *y_perm, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/* moe_expert_ffn_wna16: the expert FFN of moe_expert_ffn_w4a16 for a format
+ * given by bits and group_size:
+ *   bits 4, group 128 or 32   W = (field - 8) * s
+ *   bits 8, group 128 or 32   W = (field - 128) * s
+ *   bits 2, group 128         W = (field - z) * s   (zero-points required)
+ * with s (and z) the value of the group that holds the K index:
+ *   w13_codes [E, 2I, H*bits/32] uint32, w13_scales [E, 2I, H/G] bf16,
+ *   w13_zeros [E, 2I, H/G] uint8 (bits == 2, else ignored; may be NULL),
+ *   w2_codes [E, H, I*bits/32], w2_scales [E, H, I/G], w2_zeros [E, H, I/G].
+ * Other arguments, requirements, dispatch (the decode path streams each
+ * selected expert once; with groups of 32 each MFMA covers one group) and
+ * workspace are those of moe_expert_ffn_w4a16; (4, 128) and (2, 128) give
+ * the results of moe_expert_ffn_w4a16 / _w2a16 bit for bit.  Any other
+ * (bits, group_size) returns MOE_ERR_INVALID_ARG. */
+moe_status moe_expert_ffn_wna16(const uint16_t *x, const int32_t *expert_offsets,
+                                const int32_t *sorted_rows, const int32_t *active,
+                                int T, int k, int E, int H, int I, int bits, int group_size,
+                                const uint32_t *w13_codes, const uint16_t *w13_scales,
+                                const uint8_t *w13_zeros,
+                                const uint32_t *w2_codes, const uint16_t *w2_scales,
+                                const uint8_t *w2_zeros,
+                                uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* moe_expert_ffn_w4a16_table / moe_expert_ffn_w2a16_table: the same
  * computation, with each expert's weights found through a per-expert address
  * table instead of three stacked arrays per projection, so that every expert
@@ -285,7 +317,8 @@ moe_status moe_layer_w2a16(const uint16_t *x, const uint16_t *w_router, const fl
 /* ---------------------------------------------------------------- diagnostics
  * moe_unpack_codes: the signed codes of n_words packed words, unpacked by the
  * same device routine the decode kernels use (INT4: q = field - 8; 2-bit:
- * u = field).  out holds n_words * 32/bits int8 values in K order.
+ * u = field; INT8: q = field - 128).  out holds n_words * 32/bits int8 values
+ * in K order.  bits: 2, 4 or 8.
  */
 moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, int8_t *out,
                             void *stream);
@@ -294,9 +327,13 @@ moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, in
  * routine the grouped-GEMM kernels use: round-to-nearest-even of (q - z) * s.
  *   words [N, K*bits/32] uint32 (16-byte aligned), scales [N, K/128] bf16,
  *   zeros [N, K/128] uint8 (bits == 2 only, else NULL), out [N, K] bf16.
- * Requirements: K % 128 == 0. */
+ * Requirements: K % 128 == 0; bits 2, 4 or 8. */
 moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros,
                             int bits, int N, int K, uint16_t *out, void *stream);
+/* moe_dequant_bf16_grouped: the same with group_size 128, or 32 (bits 4 or 8;
+ * scales [N, K/32]). */
+moe_status moe_dequant_bf16_grouped(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros,
+                                    int bits, int group_size, int N, int K, uint16_t *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -136,6 +136,20 @@ def test_ffn_table_argument_errors(bits):
     assert _ffn_table(bits, T=0) == OK        # no weight arrays are needed beside the table
 
 
+def test_ffn_wna16_format_errors():
+    L = bq.lib()
+    f = lambda bits, g, **kw: L.moe_expert_ffn_wna16(A, A, A, A, 2, 2, 8, 256, 128, bits, g, A, A, kw.get("z", A), A,
+                                                      A, kw.get("z", A), A, A, 1 << 24, None)
+    assert f(4, 64) == INVALID and f(2, 32) == INVALID and f(3, 128) == INVALID and f(8, 16) == INVALID
+    assert f(2, 128, z=None) == INVALID            # 2-bit needs zero-points
+    for bits, g in ((4, 32), (8, 128), (8, 32)):
+        assert L.moe_expert_ffn_wna16(A, A, A, A, 0, 2, 8, 256, 128, bits, g, A, A, None, A, A, None, A, A, 1 << 24,
+                                      None) == OK
+    assert L.moe_unpack_codes(A, 8, 0, A, None) == OK
+    assert L.moe_dequant_bf16_grouped(A, A, None, 2, 32, 4, 128, A, None) == SHAPE
+    assert L.moe_dequant_bf16_grouped(A, A, None, 8, 32, 0, 128, A, None) == OK
+
+
 def test_device_address_argument_errors():
     L = bq.lib()
     out = ctypes.c_uint64(0)

@@ -1,0 +1,162 @@
+"""GPU parity of the further weight formats against the oracle.
+
+INT4 symmetric with groups of 32 (the draft-layer experts of page
+"Qwen3.8-Flash-Next on 2x RTX 3090", storage-format table) and INT8 symmetric
+with groups of 128 or 32 (page "Qwen3.8-Flash-Next on one 24 GB GPU", "What
+the patch does"; page "Qwen3.8-Flash-Next FP6-INT8", "Precision map" and
+"Kernel-level verification"), through moe_expert_ffn_wna16 on both FFN paths.
+Bars as for the other formats: unpacked codes and dequantised bf16 values bit
+for bit, outputs within 2e-2 relative Frobenius error (tensor-wide and per row).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_amd as bq
+import oracle
+import workload
+from gpu_util import bf16_np_to_f32, row_rel_err, to_dev, to_np, weights_to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+FORMATS = [(4, 32), (8, 128), (8, 32)]
+SIGMA = {4: 0.02, 8: 0.0015}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"[gpu-test] start {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+def test_unpack_int8_every_byte_every_position():
+    words = []
+    for pos in range(4):
+        for v in range(256):
+            w = 0
+            for f in range(4):
+                w |= (((v + 37 * f) % 256) if f != pos else v) << (8 * f)
+            words.append(w)
+    rng = np.random.default_rng(4)
+    words = np.concatenate([np.array(words, np.uint32), rng.integers(0, 2**32, 1 << 18, dtype=np.uint32)])
+    got = to_np(bq.unpack_codes(to_dev(words), 8))
+    assert np.array_equal(got, oracle.unpack_codes(words, 8).ravel())
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_dequant_bf16_is_rounded_oracle(bits, group):
+    rng = np.random.default_rng(5 + bits + group)
+    N, K = 64, 1024
+    words = rng.integers(0, 2**32, (N, K * bits // 32), dtype=np.uint32)
+    scales = workload.bf16_bits(np.abs(rng.standard_normal((N, K // group))).astype(np.float32) * 0.03)
+    got = to_np(bq.dequant_bf16(to_dev(words), to_dev(scales), None, bits, N, K, group=group))
+    exp = workload.bf16_bits(oracle.dequantize(words, scales, None, bits, group))
+    assert np.array_equal(got, exp)
+
+
+def _check_ffn(inp, ws=None):
+    sp = inp.spec
+    wd = weights_to_dev(inp.weights)
+    out = bq.moe_layer(to_dev(inp.x), to_dev(inp.w_router), to_dev(inp.logit_bias) if inp.logit_bias is not None
+                       else None, wd, sp.k, sp.bits, sp.I, ws=ws, group=sp.group)
+    got = {kk: to_np(v) for kk, v in out.items()}
+    ref = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, inp.weights, sp.k, sp.bits, sp.I, group=sp.group)
+    for key in ("ids", "offsets", "sorted_rows", "row_pos", "active"):
+        assert np.array_equal(got[key], ref[key]), key
+    yp, y = bf16_np_to_f32(got["y_perm"]), bf16_np_to_f32(got["y"])
+    e1, e2 = oracle.rel_fro(yp, ref["y_perm"]), oracle.rel_fro(y, ref["y"])
+    say(f"    T={sp.T} H={sp.H} I={sp.I} E={sp.E} k={sp.k}: y_perm rel-fro {e1:.2e}, y rel-fro {e2:.2e}")
+    assert e1 <= TOL and e2 <= TOL
+    assert np.max(row_rel_err(yp, ref["y_perm"])) <= TOL
+    return got
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (1, 256, 128, 8, 2),        # decode, one token, ragged chunks
+    (3, 512, 256, 16, 4),       # decode, a few tokens
+    (16, 512, 256, 8, 4),       # decode, experts with more rows than one pass
+    (40, 256, 128, 8, 2),       # grouped GEMM, ragged tiles
+    (300, 1024, 256, 32, 4),    # grouped GEMM, several K and N tiles
+], ids=lambda v: str(v))
+def test_ffn_formats_small_shapes(bits, group, T, H, I, E, k):
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, I=I, E=E, k=k, bits=bits, group=group,
+                       scale_sigma=SIGMA[bits], seed=4000 + T + bits + group)
+    _check_ffn(workload.make_layer_inputs(sp))
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_ffn_formats_full_chunk_decode_shapes(bits, group):
+    """H = 4096, I = 1024: the decode kernel's full-chunk path (one token
+    pipelined, and several tokens), and one workspace across calls."""
+    ws = bq.Workspaces("cuda")
+    for T, E, k in ((1, 8, 2), (1, 16, 8), (5, 8, 4), (16, 8, 4)):
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=4096, I=1024, E=E, k=k, bits=bits, group=group,
+                           scale_sigma=SIGMA[bits], seed=4100 + T + E + bits + group)
+        _check_ffn(workload.make_layer_inputs(sp), ws=ws)
+    torch.cuda.synchronize()
+    for name, buf in ws._bufs.items():
+        assert int(buf.view(torch.int32).abs().sum()) == 0, name
+
+
+@pytest.mark.parametrize("name", ["decode_t1_h4096_e256_k8_i1024_int4g32", "decode_t1_h4096_e256_k8_i1024_int8",
+                                  "decode_t1_h4096_e256_k8_i1024_int8g32"])
+def test_ffn_formats_decode_full_size(name):
+    sp = workload.spec(name)
+    _check_ffn(workload.make_layer_inputs(sp))
+
+
+def test_ffn_int8g32_prefill_full_size_sampled():
+    sp = workload.spec("prefill_t4096_h4096_e256_k8_i1024_int8g32")
+    inp = workload.make_layer_inputs(sp)
+    wd = weights_to_dev(inp.weights)
+    out = bq.moe_layer(to_dev(inp.x), to_dev(inp.w_router), to_dev(inp.logit_bias), wd, sp.k, sp.bits, sp.I,
+                       group=sp.group)
+    got = {kk: to_np(v) for kk, v in out.items()}
+    counts = np.diff(got["offsets"])
+    act = got["active"][1:1 + got["active"][0]]
+    by = sorted(act.tolist(), key=lambda e: counts[e])
+    experts = [by[-1], by[len(by) // 2], by[0]]
+    yp_ref = oracle.expert_ffn(inp.x, got["offsets"], got["sorted_rows"], sp.k, inp.weights, sp.bits, sp.I,
+                               experts=experts, group=sp.group)
+    yp = bf16_np_to_f32(got["y_perm"])
+    for e in experts:
+        o0, o1 = got["offsets"][e], got["offsets"][e + 1]
+        err = oracle.rel_fro(yp[o0:o1], yp_ref[o0:o1])
+        say(f"    expert {e} ({o1 - o0} rows): y_perm rel-fro {err:.2e}")
+        assert err <= TOL
+        assert np.max(row_rel_err(yp[o0:o1], yp_ref[o0:o1])) <= TOL
+
+
+def test_wna16_matches_the_format_entry_points():
+    """(4, 128) and (2, 128) through moe_expert_ffn_wna16 equal moe_expert_ffn_w4a16 / _w2a16 bit for bit."""
+    for bits in (4, 2):
+        for T in (1, 40):
+            sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=512, I=256, E=16, k=4, bits=bits,
+                               scale_sigma=0.02 if bits == 4 else 0.05, seed=4300 + T + bits)
+            inp = workload.make_layer_inputs(sp)
+            wd = weights_to_dev(inp.weights)
+            r = bq.route_permute(to_dev(inp.x), to_dev(inp.w_router), sp.k)
+            args = (to_dev(inp.x), r["offsets"], r["sorted_rows"], r["active"])
+            a = bq.expert_ffn(*args, sp.k, wd, bits, sp.I)
+            L = bq.lib()
+            nbytes = L.moe_expert_ffn_workspace_size(T, sp.k, sp.E, sp.H, sp.I)
+            w = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            st = torch.cuda.current_stream().cuda_stream
+            s = L.moe_expert_ffn_wna16(args[0].data_ptr(), args[1].data_ptr(), args[2].data_ptr(), args[3].data_ptr(),
+                                       T, sp.k, sp.E, sp.H, sp.I, bits, 128, wd["w13_codes"].data_ptr(),
+                                       wd["w13_scales"].data_ptr(), wd["w13_zeros"].data_ptr() if bits == 2 else None,
+                                       wd["w2_codes"].data_ptr(), wd["w2_scales"].data_ptr(),
+                                       wd["w2_zeros"].data_ptr() if bits == 2 else None, b.data_ptr(), w.data_ptr(),
+                                       nbytes, st)
+            assert s == 0
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (bits, T)
