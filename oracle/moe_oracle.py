@@ -1,4 +1,4 @@
-"""CPU oracle for the routed-expert MoE layer with low-bit (INT4 / 2-bit / INT8) experts.
+"""CPU oracle for the routed-expert MoE layer with low-bit (INT4 / 2-bit / INT8 / FP6) experts.
 
 TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference that the
 GPU library is checked against.  Only the test suite, the smoke check and the
@@ -30,7 +30,10 @@ W4A16 + FP8 PLE + MTP3", "Composition"), and INT8 symmetric with codes
 -127..127 and group 128 or 32 (page "Qwen3.8-Flash-Next on one 24 GB GPU",
 "What the patch does": dense projections re-packed to INT8 g128; page
 "Qwen3.8-Flash-Next FP6-INT8", "Precision map" and "Kernel-level
-verification": an int8 g32 tier).  The pages fix
+verification": an int8 g32 tier).  FP6 experts hold e2m3 codes (sign, 2
+exponent bits with bias 1, 3 mantissa bits; values up to 7.5, exact in bf16)
+with fp16 scales (same page: fp6 e2m3 routed experts, every one of the 64
+codes checked exactly, fp16 scales); here one scale per 128 K.  The pages fix
 activations at bf16 with float32 accumulation (page "Qwen3.8-Flash-Next
 FP6-INT8", "Precision map"), so the oracle accumulates in float32.  They keep
 the router in 16-bit precision because near-tied logits flip routing under
@@ -65,6 +68,40 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- O5, O6
+FP6 = 6  # the ``bits`` value that selects fp6 e2m3 codes with fp16 scales
+
+
+def unpack_fp6_fields(words: np.ndarray) -> np.ndarray:
+    """O5 (FP6): words [..., 3K/16] -> 6-bit codes [..., K] (uint8).
+
+    A row's codes form one little-endian bit stream: code k occupies bits
+    [6k, 6k+6) of the row (bit b of the stream is bit b % 32 of word b // 32),
+    16 codes per 3 words.
+    """
+    w = np.ascontiguousarray(words, dtype=np.uint32)
+    nw = w.shape[-1]
+    if nw % 3:
+        raise ValueError("FP6 rows hold a multiple of 3 words")
+    K = nw * 32 // 6
+    k = np.arange(K)
+    lo_word, lo_bit = (6 * k) // 32, (6 * k) % 32
+    w64 = w.astype(np.uint64)
+    nxt = np.concatenate([w64[..., 1:], np.zeros(w64.shape[:-1] + (1,), np.uint64)], axis=-1)
+    pair = w64 | (nxt << np.uint64(32))                       # word i and i+1 as one 64-bit value
+    return ((pair[..., lo_word] >> lo_bit.astype(np.uint64)) & np.uint64(63)).astype(np.uint8)
+
+
+def e2m3_value(codes: np.ndarray) -> np.ndarray:
+    """The value of fp6 e2m3 codes: bit 5 sign, bits 4..3 exponent e (bias 1),
+    bits 2..0 mantissa m; e = 0 is subnormal (m / 8), otherwise
+    2^(e-1) * (1 + m/8).  No infinities or NaNs."""
+    c = np.asarray(codes, dtype=np.int64)
+    sgn = np.where(c & 32, -1.0, 1.0)
+    e, m = (c >> 3) & 3, c & 7
+    mag = np.where(e == 0, m / 8.0, np.exp2(e - 1.0) * (1.0 + m / 8.0))
+    return (sgn * mag).astype(np.float32)
+
+
 def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
     """O5: packed words [..., K/P] -> signed integer codes q [..., K] (int8).
 
@@ -112,8 +149,16 @@ def dequantize(words: np.ndarray, scales: np.ndarray, zeros, bits: int, group: i
     W[n, k] = (q[n, k] - z[n, k // G]) * s[n, k // G] for group size G, with
     z = 0 for the symmetric INT4 and INT8 formats.  (q - z) is an integer of at
     most 8 bits and s a bf16 value (8 significant bits), so the product is
-    exact in float32.
+    exact in float32.  FP6 (bits = 6): W = e2m3(code) * s with s an fp16
+    value; 4 and 11 significant bits, again exact in float32.
     """
+    if bits == FP6:
+        v = e2m3_value(unpack_fp6_fields(words))                # [N, K]
+        N, K = v.shape
+        if K % group:
+            raise ValueError("K must be a multiple of the group size")
+        s = np.ascontiguousarray(scales, dtype=np.uint16).view(np.float16).astype(np.float32).reshape(N, K // group)
+        return (v * np.repeat(s, group, axis=1)).astype(np.float32)
     q = unpack_codes(words, bits).astype(np.float32)           # [N, K]
     N, K = q.shape
     if K % group:

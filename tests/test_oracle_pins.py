@@ -190,6 +190,84 @@ def test_int8_every_code_every_group_position_scale_and_activation_extremes(grou
                     assert Fraction(float(yv)) == Fraction(int(c)) * Fraction(sc) * Fraction(xv)
 
 
+# ------------------------------------------------------------------ FP6 e2m3
+def _golden_fp6():
+    vals, packs = {}, []
+    for line in open(os.path.join(GOLDEN, "fp6_e2m3.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        parts = line.split()
+        if parts[0] == "pack":
+            packs.append((int(parts[1]), [int(w, 16) for w in parts[2:5]]))
+        else:
+            vals[int(parts[0])] = float(parts[1])
+    return vals, packs
+
+
+def _pack_stream(codes):
+    """Test-side writer of the FP6 bit stream, one bit at a time."""
+    codes = list(codes)
+    words = [0] * (len(codes) * 6 // 32)
+    for k, c in enumerate(codes):
+        for b in range(6):
+            if (c >> b) & 1:
+                words[(6 * k + b) // 32] |= 1 << ((6 * k + b) % 32)
+    return np.array(words, np.uint32)
+
+
+def test_fp6_values_match_hand_written_table():
+    vals, _ = _golden_fp6()
+    assert sorted(vals) == list(range(64))
+    got = oracle.e2m3_value(np.arange(64))
+    for c in range(64):
+        assert got[c] == vals[c] and math.copysign(1.0, got[c]) == math.copysign(1.0, vals[c]), c
+    # every value is exact in bf16
+    assert np.array_equal(oracle.bf16_to_f32(_bf16(got)), got)
+
+
+def test_fp6_packing_hand_packed_rows():
+    _, packs = _golden_fp6()
+    assert len(packs) >= 3
+    for c, words in packs:
+        assert oracle.unpack_fp6_fields(np.array([words], np.uint32)).tolist() == [[c] * 16]
+        assert _pack_stream([c] * 16).tolist() == words
+
+
+def test_fp6_every_code_every_position_and_scale_extremes():
+    """Each code at each position of a 128-K group, under fp16 scale extremes,
+    dequantises to value * scale exactly (exact rationals) and nowhere else."""
+    from fractions import Fraction
+    vals, _ = _golden_fp6()
+    scales = [2.0 ** -14, 1.0, 65504.0]                      # fp16 min normal, one, max
+    for pos in range(0, 128, 5):
+        rows = []
+        for c in range(64):
+            codes = [0] * 128
+            codes[pos] = c
+            rows.append(_pack_stream(codes))
+        words = np.stack(rows)
+        assert np.array_equal(oracle.unpack_fp6_fields(words)[:, pos], np.arange(64))
+        for sc in scales:
+            s16 = np.full((64, 1), np.float16(sc)).view(np.uint16)
+            W = oracle.dequantize(words, s16, None, 6)
+            others = np.delete(W, pos, axis=1)
+            assert not others.any()
+            for c in range(0, 64, 3):
+                assert Fraction(float(W[c, pos])) == Fraction(vals[c]) * Fraction(sc)
+
+
+def test_fp6_random_rows_against_bitwise_reader():
+    rng = np.random.default_rng(31)
+    words = rng.integers(0, 2**32, size=(3, 24), dtype=np.uint32)   # K = 128
+    fields = oracle.unpack_fp6_fields(words)
+    for n in range(3):
+        stream = 0
+        for i, w in enumerate(words[n].tolist()):
+            stream |= w << (32 * i)
+        assert fields[n].tolist() == [(stream >> (6 * k)) & 63 for k in range(128)]
+
+
 def test_dequant_exact_against_integer_arithmetic():
     """(q - z) * s is exact: compare with exact rationals."""
     from fractions import Fraction
@@ -362,14 +440,16 @@ def test_permutation_brute_force(T, k, E):
 # ------------------------------------------------------------------ O7/O8 FFN + combine
 def _tiny(bits=4, **kw):
     sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", **kw)
-    if bits == 2:
+    if bits == 6:
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", bits=6, **kw)
+    elif bits == 2:
         sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", bits=2, scale_sigma=0.05, **kw)
     elif bits == 8:
         sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", bits=8, scale_sigma=0.0015, **kw)
     return workload.make_layer_inputs(sp)
 
 
-@pytest.mark.parametrize("bits,group", [(4, 128), (2, 128), (4, 32), (8, 128), (8, 32)])
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 128), (4, 32), (8, 128), (8, 32), (6, 128)])
 def test_ffn_all_equal_weights_closed_form(bits, group):
     """Every weight = c: A_n = c*S (S = sum of x), h = silu(cS)*cS, y = I*c*h for all rows."""
     inp = _tiny(bits, group=group)
@@ -381,14 +461,25 @@ def test_ffn_all_equal_weights_closed_form(bits, group):
         z13 = z2 = None
     elif bits == 8:
         word, c = 0x7F7F7F7F, -1.0                    # q = -1
+    elif bits == 6:
+        word, c = None, 1.0                           # e2m3 code 8 = 1.0 (tests/golden/fp6_e2m3.txt)
     else:
         word, c = 0xFFFFFFFF, 2.0                     # u = 3, z = 1 -> 2
         wt["w13_zeros"] = np.ones_like(wt["w13_zeros"])
         wt["w2_zeros"] = np.ones_like(wt["w2_zeros"])
-    wt["w13_codes"] = np.full_like(wt["w13_codes"], word)
-    wt["w2_codes"] = np.full_like(wt["w2_codes"], word)
-    wt["w13_scales"] = _bf16(np.ones(wt["w13_scales"].shape))
-    wt["w2_scales"] = _bf16(np.ones(wt["w2_scales"].shape))
+    if bits == 6:   # the hand-packed row of sixteen code-8 fields, repeated
+        trip = np.array([0x08208208, 0x82082082, 0x20820820], np.uint32)
+        for key in ("w13_codes", "w2_codes"):
+            shp = wt[key].shape
+            wt[key] = np.ascontiguousarray(np.broadcast_to(np.tile(trip, shp[-1] // 3), shp))
+        one = np.uint16(0x3C00)                       # fp16 1.0
+        wt["w13_scales"] = np.full(wt["w13_scales"].shape, one, np.uint16)
+        wt["w2_scales"] = np.full(wt["w2_scales"].shape, one, np.uint16)
+    else:
+        wt["w13_codes"] = np.full_like(wt["w13_codes"], word)
+        wt["w2_codes"] = np.full_like(wt["w2_codes"], word)
+        wt["w13_scales"] = _bf16(np.ones(wt["w13_scales"].shape))
+        wt["w2_scales"] = _bf16(np.ones(wt["w2_scales"].shape))
     out = oracle.moe_layer(inp.x, inp.w_router, inp.logit_bias, wt, sp.k, bits, I, group=group)
     xf = oracle.bf16_to_f32(inp.x).astype(np.float64)
     S = c * xf.sum(1)
@@ -472,7 +563,7 @@ def test_dense_equivalence_all_experts_selected(bits):
     assert oracle.rel_fro(out["y"], y) < 1e-5
 
 
-@pytest.mark.parametrize("bits,group", [(4, 128), (2, 128), (4, 32), (8, 128), (8, 32)])
+@pytest.mark.parametrize("bits,group", [(4, 128), (2, 128), (4, 32), (8, 128), (8, 32), (6, 128)])
 def test_float32_oracle_close_to_float64(bits, group):
     inp = _tiny(bits, group=group)
     sp = inp.spec

@@ -24,13 +24,13 @@ def test_shapes_and_determinism(name):
     small = workload.spec(name, E=4, T=min(sp.T, 16)) if sp.E > 8 else sp
     a = workload.make_layer_inputs(small)
     b = workload.make_layer_inputs(small)
-    P = 32 // small.bits
+    nw = small.words_per_row
     assert a.x.shape == (small.T, small.H) and a.x.dtype == np.uint16
     assert a.w_router.shape == (small.E, small.H)
     w = a.weights
-    assert w["w13_codes"].shape == (small.E, 2 * small.I, small.H // P)
+    assert w["w13_codes"].shape == (small.E, 2 * small.I, nw(small.H))
     assert w["w13_scales"].shape == (small.E, 2 * small.I, small.H // small.group)
-    assert w["w2_codes"].shape == (small.E, small.H, small.I // P)
+    assert w["w2_codes"].shape == (small.E, small.H, nw(small.I))
     assert w["w2_scales"].shape == (small.E, small.H, small.I // small.group)
     if small.bits == 2:
         assert set(np.unique(w["w13_zeros"]).tolist()) <= {1, 2}

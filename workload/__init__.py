@@ -28,7 +28,10 @@ INT4 and 2-bit codes are drawn as uniformly random 32-bit words: every field
 of a uniform word is uniform over its 2**bits values, so INT4 codes are
 uniform over the 16 signed values and 2-bit codes uniform over {0..3}.  INT8
 codes are drawn uniformly from -127..127 (the symmetric range, no -128) and
-stored as the bytes q + 128, four per word, least significant first.
+stored as the bytes q + 128, four per word, least significant first.  FP6
+(bits = 6) rows are uniform random words, so every 6-bit e2m3 field is
+uniform over the 64 codes; their scales are fp16 bits (|N(0,1)| * sigma,
+rounded to nearest even), one per 128 K.
 
 Each tensor gets its own PCG64 stream keyed by (workload seed, tensor tag,
 weight-set index), so any one tensor can be regenerated alone.
@@ -70,8 +73,9 @@ class Spec:
     note: str = ""
 
     @property
-    def codes_per_word(self) -> int:
-        return 32 // self.bits
+    def words_per_row(self):
+        """K -> packed uint32 words per row (FP6: 16 codes per 3 words)."""
+        return lambda K: K * self.bits // 32
 
     def weight_bytes_per_expert(self) -> int:
         """Packed bytes one expert occupies: codes + bf16 scales (+ u8 zeros)."""
@@ -115,6 +119,12 @@ SPECS: Dict[str, Spec] = {
         Spec("prefill_t4096_h4096_e256_k8_i1024_int8g32", T=4096, H=4096, E=256, k=8, I=1024, bits=8, group=32,
              seed=1010, zipf_s=1.1, scale_sigma=0.0015,
              note="prefill chunk, INT8 group-32 experts, Zipf(1.1) log-prior"),
+        Spec("decode_t1_h4096_e256_k8_i1024_fp6", T=1, H=4096, E=256, k=8, I=1024, bits=6,
+             seed=1011, router_law="uniform", n_sets=4,
+             note="batch-1 decode, fp6 e2m3 experts with fp16 group-128 scales; 4 sets of 2.5 GB cycled"),
+        Spec("prefill_t4096_h4096_e256_k8_i1024_fp6", T=4096, H=4096, E=256, k=8, I=1024, bits=6,
+             seed=1012, zipf_s=1.1,
+             note="prefill chunk, fp6 e2m3 experts, Zipf(1.1) log-prior"),
         Spec("mid_t64_h4096_e256_k8_i1024_int4", T=64, H=4096, E=256, k=8, I=1024, bits=4,
              seed=1006, router_law="uniform", x_law="ar1_streams", streams=16, n_sets=2,
              note="middle batch: 16 streams x 4 draft tokens (higher-concurrency verify), decode path"),
@@ -200,19 +210,26 @@ def _scales(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
     return bf16_bits(s)
 
 
+def _fp16_scales(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    s = np.abs(rng.standard_normal(shape, dtype=np.float32)) * np.float32(sigma)
+    return s.astype(np.float16).view(np.uint16)
+
+
 def make_weight_set(sp: Spec, set_idx: int = 0) -> Dict[str, np.ndarray]:
     """One full layer of expert weights in the packed formats described above."""
-    E, H, I, P, G = sp.E, sp.H, sp.I, sp.codes_per_word, sp.group
+    E, H, I, G = sp.E, sp.H, sp.I, sp.group
+    nw = sp.words_per_row
     if H % GROUP or I % GROUP:
         raise ValueError("H and I must be multiples of 128")
-    if G not in (32, 128) or (G == 32 and sp.bits == 2):
+    if G not in (32, 128) or (G == 32 and sp.bits in (2, 6)):
         raise ValueError("group 128, or 32 for INT4 / INT8")
     codes = _int8_words if sp.bits == 8 else _uniform_words
+    scales = _fp16_scales if sp.bits == 6 else _scales
     out = {
-        "w13_codes": codes(_rng(sp.seed, _TAG_W13C, set_idx), (E, 2 * I, H // P)),
-        "w13_scales": _scales(_rng(sp.seed, _TAG_W13S, set_idx), (E, 2 * I, H // G), sp.scale_sigma),
-        "w2_codes": codes(_rng(sp.seed, _TAG_W2C, set_idx), (E, H, I // P)),
-        "w2_scales": _scales(_rng(sp.seed, _TAG_W2S, set_idx), (E, H, I // G), sp.scale_sigma),
+        "w13_codes": codes(_rng(sp.seed, _TAG_W13C, set_idx), (E, 2 * I, nw(H))),
+        "w13_scales": scales(_rng(sp.seed, _TAG_W13S, set_idx), (E, 2 * I, H // G), sp.scale_sigma),
+        "w2_codes": codes(_rng(sp.seed, _TAG_W2C, set_idx), (E, H, nw(I))),
+        "w2_scales": scales(_rng(sp.seed, _TAG_W2S, set_idx), (E, H, I // G), sp.scale_sigma),
     }
     if sp.bits == 2:
         # integer zero-points drawn uniformly from {1, 2}
