@@ -213,7 +213,7 @@ class Plan:
             fn = L.moe_expert_ffn_w4a16_table if sp.bits == 4 else L.moe_expert_ffn_w2a16_table
             s = fn(*common, st["table"].data_ptr(), self.y_perm.data_ptr(), self.ws_ffn.data_ptr(),
                    self.ws_ffn.numel(), stream)
-        elif sp.bits == 8 or sp.group != 128:
+        elif sp.bits not in (2, 4) or sp.group != 128:
             s = L.moe_expert_ffn_wna16(*common, sp.bits, sp.group, w["w13_codes"].data_ptr(),
                                        w["w13_scales"].data_ptr(), None, w["w2_codes"].data_ptr(),
                                        w["w2_scales"].data_ptr(), None, self.y_perm.data_ptr(),
@@ -297,7 +297,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sp = workload.spec(args.workload)
-    if args.experts != "arrays" and (sp.bits == 8 or sp.group != 128):
+    if args.experts != "arrays" and (sp.bits not in (2, 4) or sp.group != 128):
         print(json.dumps({"error": "the address-table entry points take INT4 and 2-bit with groups of 128"}))
         sys.exit(2)
     # the one-launch layer takes INT4 and 2-bit with groups of 128 from stacked arrays
@@ -425,7 +425,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": sp.name, "T": sp.T, "H": sp.H, "E": sp.E, "top_k": sp.k, "I": sp.I,
-                   "weight_format": f"int{sp.bits} g{sp.group}" + (" + zero-point" if sp.bits == 2 else " sym"),
+                   "weight_format": ("fp6 e2m3 g128 (fp16 scales)" if sp.bits == 6 else
+                                     f"int{sp.bits} g{sp.group}" + (" + zero-point" if sp.bits == 2 else " sym")),
                    "weight_sets_cycled": nset, "experts": args.experts, "launch": f"hip graph of {nset} steps (one per weight set)" if use_graph else "eager",
                    "step": "moe_layer (one launch)" if fused else "stage calls",
                    "wall_s_timed": round(wall, 4)},

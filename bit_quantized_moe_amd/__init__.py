@@ -187,7 +187,8 @@ def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: D
     """Per-expert gate_up -> SwiGLU -> down on the sorted rows; bf16 [T*k, H].
 
     bits 4 or 2 with group 128 call moe_expert_ffn_w4a16 / _w2a16; other
-    formats (INT4 group 32, INT8 group 128 or 32) moe_expert_ffn_wna16."""
+    formats (INT4 group 32, INT8 group 128 or 32, FP6 e2m3 with bits = 6)
+    moe_expert_ffn_wna16."""
     dev = _dev(x)
     T, H = x.shape
     E = offsets.numel() - 1
@@ -197,7 +198,7 @@ def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: D
     nbytes = L.moe_expert_ffn_workspace_size(T, k, E, H, I)
     w = (ws or Workspaces(dev)).get("ffn", nbytes)
     st = _stream(dev)
-    if bits == 8 or group != 128:
+    if bits not in (2, 4) or group != 128:
         s = L.moe_expert_ffn_wna16(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I, bits, group,
                                    _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights.get("w13_zeros")),
                                    _p(weights["w2_codes"]), _p(weights["w2_scales"]), _p(weights.get("w2_zeros")),
@@ -323,10 +324,10 @@ def layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Te
 
 
 def unpack_codes(words: torch.Tensor, bits: int) -> torch.Tensor:
-    """Signed codes of packed words (decode-path unpack routine); int8, K order."""
+    """Signed codes of packed words (decode-path unpack routine); int8, K order (FP6: 8 * value)."""
     dev = _dev(words)
     n = words.numel()
-    out = torch.empty(n * (32 // bits), dtype=torch.int8, device=dev)
+    out = torch.empty(n * 32 // bits, dtype=torch.int8, device=dev)
     _check(lib().moe_unpack_codes(_p(words), bits, n, _p(out), _stream(dev)), "moe_unpack_codes")
     return out
 

@@ -255,7 +255,8 @@ moe_status moe_expert_ffn_wna16(const uint16_t *x, const int32_t *expert_offsets
                                 const uint32_t *w2_codes, const uint16_t *w2_scales, const uint8_t *w2_zeros,
                                 uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream) {
   const bool ok = (bits == 4 && (group_size == 128 || group_size == 32)) ||
-                  (bits == 8 && (group_size == 128 || group_size == 32)) || (bits == 2 && group_size == 128);
+                  (bits == 8 && (group_size == 128 || group_size == 32)) ||
+                  ((bits == 2 || bits == 6) && group_size == 128);
   if (!ok)
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wna16: unsupported format: %d bits, group %d", bits, group_size);
   return expert_ffn("moe_expert_ffn_wna16", bits, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
@@ -377,9 +378,11 @@ moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const flo
 }
 
 moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, int8_t *out, void *stream) {
-  if (bits != 2 && bits != 4 && bits != 8)
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2, 4 or 8 (got %d)", bits);
+  if (bits != 2 && bits != 4 && bits != 6 && bits != 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2, 4, 6 or 8 (got %d)", bits);
   if (n_words < 0) return fail(MOE_ERR_INVALID_ARG, "n_words must be >= 0");
+  if (bits == 6 && n_words % 6)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "FP6: n_words must be a multiple of 6 (32 codes)");
   if (n_words > (1LL << 36)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "n_words too large");
   if (!words || !out) return fail(MOE_ERR_INVALID_ARG, "moe_unpack_codes: words and out are required");
   if (!aligned(words, 4)) return fail(MOE_ERR_MISALIGNED, "moe_unpack_codes: words must be 4-byte aligned");
@@ -389,9 +392,9 @@ moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, in
 
 moe_status moe_dequant_bf16_grouped(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
                                     int group_size, int N, int K, uint16_t *out, void *stream) {
-  if (bits != 2 && bits != 4 && bits != 8)
-    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2, 4 or 8 (got %d)", bits);
-  if (group_size != 128 && !(group_size == 32 && bits != 2))
+  if (bits != 2 && bits != 4 && bits != 6 && bits != 8)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "bits must be 2, 4, 6 or 8 (got %d)", bits);
+  if (group_size != 128 && !(group_size == 32 && (bits == 4 || bits == 8)))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "group size 128, or 32 for INT4 / INT8 (got %d)", group_size);
   if (N < 0 || K < 0) return fail(MOE_ERR_INVALID_ARG, "N and K must be >= 0");
   if (K % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K must be a multiple of 128 (got %d)", K);

@@ -92,6 +92,20 @@ __device__ __forceinline__ u32x4 unpack8_bf16(uint32_t w0, uint32_t w1) {
   return u32x4{pr(w0, 0), pr(w0, 2), pr(w1, 0), pr(w1, 2)};
 }
 
+// FP6 e2m3: 32 codes, a little-endian stream of 6-bit fields in six words ->
+// 32 bf16 values in K order (16 pairs).  gfx950 converts the 32 codes in one
+// instruction; with scale 1 every e2m3 value is exact in bf16.
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+__device__ __forceinline__ u32x16 fp6x32_to_bf16(u32x6 v) {
+  u32x16 r;
+  asm("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, 1.0" : "=&v"(r) : "v"(v));
+  return r;
+}
+__device__ __forceinline__ float fp16_to_f32(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
 // Natural-order bf16 activations d (pairs (x0,x1), (x2,x3), ...) -> the pair
 // order of the unpacked codes: o[i] = (x[ord[2i]], x[ord[2i+1]]).  N elements.
 template <int N>

@@ -95,24 +95,34 @@ constexpr uint32_t kHReady = 1u << 16;  // tag of a written h word
 constexpr uint64_t kRecTag = 1ull << 63;  // tag of a written routing record word
 
 // ---------------------------------------------------------------- formats
-// BITS: 4 (INT4, field q + 8), 2 (field u, integer zero-point) or 8 (INT8,
-// field q + 128).  GS: quantisation group along K, 128 or 32.  The kernels
-// walk K in units of 128 (kGroup); a unit holds 128 / GS scales per row.
+// BITS: 4 (INT4, field q + 8), 2 (field u, integer zero-point), 8 (INT8,
+// field q + 128) or 6 (FP6 e2m3 codes, fp16 scales).  GS: quantisation group
+// along K, 128 or 32.  The kernels walk K in units of 128 (kGroup); a unit
+// holds 128 / GS scales per row.
 template <int GS>
 constexpr int kSPU = kGroup / GS;
 // Units whose weight loads a wave keeps in flight together: 8 of INT4 or
 // 2-bit, 4 of INT8 (the same bytes); half that with groups of 32, whose four
 // scales per unit and transposed slices take registers.
 template <int BITS, int GS>
-constexpr int kCG = (BITS == 8 ? 4 : 8) / (GS == 32 ? 2 : 1);
+constexpr int kCG = (BITS >= 6 ? 4 : 8) / (GS == 32 ? 2 : 1);
+// A scale's 16 bits as a float: fp16 for FP6, bf16 otherwise.
+template <int BITS>
+__device__ __forceinline__ float scale_f32(uint32_t b16) {
+  if constexpr (BITS == 6)
+    return fp16_to_f32(b16);
+  else
+    return bf16_to_f32(b16);
+}
 
 // ---------------------------------------------------------------- operands
 // One chunk of natural-order bf16 activations (d: pairs (x0,x1), (x2,x3), ...)
 // in the field order of the unpacked codes: INT4 chunks of 8, INT2 chunks of
-// 16; INT8 codes unpack in K order, so its chunks (of 8) stay as they are.
+// 16; INT8 and FP6 codes unpack in K order, so their chunks (of 8) stay as
+// they are.
 template <int BITS>
 __device__ __forceinline__ void permute_chunk(const uint32_t *d, uint32_t *o) {
-  if constexpr (BITS == 8) {
+  if constexpr (BITS >= 6) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = d[i];
   } else {
@@ -284,7 +294,7 @@ constexpr int kHPend = 4;
 // pair order of the unpacked codes, see order_pairs).
 template <int BITS>
 __device__ __forceinline__ int chunk_slot(int i) {
-  return BITS == 8 ? i : BITS == 4 ? (i >> 1) + 4 * (i & 1) : (i >> 2) + 4 * (i & 3);
+  return BITS >= 6 ? i : BITS == 4 ? (i >> 1) + 4 * (i & 1) : (i >> 2) + 4 * (i & 3);
 }
 
 // One polling round for the wave's lowest pending unit (bit j of pend: unit
@@ -340,12 +350,24 @@ __device__ uint32_t service_h(uint32_t pend, const uint32_t *h, uint8_t *act, fl
 
 // ---------------------------------------------------------------- weights
 // A lane reads 32 consecutive K of one weight row per 128-K unit: a 16-byte
-// (INT4), 8-byte (INT2) or 32-byte (INT8) slice at byte lsub * kGroupBytes / 4
-// of the unit.
+// (INT4), 8-byte (INT2), 32-byte (INT8) or 24-byte (FP6) slice at byte
+// lsub * kGroupBytes / 4 of the unit.
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 template <int BITS>
-using Word = typename std::conditional<BITS == 4, u32x4,
-                                       typename std::conditional<BITS == 2, u32x2, u32x8>::type>::type;
+using Word = typename std::conditional<
+    BITS == 4, u32x4,
+    typename std::conditional<BITS == 2, u32x2, typename std::conditional<BITS == 8, u32x8, u32x6>::type>::type>::type;
+// One lane slice (FP6: 16 + 8 bytes, so that no load reaches past the slice).
+template <int BITS>
+__device__ __forceinline__ Word<BITS> load_word(const uint8_t *p) {
+  if constexpr (BITS == 6) {
+    const u32x4 a = *(const u32x4 *)p;
+    const u32x2 b = *(const u32x2 *)(p + 16);
+    return u32x6{a[0], a[1], a[2], a[3], b[0], b[1]};
+  } else {
+    return *(const Word<BITS> *)p;
+  }
+}
 template <int BITS>
 constexpr int kGroupBytes = kGroup * BITS / 8;
 
@@ -396,7 +418,7 @@ __device__ __forceinline__ void load_chunk(const ExpertW &x, Off o, Chunk<BITS, 
   constexpr int CG = kCG<BITS, GS>;
   constexpr int NS = CG * kSPU<GS> / 2;  // scale words: 4 (16 bytes), 2 or 8
 #pragma unroll
-  for (int c = 0; c < CG; ++c) ch.w[c] = *(const Word<BITS> *)(x.codes + o.c + c * kGroupBytes<BITS>);
+  for (int c = 0; c < CG; ++c) ch.w[c] = load_word<BITS>(x.codes + o.c + c * kGroupBytes<BITS>);
   if constexpr (NS == 2) {
     const u32x2 v = *(const u32x2 *)(x.scales + o.s);
     ch.s[0] = v[0];
@@ -432,6 +454,21 @@ __device__ __forceinline__ void group_mfma(const Word<BITS> *w, const uint8_t *a
                                            f32x4 *cg) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) cg[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (BITS == 6) {  // the slice's 32 codes converted at once, 8 per MFMA
+    u32x16 v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = fp6x32_to_bf16(w[r]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 a = *(const bf16x8 *)(ap + j * 16);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const u32x4 b = u32x4{v[r][4 * j], v[r][4 * j + 1], v[r][4 * j + 2], v[r][4 * j + 3]};
+        cg[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b), cg[r], 0, 0, 0);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bf16x8 a = *(const bf16x8 *)(ap + j * 16);
@@ -460,6 +497,8 @@ __device__ __forceinline__ float zero_off(uint32_t z) {
     return 136.f;  // offset-binary code q + 8, plus the 128 of the unpack
   else if constexpr (BITS == 8)
     return 128.f;  // offset-binary code q + 128, unpacked as is
+  else if constexpr (BITS == 6)
+    return 0.f;    // e2m3 values are signed: no offset
   else
     return 128.f + (float)z;
 }
@@ -538,7 +577,7 @@ __device__ __forceinline__ void chunk_gemv(Chunk<BITS, GS> *ch, const uint8_t *a
       group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const float s = bf16_to_f32((ch[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
+        const float s = scale_f32<BITS>((ch[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
         const float zo = zero_off<BITS>((ch[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
         group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
       }
@@ -554,7 +593,7 @@ __device__ __forceinline__ void groups_gemv_slow(const ExpertW &x, const Off *o,
   for (int c = 0; c < ng; ++c) {
     Word<BITS> w[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) w[r] = *(const Word<BITS> *)(x.codes + o[r].c + c * kGroupBytes<BITS>);
+    for (int r = 0; r < NR; ++r) w[r] = load_word<BITS>(x.codes + o[r].c + c * kGroupBytes<BITS>);
     if constexpr (GS == 32) {
       uint32_t sc[NR][2];
 #pragma unroll
@@ -569,7 +608,7 @@ __device__ __forceinline__ void groups_gemv_slow(const ExpertW &x, const Off *o,
       group_mfma<BITS, NR>(w, ap + c * (kGroup * 2), magic, cg);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const float s = bf16_to_f32(*(const uint16_t *)(x.scales + o[r].s + 2 * c));
+        const float s = scale_f32<BITS>(*(const uint16_t *)(x.scales + o[r].s + 2 * c));
         const float zo = zero_off<BITS>(BITS == 2 ? x.zeros[o[r].z + c] : 0u);
         group_acc<ONE>(cg[r], s, zo, xs + c * 16, acc[r]);
       }
@@ -1005,7 +1044,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
               group_mfma<BITS, 2>(w2, ap + g * (kGroup * 2), magic, cg);
 #pragma unroll
               for (int r = 0; r < 2; ++r) {
-                const float sc = bf16_to_f32((wd[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
+                const float sc = scale_f32<BITS>((wd[r].s[c / 2] >> (16 * (c & 1))) & 0xFFFFu);
                 const float zo = zero_off<BITS>((wd[r].z[c / 4] >> (8 * (c % 4))) & 0xFFu);
                 group_acc<ONE>(cg[r], sc, zo, Xs + g * 16, ty[r]);
               }
@@ -1190,12 +1229,13 @@ const void *decode_kernel_fn(int bits, int group, bool one, bool fast, bool laye
   if (layer) return decode_fn_layer<true, false>(bits, one, fast);
   if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, false, false>(one, fast)
                                     : decode_fn_fast<8, 128, false, false>(one, fast);
+  if (bits == 6) return decode_fn_fast<6, 128, false, false>(one, fast);
   if (group == 32) return decode_fn_fast<4, 32, false, false>(one, fast);
   return tab ? decode_fn_layer<false, true>(bits, one, fast) : decode_fn_layer<false, false>(bits, one, fast);
 }
 
 // Units per chunk of a format (kCG on the host).
-int chunk_units(int bits, int group) { return (bits == 8 ? 4 : 8) / (group == 32 ? 2 : 1); }
+int chunk_units(int bits, int group) { return (bits >= 6 ? 4 : 8) / (group == 32 ? 2 : 1); }
 
 // LDS of the fused layer's routing results (after the FFN's own arrays).
 size_t layer_lds_bytes(int T, int k, int E) {

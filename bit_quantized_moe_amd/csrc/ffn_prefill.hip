@@ -14,8 +14,8 @@
 //    M-tile) is derived on the device from the permutation offsets, so the
 //    host launches an upper bound of M-tile slots and surplus blocks exit;
 //  * A rows (gathered activations for G1, contiguous h rows for G2) and the B
-//    tile, dequantised once per block to bf16 (q - z) * s (INT4, 2-bit or INT8
-//    codes; one scale per 128 or per 32 K), go through two LDS
+//    tile, dequantised once per block to bf16 (q - z) * s (INT4, 2-bit, INT8
+//    or FP6 e2m3 codes; one scale per 128 or per 32 K), go through two LDS
 //    buffers with an XOR swizzle of 16-byte chunks, so both the staging
 //    writes and the MFMA operand reads are free of bank conflicts;
 //  * 4 waves in a 2 x 2 arrangement each own a 64 x 64 sub-tile computed with
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   // B staging: thread -> weight row tid / 2 of the tile, code words
   // (tid % 2) * WPL .. + WPL of the K tile, i.e. LDS chunks (tid % 2) * 4 .. + 4.
   // G1 tiles give each wave column 32 gate rows then the 32 matching up rows.
-  constexpr int WPT = BK * BITS / 32;         // code words per tile row: 8 (INT4), 4 (INT2), 16 (INT8)
+  constexpr int WPT = BK * BITS / 32;         // code words per tile row: 8 (INT4), 4 (INT2), 16 (INT8), 12 (FP6)
   constexpr int WPL = WPT / 2;                // words per thread: 32 K of one row
   const int br = tid >> 1, bh = tid & 1;
   int wrow;
@@ -201,7 +201,14 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
     auto load_tile = [&](int kt, int s) {
   #pragma unroll
       for (int j = 0; j < 4; ++j) a_st[s][j] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_off[j], kt * (BK * 2), 0);
-      if constexpr (BITS == 8) {
+      if constexpr (BITS == 6) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off, kt * (WPT * 4), 0);
+        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(b_rs, b_off + 16, kt * (WPT * 4), 0);
+  #pragma unroll
+        for (int w = 0; w < 4; ++w) b_st[s][w] = v[w];
+        b_st[s][4] = u[0];
+        b_st[s][5] = u[1];
+      } else if constexpr (BITS == 8) {
   #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b_rs, b_off + 16 * h, kt * (WPT * 4), 0);
@@ -224,8 +231,20 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   #pragma unroll
       for (int j = 0; j < 4; ++j) *(u32x4 *)(buf + swz(ar + 32 * j, ac)) = a_st[s][j];
       uint8_t *bb = buf + kTileBytes;
-      const float sc = bf16_to_f32(sc_st[s]);
-      const float zs = -((BITS == 4) ? 8.f : BITS == 8 ? 128.f : (float)z_st[s]) * sc;
+      const float sc = BITS == 6 ? fp16_to_f32(sc_st[s]) : bf16_to_f32(sc_st[s]);
+      const float zs = -((BITS == 4) ? 8.f : BITS == 8 ? 128.f : BITS == 6 ? 0.f : (float)z_st[s]) * sc;
+      if constexpr (BITS == 6) {
+        // the thread's 32 codes at once (exact bf16 values), then times the scale
+        const u32x16 v = fp6x32_to_bf16(u32x6{b_st[s][0], b_st[s][1], b_st[s][2], b_st[s][3], b_st[s][4], b_st[s][5]});
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t o[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16lo(v[4 * c + i]) * sc, bf16hi(v[4 * c + i]) * sc);
+          *(u32x4 *)(bb + swz(br, bh * 4 + c)) = u32x4{o[0], o[1], o[2], o[3]};
+        }
+        return;
+      }
   #pragma unroll
       for (int w = 0; w < WPL; ++w) {
         if constexpr (BITS == 8) {
@@ -380,6 +399,8 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
     run(ffn_gemm_kernel<8, 128, true, 2>, ffn_gemm_kernel<8, 128, false, 2>);
   else if (a.bits == 8)
     run(ffn_gemm_kernel<8, 32, true, 2>, ffn_gemm_kernel<8, 32, false, 2>);
+  else if (a.bits == 6)
+    run(ffn_gemm_kernel<6, 128, true, 2>, ffn_gemm_kernel<6, 128, false, 2>);
   else
     run(ffn_gemm_kernel<2, 128, true, 2>, ffn_gemm_kernel<2, 128, false, 2>);
   // h is T*k*I bf16 (I % 128 == 0, so a whole number of 16-byte chunks)

@@ -1,7 +1,7 @@
 // Diagnostic kernels that expose the two device dequantisation routines:
 //  - moe_unpack_codes: the bf16 unpack of the decode GEMV kernels (offset
-//    form for INT4 and 2-bit, a float conversion for INT8), converted back to
-//    signed integer codes;
+//    form for INT4 and 2-bit, a float conversion for INT8, the FP6 e2m3
+//    conversion), converted back to signed integer codes (FP6: 8 * value);
 //  - moe_dequant_bf16 / _grouped: the bf16 (q - z) * s of the grouped-GEMM
 //    kernels.
 #include "common.cuh"
@@ -47,6 +47,35 @@ __global__ void unpack_kernel(const uint32_t *__restrict__ words, int64_t n_word
   for (int p = 0; p < P; ++p) out[i * P + p] = q[p];
 }
 
+// FP6: thread i converts the 32 codes of words 6i .. 6i+5 (the decode routine)
+// and stores 8 * value, an integer in [-60, 60].
+__global__ void unpack6_kernel(const uint32_t *__restrict__ words, int64_t n_groups, int8_t *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_groups) return;
+  const uint32_t *w = words + i * 6;
+  const u32x16 v = fp6x32_to_bf16(u32x6{w[0], w[1], w[2], w[3], w[4], w[5]});
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    out[i * 32 + 2 * p] = (int8_t)(int)(bf16lo(v[p]) * 8.f);
+    out[i * 32 + 2 * p + 1] = (int8_t)(int)(bf16hi(v[p]) * 8.f);
+  }
+}
+
+// FP6 dequant: thread i takes 32 codes (6 words) of one row, the GEMM routine.
+__global__ void dequant6_kernel(const uint32_t *__restrict__ words, const uint16_t *__restrict__ scales, int N, int K,
+                                uint16_t *__restrict__ out) {
+  const int gpr = K / 32;  // 32-code groups per row
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)N * gpr) return;
+  const int n = (int)(i / gpr), gi = (int)(i % gpr);
+  const float s = fp16_to_f32(scales[(size_t)n * (K / kGroup) + gi * 32 / kGroup]);
+  const uint32_t *w = words + i * 6;
+  const u32x16 v = fp6x32_to_bf16(u32x6{w[0], w[1], w[2], w[3], w[4], w[5]});
+  uint32_t *dst = (uint32_t *)(out + (size_t)n * K + (size_t)gi * 32);
+#pragma unroll
+  for (int p = 0; p < 16; ++p) dst[p] = pack_bf16x2(bf16lo(v[p]) * s, bf16hi(v[p]) * s);
+}
+
 template <int BITS, int GS>
 __global__ void dequant_kernel(const uint32_t *__restrict__ words, const uint16_t *__restrict__ scales,
                                const uint8_t *__restrict__ zeros, int N, int K, uint16_t *__restrict__ out) {
@@ -77,7 +106,10 @@ __global__ void dequant_kernel(const uint32_t *__restrict__ words, const uint16_
 hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_t *out, hipStream_t st) {
   const int threads = 256;
   const int64_t blocks = (n_words + threads - 1) / threads;
-  if (bits == 8)
+  if (bits == 6) {
+    const int64_t groups = n_words / 6;
+    unpack6_kernel<<<(unsigned)((groups + threads - 1) / threads), threads, 0, st>>>(words, groups, out);
+  } else if (bits == 8)
     unpack_kernel<8><<<(unsigned)blocks, threads, 0, st>>>(words, n_words, out);
   else if (bits == 4)
     unpack_kernel<4><<<(unsigned)blocks, threads, 0, st>>>(words, n_words, out);
@@ -91,7 +123,10 @@ hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, co
   const int threads = 256;
   const int64_t n_words = (int64_t)N * K * bits / 32;
   const unsigned blocks = (unsigned)((n_words + threads - 1) / threads);
-  if (bits == 8 && group == 32)
+  if (bits == 6) {
+    const int64_t groups = (int64_t)N * (K / 32);
+    dequant6_kernel<<<(unsigned)((groups + threads - 1) / threads), threads, 0, st>>>(words, scales, N, K, out);
+  } else if (bits == 8 && group == 32)
     dequant_kernel<8, 32><<<blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);
   else if (bits == 8)
     dequant_kernel<8, 128><<<blocks, threads, 0, st>>>(words, scales, zeros, N, K, out);

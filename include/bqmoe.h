@@ -1,6 +1,7 @@
 /*
  * bqmoe.h -- C ABI of the routed-expert mixture-of-experts layer with low-bit
- * (weight-only INT4 / 2-bit / INT8) experts, for AMD Instinct MI355X (gfx950).
+ * (weight-only INT4 / 2-bit / INT8 / FP6) experts, for AMD Instinct MI355X
+ * (gfx950).
  *
  * The layer, per batch of T tokens with hidden size H, E experts, top-k routing
  * and expert intermediate size I:
@@ -12,7 +13,7 @@
  *                   dequantised on the fly from packed codes
  *   moe_expert_ffn_wna16
  *                   the same for any supported format: INT4 or INT8 with
- *                   groups of 128 or 32, 2-bit with groups of 128
+ *                   groups of 128 or 32, 2-bit or FP6 e2m3 with groups of 128
  *   moe_expert_ffn_w4a16_table / _w2a16_table
  *                   the same, each expert's weights located through a
  *                   per-expert address table
@@ -32,7 +33,13 @@
  * pages' format tables), and INT8 symmetric, fields q + 128 with q in
  * [-127, 127], group 128 or 32 (page "Qwen3.8-Flash-Next on one 24 GB GPU",
  * "What the patch does": INT8 g128; page "Qwen3.8-Flash-Next FP6-INT8",
- * "Precision map" and "Kernel-level verification": an int8 g32 tier).
+ * "Precision map" and "Kernel-level verification": an int8 g32 tier).  FP6
+ * e2m3 codes with fp16 scales (same page, opening paragraph and
+ * "Kernel-level verification"): a row's codes form one little-endian bit
+ * stream, code k in bits [6k, 6k+6) (16 codes per 3 words); bit 5 is the
+ * sign, bits 4..3 the exponent e (bias 1), bits 2..0 the mantissa m; the
+ * value is m/8 for e = 0 and 2^(e-1) * (1 + m/8) otherwise; W = value * s
+ * with one fp16 scale per 128 K.
  *
  * Conventions shared by every entry point:
  *  - Every array argument is a DEVICE pointer owned by the caller.  The library
@@ -207,8 +214,9 @@ moe_status moe_expert_ffn_w2a16(const uint16_t *x, const int32_t *expert_offsets
  *   bits 4, group 128 or 32   W = (field - 8) * s
  *   bits 8, group 128 or 32   W = (field - 128) * s
  *   bits 2, group 128         W = (field - z) * s   (zero-points required)
+ *   bits 6, group 128         W = e2m3(code) * s    (FP6; s is fp16)
  * with s (and z) the value of the group that holds the K index:
- *   w13_codes [E, 2I, H*bits/32] uint32, w13_scales [E, 2I, H/G] bf16,
+ *   w13_codes [E, 2I, H*bits/32] uint32, w13_scales [E, 2I, H/G] bf16 (fp16 for FP6),
  *   w13_zeros [E, 2I, H/G] uint8 (bits == 2, else ignored; may be NULL),
  *   w2_codes [E, H, I*bits/32], w2_scales [E, H, I/G], w2_zeros [E, H, I/G].
  * Other arguments, requirements, dispatch (the decode path streams each
@@ -317,8 +325,9 @@ moe_status moe_layer_w2a16(const uint16_t *x, const uint16_t *w_router, const fl
 /* ---------------------------------------------------------------- diagnostics
  * moe_unpack_codes: the signed codes of n_words packed words, unpacked by the
  * same device routine the decode kernels use (INT4: q = field - 8; 2-bit:
- * u = field; INT8: q = field - 128).  out holds n_words * 32/bits int8 values
- * in K order.  bits: 2, 4 or 8.
+ * u = field; INT8: q = field - 128; FP6: 8 * e2m3 value, an integer in
+ * [-60, 60]).  out holds n_words * 32/bits int8 values in K order.  bits: 2,
+ * 4, 6 (n_words a multiple of 6) or 8.
  */
 moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, int8_t *out,
                             void *stream);
@@ -331,7 +340,7 @@ moe_status moe_unpack_codes(const uint32_t *words, int bits, int64_t n_words, in
 moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros,
                             int bits, int N, int K, uint16_t *out, void *stream);
 /* moe_dequant_bf16_grouped: the same with group_size 128, or 32 (bits 4 or 8;
- * scales [N, K/32]). */
+ * scales [N, K/32]); bits 6 (FP6, group 128) takes fp16 scales. */
 moe_status moe_dequant_bf16_grouped(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros,
                                     int bits, int group_size, int N, int K, uint16_t *out, void *stream);
 

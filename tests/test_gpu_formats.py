@@ -4,7 +4,9 @@ INT4 symmetric with groups of 32 (the draft-layer experts of page
 "Qwen3.8-Flash-Next on 2x RTX 3090", storage-format table) and INT8 symmetric
 with groups of 128 or 32 (page "Qwen3.8-Flash-Next on one 24 GB GPU", "What
 the patch does"; page "Qwen3.8-Flash-Next FP6-INT8", "Precision map" and
-"Kernel-level verification"), through moe_expert_ffn_wna16 on both FFN paths.
+"Kernel-level verification"), and FP6 e2m3 with fp16 group-128 scales (same
+page, opening paragraph and "Kernel-level verification"), through
+moe_expert_ffn_wna16 on both FFN paths.
 Bars as for the other formats: unpacked codes and dequantised bf16 values bit
 for bit, outputs within 2e-2 relative Frobenius error (tensor-wide and per row).
 """
@@ -21,8 +23,8 @@ from gpu_util import bf16_np_to_f32, row_rel_err, to_dev, to_np, weights_to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
-FORMATS = [(4, 32), (8, 128), (8, 32)]
-SIGMA = {4: 0.02, 8: 0.0015}
+FORMATS = [(4, 32), (8, 128), (8, 32), (6, 128)]
+SIGMA = {4: 0.02, 8: 0.0015, 6: 0.02}
 
 
 def say(msg):
@@ -51,12 +53,32 @@ def test_unpack_int8_every_byte_every_position():
     assert np.array_equal(got, oracle.unpack_codes(words, 8).ravel())
 
 
+def test_unpack_fp6_every_code_every_position():
+    """The decode routine's e2m3 conversion, as 8 * value: every code at every
+    position of a 32-code group, then random words."""
+    rows = []
+    for pos in range(32):
+        for c in range(64):
+            stream = 0
+            for f in range(32):
+                stream |= ((c if f == pos else (c + 7 * f) % 64) << (6 * f))
+            rows.append([(stream >> (32 * i)) & 0xFFFFFFFF for i in range(6)])
+    rng = np.random.default_rng(6)
+    words = np.concatenate([np.array(rows, np.uint32).ravel(), rng.integers(0, 2**32, 6 << 14, dtype=np.uint32)])
+    got = to_np(bq.unpack_codes(to_dev(words), 6)).astype(np.int64)
+    exp = (8 * oracle.e2m3_value(oracle.unpack_fp6_fields(words.reshape(-1, 6)).ravel())).astype(np.int64)
+    assert np.array_equal(got, exp)
+
+
 @pytest.mark.parametrize("bits,group", FORMATS)
 def test_dequant_bf16_is_rounded_oracle(bits, group):
     rng = np.random.default_rng(5 + bits + group)
     N, K = 64, 1024
     words = rng.integers(0, 2**32, (N, K * bits // 32), dtype=np.uint32)
-    scales = workload.bf16_bits(np.abs(rng.standard_normal((N, K // group))).astype(np.float32) * 0.03)
+    if bits == 6:
+        scales = (np.abs(rng.standard_normal((N, K // group))) * 0.03).astype(np.float16).view(np.uint16)
+    else:
+        scales = workload.bf16_bits(np.abs(rng.standard_normal((N, K // group))).astype(np.float32) * 0.03)
     got = to_np(bq.dequant_bf16(to_dev(words), to_dev(scales), None, bits, N, K, group=group))
     exp = workload.bf16_bits(oracle.dequantize(words, scales, None, bits, group))
     assert np.array_equal(got, exp)
@@ -108,14 +130,15 @@ def test_ffn_formats_full_chunk_decode_shapes(bits, group):
 
 
 @pytest.mark.parametrize("name", ["decode_t1_h4096_e256_k8_i1024_int4g32", "decode_t1_h4096_e256_k8_i1024_int8",
-                                  "decode_t1_h4096_e256_k8_i1024_int8g32"])
+                                  "decode_t1_h4096_e256_k8_i1024_int8g32", "decode_t1_h4096_e256_k8_i1024_fp6"])
 def test_ffn_formats_decode_full_size(name):
     sp = workload.spec(name)
     _check_ffn(workload.make_layer_inputs(sp))
 
 
-def test_ffn_int8g32_prefill_full_size_sampled():
-    sp = workload.spec("prefill_t4096_h4096_e256_k8_i1024_int8g32")
+@pytest.mark.parametrize("name", ["prefill_t4096_h4096_e256_k8_i1024_int8g32", "prefill_t4096_h4096_e256_k8_i1024_fp6"])
+def test_ffn_formats_prefill_full_size_sampled(name):
+    sp = workload.spec(name)
     inp = workload.make_layer_inputs(sp)
     wd = weights_to_dev(inp.weights)
     out = bq.moe_layer(to_dev(inp.x), to_dev(inp.w_router), to_dev(inp.logit_bias), wd, sp.k, sp.bits, sp.I,
