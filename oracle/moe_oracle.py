@@ -335,3 +335,135 @@ def rel_fro(a: np.ndarray, ref: np.ndarray) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(a - ref) / (den if den > 0 else 1.0))
+
+
+# ---------------------------------------------------------------- NVFP4 (W4A4)
+# Page "Qwen3.8-Flash-Next NVFP4", "Format": routed experts in NVFP4 W4A4, E2M1
+# values in groups of 16.  The rest of the format is NVFP4's public
+# definition, taken as the reading: each group of 16 consecutive K carries one
+# FP8 E4M3 scale, a tensor carries one float32 scale, and activations are
+# quantised the same way on the fly.  Every rounding below is to nearest,
+# ties to even.
+NVFP4_GROUP = 16
+E2M1_MAX = 6.0
+E4M3_MAX = 448.0
+
+
+def e2m1_value(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1: bit 3 sign, bits 2..1 exponent e (bias 1), bit 0 mantissa m;
+    e = 0 is subnormal (m / 2), otherwise 2^(e-1) * (1 + m/2)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sgn = np.where(c & 8, -1.0, 1.0)
+    e, m = (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, m / 2.0, np.exp2(e - 1.0) * (1.0 + m / 2.0))
+    return (sgn * mag).astype(np.float32)
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 (the finite codes): bit 7 sign, bits 6..3 exponent e (bias 7),
+    bits 2..0 mantissa m; e = 0 is subnormal (m / 8 * 2^-6)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sgn = np.where(c & 128, -1.0, 1.0)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, np.exp2(e - 7.0) * (1.0 + m / 8.0))
+    return (sgn * mag).astype(np.float32)
+
+
+def _round_to_grid(v: np.ndarray, min_exp: int, mbits: int, vmax: float) -> np.ndarray:
+    """|v| rounded to a float grid with mbits mantissa bits whose smallest
+    binade starts at 2^min_exp (below it the spacing stays 2^(min_exp-mbits)),
+    ties to even, saturating at vmax; sign kept."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)                      # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, min_exp)          # floor(log2 a), at least min_exp
+    q = np.exp2(e - mbits)                   # spacing in that binade
+    r = np.minimum(np.rint(a / q) * q, vmax)
+    return np.where(v < 0, -r, r)
+
+
+def round_e4m3(v):
+    return _round_to_grid(v, -6, 3, E4M3_MAX).astype(np.float32)
+
+
+def round_e2m1(v):
+    return _round_to_grid(v, 0, 1, E2M1_MAX).astype(np.float32)
+
+
+def quant_nvfp4(x: np.ndarray, gscale: float):
+    """NVFP4 quantisation of float32 rows [..., K] with tensor scale G.
+
+    Per group of 16: amax = max |x|; s = E4M3(amax / (6 G)); the codes are
+    E2M1(x / (s G)) (all zero when s = 0).  Each step is one float32
+    operation (6 G, then the division; s G, then the division), as written.
+    Returns the group scales s [..., K/16] and the values q * s [..., K],
+    both exact in float32 (and in bf16).
+    """
+    xf = np.asarray(x, dtype=np.float32)
+    K = xf.shape[-1]
+    g = xf.reshape(xf.shape[:-1] + (K // NVFP4_GROUP, NVFP4_GROUP))
+    G = np.float32(gscale)
+    amax = np.abs(g).max(axis=-1)
+    s = round_e4m3(amax / (np.float32(6.0) * G))
+    sg = (s * G).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(sg[..., None] > 0, g / sg[..., None], np.float32(0.0)).astype(np.float32)
+    q = round_e2m1(t)
+    return s, (q * s[..., None]).reshape(xf.shape).astype(np.float32)
+
+
+def unpack_e2m1_fields(words: np.ndarray) -> np.ndarray:
+    """NVFP4 weight words [..., K/8] -> 4-bit codes [..., K] (field i of word w is K index 8w + i)."""
+    w = np.ascontiguousarray(words, dtype=np.uint32)
+    f = np.stack([(w >> np.uint32(4 * i)) & np.uint32(15) for i in range(8)], axis=-1)
+    return f.reshape(w.shape[:-1] + (w.shape[-1] * 8,)).astype(np.uint8)
+
+
+def dequantize_nvfp4(words: np.ndarray, bscales: np.ndarray) -> np.ndarray:
+    """One NVFP4 weight matrix without its tensor scale: e2m1(code) * e4m3(s) [N, K], exact."""
+    v = e2m1_value(unpack_e2m1_fields(words))
+    s = e4m3_value(bscales)
+    return (v * np.repeat(s, NVFP4_GROUP, axis=-1)).astype(np.float32)
+
+
+def expert_ffn_nvfp4(x, offsets, sorted_rows, k: int, weights: dict, I: int, x_gscale: float, h_gscale: float,
+                     experts=None, dtype=np.float32) -> np.ndarray:
+    """O7 for NVFP4 W4A4: y_perm [T*k, H].
+
+    For expert e with rows R (tokens R // k):
+        X' = NVFP4(x rows, G_x)                  (activation quantisation)
+        A  = (X' W13'^T) * (G_x * G_w13[e])      (W' = e2m1 * e4m3 group scale)
+        h  = silu(A[:, :I]) * A[:, I:]
+        H' = NVFP4(h, G_h)
+        Y  = (H' W2'^T) * (G_h * G_w2[e])
+    """
+    xf = bf16_to_f32(x).astype(np.float32)
+    T, H = xf.shape
+    E = offsets.size - 1
+    y = np.full((sorted_rows.size, H), np.nan, dtype=dtype)
+    gx, gh = np.float32(x_gscale), np.float32(h_gscale)
+    for e in (range(E) if experts is None else experts):
+        o0, o1 = int(offsets[e]), int(offsets[e + 1])
+        if o1 == o0:
+            continue
+        _, Xq = quant_nvfp4(xf[sorted_rows[o0:o1] // k], gx)
+        W13 = dequantize_nvfp4(weights["w13_codes"][e], weights["w13_scales"][e]).astype(dtype)
+        A = (Xq.astype(dtype) @ W13.T) * dtype(gx * np.float32(weights["w13_gscale"][e]))
+        h = (silu(A[:, :I]) * A[:, I:]).astype(np.float32)
+        _, Hq = quant_nvfp4(h, gh)
+        W2 = dequantize_nvfp4(weights["w2_codes"][e], weights["w2_scales"][e]).astype(dtype)
+        y[o0:o1] = (Hq.astype(dtype) @ W2.T) * dtype(gh * np.float32(weights["w2_gscale"][e]))
+    return y
+
+
+def moe_layer_nvfp4(x, w_router, logit_bias, weights, k: int, I: int, x_gscale: float, h_gscale: float,
+                    dtype=np.float32) -> dict:
+    """O1..O8 with NVFP4 W4A4 experts."""
+    E = w_router.shape[0]
+    logits = router_logits(x, w_router, logit_bias)
+    ids, gates = topk_softmax(logits, k)
+    offsets, sorted_rows, row_pos, active = permute(ids, E)
+    y_perm = expert_ffn_nvfp4(x, offsets, sorted_rows, k, weights, I, x_gscale, h_gscale, dtype=dtype)
+    y = combine(y_perm, row_pos, gates)
+    return dict(logits=logits, ids=ids, gates=gates, offsets=offsets, sorted_rows=sorted_rows,
+                row_pos=row_pos, active=active, y_perm=y_perm, y=y)

@@ -268,6 +268,89 @@ def test_fp6_random_rows_against_bitwise_reader():
         assert fields[n].tolist() == [(stream >> (6 * k)) & 63 for k in range(128)]
 
 
+# ------------------------------------------------------------------ NVFP4
+def _golden_nvfp4():
+    rows = {"e2m1": [], "e4m3": [], "r2": [], "r8": []}
+    for line in open(os.path.join(GOLDEN, "nvfp4.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            t, a, b = line.split()
+            rows[t].append((int(a, 0) if t in ("e2m1", "e4m3") else float(a), float(b)))
+    return rows
+
+
+def test_nvfp4_codes_and_rounding_match_hand_written_values():
+    g = _golden_nvfp4()
+    assert len(g["e2m1"]) == 16 and len(g["e4m3"]) >= 8
+    for c, v in g["e2m1"]:
+        got = float(oracle.e2m1_value(np.array([c]))[0])
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), c
+    for c, v in g["e4m3"]:
+        assert float(oracle.e4m3_value(np.array([c]))[0]) == v, hex(c)
+    for a, b in g["r2"]:
+        assert float(oracle.round_e2m1(np.array([a]))[0]) == b, a
+    for a, b in g["r8"]:
+        assert float(oracle.round_e4m3(np.array([a]))[0]) == b, a
+
+
+def test_nvfp4_rounding_lands_on_the_grids_and_is_nearest():
+    """Brute force: every rounding result is a grid value, and no grid value is nearer."""
+    rng = np.random.default_rng(41)
+    grid2 = np.unique(np.abs(oracle.e2m1_value(np.arange(16))))
+    grid8 = np.unique(oracle.e4m3_value(np.arange(0x7F)))
+    for grid, fn, hi in ((grid2, oracle.round_e2m1, 6.0), (grid8, oracle.round_e4m3, 448.0)):
+        v = np.abs(rng.standard_normal(4000)).astype(np.float32) * np.float32(hi / 3)
+        r = fn(v)
+        assert np.isin(r, grid).all()
+        d = np.abs(v[:, None].astype(np.float64) - grid[None, :])
+        best = d.min(axis=1)
+        assert np.all(np.abs(v - r) <= best + 1e-12)
+
+
+def test_nvfp4_quantiser_properties():
+    """Group scale from the group maximum; values exact multiples of it; zero
+    groups stay zero; a group already on the grid comes back as its codes times
+    its scale (the tensor scale is applied after the product)."""
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((5, 64)).astype(np.float32)
+    x[2, 16:32] = 0.0
+    G = 2.0 ** -8
+    s, xq = oracle.quant_nvfp4(x, G)
+    assert s.shape == (5, 4) and xq.shape == x.shape
+    assert np.all(s[2, 1] == 0) and not xq[2, 16:32].any()
+    grid = np.unique(np.abs(oracle.e2m1_value(np.arange(16))))
+    ratio = np.abs(xq.reshape(5, 4, 16)) / np.where(s > 0, s, 1)[..., None]
+    assert np.isin(ratio, grid).all()
+    amax = np.abs(x.reshape(5, 4, 16)).max(-1)
+    assert np.allclose(s[s > 0], (amax / (6 * G))[s > 0], rtol=2 ** -4)
+    # a group already on the grid with scale exactly amax / (6 G) quantises to itself
+    y = np.zeros((1, 16), np.float32)
+    y[0, :8] = np.array([6, -6, 4, 3, 2, 1.5, 1, 0.5], np.float32) * np.float32(G)
+    assert np.array_equal(oracle.quant_nvfp4(y, G)[1], y / np.float32(G))
+
+
+def test_nvfp4_dequant_and_ffn_closed_form():
+    """Weights e2m1 code 2 (1.0) with scale code 0x38 (1.0) and tensor scale 1:
+    every weight is 1; with x quantising to itself the FFN has a closed form."""
+    words = np.full((3, 4), 0x22222222, np.uint32)               # K = 32
+    W = oracle.dequantize_nvfp4(words, np.full((3, 2), 0x38, np.uint8))
+    assert np.array_equal(W, np.ones((3, 32), np.float32))
+    E, H, I = 2, 32, 16
+    wt = {"w13_codes": np.full((E, 2 * I, H // 8), 0x22222222, np.uint32),
+          "w13_scales": np.full((E, 2 * I, H // 16), 0x38, np.uint8), "w13_gscale": np.ones(E, np.float32),
+          "w2_codes": np.full((E, H, I // 8), 0x22222222, np.uint32),
+          "w2_scales": np.full((E, H, I // 16), 0x38, np.uint8), "w2_gscale": np.ones(E, np.float32)}
+    G = 2.0 ** -8
+    x = np.zeros((1, H), np.float32)
+    x[0, :2] = np.float32(6 * G)                                 # groups quantise to themselves
+    off = np.array([0, 1, 1], np.int32)
+    y = oracle.expert_ffn_nvfp4(_bf16(x), off, np.array([0], np.int32), 1, wt, I, G, G)
+    S = 12 * G
+    h = S / (1 + np.exp(-S)) * S
+    _, hq = oracle.quant_nvfp4(np.full((1, I), h, np.float32), G)
+    assert np.allclose(y[0], hq.sum() * G * np.ones(H), rtol=1e-6)
+
+
 def test_dequant_exact_against_integer_arithmetic():
     """(q - z) * s is exact: compare with exact rationals."""
     from fractions import Fraction

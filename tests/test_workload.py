@@ -30,6 +30,8 @@ def test_shapes_and_determinism(name):
     w = a.weights
     assert w["w13_codes"].shape == (small.E, 2 * small.I, nw(small.H))
     assert w["w13_scales"].shape == (small.E, 2 * small.I, small.H // small.group)
+    if small.nvfp4:
+        assert w["w13_scales"].dtype == np.uint8 and w["w13_gscale"].shape == (small.E,)
     assert w["w2_codes"].shape == (small.E, small.H, nw(small.I))
     assert w["w2_scales"].shape == (small.E, small.H, small.I // small.group)
     if small.bits == 2:

@@ -68,7 +68,9 @@ class Spec:
     streams: int = 0               # ar1_streams: number of independent streams
     ar1_alpha: float = 0.85
     scale_sigma: float = 0.02      # scales are |N(0,1)| * scale_sigma
-    group: int = 128               # quantisation group along K (128 or 32)
+    group: int = 128               # quantisation group along K (128 or 32; 16 marks NVFP4)
+    nv_gx: float = 2.0 ** -8       # NVFP4: tensor scales of the activation and h quantisers
+    nv_gh: float = 2.0 ** -8
     n_sets: int = 1                # distinct weight sets cycled by the bench
     note: str = ""
 
@@ -83,8 +85,14 @@ class Spec:
         n_w = 2 * I * H + H * I                  # weights in gate_up and down
         codes = n_w * self.bits // 8
         groups = n_w // self.group
+        if self.nvfp4:
+            return codes + groups                # one E4M3 byte per group of 16
         zeros = groups if self.bits == 2 else 0
         return codes + 2 * groups + zeros
+
+    @property
+    def nvfp4(self) -> bool:
+        return self.bits == 4 and self.group == 16
 
 
 SPECS: Dict[str, Spec] = {
@@ -125,6 +133,11 @@ SPECS: Dict[str, Spec] = {
         Spec("prefill_t4096_h4096_e256_k8_i1024_fp6", T=4096, H=4096, E=256, k=8, I=1024, bits=6,
              seed=1012, zipf_s=1.1,
              note="prefill chunk, fp6 e2m3 experts, Zipf(1.1) log-prior"),
+        Spec("decode_t1_h4096_e256_k8_i1024_nvfp4", T=1, H=4096, E=256, k=8, I=1024, bits=4, group=16,
+             seed=1013, router_law="uniform", n_sets=8,
+             note="batch-1 decode, NVFP4 W4A4 experts (E2M1, E4M3 scales per 16, tensor scales)"),
+        Spec("prefill_t4096_h4096_e256_k8_i1024_nvfp4", T=4096, H=4096, E=256, k=8, I=1024, bits=4, group=16,
+             seed=1014, zipf_s=1.1, note="prefill chunk, NVFP4 W4A4 experts, Zipf(1.1) log-prior"),
         Spec("mid_t64_h4096_e256_k8_i1024_int4", T=64, H=4096, E=256, k=8, I=1024, bits=4,
              seed=1006, router_law="uniform", x_law="ar1_streams", streams=16, n_sets=2,
              note="middle batch: 16 streams x 4 draft tokens (higher-concurrency verify), decode path"),
@@ -215,10 +228,27 @@ def _fp16_scales(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
     return s.astype(np.float16).view(np.uint16)
 
 
+def _nvfp4_weight_set(sp: Spec, set_idx: int) -> Dict[str, np.ndarray]:
+    """NVFP4 experts: E2M1 codes uniform over the 16 codes (uniform words, 8
+    per word along K), E4M3 group scales drawn uniformly from the codes
+    0x28..0x47 (0.25 .. 3.75), float32 tensor scales 0.004 * U(1, 1.25) per
+    expert and projection."""
+    E, H, I = sp.E, sp.H, sp.I
+    out = {}
+    for name, tc, ts, tz, (N, K) in (("w13", _TAG_W13C, _TAG_W13S, _TAG_W13Z, (2 * I, H)),
+                                     ("w2", _TAG_W2C, _TAG_W2S, _TAG_W2Z, (H, I))):
+        out[f"{name}_codes"] = _uniform_words(_rng(sp.seed, tc, set_idx), (E, N, K // 8))
+        out[f"{name}_scales"] = _rng(sp.seed, ts, set_idx).integers(0x28, 0x48, size=(E, N, K // 16), dtype=np.uint8)
+        out[f"{name}_gscale"] = (0.004 * _rng(sp.seed, tz, set_idx).uniform(1.0, 1.25, size=E)).astype(np.float32)
+    return out
+
+
 def make_weight_set(sp: Spec, set_idx: int = 0) -> Dict[str, np.ndarray]:
     """One full layer of expert weights in the packed formats described above."""
     E, H, I, G = sp.E, sp.H, sp.I, sp.group
     nw = sp.words_per_row
+    if sp.nvfp4:
+        return _nvfp4_weight_set(sp, set_idx)
     if H % GROUP or I % GROUP:
         raise ValueError("H and I must be multiples of 128")
     if G not in (32, 128) or (G == 32 and sp.bits in (2, 6)):
