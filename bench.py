@@ -185,7 +185,8 @@ class Plan:
         self.y_perm = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.ws_route = torch.zeros(self.L.moe_route_permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
-        self.ws_ffn = torch.zeros(self.L.moe_expert_ffn_workspace_size(T, k, E, H, I), dtype=torch.uint8, device=dev)
+        ffn_ws = (self.L.moe_expert_ffn_nvfp4_workspace_size if sp.nvfp4 else self.L.moe_expert_ffn_workspace_size)
+        self.ws_ffn = torch.zeros(ffn_ws(T, k, E, H, I), dtype=torch.uint8, device=dev)
         self.ws_layer = (torch.zeros(self.L.moe_layer_workspace_size(T, k, E, H, I), dtype=torch.uint8, device=dev)
                          if fused else None)
         self.torch = torch
@@ -209,7 +210,12 @@ class Plan:
         w = st["w"]
         common = (st["x"].data_ptr(), st["offsets"].data_ptr(), st["sorted_rows"].data_ptr(), st["active"].data_ptr(),
                   sp.T, sp.k, sp.E, sp.H, sp.I)
-        if self.experts != "arrays":
+        if sp.nvfp4:
+            s = L.moe_expert_ffn_nvfp4(*common, sp.nv_gx, sp.nv_gh, w["w13_codes"].data_ptr(),
+                                       w["w13_scales"].data_ptr(), w["w13_gscale"].data_ptr(), w["w2_codes"].data_ptr(),
+                                       w["w2_scales"].data_ptr(), w["w2_gscale"].data_ptr(), self.y_perm.data_ptr(),
+                                       self.ws_ffn.data_ptr(), self.ws_ffn.numel(), stream)
+        elif self.experts != "arrays":
             fn = L.moe_expert_ffn_w4a16_table if sp.bits == 4 else L.moe_expert_ffn_w2a16_table
             s = fn(*common, st["table"].data_ptr(), self.y_perm.data_ptr(), self.ws_ffn.data_ptr(),
                    self.ws_ffn.numel(), stream)
@@ -303,6 +309,9 @@ def main():
     # the one-launch layer takes INT4 and 2-bit with groups of 128 from stacked arrays
     fused = (sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays" and sp.bits in (2, 4)
              and sp.group == 128)
+    if args.experts != "arrays" and sp.nvfp4:
+        print(json.dumps({"error": "NVFP4 experts take stacked arrays"}))
+        sys.exit(2)
     plan = Plan(sp, dev, fused=fused, experts=args.experts)
     nset = plan.n_sets
     stream = torch.cuda.Stream(dev)
@@ -381,7 +390,9 @@ def main():
     distinct = [int(st["active"][0].item()) for st in plan.sets]
     mean_distinct = sum(distinct) / len(distinct)
     bpe = sp.weight_bytes_per_expert()
-    decode = sp.T <= 512 and sp.T * sp.k <= 6 * sp.E   # the library's decode-path dispatch (HBM-bound)
+    # the library's decode-path dispatch (HBM-bound); NVFP4 always runs the
+    # grouped GEMMs, and is rated on weight bytes at the same batch sizes
+    decode = sp.T <= 512 and sp.T * sp.k <= 6 * sp.E
     ffn_stage = None
     if decode and args.experts == "host":
         alg = mean_distinct * bpe
@@ -398,7 +409,8 @@ def main():
         ffn_stage = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(sp.name, "decode") if args.experts == "arrays" else None,
-                     "kernel": "ffn_decode_kernel (expert-FFN stage: gate_up+SwiGLU+down GEMV)",
+                     "kernel": ("NVFP4 expert FFN (quant_nvfp4_kernel, ffn_gemm_kernel<4, 16, ...> x2)" if sp.nvfp4
+                                else "ffn_decode_kernel (expert-FFN stage: gate_up+SwiGLU+down GEMV)"),
                      "algorithmic_bytes_per_launch": int(alg), "avg_launch_us": round(ffn_ms * 1e3, 3),
                      "distinct_experts_per_launch": mean_distinct}
         roof = ffn_stage
@@ -425,7 +437,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": sp.name, "T": sp.T, "H": sp.H, "E": sp.E, "top_k": sp.k, "I": sp.I,
-                   "weight_format": ("fp6 e2m3 g128 (fp16 scales)" if sp.bits == 6 else
+                   "weight_format": ("nvfp4 w4a4 (e2m1, e4m3 scales per 16)" if sp.nvfp4 else
+                                     "fp6 e2m3 g128 (fp16 scales)" if sp.bits == 6 else
                                      f"int{sp.bits} g{sp.group}" + (" + zero-point" if sp.bits == 2 else " sym")),
                    "weight_sets_cycled": nset, "experts": args.experts, "launch": f"hip graph of {nset} steps (one per weight set)" if use_graph else "eager",
                    "step": "moe_layer (one launch)" if fused else "stage calls",

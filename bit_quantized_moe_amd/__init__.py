@@ -20,6 +20,7 @@ import torch
 
 __all__ = [
     "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "expert_table", "expert_ffn_table",
+    "expert_ffn_nvfp4", "quant_act_nvfp4",
     "layer", "combine", "unpack_codes",
     "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH",
 ]
@@ -42,6 +43,10 @@ _SIGS = {
     "moe_expert_ffn_w4a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 5 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 7 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_wna16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 7 + [_vp] * 6 + [_vp, _vp, _c_size, _vp]),
+    "moe_expert_ffn_nvfp4_workspace_size": (_c_size, [_c_int] * 5),
+    "moe_expert_ffn_nvfp4": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [ctypes.c_float] * 2 + [_vp] * 6
+                             + [_vp, _vp, _c_size, _vp]),
+    "moe_quant_act_nvfp4": (_c_int, [_vp, _c_i64, ctypes.c_float, _vp, _vp, _vp]),
     "moe_expert_ffn_w4a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
     "moe_device_address": (_c_int, [_vp, ctypes.POINTER(ctypes.c_uint64)]),
@@ -285,6 +290,35 @@ def expert_ffn_table(x: torch.Tensor, offsets, sorted_rows, active, k: int, tabl
     s = getattr(L, name)(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I, tab_ptr, _p(y_perm),
                          _p(w), w.numel(), _stream(dev))
     _check(s, name)
+    return y_perm
+
+
+def quant_act_nvfp4(x: torch.Tensor, gscale: float, want_scales: bool = False):
+    """NVFP4 activation quantiser: bf16 q * s of each value (and the E4M3 group-scale codes)."""
+    dev = _dev(x)
+    vals = torch.empty_like(x, dtype=torch.bfloat16)
+    sc = torch.empty(x.numel() // 16, dtype=torch.uint8, device=dev) if want_scales else None
+    _check(lib().moe_quant_act_nvfp4(_p(x), x.numel(), float(gscale), _p(vals), _p(sc), _stream(dev)),
+           "moe_quant_act_nvfp4")
+    return (vals, sc) if want_scales else vals
+
+
+def expert_ffn_nvfp4(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: Dict[str, torch.Tensor], I: int,
+                     x_gscale: float, h_gscale: float, ws: Optional[Workspaces] = None,
+                     y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Expert FFN with NVFP4 W4A4 experts (weights: *_codes, *_scales (E4M3 uint8), *_gscale (float32 [E]))."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = offsets.numel() - 1
+    if y_perm is None:
+        y_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    L = lib()
+    w = (ws or Workspaces(dev)).get("ffn_nvfp4", L.moe_expert_ffn_nvfp4_workspace_size(T, k, E, H, I))
+    _check(L.moe_expert_ffn_nvfp4(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I, float(x_gscale),
+                                  float(h_gscale), _p(weights["w13_codes"]), _p(weights["w13_scales"]),
+                                  _p(weights["w13_gscale"]), _p(weights["w2_codes"]), _p(weights["w2_scales"]),
+                                  _p(weights["w2_gscale"]), _p(y_perm), _p(w), w.numel(), _stream(dev)),
+           "moe_expert_ffn_nvfp4")
     return y_perm
 
 

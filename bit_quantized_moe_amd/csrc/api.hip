@@ -70,6 +70,11 @@ hipError_t current_device_info(DeviceInfo *out) {
   return hipSuccess;
 }
 
+// NVFP4 (always the grouped GEMMs): control block, bf16 h, the quantised activations
+static size_t ffn_nvfp4_workspace_bytes(int T, int k, int E, int H, int I) {
+  return round_up(ffn_ctl_bytes(T, k, E) + ((size_t)T * k * I + (size_t)T * H) * sizeof(uint16_t), 256);
+}
+
 size_t ffn_workspace_bytes(int T, int k, int E, int H, int I) {
   (void)E;
   (void)H;
@@ -262,6 +267,61 @@ moe_status moe_expert_ffn_wna16(const uint16_t *x, const int32_t *expert_offsets
   return expert_ffn("moe_expert_ffn_wna16", bits, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
                     w13_scales, bits == 2 ? w13_zeros : nullptr, w2_codes, w2_scales, bits == 2 ? w2_zeros : nullptr,
                     y_perm, workspace, workspace_bytes, stream, nullptr, group_size);
+}
+
+size_t moe_expert_ffn_nvfp4_workspace_size(int T, int k, int E, int H, int I) {
+  if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return 0;
+  return ffn_nvfp4_workspace_bytes(T, k, E, H, I);
+}
+
+moe_status moe_expert_ffn_nvfp4(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                const int32_t *active, int T, int k, int E, int H, int I, float x_gscale,
+                                float h_gscale, const uint32_t *w13_codes, const uint8_t *w13_scales,
+                                const float *w13_gscale, const uint32_t *w2_codes, const uint8_t *w2_scales,
+                                const float *w2_gscale, uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  const char *name = "moe_expert_ffn_nvfp4";
+  moe_status s = check_common_moe(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
+  if (!x || !expert_offsets || !sorted_rows || !active || !y_perm || !workspace || !w13_codes || !w13_scales ||
+      !w13_gscale || !w2_codes || !w2_scales || !w2_gscale)
+    return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+  if (!(x_gscale > 0.f) || !(h_gscale > 0.f) || x_gscale > 3.0e38f || h_gscale > 3.0e38f)
+    return fail(MOE_ERR_INVALID_ARG, "%s: the tensor scales must be positive and finite", name);
+  if (!aligned(x, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16))
+    return fail(MOE_ERR_MISALIGNED, "%s: x and code arrays need 16-byte alignment", name);
+  if (!aligned(w13_scales, 2) || !aligned(w2_scales, 2) || !aligned(w13_gscale, 4) || !aligned(w2_gscale, 4) ||
+      !aligned(y_perm, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_rows, 4) || !aligned(active, 4))
+    return fail(MOE_ERR_MISALIGNED, "%s: array alignment", name);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
+  const size_t need = ffn_nvfp4_workspace_bytes(T, k, E, H, I);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", name, workspace_bytes, need);
+  if (T == 0) return MOE_OK;
+  if ((long long)T * H > (1LL << 30) || (long long)I * H > (1LL << 30))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: T*H and I*H must be <= 2^30 (T=%d)", name, T);
+  DeviceInfo dev;
+  hipError_t he = current_device_info(&dev);
+  if (he != hipSuccess) return from_hip(he, name);
+  FfnArgs a{x, expert_offsets, sorted_rows, active, T, k, E, H, I, 4, w13_codes, (const uint16_t *)w13_scales, nullptr,
+            w2_codes, (const uint16_t *)w2_scales, nullptr, y_perm, workspace, nullptr, 16};
+  a.nvfp4 = true;
+  a.w13_g = w13_gscale;
+  a.w2_g = w2_gscale;
+  a.gx = x_gscale;
+  a.gh = h_gscale;
+  return from_hip(launch_ffn_prefill(a, dev, (hipStream_t)stream), name);
+}
+
+moe_status moe_quant_act_nvfp4(const uint16_t *x, int64_t n, float gscale, uint16_t *values, uint8_t *scales,
+                               void *stream) {
+  if (n < 0 || n % 16) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "moe_quant_act_nvfp4: n must be a multiple of 16");
+  if (!x || !values) return fail(MOE_ERR_INVALID_ARG, "moe_quant_act_nvfp4: x and values are required");
+  if (!(gscale > 0.f) || gscale > 3.0e38f) return fail(MOE_ERR_INVALID_ARG, "moe_quant_act_nvfp4: bad tensor scale");
+  if (!aligned(x, 16) || !aligned(values, 16)) return fail(MOE_ERR_MISALIGNED, "moe_quant_act_nvfp4: 16-byte alignment");
+  if (n == 0) return MOE_OK;
+  return from_hip(launch_quant_nvfp4(x, n, gscale, values, scales, (hipStream_t)stream), "moe_quant_act_nvfp4");
 }
 
 moe_status moe_expert_ffn_w4a16_table(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,

@@ -106,6 +106,54 @@ __device__ __forceinline__ float fp16_to_f32(uint32_t h16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
 }
 
+// ---------------------------------------------------------------- NVFP4
+// E2M1 elements in groups of 16 with an FP8 E4M3 scale per group and a
+// float32 tensor scale.  Rounding to either grid is to nearest, ties to even
+// (rintf), with saturation; powers of two are applied with ldexp, so every
+// step other than the rint is exact.
+__device__ __forceinline__ int floor_log2_f32(float v) {  // v >= 0; zero and denormals give <= -127
+  return (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;
+}
+// v >= 0 to the E4M3 grid (3 mantissa bits, smallest binade 2^-6, max 448)
+__device__ __forceinline__ float round_e4m3(float v) {
+  const int e = max(floor_log2_f32(v), -6);
+  const float q = __builtin_ldexpf(1.f, e - 3);
+  return fminf(__builtin_rintf(v / q) * q, 448.f);
+}
+// v to the E2M1 grid (1 mantissa bit, smallest binade 2^0, max 6), sign kept
+__device__ __forceinline__ float round_e2m1(float v) {
+  const float a = fabsf(v);
+  const int e = max(floor_log2_f32(a), 0);
+  const float q = __builtin_ldexpf(1.f, e - 1);
+  return copysignf(fminf(__builtin_rintf(a / q) * q, 6.f), v);
+}
+// E4M3 code (sign ignored: scales are positive) -> its value
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+// an E4M3 grid value (>= 0) -> its code
+__device__ __forceinline__ uint32_t f32_to_e4m3_code(float r) {
+  if (r < 0.015625f) return (uint32_t)(r * 512.f);  // subnormal: m * 2^-9
+  const uint32_t b = __float_as_uint(r);
+  return ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
+}
+// Eight E2M1 codes of w (K order) times the group scale s -> four bf16 pairs,
+// exact (2 x 4 significant bits).  The magnitudes come from a byte table
+// (2|v| = 0 1 2 3 4 6 8 12) indexed with v_perm.
+__device__ __forceinline__ void dequant8_e2m1(uint32_t w, float s, uint32_t out[4]) {
+  const float hs = 0.5f * s;
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // fields 0 2 4 6 / 1 3 5 7
+  const uint32_t mlo = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, lo & 0x07070707u);
+  const uint32_t mhi = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, hi & 0x07070707u);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float f0 = (float)((mlo >> (8 * b)) & 0xFFu) * hs, f1 = (float)((mhi >> (8 * b)) & 0xFFu) * hs;
+    const float v0 = ((lo >> (8 * b)) & 8u) ? -f0 : f0, v1 = ((hi >> (8 * b)) & 8u) ? -f1 : f1;
+    out[b] = pack_bf16x2(v0, v1);
+  }
+}
+
 // Natural-order bf16 activations d (pairs (x0,x1), (x2,x3), ...) -> the pair
 // order of the unpacked codes: o[i] = (x[ord[2i]], x[ord[2i+1]]).  N elements.
 template <int N>

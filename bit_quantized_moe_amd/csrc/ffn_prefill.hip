@@ -15,7 +15,8 @@
 //    host launches an upper bound of M-tile slots and surplus blocks exit;
 //  * A rows (gathered activations for G1, contiguous h rows for G2) and the B
 //    tile, dequantised once per block to bf16 (q - z) * s (INT4, 2-bit, INT8
-//    or FP6 e2m3 codes; one scale per 128 or per 32 K), go through two LDS
+//    or FP6 e2m3 codes; one scale per 128 or per 32 K; NVFP4: E2M1 codes with
+//    an E4M3 scale per 16 K, exact in bf16), go through two LDS
 //    buffers with an XOR swizzle of 16-byte chunks, so both the staging
 //    writes and the MFMA operand reads are free of bank conflicts;
 //  * 4 waves in a 2 x 2 arrangement each own a 64 x 64 sub-tile computed with
@@ -52,7 +53,23 @@ struct GemmParams {
   const uint64_t *tab;     // per-expert address table or null; this GEMM's entries start at tab_off
   int tab_off;
   int n_blocks;            // N tiles: I / 64 (G1) or H / BN (G2)
+  // NVFP4: per-expert float32 tensor scales of the weights, the tensor scale
+  // of this GEMM's (quantised) A operand, and G1's h quantiser scale
+  const float *gscale;
+  float act_g, out_g;
 };
+
+// NVFP4 quantisation of a group of 16 h values held by 16 consecutive lanes
+// (one value each): the group maximum through xor shuffles inside the 16
+// lanes, then the steps of the activation quantiser.  Returns q * s.
+__device__ __forceinline__ float quant16_lanes(float hv, float G) {
+  float amax = fabsf(hv);
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+  const float s = round_e4m3(amax / (6.f * G));
+  const float sg = s * G;
+  return (sg > 0.f ? round_e2m1(hv / sg) : 0.f) * s;
+}
 
 // LDS position of 16-byte chunk `chunk` of tile row `row`.  Eight lanes that
 // read (or write) the same chunk of eight consecutive rows, or eight chunks
@@ -111,7 +128,7 @@ using IntC = std::integral_constant<int, N>;
 
 // S: K tiles held in registers ahead of LDS (K / BK must be a multiple of S).
 // GS: quantisation group along K, 128 or 32 (a thread's 32 K of a tile then
-// form one group).
+// form one group); 16 with BITS = 4 is NVFP4 (a thread's 32 K hold two groups).
 template <int BITS, int GS, bool GATEUP, int S>
 __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   // two LDS buffers, each an A tile then a B tile (BM and BN rows of BK bf16)
@@ -124,6 +141,7 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   const int mslot = (local / p.n_blocks) * 8 + xcd;
   int e, m0, rows;
   if (!find_tile(p, mslot, &e, &m0, &rows)) return;
+  constexpr bool NV = GS == 16;
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -166,17 +184,20 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   const size_t erow0 = (size_t)e * p.n_rows_w;          // the expert's first weight row
   const uint64_t *te = p.tab ? p.tab + (size_t)e * kTabStride + p.tab_off : nullptr;
   const uint32_t *e_codes = te ? (const uint32_t *)sload(te) : p.codes + erow0 * wpr;
-  const uint16_t *e_scales = te ? (const uint16_t *)sload(te + 1) : p.scales + erow0 * gpr;
+  // NVFP4 scales are single bytes
+  const uint16_t *e_scales = te ? (const uint16_t *)sload(te + 1)
+                                : (NV ? (const uint16_t *)((const uint8_t *)p.scales + erow0 * gpr) : p.scales + erow0 * gpr);
   const uint8_t *e_zeros = te ? (const uint8_t *)sload(te + 2) : (BITS == 2 ? p.zeros + erow0 * gpr : p.zeros);
   const __amdgpu_buffer_rsrc_t b_rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)e_codes, (short)0, p.n_rows_w * wpr * 4, kBufWord3);
   const __amdgpu_buffer_rsrc_t s_rs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)e_scales, (short)0, p.n_rows_w * gpr * 2, kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)e_scales, (short)0, p.n_rows_w * gpr * (NV ? 1 : 2), kBufWord3);
   const __amdgpu_buffer_rsrc_t z_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)e_zeros, (short)0, BITS == 2 ? p.n_rows_w * gpr : 0, kBufWord3);
   const uint32_t b_off = (uint32_t)(wrow * wpr + bh * WPL) * 4u;  // bytes
-  // elements; with GS = 32 the thread's half of a tile is group 2 kt + bh
-  const uint32_t s_off = (uint32_t)(wrow * gpr) + (GS == 32 ? bh : 0);
+  // elements; with GS = 32 the thread's half of a tile is group 2 kt + bh,
+  // with NVFP4 groups 4 kt + 2 bh and + 1
+  const uint32_t s_off = (uint32_t)(wrow * gpr) + (GS == 32 ? bh : NV ? 2 * bh : 0);
 
   // ---- pipeline: one barrier per K tile.  While the MFMAs read buffer kt & 1,
   // tile kt + 1 is dequantised into the other buffer and tile kt + 1 + S is
@@ -224,13 +245,26 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
         b_st[s][0] = v[0];
         b_st[s][1] = v[1];
       }
-      sc_st[s] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off * 2u, GS == 32 ? kt * 4 : (kt / 2) * 2, 0);
+      if constexpr (NV)
+        sc_st[s] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off, kt * 4, 0);  // two E4M3 bytes
+      else
+        sc_st[s] = __builtin_amdgcn_raw_buffer_load_b16(s_rs, s_off * 2u, GS == 32 ? kt * 4 : (kt / 2) * 2, 0);
       if constexpr (BITS == 2) z_st[s] = __builtin_amdgcn_raw_buffer_load_b8(z_rs, s_off, kt / 2, 0);
     };
     auto store_tile = [&](int s, uint8_t *buf) {
   #pragma unroll
       for (int j = 0; j < 4; ++j) *(u32x4 *)(buf + swz(ar + 32 * j, ac)) = a_st[s][j];
       uint8_t *bb = buf + kTileBytes;
+      if constexpr (NV) {  // words 0, 1: the first group of 16, words 2, 3: the second
+        const float s0 = e4m3_to_f32(sc_st[s] & 0xFFu), s1 = e4m3_to_f32((sc_st[s] >> 8) & 0xFFu);
+  #pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t o[4];
+          dequant8_e2m1(b_st[s][w], w < 2 ? s0 : s1, o);
+          *(u32x4 *)(bb + swz(br, bh * 4 + w)) = u32x4{o[0], o[1], o[2], o[3]};
+        }
+        return;
+      }
       const float sc = BITS == 6 ? fp16_to_f32(sc_st[s]) : bf16_to_f32(sc_st[s]);
       const float zs = -((BITS == 4) ? 8.f : BITS == 8 ? 128.f : BITS == 6 ? 0.f : (float)z_st[s]) * sc;
       if constexpr (BITS == 6) {
@@ -305,6 +339,9 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
       }
     }
     // ---- epilogue: C[m][n] of (mi, ni, r) is m = 4*(lane/16) + r, n = lane % 16
+    // NVFP4: the products carry the A and weight tensor scales; G1 quantises h
+    // in groups of 16 columns (the 16 lanes of one m)
+    const float osc = NV ? p.act_g * sload(p.gscale + e) : 1.f;
 #pragma unroll
     for (int mi = 0; mi < MV; ++mi)
 #pragma unroll
@@ -315,8 +352,9 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
         if (GATEUP) {
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni) {
-            const float g = acc[mi][ni][r], u = acc[mi][ni + 2][r];
-            const float hv = g / (1.f + __expf(-g)) * u;
+            const float g = acc[mi][ni][r] * osc, u = acc[mi][ni + 2][r] * osc;
+            float hv = g / (1.f + __expf(-g)) * u;
+            if constexpr (NV) hv = quant16_lanes(hv, p.out_g);
             const int col = nb * 64 + wn * 32 + ni * 16 + lane % 16;
             p.out[orow * p.I + col] = f32_to_bf16(hv);
           }
@@ -324,7 +362,7 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni) {
             const int col = nb * BN + wn * 64 + ni * 16 + lane % 16;
-            p.out[orow * p.H + col] = f32_to_bf16(acc[mi][ni][r]);
+            p.out[orow * p.H + col] = f32_to_bf16(acc[mi][ni][r] * osc);
           }
         }
       }
@@ -372,6 +410,16 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   g1.n_rows_w = 2 * a.I;
   g1.tab = a.tab;
   g1.tab_off = 0;
+  g1.gscale = a.w13_g;
+  g1.act_g = a.gx;
+  g1.out_g = a.gh;
+  // NVFP4: the quantised activations (q * s, bf16) follow h in the workspace
+  uint16_t *xq = hbuf + (size_t)nrows * a.I;
+  if (a.nvfp4) {
+    const hipError_t e = launch_quant_nvfp4(a.x, (int64_t)a.T * a.H, a.gx, xq, nullptr, st);
+    if (e != hipSuccess) return e;
+    g1.a_src = xq;
+  }
 
   GemmParams g2 = g1;
   g2.a_src = hbuf;
@@ -382,6 +430,8 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   g2.out = a.y_perm;
   g2.n_rows_w = a.H;
   g2.tab_off = 3;
+  g2.gscale = a.w2_g;
+  g2.act_g = a.gh;
 
   g1.n_blocks = a.I / 64;
   g2.n_blocks = a.H / BN;
@@ -391,7 +441,9 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
     g1k<<<grid1, 256, 0, st>>>(g1);
     g2k<<<grid2, 256, 0, st>>>(g2);
   };
-  if (a.bits == 4 && a.group == 128)
+  if (a.nvfp4)
+    run(ffn_gemm_kernel<4, 16, true, 2>, ffn_gemm_kernel<4, 16, false, 2>);
+  else if (a.bits == 4 && a.group == 128)
     run(ffn_gemm_kernel<4, 128, true, 2>, ffn_gemm_kernel<4, 128, false, 2>);
   else if (a.bits == 4)
     run(ffn_gemm_kernel<4, 32, true, 2>, ffn_gemm_kernel<4, 32, false, 2>);
@@ -403,8 +455,9 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
     run(ffn_gemm_kernel<6, 128, true, 2>, ffn_gemm_kernel<6, 128, false, 2>);
   else
     run(ffn_gemm_kernel<2, 128, true, 2>, ffn_gemm_kernel<2, 128, false, 2>);
-  // h is T*k*I bf16 (I % 128 == 0, so a whole number of 16-byte chunks)
-  const size_t n16 = (size_t)nrows * a.I * sizeof(uint16_t) / 16;
+  // h is T*k*I bf16 (I % 128 == 0, so a whole number of 16-byte chunks),
+  // followed for NVFP4 by the T*H quantised activations
+  const size_t n16 = ((size_t)nrows * a.I + (a.nvfp4 ? (size_t)a.T * a.H : 0)) * sizeof(uint16_t) / 16;
   const size_t zb = (n16 + 255) / 256;
   zero_kernel<<<(unsigned)(zb < 2048 ? zb : 2048), 256, 0, st>>>((u32x4 *)hbuf, n16);
   return hipGetLastError();

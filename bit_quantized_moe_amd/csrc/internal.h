@@ -69,6 +69,11 @@ struct FfnArgs {
   const uint64_t *tab = nullptr;
   // quantisation group along K: 128, or 32 for the INT4 / INT8 group-32 formats
   int group = 128;
+  // NVFP4 W4A4 (bits 4, E2M1 codes, E4M3 scales per 16 K in the scale arrays):
+  // per-expert float32 weight tensor scales and the activation / h tensor scales
+  bool nvfp4 = false;
+  const float *w13_g = nullptr, *w2_g = nullptr;
+  float gx = 0.f, gh = 0.f;
 };
 constexpr int kTabStride = 6;
 hipError_t launch_ffn_decode(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
@@ -93,6 +98,7 @@ hipError_t launch_combine(const uint16_t *y_perm, const int32_t *row_pos, const 
 
 // unpack.hip
 hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_t *out, hipStream_t st);
+hipError_t launch_quant_nvfp4(const uint16_t *x, int64_t n, float G, uint16_t *vals, uint8_t *scales, hipStream_t st);
 hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
                                int group, int N, int K, uint16_t *out, hipStream_t st);
 

@@ -14,6 +14,8 @@
  *   moe_expert_ffn_wna16
  *                   the same for any supported format: INT4 or INT8 with
  *                   groups of 128 or 32, 2-bit or FP6 e2m3 with groups of 128
+ *   moe_expert_ffn_nvfp4 (+ moe_quant_act_nvfp4)
+ *                   the same with NVFP4 W4A4 experts (activations quantised too)
  *   moe_expert_ffn_w4a16_table / _w2a16_table
  *                   the same, each expert's weights located through a
  *                   per-expert address table
@@ -233,6 +235,40 @@ moe_status moe_expert_ffn_wna16(const uint16_t *x, const int32_t *expert_offsets
                                 const uint8_t *w2_zeros,
                                 uint16_t *y_perm, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/* moe_expert_ffn_nvfp4: the expert FFN with NVFP4 W4A4 experts (page
+ * "Qwen3.8-Flash-Next NVFP4", "Format": E2M1 values in groups of 16; the
+ * group scale is FP8 E4M3 and one float32 scale covers a tensor, as NVFP4
+ * defines them).  Weights: w13_codes [E, 2I, H/8], w2_codes [E, H, I/8] uint32
+ * with eight 4-bit E2M1 codes per word along K (field i of word w is K index
+ * 8w + i; bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa),
+ * w13_scales [E, 2I, H/16] and w2_scales [E, H, I/16] E4M3 codes (uint8, one
+ * per 16 K), w13_gscale [E] and w2_gscale [E] float32 tensor scales.  The
+ * activations are quantised on the fly (moe_quant_act_nvfp4) with tensor
+ * scale x_gscale before gate_up, and h with h_gscale before down:
+ *   a = NVFP4(x) . W13' * (x_gscale * w13_gscale[e]),  h = silu(a_gate) * a_up
+ *   y = NVFP4(h) . W2'  * (h_gscale * w2_gscale[e])
+ * with W' = e2m1 * e4m3 (exact in bf16) and float32 accumulation.  Always the
+ * grouped-GEMM path.  Workspace: moe_expert_ffn_nvfp4_workspace_size bytes,
+ * zero before the first call and left zero.  Other arguments and
+ * requirements as for moe_expert_ffn_w4a16; the scales must be positive and
+ * finite. */
+size_t moe_expert_ffn_nvfp4_workspace_size(int T, int k, int E, int H, int I);
+moe_status moe_expert_ffn_nvfp4(const uint16_t *x, const int32_t *expert_offsets,
+                                const int32_t *sorted_rows, const int32_t *active,
+                                int T, int k, int E, int H, int I, float x_gscale, float h_gscale,
+                                const uint32_t *w13_codes, const uint8_t *w13_scales, const float *w13_gscale,
+                                const uint32_t *w2_codes, const uint8_t *w2_scales, const float *w2_gscale,
+                                uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_quant_act_nvfp4: the NVFP4 activation quantiser of moe_expert_ffn_nvfp4
+ * on n bf16 values (n % 16 == 0; groups of 16 consecutive values).  Per group:
+ * amax = max |x|, s = E4M3(amax / (6 G)), q = E2M1(x / (s G)) (0 when s = 0),
+ * every rounding to nearest even and saturating (448, 6), every step one
+ * float32 operation in that order.  values [n] bf16 = q * s (exact); scales
+ * [n/16] uint8 E4M3 codes of s, or NULL. */
+moe_status moe_quant_act_nvfp4(const uint16_t *x, int64_t n, float gscale, uint16_t *values, uint8_t *scales,
+                               void *stream);
 
 /* moe_expert_ffn_w4a16_table / moe_expert_ffn_w2a16_table: the same
  * computation, with each expert's weights found through a per-expert address

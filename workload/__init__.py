@@ -70,7 +70,7 @@ class Spec:
     scale_sigma: float = 0.02      # scales are |N(0,1)| * scale_sigma
     group: int = 128               # quantisation group along K (128 or 32; 16 marks NVFP4)
     nv_gx: float = 2.0 ** -8       # NVFP4: tensor scales of the activation and h quantisers
-    nv_gh: float = 2.0 ** -8
+    nv_gh: float = 2.0 ** -7
     n_sets: int = 1                # distinct weight sets cycled by the bench
     note: str = ""
 
