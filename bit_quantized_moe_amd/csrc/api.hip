@@ -70,9 +70,13 @@ hipError_t current_device_info(DeviceInfo *out) {
   return hipSuccess;
 }
 
-// NVFP4 (always the grouped GEMMs): control block, bf16 h, the quantised activations
+// NVFP4: control block, h (tagged 32-bit words on the decode path, bf16 on
+// the grouped GEMMs), then the quantised activations (bf16)
+static size_t ffn_nvfp4_h_bytes(int T, int k, int E, int I) {
+  return (size_t)T * k * I * (decode_path(T, k, E) ? sizeof(uint32_t) : sizeof(uint16_t));
+}
 static size_t ffn_nvfp4_workspace_bytes(int T, int k, int E, int H, int I) {
-  return round_up(ffn_ctl_bytes(T, k, E) + ((size_t)T * k * I + (size_t)T * H) * sizeof(uint16_t), 256);
+  return round_up(ffn_ctl_bytes(T, k, E) + ffn_nvfp4_h_bytes(T, k, E, I) + (size_t)T * H * sizeof(uint16_t), 256);
 }
 
 size_t ffn_workspace_bytes(int T, int k, int E, int H, int I) {
@@ -311,7 +315,20 @@ moe_status moe_expert_ffn_nvfp4(const uint16_t *x, const int32_t *expert_offsets
   a.w2_g = w2_gscale;
   a.gx = x_gscale;
   a.gh = h_gscale;
-  return from_hip(launch_ffn_prefill(a, dev, (hipStream_t)stream), name);
+  const hipStream_t st = (hipStream_t)stream;
+  if (decode_path(T, k, E) && decode_layout_ok(H, I, 4, 32)) {
+    // decode path: quantise x after the h words, run the GEMV kernel on it, clear it again
+    uint16_t *xq = (uint16_t *)((char *)workspace + ffn_ctl_bytes(T, k, E) + ffn_nvfp4_h_bytes(T, k, E, I));
+    hipError_t e = launch_quant_nvfp4(x, (int64_t)T * H, x_gscale, xq, nullptr, st);
+    if (e == hipSuccess) {
+      FfnArgs d = a;
+      d.x = xq;
+      e = launch_ffn_decode(d, dev, st);
+    }
+    if (e == hipSuccess) e = launch_zero16(xq, (size_t)T * H * sizeof(uint16_t), st);
+    return from_hip(e, name);
+  }
+  return from_hip(launch_ffn_prefill(a, dev, st), name);
 }
 
 moe_status moe_quant_act_nvfp4(const uint16_t *x, int64_t n, float gscale, uint16_t *values, uint8_t *scales,

@@ -138,6 +138,18 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_code(float r) {
   const uint32_t b = __float_as_uint(r);
   return ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
 }
+// NVFP4 quantisation of a group of 16 h values held by 16 consecutive lanes
+// (one value each): the group maximum through xor shuffles inside the 16
+// lanes, then the steps of the activation quantiser.  Returns q * s.
+__device__ __forceinline__ float quant16_lanes(float hv, float G) {
+  float amax = fabsf(hv);
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+  const float s = round_e4m3(amax / (6.f * G));
+  const float sg = s * G;
+  return (sg > 0.f ? round_e2m1(hv / sg) : 0.f) * s;
+}
+
 // Eight E2M1 codes of w (K order) times the group scale s -> four bf16 pairs,
 // exact (2 x 4 significant bits).  The magnitudes come from a byte table
 // (2|v| = 0 1 2 3 4 6 8 12) indexed with v_perm.

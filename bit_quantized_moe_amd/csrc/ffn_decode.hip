@@ -66,6 +66,8 @@ struct DecodeParams {
   const uint16_t *w2s;
   const uint8_t *w2z;
   const uint64_t *tab;  // per-expert address table (kTabStride entries per expert) or null
+  const float *g13, *g2;  // NVFP4: per-expert weight tensor scales
+  float gx, gh;           // NVFP4: tensor scales of the (quantised) x and of h
   uint16_t *y_perm;
   uint32_t *hbuf;  // [T*k, I] words: kHReady | bf16 bits once written, 0 before
   int *ctl;
@@ -96,16 +98,20 @@ constexpr uint64_t kRecTag = 1ull << 63;  // tag of a written routing record wor
 
 // ---------------------------------------------------------------- formats
 // BITS: 4 (INT4, field q + 8), 2 (field u, integer zero-point), 8 (INT8,
-// field q + 128) or 6 (FP6 e2m3 codes, fp16 scales).  GS: quantisation group
-// along K, 128 or 32.  The kernels walk K in units of 128 (kGroup); a unit
-// holds 128 / GS scales per row.
+// field q + 128), 6 (FP6 e2m3 codes, fp16 scales) or 5, which stands for
+// NVFP4 (4-bit E2M1 codes with an E4M3 scale per 16 K, the scale applied to B
+// exactly; the activations arrive quantised).  GS: quantisation group along
+// K, 128 or 32 (128 for NVFP4: the kernels' unit).  The kernels walk K in
+// units of 128 (kGroup); a unit holds 128 / GS scales per row.
+template <int BITS>
+constexpr int kCodeBits = BITS == 5 ? 4 : BITS;
 template <int GS>
 constexpr int kSPU = kGroup / GS;
 // Units whose weight loads a wave keeps in flight together: 8 of INT4 or
 // 2-bit, 4 of INT8 (the same bytes); half that with groups of 32, whose four
 // scales per unit and transposed slices take registers.
 template <int BITS, int GS>
-constexpr int kCG = (BITS >= 6 ? 4 : 8) / (GS == 32 ? 2 : 1);
+constexpr int kCG = (BITS >= 5 ? 4 : 8) / (GS == 32 ? 2 : 1);
 // A scale's 16 bits as a float: fp16 for FP6, bf16 otherwise.
 template <int BITS>
 __device__ __forceinline__ float scale_f32(uint32_t b16) {
@@ -122,7 +128,7 @@ __device__ __forceinline__ float scale_f32(uint32_t b16) {
 // they are.
 template <int BITS>
 __device__ __forceinline__ void permute_chunk(const uint32_t *d, uint32_t *o) {
-  if constexpr (BITS >= 6) {
+  if constexpr (BITS >= 5) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = d[i];
   } else {
@@ -294,7 +300,7 @@ constexpr int kHPend = 4;
 // pair order of the unpacked codes, see order_pairs).
 template <int BITS>
 __device__ __forceinline__ int chunk_slot(int i) {
-  return BITS >= 6 ? i : BITS == 4 ? (i >> 1) + 4 * (i & 1) : (i >> 2) + 4 * (i & 3);
+  return BITS >= 5 ? i : BITS == 4 ? (i >> 1) + 4 * (i & 1) : (i >> 2) + 4 * (i & 3);
 }
 
 // One polling round for the wave's lowest pending unit (bit j of pend: unit
@@ -355,7 +361,7 @@ __device__ uint32_t service_h(uint32_t pend, const uint32_t *h, uint8_t *act, fl
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 template <int BITS>
 using Word = typename std::conditional<
-    BITS == 4, u32x4,
+    BITS == 4 || BITS == 5, u32x4,
     typename std::conditional<BITS == 2, u32x2, typename std::conditional<BITS == 8, u32x8, u32x6>::type>::type>::type;
 // One lane slice (FP6: 16 + 8 bytes, so that no load reaches past the slice).
 template <int BITS>
@@ -369,7 +375,7 @@ __device__ __forceinline__ Word<BITS> load_word(const uint8_t *p) {
   }
 }
 template <int BITS>
-constexpr int kGroupBytes = kGroup * BITS / 8;
+constexpr int kGroupBytes = kGroup * kCodeBits<BITS> / 8;
 
 // kCG consecutive units of one row (the lane's slices), their bf16 scales
 // (kCG * 128 / GS of them, two per word) and, for INT2, their zero-points
@@ -377,7 +383,8 @@ constexpr int kGroupBytes = kGroup * BITS / 8;
 template <int BITS, int GS>
 struct Chunk {
   Word<BITS> w[kCG<BITS, GS>];
-  uint32_t s[kCG<BITS, GS> * kSPU<GS> / 2];
+  // NVFP4: per unit the lane's two E4M3 group scales (its 32 K)
+  uint32_t s[BITS == 5 ? kCG<BITS, GS> : kCG<BITS, GS> * kSPU<GS> / 2];
   u32x2 z;
 };
 
@@ -419,7 +426,10 @@ __device__ __forceinline__ void load_chunk(const ExpertW &x, Off o, Chunk<BITS, 
   constexpr int NS = CG * kSPU<GS> / 2;  // scale words: 4 (16 bytes), 2 or 8
 #pragma unroll
   for (int c = 0; c < CG; ++c) ch.w[c] = load_word<BITS>(x.codes + o.c + c * kGroupBytes<BITS>);
-  if constexpr (NS == 2) {
+  if constexpr (BITS == 5) {  // 8 scale bytes per unit; o.s already points at the lane's two
+#pragma unroll
+    for (int c = 0; c < CG; ++c) ch.s[c] = *(const uint16_t *)(x.scales + o.s + 8 * c);
+  } else if constexpr (NS == 2) {
     const u32x2 v = *(const u32x2 *)(x.scales + o.s);
     ch.s[0] = v[0];
     ch.s[1] = v[1];
@@ -497,8 +507,8 @@ __device__ __forceinline__ float zero_off(uint32_t z) {
     return 136.f;  // offset-binary code q + 8, plus the 128 of the unpack
   else if constexpr (BITS == 8)
     return 128.f;  // offset-binary code q + 128, unpacked as is
-  else if constexpr (BITS == 6)
-    return 0.f;    // e2m3 values are signed: no offset
+  else if constexpr (BITS == 6 || BITS == 5)
+    return 0.f;    // e2m3 / e2m1 values are signed: no offset
   else
     return 128.f + (float)z;
 }
@@ -554,6 +564,30 @@ __device__ __forceinline__ void unit32_acc(Word<BITS> *w, const uint8_t *ap, con
   }
 }
 
+// NVFP4: one unit of NR row sets, B = e2m1 * the lane's E4M3 group scale
+// (exact in bf16), so acc += C with no correction.  sc[r]: the two scale
+// bytes of row set r (K 32 lsub .. +16 and +16 .. +32).
+template <int NR>
+__device__ __forceinline__ void nv_unit_acc(const u32x4 *w, const uint32_t *sc, const uint8_t *ap, f32x4 *acc) {
+  float s0[NR], s1[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    s0[r] = e4m3_to_f32(sc[r] & 0xFFu);
+    s1[r] = e4m3_to_f32((sc[r] >> 8) & 0xFFu);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x8 a = *(const bf16x8 *)(ap + j * 16);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      uint32_t o[4];
+      dequant8_e2m1(w[r][j], j < 2 ? s0[r] : s1[r], o);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]}),
+                                                       acc[r], 0, 0, 0);
+    }
+  }
+}
+
 // A full chunk (units G0 .. G0+kCG-1) of NR row sets.  ap: activation bytes of
 // unit G0 for the lane; xs: Xs of unit G0's first group (+ 4 * lsub unless ONE).
 template <int BITS, int GS, bool ONE, int NR>
@@ -564,7 +598,12 @@ __device__ __forceinline__ void chunk_gemv(Chunk<BITS, GS> *ch, const uint8_t *a
     Word<BITS> w[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[r] = ch[r].w[c];
-    if constexpr (GS == 32) {
+    if constexpr (BITS == 5) {
+      uint32_t sc[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) sc[r] = ch[r].s[c];
+      nv_unit_acc<NR>(w, sc, ap + c * (kGroup * 2), acc);
+    } else if constexpr (GS == 32) {
       uint32_t sc[NR][2];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -594,7 +633,12 @@ __device__ __forceinline__ void groups_gemv_slow(const ExpertW &x, const Off *o,
     Word<BITS> w[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) w[r] = load_word<BITS>(x.codes + o[r].c + c * kGroupBytes<BITS>);
-    if constexpr (GS == 32) {
+    if constexpr (BITS == 5) {
+      uint32_t sc[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) sc[r] = *(const uint16_t *)(x.scales + o[r].s + 8 * c);
+      nv_unit_acc<NR>(w, sc, ap + c * (kGroup * 2), acc);
+    } else if constexpr (GS == 32) {
       uint32_t sc[NR][2];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -785,7 +829,9 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int RM = ONE ? 1 : kRMax;
   constexpr int GB = kGroupBytes<BITS>;
-  constexpr int CG = kCG<BITS, GS>, SPU = kSPU<GS>;
+  // SPU: scales per 128-K unit (NVFP4: its 8 scale bytes counted as 4 pairs)
+  constexpr int CG = kCG<BITS, GS>, SPU = BITS == 5 ? 4 : kSPU<GS>;
+  constexpr bool NV = BITS == 5;
   // a lane's activation bytes within a unit: K 32 lsub (groups of 128) or
   // 8 lsub, then +32 per MFMA (groups of 32, after the slice transpose)
   constexpr int LA = GS == 32 ? 16 : 64;
@@ -922,7 +968,11 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const ExpertW xw = TAB ? expert_from_table(p.tab, md.e, 0)
                              : ExpertW{(const uint8_t *)p.w13c + erows * (G1 * GB),
                                          (const uint8_t *)p.w13s + erows * (G1 * 2 * SPU), p.w13z + erows * G1};
-      const Off o2[2] = {row_off<SPU>(i0 + m, G1, g0, GB, lsub), row_off<SPU>(p.I + i0 + m, G1, g0, GB, lsub)};
+      Off o2[2] = {row_off<SPU>(i0 + m, G1, g0, GB, lsub), row_off<SPU>(p.I + i0 + m, G1, g0, GB, lsub)};
+      if constexpr (NV) {  // the lane's two scale bytes of each unit
+        o2[0].s += 2 * lsub;
+        o2[1].s += 2 * lsub;
+      }
       const int nch = ng / CG;
       // activation row of sorted position q
       auto xrow = [&](int q) -> const uint16_t * {
@@ -979,9 +1029,15 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
             gv += red[w * 512 + mm * 16 + n];
             uv += red[w * 512 + 256 + mm * 16 + n];
           }
-          __hip_atomic_store(p.hbuf + (size_t)(rb + mm) * p.I + i0 + n,
-                             kHReady | (uint32_t)f32_to_bf16(silu_f(gv) * uv), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+          float hv;
+          if constexpr (NV) {  // tensor scales, then h quantised in its group of 16 (lanes 16 mm .. +15)
+            const float osc = p.gx * sload(p.g13 + md.e);
+            hv = quant16_lanes(silu_f(gv * osc) * (uv * osc), p.gh);
+          } else {
+            hv = silu_f(gv) * uv;
+          }
+          __hip_atomic_store(p.hbuf + (size_t)(rb + mm) * p.I + i0 + n, kHReady | (uint32_t)f32_to_bf16(hv),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         lds_barrier();
       }
@@ -994,8 +1050,13 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       const ExpertW xw = TAB ? expert_from_table(p.tab, md.e, 3)
                              : ExpertW{(const uint8_t *)p.w2c + erows * (G2 * GB),
                                          (const uint8_t *)p.w2s + erows * (G2 * 2 * SPU), p.w2z + erows * G2};
-      const Off o2[2] = {row_off<SPU>(n0 + m, G2, 0, GB, lsub), row_off<SPU>(n0 + 16 + m, G2, 0, GB, lsub)};
+      Off o2[2] = {row_off<SPU>(n0 + m, G2, 0, GB, lsub), row_off<SPU>(n0 + 16 + m, G2, 0, GB, lsub)};
+      if constexpr (NV) {
+        o2[0].s += 2 * lsub;
+        o2[1].s += 2 * lsub;
+      }
       const int nch = G2 / CG;
+      const float osc2 = NV ? p.gh * sload(p.g2 + md.e) : 1.f;  // NVFP4 output scale
       Chunk<BITS, GS> wd[2];
       if constexpr (FAST) {
         load_chunk<BITS, GS>(xw, o2[0], wd[0]);
@@ -1036,7 +1097,10 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
             Word<BITS> w2[2];
             w2[0] = wd[0].w[c];
             w2[1] = wd[1].w[c];
-            if constexpr (GS == 32) {
+            if constexpr (NV) {
+              const uint32_t sc[2] = {wd[0].s[c], wd[1].s[c]};
+              nv_unit_acc<2>(w2, sc, ap + g * (kGroup * 2), ty);
+            } else if constexpr (GS == 32) {
               const uint32_t sc[2][2] = {{wd[0].s[2 * c], wd[0].s[2 * c + 1]}, {wd[1].s[2 * c], wd[1].s[2 * c + 1]}};
               unit32_acc<BITS, ONE, 2>(w2, ap + g * (kGroup * 2), sc, Xs + g * 64, magic, ty);
             } else {
@@ -1060,7 +1124,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
               __hip_atomic_store(p.ybuf + yo, kHReady | (uint32_t)f32_to_bf16(ty[s2][0]), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
             else
-              p.y_perm[yo] = f32_to_bf16(ty[s2][0]);
+              p.y_perm[yo] = f32_to_bf16(ty[s2][0] * osc2);
           }
         }
         lds_barrier();  // LDS is rewritten by the next item
@@ -1096,7 +1160,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
               __hip_atomic_store(p.ybuf + o, kHReady | (uint32_t)f32_to_bf16(v), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
             else
-              p.y_perm[o] = f32_to_bf16(v);
+              p.y_perm[o] = f32_to_bf16(v * osc2);
           };
           if (ONE) {
             if (lsub == 0) put(yo, ty[s2][0]);
@@ -1230,12 +1294,15 @@ const void *decode_kernel_fn(int bits, int group, bool one, bool fast, bool laye
   if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, false, false>(one, fast)
                                     : decode_fn_fast<8, 128, false, false>(one, fast);
   if (bits == 6) return decode_fn_fast<6, 128, false, false>(one, fast);
+  if (bits == 4 && group == 16) return decode_fn_fast<5, 128, false, false>(one, fast);  // NVFP4
   if (group == 32) return decode_fn_fast<4, 32, false, false>(one, fast);
   return tab ? decode_fn_layer<false, true>(bits, one, fast) : decode_fn_layer<false, false>(bits, one, fast);
 }
 
 // Units per chunk of a format (kCG on the host).
-int chunk_units(int bits, int group) { return (bits >= 6 ? 4 : 8) / (group == 32 ? 2 : 1); }
+int chunk_units(int bits, int group) {
+  return group == 16 ? 4 : (bits >= 6 ? 4 : 8) / (group == 32 ? 2 : 1);  // group 16: NVFP4
+}
 
 // LDS of the fused layer's routing results (after the FFN's own arrays).
 size_t layer_lds_bytes(int T, int k, int E) {
@@ -1311,6 +1378,10 @@ static void fill_params(DecodeParams &p, const FfnArgs &a, void *ws) {
   p.w2s = a.w2_scales;
   p.w2z = a.w2_zeros;
   p.tab = a.tab;
+  p.g13 = a.w13_g;
+  p.g2 = a.w2_g;
+  p.gx = a.gx;
+  p.gh = a.gh;
   p.y_perm = a.y_perm;
   p.ctl = (int *)ws;
   p.hbuf = (uint32_t *)((char *)ws + ffn_ctl_bytes(a.T, a.k, a.E));
@@ -1324,8 +1395,9 @@ static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, c
   const int cg = chunk_units(a.bits, a.group);
   const bool fast = (a.H / kGroup) % (4 * cg) == 0 && (a.I / kGroup) % cg == 0 && (!one || a.I / kGroup <= 4 * kHPend);
   const void *fn = decode_kernel_fn(a.bits, a.group, one, fast, layer, a.tab != nullptr);
-  const size_t lds =
-      layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I) : decode_lds_bytes(a.H, a.I, one, a.group);
+  // NVFP4 (group 16) sizes its LDS like groups of 32 (SPU = 4 in the kernel)
+  const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I)
+                           : decode_lds_bytes(a.H, a.I, one, a.group == 16 ? 32 : a.group);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long blocks = (long)p.Amax * (a.I / kRows1 + a.H / kRows2);

@@ -59,17 +59,7 @@ struct GemmParams {
   float act_g, out_g;
 };
 
-// NVFP4 quantisation of a group of 16 h values held by 16 consecutive lanes
-// (one value each): the group maximum through xor shuffles inside the 16
-// lanes, then the steps of the activation quantiser.  Returns q * s.
-__device__ __forceinline__ float quant16_lanes(float hv, float G) {
-  float amax = fabsf(hv);
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
-  const float s = round_e4m3(amax / (6.f * G));
-  const float sg = s * G;
-  return (sg > 0.f ? round_e2m1(hv / sg) : 0.f) * s;
-}
+
 
 // LDS position of 16-byte chunk `chunk` of tile row `row`.  Eight lanes that
 // read (or write) the same chunk of eight consecutive rows, or eight chunks
@@ -384,6 +374,14 @@ __global__ void __launch_bounds__(256) zero_kernel(u32x4 *p, size_t n16) {
 }
 
 }  // namespace
+
+hipError_t launch_zero16(void *p, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t zb = (n16 + 255) / 256;
+  zero_kernel<<<(unsigned)(zb < 2048 ? zb : 2048), 256, 0, st>>>((u32x4 *)p, n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t st) {
   const int nrows = a.T * a.k;

@@ -98,6 +98,7 @@ hipError_t launch_combine(const uint16_t *y_perm, const int32_t *row_pos, const 
 
 // unpack.hip
 hipError_t launch_unpack(const uint32_t *words, int bits, int64_t n_words, int8_t *out, hipStream_t st);
+hipError_t launch_zero16(void *p, size_t bytes, hipStream_t st);  // bytes % 16 == 0, 16-byte aligned
 hipError_t launch_quant_nvfp4(const uint16_t *x, int64_t n, float G, uint16_t *vals, uint8_t *scales, hipStream_t st);
 hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
                                int group, int N, int K, uint16_t *out, hipStream_t st);

@@ -248,8 +248,10 @@ moe_status moe_expert_ffn_wna16(const uint16_t *x, const int32_t *expert_offsets
  * scale x_gscale before gate_up, and h with h_gscale before down:
  *   a = NVFP4(x) . W13' * (x_gscale * w13_gscale[e]),  h = silu(a_gate) * a_up
  *   y = NVFP4(h) . W2'  * (h_gscale * w2_gscale[e])
- * with W' = e2m1 * e4m3 (exact in bf16) and float32 accumulation.  Always the
- * grouped-GEMM path.  Workspace: moe_expert_ffn_nvfp4_workspace_size bytes,
+ * with W' = e2m1 * e4m3 (exact in bf16) and float32 accumulation.  Dispatch
+ * as for moe_expert_ffn_w4a16 (the decode GEMV kernel, which quantises each
+ * item's 16 h outputs itself, while T <= 512 and T*k <= 6*E; the grouped
+ * GEMMs above).  Workspace: moe_expert_ffn_nvfp4_workspace_size bytes,
  * zero before the first call and left zero.  Other arguments and
  * requirements as for moe_expert_ffn_w4a16; the scales must be positive and
  * finite. */
