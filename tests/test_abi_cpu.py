@@ -150,6 +150,30 @@ def test_ffn_wna16_format_errors():
     assert L.moe_dequant_bf16_grouped(A, A, None, 8, 32, 0, 128, A, None) == OK
 
 
+def _nv(T=2, k=2, E=8, H=256, I=128, gx=0.01, gh=0.01, x=A, codes=A, sc=A, g=A, ws=A, wsb=1 << 24):
+    L = bq.lib()
+    return L.moe_expert_ffn_nvfp4(x, A, A, A, T, k, E, H, I, gx, gh, codes, sc, g, codes, sc, g, A, ws, wsb, None)
+
+
+def test_nvfp4_argument_errors():
+    L = bq.lib()
+    assert _nv(I=100) == SHAPE
+    assert _nv(x=None) == INVALID and _nv(g=None) == INVALID and _nv(sc=None) == INVALID
+    assert _nv(gx=0.0) == INVALID and _nv(gh=-1.0) == INVALID and _nv(gx=float("inf")) == INVALID
+    assert _nv(gh=float("nan")) == INVALID
+    assert _nv(codes=A + 8) == MISALIGNED and _nv(sc=A + 1) == MISALIGNED
+    assert _nv(wsb=100) == WS_SMALL
+    assert _nv(T=0) == OK
+    need = L.moe_expert_ffn_nvfp4_workspace_size(16, 8, 256, 4096, 1024)
+    assert need >= L.moe_expert_ffn_workspace_size(16, 8, 256, 4096, 1024) + 16 * 4096 * 2 and need % 256 == 0
+    q = L.moe_quant_act_nvfp4
+    assert q(A, 17, 0.1, A, None, None) == SHAPE
+    assert q(None, 16, 0.1, A, None, None) == INVALID
+    assert q(A, 16, 0.0, A, None, None) == INVALID
+    assert q(A + 8, 16, 0.1, A, None, None) == MISALIGNED
+    assert q(A, 0, 0.1, A, None, None) == OK
+
+
 def test_device_address_argument_errors():
     L = bq.lib()
     out = ctypes.c_uint64(0)

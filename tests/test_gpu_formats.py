@@ -183,3 +183,19 @@ def test_wna16_matches_the_format_entry_points():
                                        nbytes, st)
             assert s == 0
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (bits, T)
+
+
+def test_formats_alternate_on_one_workspace_and_route_edge_cases():
+    """Every format on one set of workspaces, decode and GEMM paths in turn,
+    including k = E (every expert active) and experts with no rows; the
+    workspaces are all-zero at the end."""
+    ws = bq.Workspaces("cuda")
+    cases = [(4, 32, 1, 8, 8), (8, 128, 40, 8, 2), (6, 128, 3, 8, 8), (8, 32, 2, 16, 1), (4, 32, 300, 8, 2),
+             (6, 128, 17, 32, 4), (2, 128, 1, 8, 8), (4, 128, 5, 16, 4)]
+    for i, (bits, group, T, E, k) in enumerate(cases):
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=512, I=256, E=E, k=k, bits=bits, group=group,
+                           scale_sigma=SIGMA.get(bits, 0.05), seed=4400 + i)
+        _check_ffn(workload.make_layer_inputs(sp), ws=ws)
+    torch.cuda.synchronize()
+    for name, buf in ws._bufs.items():
+        assert int(buf.view(torch.int32).abs().sum()) == 0, name

@@ -114,3 +114,23 @@ def test_nvfp4_ffn_prefill_full_size_sampled():
         rows = row_rel_err(ypf[o0:o1], ref[o0:o1])
         say(f"    expert {e} ({o1 - o0} rows): y_perm rel-fro {err:.2e}, rows over {TOL}: {(rows > TOL).sum()}")
         assert err <= TOL and (rows <= TOL).mean() >= 0.99 and rows.max() <= 5e-2
+
+
+def test_nvfp4_every_expert_and_empty_experts_one_workspace():
+    """k = E (every expert active), k = 1 with E = 16 (empty experts), decode
+    and GEMM paths on one workspace, left all-zero."""
+    ws = bq.Workspaces("cuda")
+    for i, (T, E, k) in enumerate([(1, 8, 8), (3, 16, 1), (40, 8, 8), (2, 8, 8)]):
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=512, I=256, E=E, k=k, bits=4, group=16,
+                           seed=5200 + i)
+        inp = workload.make_layer_inputs(sp)
+        r = bq.route_permute(to_dev(inp.x), to_dev(inp.w_router), sp.k)
+        off, srt = to_np(r["offsets"]), to_np(r["sorted_rows"])
+        yp = bq.expert_ffn_nvfp4(to_dev(inp.x), r["offsets"], r["sorted_rows"], r["active"], sp.k,
+                                 _weights_dev(inp.weights), sp.I, sp.nv_gx, sp.nv_gh, ws=ws)
+        ref = oracle.expert_ffn_nvfp4(inp.x, off, srt, sp.k, inp.weights, sp.I, sp.nv_gx, sp.nv_gh)
+        err = oracle.rel_fro(bf16_np_to_f32(to_np(yp)), ref)
+        say(f"    T={T} E={E} k={k}: y_perm rel-fro {err:.2e}")
+        assert err <= TOL
+    torch.cuda.synchronize()
+    assert int(ws._bufs["ffn_nvfp4"].view(torch.int32).abs().sum()) == 0
