@@ -151,19 +151,19 @@ __device__ __forceinline__ float quant16_lanes(float hv, float G) {
 }
 
 // Eight E2M1 codes of w (K order) times the group scale s -> four bf16 pairs,
-// exact (2 x 4 significant bits).  The magnitudes come from a byte table
-// (2|v| = 0 1 2 3 4 6 8 12) indexed with v_perm.
+// exact (2 x 4 significant bits).  gfx950 converts the two codes of a byte
+// to bf16 in one instruction; its scale operand takes only a power of two,
+// so it runs with scale 1 (exact values, low nibble first) and s is applied
+// in float32.
 __device__ __forceinline__ void dequant8_e2m1(uint32_t w, float s, uint32_t out[4]) {
-  const float hs = 0.5f * s;
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // fields 0 2 4 6 / 1 3 5 7
-  const uint32_t mlo = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, lo & 0x07070707u);
-  const uint32_t mhi = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, hi & 0x07070707u);
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+  const uint32_t q[4] = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                         __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const float f0 = (float)((mlo >> (8 * b)) & 0xFFu) * hs, f1 = (float)((mhi >> (8 * b)) & 0xFFu) * hs;
-    const float v0 = ((lo >> (8 * b)) & 8u) ? -f0 : f0, v1 = ((hi >> (8 * b)) & 8u) ? -f1 : f1;
-    out[b] = pack_bf16x2(v0, v1);
-  }
+  for (int b = 0; b < 4; ++b) out[b] = pack_bf16x2(bf16lo(q[b]) * s, bf16hi(q[b]) * s);
 }
 
 // Natural-order bf16 activations d (pairs (x0,x1), (x2,x3), ...) -> the pair
