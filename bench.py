@@ -249,7 +249,10 @@ class Plan:
                 sp.T, sp.H, sp.E, sp.k, sp.I)
         tail = (self.y.data_ptr(), st["ids"].data_ptr(), st["gates"].data_ptr(), self.ws_layer.data_ptr(),
                 self.ws_layer.numel(), stream)
-        if sp.bits == 4:
+        if sp.bits not in (2, 4) or sp.group != 128:
+            s = L.moe_layer_wna16(*head, sp.bits, sp.group, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
+                                  None, w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(), None, *tail)
+        elif sp.bits == 4:
             s = L.moe_layer_w4a16(*head, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
                                   w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(), *tail)
         else:
@@ -306,9 +309,8 @@ def main():
     if args.experts != "arrays" and (sp.bits not in (2, 4) or sp.group != 128):
         print(json.dumps({"error": "the address-table entry points take INT4 and 2-bit with groups of 128"}))
         sys.exit(2)
-    # the one-launch layer takes INT4 and 2-bit with groups of 128 from stacked arrays
-    fused = (sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays" and sp.bits in (2, 4)
-             and sp.group == 128)
+    # the one-launch layer takes every W.A16 format from stacked arrays (NVFP4 takes the stages)
+    fused = sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays" and not sp.nvfp4
     if args.experts != "arrays" and sp.nvfp4:
         print(json.dumps({"error": "NVFP4 experts take stacked arrays"}))
         sys.exit(2)

@@ -53,6 +53,7 @@ _SIGS = {
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_layer_workspace_size": (_c_size, [_c_int] * 5),
     "moe_layer_w4a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp] * 3 + [_vp, _c_size, _vp]),
+    "moe_layer_wna16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_layer_w2a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_unpack_codes": (_c_int, [_vp, _c_int, _c_i64, _vp, _vp]),
     "moe_dequant_bf16": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
@@ -333,7 +334,7 @@ def combine(y_perm: torch.Tensor, row_pos: torch.Tensor, gates: torch.Tensor) ->
 
 
 def layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor], weights: Dict[str, torch.Tensor],
-          k: int, bits: int, I: int, ws: Optional[Workspaces] = None, want_routing: bool = False):
+          k: int, bits: int, I: int, ws: Optional[Workspaces] = None, want_routing: bool = False, group: int = 128):
     """The whole decode layer (T <= 16) in one library call; returns y (and ids, gates)."""
     dev = _dev(x)
     T, H = x.shape
@@ -345,6 +346,12 @@ def layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Te
     w = (ws or Workspaces(dev)).get("layer", L.moe_layer_workspace_size(T, k, E, H, I))
     head = (_p(x), _p(w_router), _p(logit_bias), T, H, E, k, I)
     tail = (_p(y), _p(ids), _p(gates), _p(w), w.numel(), _stream(dev))
+    if bits not in (2, 4) or group != 128:
+        s = L.moe_layer_wna16(*head, bits, group, _p(weights["w13_codes"]), _p(weights["w13_scales"]),
+                              _p(weights.get("w13_zeros")), _p(weights["w2_codes"]), _p(weights["w2_scales"]),
+                              _p(weights.get("w2_zeros")), *tail)
+        _check(s, "moe_layer_wna16")
+        return (y, ids, gates) if want_routing else y
     if bits == 4:
         s = L.moe_layer_w4a16(*head, _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights["w2_codes"]),
                               _p(weights["w2_scales"]), *tail)

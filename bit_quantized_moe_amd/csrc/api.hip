@@ -393,12 +393,13 @@ static moe_status layer(const char *name, int bits, const uint16_t *x, const uin
                         const float *logit_bias, int T, int H, int E, int k, int I, const uint32_t *w13_codes,
                         const uint16_t *w13_scales, const uint8_t *w13_zeros, const uint32_t *w2_codes,
                         const uint16_t *w2_scales, const uint8_t *w2_zeros, uint16_t *y, int32_t *topk_ids,
-                        float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+                        float *topk_weights, void *workspace, size_t workspace_bytes, void *stream,
+                        int group = 128) {
   moe_status s = check_common_moe(T, H, E, k);
   if (s != MOE_OK) return s;
   if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
   if (T == 0) return MOE_OK;
-  if (!layer_shape_ok(T, k, E, H, I, bits))
+  if (!layer_shape_ok(T, k, E, H, I, bits, group))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE,
                 "%s: one-launch layer needs 1 <= T <= %d and a decode-path shape (T=%d, k=%d, E=%d, H=%d, I=%d); "
                 "call the stages instead",
@@ -419,9 +420,23 @@ static moe_status layer(const char *name, int bits, const uint16_t *x, const uin
   hipError_t he = current_device_info(&dev);
   if (he != hipSuccess) return from_hip(he, name);
   FfnArgs a{x, nullptr, nullptr, nullptr, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
-            w2_codes, w2_scales, w2_zeros, nullptr, workspace};
+            w2_codes, w2_scales, w2_zeros, nullptr, workspace, nullptr, group};
   LayerArgs l{w_router, logit_bias, y, topk_ids, topk_weights, nullptr};
   return from_hip(launch_layer_decode(a, l, dev, (hipStream_t)stream), name);
+}
+
+moe_status moe_layer_wna16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,
+                           int k, int I, int bits, int group_size, const uint32_t *w13_codes,
+                           const uint16_t *w13_scales, const uint8_t *w13_zeros, const uint32_t *w2_codes,
+                           const uint16_t *w2_scales, const uint8_t *w2_zeros, uint16_t *y, int32_t *topk_ids,
+                           float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+  const bool ok = ((bits == 4 || bits == 8) && (group_size == 128 || group_size == 32)) ||
+                  ((bits == 2 || bits == 6) && group_size == 128);
+  if (!ok)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_wna16: unsupported format: %d bits, group %d", bits, group_size);
+  return layer("moe_layer_wna16", bits, x, w_router, logit_bias, T, H, E, k, I, w13_codes, w13_scales,
+               bits == 2 ? w13_zeros : nullptr, w2_codes, w2_scales, bits == 2 ? w2_zeros : nullptr, y, topk_ids,
+               topk_weights, workspace, workspace_bytes, stream, group_size);
 }
 
 moe_status moe_layer_w4a16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,

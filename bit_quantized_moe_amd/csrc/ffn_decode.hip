@@ -1290,7 +1290,13 @@ const void *decode_fn_layer(int bits, bool one, bool fast) {
 // separate instantiation so that the array kernels keep their registers.  The
 // group-32 and INT8 formats take the stage call with stacked arrays.
 const void *decode_kernel_fn(int bits, int group, bool one, bool fast, bool layer, bool tab) {
-  if (layer) return decode_fn_layer<true, false>(bits, one, fast);
+  if (layer) {  // every W.A16 format; NVFP4 (which quantises x first) takes the stage calls
+    if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, true, false>(one, fast)
+                                      : decode_fn_fast<8, 128, true, false>(one, fast);
+    if (bits == 6) return decode_fn_fast<6, 128, true, false>(one, fast);
+    if (group == 32) return decode_fn_fast<4, 32, true, false>(one, fast);
+    return decode_fn_layer<true, false>(bits, one, fast);
+  }
   if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, false, false>(one, fast)
                                     : decode_fn_fast<8, 128, false, false>(one, fast);
   if (bits == 6) return decode_fn_fast<6, 128, false, false>(one, fast);
@@ -1318,8 +1324,8 @@ size_t decode_lds_bytes(int H, int I, bool one, int group = kGroup) {
 
 // Fused layer: the router rows (shared start of LDS) or the FFN arrays,
 // whichever is larger, then the routing results.
-size_t layer_lds_total(int T, int k, int E, int H, int I) {
-  const size_t f = decode_lds_bytes(H, I, T == 1);
+size_t layer_lds_total(int T, int k, int E, int H, int I, int group = kGroup) {
+  const size_t f = decode_lds_bytes(H, I, T == 1, group);
   const size_t r = router_lds_ok(H) ? router_lds_bytes(H) : 0;
   return (f > r ? f : r) + layer_lds_bytes(T, k, E);
 }
@@ -1396,7 +1402,7 @@ static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, c
   const bool fast = (a.H / kGroup) % (4 * cg) == 0 && (a.I / kGroup) % cg == 0 && (!one || a.I / kGroup <= 4 * kHPend);
   const void *fn = decode_kernel_fn(a.bits, a.group, one, fast, layer, a.tab != nullptr);
   // NVFP4 (group 16) sizes its LDS like groups of 32 (SPU = 4 in the kernel)
-  const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I)
+  const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I, a.group)
                            : decode_lds_bytes(a.H, a.I, one, a.group == 16 ? 32 : a.group);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
@@ -1421,9 +1427,9 @@ size_t layer_workspace_bytes(int T, int k, int E, int H, int I) {
   return ffn_ctl_bytes(T, k, E) + al256(n * I * 4) + al256((size_t)T * E * 8) + al256(n * H * 4) + al256(n * 8);
 }
 
-bool layer_shape_ok(int T, int k, int E, int H, int I, int bits) {
-  return T >= 1 && T <= kLayerMaxT && (long)T * k <= 4 * kWave && E <= (1 << kRecIdBits) && decode_layout_ok(H, I, bits) &&
-         layer_lds_total(T, k, E, H, I) <= 64 * 1024;
+bool layer_shape_ok(int T, int k, int E, int H, int I, int bits, int group) {
+  return T >= 1 && T <= kLayerMaxT && (long)T * k <= 4 * kWave && E <= (1 << kRecIdBits) &&
+         decode_layout_ok(H, I, bits, group) && layer_lds_total(T, k, E, H, I, group) <= 64 * 1024;
 }
 
 hipError_t launch_layer_decode(const FfnArgs &a, const LayerArgs &l, const DeviceInfo &dev, hipStream_t st) {

@@ -87,7 +87,7 @@ struct LayerArgs {
   float *gates;
   float *logits;
 };
-bool layer_shape_ok(int T, int k, int E, int H, int I, int bits);
+bool layer_shape_ok(int T, int k, int E, int H, int I, int bits, int group = 128);
 size_t layer_workspace_bytes(int T, int k, int E, int H, int I);
 hipError_t launch_layer_decode(const FfnArgs &a, const LayerArgs &l, const DeviceInfo &dev, hipStream_t st);
 hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);

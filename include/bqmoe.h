@@ -347,6 +347,17 @@ moe_status moe_combine(const uint16_t *y_perm, const int32_t *row_pos, const flo
  * calls are the way to run the layer.
  */
 size_t moe_layer_workspace_size(int T, int k, int E, int H, int I);
+/* moe_layer_wna16: the one-launch layer for any format of moe_expert_ffn_wna16
+ * (bits / group_size: 4 / 128 or 32, 8 / 128 or 32, 2 / 128, 6 / 128 (FP6,
+ * fp16 scales)); arguments as for moe_layer_w2a16 with the two format
+ * integers after I (zero-points used for bits == 2 only).  Results equal the
+ * stage calls with moe_expert_ffn_wna16 bit for bit. */
+moe_status moe_layer_wna16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
+                           int T, int H, int E, int k, int I, int bits, int group_size,
+                           const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
+                           const uint32_t *w2_codes, const uint16_t *w2_scales, const uint8_t *w2_zeros,
+                           uint16_t *y, int32_t *topk_ids, float *topk_weights,
+                           void *workspace, size_t workspace_bytes, void *stream);
 moe_status moe_layer_w4a16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
                            int T, int H, int E, int k, int I,
                            const uint32_t *w13_codes, const uint16_t *w13_scales,

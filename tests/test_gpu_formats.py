@@ -199,3 +199,27 @@ def test_formats_alternate_on_one_workspace_and_route_edge_cases():
     torch.cuda.synchronize()
     for name, buf in ws._bufs.items():
         assert int(buf.view(torch.int32).abs().sum()) == 0, name
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (8, 128), (8, 32), (6, 128)])
+def test_one_launch_layer_formats_match_stages(bits, group):
+    """moe_layer_wna16 (one launch) gives the stage calls' y, ids and gates bit for bit, and the oracle's y."""
+    ws = bq.Workspaces("cuda")
+    for T, H, I, E, k in ((1, 4096, 1024, 256, 8), (5, 512, 256, 16, 4), (16, 1024, 256, 32, 4)):
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, I=I, E=E, k=k, bits=bits, group=group,
+                           scale_sigma=SIGMA[bits], seed=4600 + T + bits + group)
+        inp = workload.make_layer_inputs(sp)
+        wd = weights_to_dev(inp.weights)
+        for rep in range(2):
+            y, ids, gates = bq.layer(to_dev(inp.x), to_dev(inp.w_router), None, wd, sp.k, bits, sp.I, ws=ws,
+                                     want_routing=True, group=group)
+            st = bq.moe_layer(to_dev(inp.x), to_dev(inp.w_router), None, wd, sp.k, bits, sp.I, ws=ws, group=group)
+            assert torch.equal(ids, st["ids"]) and torch.equal(gates.view(torch.int32), st["gates"].view(torch.int32))
+            assert torch.equal(y.view(torch.int16), st["y"].view(torch.int16)), (T, rep)
+        ref = oracle.moe_layer(inp.x, inp.w_router, None, inp.weights, sp.k, bits, sp.I, group=group)
+        err = oracle.rel_fro(bf16_np_to_f32(to_np(y)), ref["y"])
+        say(f"    T={T} H={H}: one launch = stages bit for bit, y rel-fro {err:.2e}")
+        assert err <= TOL
+    torch.cuda.synchronize()
+    for name, buf in ws._bufs.items():
+        assert int(buf.view(torch.int32).abs().sum()) == 0, name
