@@ -249,7 +249,11 @@ class Plan:
                 sp.T, sp.H, sp.E, sp.k, sp.I)
         tail = (self.y.data_ptr(), st["ids"].data_ptr(), st["gates"].data_ptr(), self.ws_layer.data_ptr(),
                 self.ws_layer.numel(), stream)
-        if sp.bits not in (2, 4) or sp.group != 128:
+        if sp.nvfp4:
+            s = L.moe_layer_nvfp4(*head[:8], sp.nv_gx, sp.nv_gh, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
+                                  w["w13_gscale"].data_ptr(), w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(),
+                                  w["w2_gscale"].data_ptr(), *tail)
+        elif sp.bits not in (2, 4) or sp.group != 128:
             s = L.moe_layer_wna16(*head, sp.bits, sp.group, w["w13_codes"].data_ptr(), w["w13_scales"].data_ptr(),
                                   None, w["w2_codes"].data_ptr(), w["w2_scales"].data_ptr(), None, *tail)
         elif sp.bits == 4:
@@ -309,8 +313,8 @@ def main():
     if args.experts != "arrays" and (sp.bits not in (2, 4) or sp.group != 128):
         print(json.dumps({"error": "the address-table entry points take INT4 and 2-bit with groups of 128"}))
         sys.exit(2)
-    # the one-launch layer takes every W.A16 format from stacked arrays (NVFP4 takes the stages)
-    fused = sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays" and not sp.nvfp4
+    # the one-launch layer takes every format from stacked arrays
+    fused = sp.T <= FUSED_MAX_T and not args.stages and args.experts == "arrays"
     if args.experts != "arrays" and sp.nvfp4:
         print(json.dumps({"error": "NVFP4 experts take stacked arrays"}))
         sys.exit(2)

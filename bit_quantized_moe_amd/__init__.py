@@ -53,6 +53,8 @@ _SIGS = {
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_layer_workspace_size": (_c_size, [_c_int] * 5),
     "moe_layer_w4a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp] * 3 + [_vp, _c_size, _vp]),
+    "moe_layer_nvfp4": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [ctypes.c_float] * 2 + [_vp] * 6 + [_vp] * 3
+                        + [_vp, _c_size, _vp]),
     "moe_layer_wna16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_layer_w2a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_unpack_codes": (_c_int, [_vp, _c_int, _c_i64, _vp, _vp]),
@@ -361,6 +363,25 @@ def layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Te
     else:
         raise MoEError("bits must be 2 or 4")
     _check(s, f"moe_layer_w{bits}a16")
+    return (y, ids, gates) if want_routing else y
+
+
+def layer_nvfp4(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
+                weights: Dict[str, torch.Tensor], k: int, I: int, x_gscale: float, h_gscale: float,
+                ws: Optional[Workspaces] = None, want_routing: bool = False):
+    """The whole decode layer (T <= 16) with NVFP4 W4A4 experts in one library call."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = w_router.shape[0]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if want_routing else None
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev) if want_routing else None
+    L = lib()
+    w = (ws or Workspaces(dev)).get("layer", L.moe_layer_workspace_size(T, k, E, H, I))
+    _check(L.moe_layer_nvfp4(_p(x), _p(w_router), _p(logit_bias), T, H, E, k, I, float(x_gscale), float(h_gscale),
+                             _p(weights["w13_codes"]), _p(weights["w13_scales"]), _p(weights["w13_gscale"]),
+                             _p(weights["w2_codes"]), _p(weights["w2_scales"]), _p(weights["w2_gscale"]), _p(y),
+                             _p(ids), _p(gates), _p(w), w.numel(), _stream(dev)), "moe_layer_nvfp4")
     return (y, ids, gates) if want_routing else y
 
 

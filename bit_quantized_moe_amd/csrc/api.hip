@@ -425,6 +425,50 @@ static moe_status layer(const char *name, int bits, const uint16_t *x, const uin
   return from_hip(launch_layer_decode(a, l, dev, (hipStream_t)stream), name);
 }
 
+moe_status moe_layer_nvfp4(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,
+                           int k, int I, float x_gscale, float h_gscale, const uint32_t *w13_codes,
+                           const uint8_t *w13_scales, const float *w13_gscale, const uint32_t *w2_codes,
+                           const uint8_t *w2_scales, const float *w2_gscale, uint16_t *y, int32_t *topk_ids,
+                           float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+  const char *name = "moe_layer_nvfp4";
+  moe_status s = check_common_moe(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
+  if (T == 0) return MOE_OK;
+  if (!layer_shape_ok(T, k, E, H, I, 4, 16))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "%s: one-launch layer needs 1 <= T <= %d and a decode-path shape (T=%d, k=%d, E=%d, H=%d, I=%d); "
+                "call the stages instead",
+                name, kLayerMaxT, T, k, E, H, I);
+  if (!x || !w_router || !w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale || !y ||
+      !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+  if (!(x_gscale > 0.f) || !(h_gscale > 0.f) || x_gscale > 3.0e38f || h_gscale > 3.0e38f)
+    return fail(MOE_ERR_INVALID_ARG, "%s: the tensor scales must be positive and finite", name);
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16))
+    return fail(MOE_ERR_MISALIGNED, "%s: x, w_router and code arrays need 16-byte alignment", name);
+  if (!aligned(w13_scales, 2) || !aligned(w2_scales, 2) || !aligned(w13_gscale, 4) || !aligned(w2_gscale, 4) ||
+      !aligned(y, 4) || (topk_ids && !aligned(topk_ids, 4)) || (topk_weights && !aligned(topk_weights, 4)) ||
+      (logit_bias && !aligned(logit_bias, 4)))
+    return fail(MOE_ERR_MISALIGNED, "%s: array alignment", name);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
+  const size_t need = moe_layer_workspace_size(T, k, E, H, I);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", name, workspace_bytes, need);
+  DeviceInfo dev;
+  hipError_t he = current_device_info(&dev);
+  if (he != hipSuccess) return from_hip(he, name);
+  FfnArgs a{x, nullptr, nullptr, nullptr, T, k, E, H, I, 4, w13_codes, (const uint16_t *)w13_scales, nullptr,
+            w2_codes, (const uint16_t *)w2_scales, nullptr, nullptr, workspace, nullptr, 16};
+  a.nvfp4 = true;
+  a.w13_g = w13_gscale;
+  a.w2_g = w2_gscale;
+  a.gx = x_gscale;
+  a.gh = h_gscale;
+  LayerArgs l{w_router, logit_bias, y, topk_ids, topk_weights, nullptr};
+  return from_hip(launch_layer_decode(a, l, dev, (hipStream_t)stream), name);
+}
+
 moe_status moe_layer_wna16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,
                            int k, int I, int bits, int group_size, const uint32_t *w13_codes,
                            const uint16_t *w13_scales, const uint8_t *w13_zeros, const uint32_t *w2_codes,

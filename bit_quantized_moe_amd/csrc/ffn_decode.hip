@@ -229,9 +229,45 @@ __device__ __forceinline__ void stage_group_sums(const uint8_t *act, float *Xs, 
 
 // Stages activation rows 0..R-1 (src(r): row r's global address); chunks
 // q < q0 of row 0 come from pa (q0 = 256 * NPRE or 0).  Ends with a block barrier.
-template <int BITS, int GS, int NPRE, typename Src>
+// NVFP4 activations quantised in LDS: rows 0..R-1 (natural order), one
+// thread per group of 16 (the steps of the activation quantiser, tensor
+// scale G), each group replaced by q * s.  Starts and ends with a barrier.
+__device__ __forceinline__ void quantize_rows_lds(uint8_t *act, int R, int K, float G) {
+  const int pitch = K * 2 + 16, ng = K / 16;
+  lds_barrier();
+  for (int t = threadIdx.x; t < R * ng; t += 256) {
+    u32x4 *p = (u32x4 *)(act + (t / ng) * pitch + (t % ng) * 32);
+    const u32x4 a = p[0], b = p[1];
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16lo(a[j]);
+      v[2 * j + 1] = bf16hi(a[j]);
+      v[8 + 2 * j] = bf16lo(b[j]);
+      v[8 + 2 * j + 1] = bf16hi(b[j]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    const float s = round_e4m3(amax / (6.f * G));
+    const float sg = s * G;
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float q0 = sg > 0.f ? round_e2m1(v[2 * j] / sg) : 0.f;
+      const float q1 = sg > 0.f ? round_e2m1(v[2 * j + 1] / sg) : 0.f;
+      o[j] = pack_bf16x2(q0 * s, q1 * s);
+    }
+    p[0] = u32x4{o[0], o[1], o[2], o[3]};
+    p[1] = u32x4{o[4], o[5], o[6], o[7]};
+  }
+  lds_barrier();
+}
+
+// QX: quantise the staged rows to NVFP4 first (tensor scale G; the fused layer).
+template <int BITS, int GS, int NPRE, bool QX = false, typename Src>
 __device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int R, int K, int q0,
-                                           const PreAct *pa) {
+                                           const PreAct *pa, float G = 0.f) {
   const int pitch = K * 2 + 16;
   const int nch = K / kChunkE<BITS>;
   if (q0 > 0) {
@@ -249,6 +285,7 @@ __device__ __forceinline__ void stage_rows(uint8_t *act, float *Xs, Src src, int
       store_act_chunk<BITS>(act + r * pitch, q, d);
     }
   }
+  if constexpr (QX) quantize_rows_lds(act, R, K, G);
   stage_group_sums<GS>(act, Xs, R, K);
 }
 
@@ -992,7 +1029,10 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       }
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
-        stage_rows<BITS, GS, NPRE>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H, rb == md.o0 ? q0 : 0, &pa);
+        // the fused NVFP4 layer quantises the activations it stages (the stage
+        // call gets them quantised already)
+        stage_rows<BITS, GS, NPRE, LAYER && NV>(act, Xs, [&](int r) { return xrow(rb + r); }, R, p.H,
+                                                 rb == md.o0 ? q0 : 0, &pa, p.gx);
         const int arow = ONE ? 0 : min(m, R - 1);
         const uint8_t *ap = act + arow * pitch1 + lsub * LA + g0 * (kGroup * 2);
         const float *xs = Xs + g0 * 16 * SPU + (ONE ? 0 : 4 * lsub);
@@ -1121,7 +1161,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
           const size_t yo = (size_t)md.o0 * p.H + n0 + 16 * s2 + m;
           if (lsub == 0) {
             if constexpr (LAYER)
-              __hip_atomic_store(p.ybuf + yo, kHReady | (uint32_t)f32_to_bf16(ty[s2][0]), __ATOMIC_RELAXED,
+              __hip_atomic_store(p.ybuf + yo, kHReady | (uint32_t)f32_to_bf16(ty[s2][0] * osc2), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
             else
               p.y_perm[yo] = f32_to_bf16(ty[s2][0] * osc2);
@@ -1157,7 +1197,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
           const size_t yo = (size_t)rb * p.H + n0 + 16 * s2 + m;
           auto put = [&](size_t o, float v) {
             if constexpr (LAYER)
-              __hip_atomic_store(p.ybuf + o, kHReady | (uint32_t)f32_to_bf16(v), __ATOMIC_RELAXED,
+              __hip_atomic_store(p.ybuf + o, kHReady | (uint32_t)f32_to_bf16(v * osc2), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
             else
               p.y_perm[o] = f32_to_bf16(v * osc2);
@@ -1290,11 +1330,12 @@ const void *decode_fn_layer(int bits, bool one, bool fast) {
 // separate instantiation so that the array kernels keep their registers.  The
 // group-32 and INT8 formats take the stage call with stacked arrays.
 const void *decode_kernel_fn(int bits, int group, bool one, bool fast, bool layer, bool tab) {
-  if (layer) {  // every W.A16 format; NVFP4 (which quantises x first) takes the stage calls
+  if (layer) {  // every format; the NVFP4 layer quantises x as it stages it
     if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, true, false>(one, fast)
                                       : decode_fn_fast<8, 128, true, false>(one, fast);
     if (bits == 6) return decode_fn_fast<6, 128, true, false>(one, fast);
     if (group == 32) return decode_fn_fast<4, 32, true, false>(one, fast);
+    if (group == 16) return decode_fn_fast<5, 128, true, false>(one, fast);  // NVFP4
     return decode_fn_layer<true, false>(bits, one, fast);
   }
   if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, false, false>(one, fast)
@@ -1402,7 +1443,7 @@ static hipError_t launch_decode(DecodeParams &p, const FfnArgs &a, bool layer, c
   const bool fast = (a.H / kGroup) % (4 * cg) == 0 && (a.I / kGroup) % cg == 0 && (!one || a.I / kGroup <= 4 * kHPend);
   const void *fn = decode_kernel_fn(a.bits, a.group, one, fast, layer, a.tab != nullptr);
   // NVFP4 (group 16) sizes its LDS like groups of 32 (SPU = 4 in the kernel)
-  const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I, a.group)
+  const size_t lds = layer ? layer_lds_total(a.T, a.k, a.E, a.H, a.I, a.group == 16 ? 32 : a.group)
                            : decode_lds_bytes(a.H, a.I, one, a.group == 16 ? 32 : a.group);
   const int per_cu = resident_blocks_per_cu(fn, dev.device, lds);
   if (per_cu < 1) return hipErrorInvalidConfiguration;
@@ -1428,6 +1469,7 @@ size_t layer_workspace_bytes(int T, int k, int E, int H, int I) {
 }
 
 bool layer_shape_ok(int T, int k, int E, int H, int I, int bits, int group) {
+  if (group == 16) group = 32;  // NVFP4 sizes its LDS like groups of 32
   return T >= 1 && T <= kLayerMaxT && (long)T * k <= 4 * kWave && E <= (1 << kRecIdBits) &&
          decode_layout_ok(H, I, bits, group) && layer_lds_total(T, k, E, H, I, group) <= 64 * 1024;
 }

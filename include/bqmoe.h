@@ -352,6 +352,18 @@ size_t moe_layer_workspace_size(int T, int k, int E, int H, int I);
  * fp16 scales)); arguments as for moe_layer_w2a16 with the two format
  * integers after I (zero-points used for bits == 2 only).  Results equal the
  * stage calls with moe_expert_ffn_wna16 bit for bit. */
+/* moe_layer_nvfp4: the one-launch layer with NVFP4 W4A4 experts (the weights,
+ * scales and the two tensor scales of moe_expert_ffn_nvfp4).  The router
+ * reads x as given; each block quantises the activation rows it stages for
+ * the experts (moe_quant_act_nvfp4's steps), so the results equal the stage
+ * calls (moe_route_permute, moe_expert_ffn_nvfp4, moe_combine) bit for bit.
+ * Workspace: moe_layer_workspace_size. */
+moe_status moe_layer_nvfp4(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
+                           int T, int H, int E, int k, int I, float x_gscale, float h_gscale,
+                           const uint32_t *w13_codes, const uint8_t *w13_scales, const float *w13_gscale,
+                           const uint32_t *w2_codes, const uint8_t *w2_scales, const float *w2_gscale,
+                           uint16_t *y, int32_t *topk_ids, float *topk_weights,
+                           void *workspace, size_t workspace_bytes, void *stream);
 moe_status moe_layer_wna16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
                            int T, int H, int E, int k, int I, int bits, int group_size,
                            const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,

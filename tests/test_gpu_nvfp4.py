@@ -134,3 +134,28 @@ def test_nvfp4_every_expert_and_empty_experts_one_workspace():
         assert err <= TOL
     torch.cuda.synchronize()
     assert int(ws._bufs["ffn_nvfp4"].view(torch.int32).abs().sum()) == 0
+
+
+def test_nvfp4_one_launch_layer_matches_stages():
+    """moe_layer_nvfp4 equals route_permute + expert_ffn_nvfp4 + combine bit for bit (each block quantises
+    the rows it stages with the same steps), and the oracle within the bar."""
+    ws = bq.Workspaces("cuda")
+    for i, (T, H, I, E, k) in enumerate([(1, 4096, 1024, 256, 8), (4, 512, 256, 16, 4), (16, 1024, 256, 32, 4)]):
+        sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, I=I, E=E, k=k, bits=4, group=16, seed=5400 + i)
+        inp = workload.make_layer_inputs(sp)
+        wd = _weights_dev(inp.weights)
+        x, wr = to_dev(inp.x), to_dev(inp.w_router)
+        for rep in range(2):
+            y, ids, gates = bq.layer_nvfp4(x, wr, None, wd, sp.k, sp.I, sp.nv_gx, sp.nv_gh, ws=ws, want_routing=True)
+            r = bq.route_permute(x, wr, sp.k)
+            yp = bq.expert_ffn_nvfp4(x, r["offsets"], r["sorted_rows"], r["active"], sp.k, wd, sp.I, sp.nv_gx,
+                                     sp.nv_gh, ws=ws)
+            ys = bq.combine(yp, r["row_pos"], r["gates"])
+            assert torch.equal(ids, r["ids"]) and torch.equal(y.view(torch.int16), ys.view(torch.int16)), (T, rep)
+        ref = oracle.moe_layer_nvfp4(inp.x, inp.w_router, None, inp.weights, sp.k, sp.I, sp.nv_gx, sp.nv_gh)
+        err = oracle.rel_fro(bf16_np_to_f32(to_np(y)), ref["y"])
+        say(f"    T={T} H={H}: one launch = stages bit for bit, y rel-fro {err:.2e}")
+        assert err <= TOL
+    torch.cuda.synchronize()
+    for name, buf in ws._bufs.items():
+        assert int(buf.view(torch.int32).abs().sum()) == 0, name
