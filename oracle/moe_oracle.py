@@ -191,17 +191,28 @@ def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
     if H % SLICES:
         raise ValueError("H must be a multiple of 64")
     L = H // SLICES
-    xs = xf.reshape(T, SLICES, L)
-    ws = wf.reshape(E, SLICES, L)
-    part = np.zeros((T, E, SLICES), dtype=np.float32)
-    for i in range(L):                                          # ascending h in each slice
-        part = part + xs[:, None, :, i] * ws[None, :, :, i]    # float32 product and add
-    while part.shape[-1] > 1:                                   # pairwise tree
-        part = part[..., 0::2] + part[..., 1::2]
-    logits = part[..., 0]
+    ws = np.ascontiguousarray(wf.reshape(E, SLICES, L).transpose(2, 0, 1))      # [L, E, 64]: element i of each slice
+    logits = np.empty((T, E), dtype=np.float32)
+    # Tokens are independent, so they are taken a few at a time (the arrays
+    # then stay in cache); every logit sees the same operations in the same
+    # order whatever the block size.
+    for t0 in range(0, T, _ROUTER_TOKENS):
+        xs = np.ascontiguousarray(xf[t0:t0 + _ROUTER_TOKENS].reshape(-1, SLICES, L).transpose(2, 0, 1))  # [L, n, 64]
+        n = xs.shape[1]
+        part = np.zeros((n, E, SLICES), dtype=np.float32)
+        prod = np.empty_like(part)
+        for i in range(L):                                      # ascending h in each slice
+            np.multiply(xs[i][:, None, :], ws[i][None, :, :], out=prod)   # float32 product (exact)
+            np.add(part, prod, out=part)                        # float32 add
+        while part.shape[-1] > 1:                               # pairwise tree
+            part = part[..., 0::2] + part[..., 1::2]
+        logits[t0:t0 + n] = part[..., 0]
     if bias is not None:
         logits = logits + np.asarray(bias, dtype=np.float32)[None, :]
     return logits.astype(np.float32)
+
+
+_ROUTER_TOKENS = 16  # tokens per block of the router loop (speed only)
 
 
 # ---------------------------------------------------------------- O2, O3

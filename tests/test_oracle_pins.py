@@ -423,7 +423,7 @@ def test_router_within_float32_error_bound_of_exact():
     bound = depth * 2.0**-24 * absum * 1.01
     assert np.all(np.abs(l - exact) <= bound)
     # and it is not trivially exact: some logits differ from the float64 value
-    assert np.any(l != exact.astype(np.float32)) or True
+    assert np.any(l != exact.astype(np.float32))
 
 
 def test_router_transposition_pinned():
@@ -676,3 +676,125 @@ def test_combine_weights_rows_by_gates():
     assert y[0].tolist() == y_perm[4].tolist()
     assert y[1].tolist() == y_perm[5].tolist()
     assert np.allclose(y[2], 0.25 * y_perm[2] + 0.75 * y_perm[3])
+
+
+# ------------------------------------------------------------------ helpers the parity bars rest on
+def test_rel_fro_hand_computed_values():
+    """||a - ref||_F / ||ref||_F on hand-computed cases: the right numerator, the
+    reference's norm as denominator (not a's), Frobenius over every element
+    (not a per-row or spectral norm)."""
+    ref = np.array([6.0, 8.0])                                   # norm 10
+    assert oracle.rel_fro(np.array([9.0, 12.0]), ref) == 0.5     # diff (3, 4): norm 5
+    assert oracle.rel_fro(ref, ref) == 0.0
+    assert abs(oracle.rel_fro(np.array([6.0, 8.0]), np.array([9.0, 12.0])) - 5.0 / 15.0) < 1e-15
+    # matrix: diff = identity (Frobenius sqrt 2, spectral 1), ref Frobenius 2
+    r2 = np.array([[2.0, 0.0], [0.0, 0.0]])
+    a2 = r2 + np.eye(2)
+    assert abs(oracle.rel_fro(a2, r2) - math.sqrt(2.0) / 2.0) < 1e-15
+    # float32 inputs are measured in float64: a 1-ulp difference is not lost
+    one = np.float32(1.0)
+    assert oracle.rel_fro(np.array([np.nextafter(one, np.float32(2))], np.float32), np.array([one])) == 2.0 ** -23
+
+
+def test_bf16_bits_and_silu_closed_forms():
+    """bf16 bits are the top half of float32; silu(v) = v * sigmoid(v)."""
+    assert oracle.bf16_to_f32(np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x4049], np.uint16)).tolist() == \
+        [1.0, -2.0, 0.0, -0.0, 3.140625]
+    v = np.array([0.0, math.log(3.0), -math.log(3.0)], np.float32)
+    got = oracle.silu(v).astype(np.float64)
+    # sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4
+    assert got[0] == 0.0
+    assert abs(got[1] - 0.75 * math.log(3.0)) < 1e-6 and abs(got[2] + 0.25 * math.log(3.0)) < 1e-6
+
+
+def test_router_token_blocks_do_not_change_bits():
+    """Tokens are independent: a batch crossing the oracle's token blocks gives
+    each token's logits bit for bit as a call with that token alone."""
+    rng = np.random.default_rng(17)
+    T, E, H = 37, 9, 256
+    x = _bf16(rng.standard_normal((T, H)))
+    w = _bf16(rng.standard_normal((E, H)) * 0.05)
+    b = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    full = oracle.router_logits(x, w, b)
+    for t in (0, 15, 16, 17, 36):
+        one = oracle.router_logits(x[t:t + 1], w, b)
+        assert np.array_equal(one[0].view(np.uint32), full[t].view(np.uint32)), t
+
+
+# ------------------------------------------------------------------ NVFP4 field order, scale placement, tensor scales
+def test_nvfp4_nibble_order_distinct_fields():
+    """Field i of word w is K index 8w + i, least significant nibble first:
+    words with eight distinct nibbles fix the order."""
+    words = np.array([[0x76543210, 0xFEDCBA98]], np.uint32)
+    assert oracle.unpack_e2m1_fields(words).tolist() == [list(range(16))]
+    # and the value table applied in that order: codes 0..7 positive, 8..15 their negatives
+    v = oracle.e2m1_value(oracle.unpack_e2m1_fields(words))[0]
+    assert v.tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                          -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_nvfp4_group_scale_lands_on_its_own_16_columns():
+    """A different E4M3 scale per group of 16 (and per row): each scale
+    multiplies exactly its own 16 consecutive K (np.tile or a transposed
+    scale array would not)."""
+    words = np.full((2, 8), 0x22222222, np.uint32)               # every code 2 = 1.0, K = 64
+    sc = np.array([[0x38, 0x40, 0x30, 0x48],                     # 1, 2, 0.5, 4
+                   [0x3C, 0x28, 0x01, 0x7E]], np.uint8)          # 1.5, 0.25, 2^-9, 448
+    W = oracle.dequantize_nvfp4(words, sc)
+    exp = np.array([[1.0] * 16 + [2.0] * 16 + [0.5] * 16 + [4.0] * 16,
+                    [1.5] * 16 + [0.25] * 16 + [2.0 ** -9] * 16 + [448.0] * 16], np.float32)
+    assert np.array_equal(W, exp)
+
+
+def test_nvfp4_ffn_tensor_scales_closed_form():
+    """G_x != G_h and w13_gscale != w2_gscale (powers of two, different per
+    expert): the closed form below changes by a factor of 8 or more if any
+    two of them are exchanged.  Every weight is 1 (code 2, scale 1.0); the
+    token's first two values are 6 G_x, so its quantised row is (6, 6, 0...)
+    (scale E4M3(1) = 1), A = 12 G_x g13[e] on every output, h = silu(A) A on
+    all I values, which quantise to 6 s with s = E4M3(h / (6 G_h)) (within
+    2^-4 of h / (6 G_h), and on the E4M3 grid), and y = I * 6 s * G_h * g2[e]."""
+    E, H, I = 2, 32, 16
+    Gx, Gh = 2.0 ** -8, 2.0 ** -5
+    g13 = np.array([2.0, 8.0], np.float32)
+    g2 = np.array([0.25, 16.0], np.float32)
+    wt = {"w13_codes": np.full((E, 2 * I, H // 8), 0x22222222, np.uint32),
+          "w13_scales": np.full((E, 2 * I, H // 16), 0x38, np.uint8), "w13_gscale": g13,
+          "w2_codes": np.full((E, H, I // 8), 0x22222222, np.uint32),
+          "w2_scales": np.full((E, H, I // 16), 0x38, np.uint8), "w2_gscale": g2}
+    x = np.zeros((1, H), np.float32)
+    x[0, :2] = np.float32(6 * Gx)
+    grid8 = set(oracle.e4m3_value(np.arange(0x7F)).tolist())
+    for e in range(E):
+        off = np.array([0] * (e + 1) + [1] * (E - e), np.int32)
+        y = oracle.expert_ffn_nvfp4(_bf16(x), off, np.array([0], np.int32), 1, wt, I, Gx, Gh)[0].astype(np.float64)
+        A = 12.0 * Gx * float(g13[e])
+        h = A / (1.0 + math.exp(-A)) * A
+        s = y[0] / (I * 6.0 * Gh * float(g2[e]))                  # the group scale the quantiser chose
+        assert np.all(y == y[0])
+        assert s in grid8, s
+        assert abs(s / (h / (6.0 * Gh)) - 1.0) <= 2.0 ** -4, (e, s, h)
+
+
+def test_nvfp4_dense_equivalence_all_experts_selected():
+    """k = E with NVFP4 experts: the routed layer equals sum_e softmax(l)_e
+    FFN_e(x), each FFN_e written out densely from the format's definition
+    (quantise x, dequantise both matrices, tensor scales after the products)."""
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", group=16, k=8)
+    inp = workload.make_layer_inputs(sp)
+    out = oracle.moe_layer_nvfp4(inp.x, inp.w_router, None, inp.weights, sp.k, sp.I, sp.nv_gx, sp.nv_gh)
+    xf = oracle.bf16_to_f32(inp.x)
+    l = out["logits"].astype(np.float64)
+    p = np.exp(l - l.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    _, xq = oracle.quant_nvfp4(xf, sp.nv_gx)
+    y = np.zeros((sp.T, sp.H))
+    w = inp.weights
+    for e in range(sp.E):
+        W13 = oracle.dequantize_nvfp4(w["w13_codes"][e], w["w13_scales"][e]).astype(np.float64)
+        W2 = oracle.dequantize_nvfp4(w["w2_codes"][e], w["w2_scales"][e]).astype(np.float64)
+        A = (xq.astype(np.float64) @ W13.T) * (sp.nv_gx * float(w["w13_gscale"][e]))
+        h = (A[:, :sp.I] / (1 + np.exp(-A[:, :sp.I])) * A[:, sp.I:]).astype(np.float32)
+        _, hq = oracle.quant_nvfp4(h, sp.nv_gh)
+        y += p[:, e:e + 1] * ((hq.astype(np.float64) @ W2.T) * (sp.nv_gh * float(w["w2_gscale"][e])))
+    assert oracle.rel_fro(out["y"], y) < 1e-4
