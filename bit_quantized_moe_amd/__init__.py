@@ -22,7 +22,7 @@ __all__ = [
     "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "expert_table", "expert_ffn_table",
     "expert_ffn_nvfp4", "quant_act_nvfp4",
     "layer", "combine", "unpack_codes",
-    "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH",
+    "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH", "workspace_status", "set_wait_limit", "WS_WAIT_TIMEOUT",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbqmoe.so")
@@ -33,6 +33,8 @@ _SIGS = {
     "moe_abi_version": (_c_int, []),
     "moe_status_string": (ctypes.c_char_p, [_c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
+    "moe_workspace_status": (_c_int, [_vp, _c_size, _c_int, ctypes.POINTER(ctypes.c_uint32), _vp]),
+    "moe_set_wait_limit": (_c_int, [_c_int]),
     "moe_route_workspace_size": (_c_size, [_c_int, _c_int]),
     "moe_route": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_permute_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
@@ -108,11 +110,33 @@ def _dev(t: torch.Tensor) -> torch.device:
     return t.device
 
 
+WS_WAIT_TIMEOUT = 1  # MOE_WS_WAIT_TIMEOUT: a bounded cross-block wait gave up
+
+
+def workspace_status(buf: torch.Tensor, clear: bool = True) -> int:
+    """Sticky error flags of a workspace (moe_workspace_status; waits for the current stream)."""
+    dev = _dev(buf)
+    flags = ctypes.c_uint32(0)
+    _check(lib().moe_workspace_status(_p(buf), buf.numel() * buf.element_size(), int(bool(clear)),
+                                      ctypes.byref(flags), _stream(dev)), "moe_workspace_status")
+    return int(flags.value)
+
+
+def set_wait_limit(spins: int) -> int:
+    """Polling rounds before a bounded wait gives up (a test hook; < 0 restores the default).  Returns the old limit."""
+    return int(lib().moe_set_wait_limit(int(spins)))
+
+
+# workspaces that start with a control block (the rest hold none)
+_CTL_WORKSPACES = ("route", "ffn", "ffn_nvfp4", "layer")
+
+
 class Workspaces:
     """Zero-initialised device workspaces, grown on demand and reused across calls.
 
     Each workspace starts with a control block that the kernels leave zeroed,
-    so a buffer can be reused by consecutive calls on one stream.
+    so a buffer can be reused by consecutive calls on one stream.  check()
+    reads the control blocks' error flags and raises if a wait timed out.
     """
 
     def __init__(self, device):
@@ -125,6 +149,19 @@ class Workspaces:
             b = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
             self._bufs[name] = b
         return b
+
+    def check(self) -> None:
+        """Raise MoEError if a bounded wait of a call made with these workspaces
+        gave up (its outputs are unreliable); the flags are cleared and the
+        affected workspace zeroed, so the buffers can be used again."""
+        bad = []
+        for name, b in self._bufs.items():
+            if name in _CTL_WORKSPACES and b.numel() >= 4096 and workspace_status(b, clear=True):
+                b.zero_()
+                bad.append(name)
+        if bad:
+            raise MoEError(f"a bounded wait timed out in the {', '.join(bad)} workspace(s): "
+                           "the outputs of those calls are unreliable (workspaces zeroed)")
 
 
 def route(x: torch.Tensor, w_router: torch.Tensor, k: int, logit_bias: Optional[torch.Tensor] = None,

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "bqmoe.h"
@@ -39,6 +40,8 @@ bool g_dev_ok[kMaxDevices];
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+std::atomic<int> g_wait_spins{kDefaultWaitSpins};
+
 moe_status check_common_moe(int T, int H, int E, int k) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
   if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E must be in [1, 1024] (got %d)", E);
@@ -51,6 +54,8 @@ moe_status check_common_moe(int T, int H, int E, int k) {
 }  // namespace
 
 namespace bqmoe {
+
+int wait_spin_limit() { return g_wait_spins.load(std::memory_order_relaxed); }
 
 hipError_t current_device_info(DeviceInfo *out) {
   int dev = 0;
@@ -106,6 +111,30 @@ const char *moe_status_string(int s) {
 }
 
 const char *moe_last_error(void) { return g_err; }
+
+moe_status moe_workspace_status(void *workspace, size_t workspace_bytes, int clear, uint32_t *flags, void *stream) {
+  if (!workspace || !flags) return fail(MOE_ERR_INVALID_ARG, "moe_workspace_status: workspace and flags are required");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "moe_workspace_status: workspace needs 256-byte alignment");
+  if (workspace_bytes < kCtlBytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_workspace_status: %zu bytes hold no control block (%zu)",
+                workspace_bytes, (size_t)kCtlBytes);
+  const hipStream_t st = (hipStream_t)stream;
+  int *ctl = (int *)workspace;
+  int host = 0;
+  hipError_t e = hipMemcpyAsync(&host, ctl + kCtlError, sizeof host, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return from_hip(e, "moe_workspace_status");
+  *flags = (uint32_t)host;
+  // words 0..3 of the control block hold only the flags word
+  if (clear && host) return from_hip(launch_zero16(ctl, 16, st), "moe_workspace_status clear");
+  return MOE_OK;
+}
+
+int moe_set_wait_limit(int spins) {
+  const int prev = g_wait_spins.load();
+  g_wait_spins.store(spins < 0 ? kDefaultWaitSpins : spins);
+  return prev;
+}
 
 size_t moe_route_workspace_size(int T, int E) {
   if (T < 0 || E < 1) return 0;

@@ -95,11 +95,18 @@ __device__ __forceinline__ u32x4 unpack8_bf16(uint32_t w0, uint32_t w1) {
 // FP6 e2m3: 32 codes, a little-endian stream of 6-bit fields in six words ->
 // 32 bf16 values in K order (16 pairs).  gfx950 converts the 32 codes in one
 // instruction; with scale 1 every e2m3 value is exact in bf16.
+//
+// The conversion is written in inline asm, and the compiler's hazard
+// recognizer does not look inside asm: it cannot count the wait states
+// between this VALU write and a following MFMA that reads the result as its
+// A or B operand (the ISA asks for two).  The s_nop after it, in the same
+// statement, supplies five, so the result is safe to feed straight into an
+// MFMA whatever the compiler schedules next.
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 __device__ __forceinline__ u32x16 fp6x32_to_bf16(u32x6 v) {
   u32x16 r;
-  asm("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, 1.0" : "=&v"(r) : "v"(v));
+  asm("v_cvt_scalef32_pk32_bf16_fp6 %0, %1, 1.0\n\ts_nop 4" : "=&v"(r) : "v"(v));
   return r;
 }
 __device__ __forceinline__ float fp16_to_f32(uint32_t h16) {

@@ -985,8 +985,11 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   auto get_meta = [&](int a) -> Meta {
     if constexpr (LAYER) {
       Meta r;
+      // A slot's first row is below nrows whatever the record held (one
+      // token's phase 2 reads and writes row o0 even for an empty slot, which
+      // only a record read after a timed-out wait can produce).
       r.e = min(max(s_act[1 + a], 0), p.E - 1);
-      r.o0 = min(max(s_start[a], 0), nrows);
+      r.o0 = min(max(s_start[a], 0), nrows - 1);
       r.o1 = min(max(s_start[a + 1], r.o0), nrows);
       return r;
     } else {
@@ -1432,7 +1435,7 @@ static void fill_params(DecodeParams &p, const FfnArgs &a, void *ws) {
   p.y_perm = a.y_perm;
   p.ctl = (int *)ws;
   p.hbuf = (uint32_t *)((char *)ws + ffn_ctl_bytes(a.T, a.k, a.E));
-  p.max_spins = 1 << 22;
+  p.max_spins = wait_spin_limit();
   p.magic = kMagic43;
 }
 

@@ -16,6 +16,12 @@ struct DeviceInfo {
 // Properties of the current device (cached per device, thread-safe).
 hipError_t current_device_info(DeviceInfo *out);
 
+// Polling rounds after which a bounded cross-block wait gives up and raises
+// the workspace's sticky error flag (kDefaultWaitSpins unless a test lowered
+// it through moe_set_wait_limit).
+constexpr int kDefaultWaitSpins = 1 << 22;
+int wait_spin_limit();
+
 // route.hip
 constexpr int kRouteSmallT = 256;  // T at or below: one block per expert (tagged logits) + selector blocks (measured faster than the token-tiled kernel up to T = 256 at H = 4096, E = 256)
 size_t route_workspace_bytes(int T, int E);

@@ -395,7 +395,7 @@ static void launch_route_small(const uint16_t *x, const uint16_t *w_router, cons
   int *ctl = (int *)ws;
   uint64_t *tl = (uint64_t *)((char *)ws + kCtlBytes);
   const int L = H / 64;
-  const int spins = 1 << 22;
+  const int spins = wait_spin_limit();
   dim3 grid(E), block(kWave);
   const size_t lds = GROUP ? (size_t)(kFusedRows + E) * sizeof(int) : 0;
   if (L % 8 == 0)

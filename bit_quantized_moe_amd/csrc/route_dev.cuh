@@ -65,6 +65,7 @@ __device__ void topk_softmax_wave(Load load, int E, int k, int32_t *ids_out, flo
       const uint64_t b = __ballot(key[j] == mx);
       if (b) be = kWave * j + (__ffsll((unsigned long long)b) - 1);
     }
+    be = min(be, E - 1);  // only reachable with non-finite logits (key 0): ids stay valid experts
 #pragma unroll
     for (int j = 0; j < NV; ++j)
       if (lane + kWave * j == be) key[j] = 0u;

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
     MOE_OK = 0,
@@ -95,6 +95,39 @@ const char *moe_status_string(int status);
 
 /* Thread-local detail of the last non-OK status returned on this thread. */
 const char *moe_last_error(void);
+
+/* ---------------------------------------------------------------- workspace status
+ * Kernels that hand values from one block to another (the decode-path expert
+ * FFN, the one-launch layer, the small-batch router) wait for them in bounded
+ * polling loops.  Those kernels size their grids so that every block is
+ * resident at once (from the device's occupancy), so in a lone launch every
+ * wait ends.  A kernel of another stream or process that holds compute units
+ * at the same time can keep some blocks from starting; a wait then gives up
+ * after moe_set_wait_limit rounds (several seconds by default), the kernel
+ * finishes with unreliable outputs and sets a sticky flag in the control
+ * block at the start of the workspace, and the workspace may keep nonzero
+ * words.  Concurrent launches of these kernels on one device are therefore
+ * not supported.
+ *
+ * moe_workspace_status: reads the flags of a workspace of moe_route,
+ * moe_route_permute, moe_expert_ffn_* or moe_layer_* (each starts with the
+ * control block) once the calls that used it have finished.  It enqueues a
+ * 4-byte copy on `stream` and waits for the stream: the one entry point that
+ * synchronises.  flags (out): 0, or MOE_WS_WAIT_TIMEOUT when some wait gave
+ * up; the outputs of the calls since the flags were last cleared are then
+ * unreliable and the workspace must be zeroed before it is used again.
+ * clear != 0 resets the flags (enqueued on `stream`).  workspace: 256-byte
+ * aligned, workspace_bytes >= 4096.
+ */
+#define MOE_WS_WAIT_TIMEOUT 1u
+moe_status moe_workspace_status(void *workspace, size_t workspace_bytes, int clear, uint32_t *flags, void *stream);
+
+/* moe_set_wait_limit: polling rounds after which the bounded waits above give
+ * up, for launches made after the call (process-wide; spins < 0 restores the
+ * default of 4194304).  Returns the previous limit.  A test hook: a small
+ * limit forces the timeout path (outputs unreliable, MOE_WS_WAIT_TIMEOUT set,
+ * every kernel still ends normally). */
+int moe_set_wait_limit(int spins);
 
 /* ---------------------------------------------------------------- routing
  * moe_route: logits l[t,e] = sum_h x[t,h] * w_router[e,h] (+ logit_bias[e]),
@@ -125,6 +158,10 @@ moe_status moe_route(const uint16_t *x, const uint16_t *w_router, const float *l
 /* ---------------------------------------------------------------- permutation
  * moe_permute: groups the n = T*k rows r = t*k + j (token t, slot j) by expert
  * topk_ids[r], keeping r ascending inside each expert (a stable counting sort).
+ * Grouping the rows is what lets each selected expert's weights be read once
+ * for all of its rows, and only the selected experts at all (page
+ * "Qwen3.8-Flash-Next on one 24 GB GPU", "What the patch does": the decode
+ * GEMV reads only the selected experts, in place).
  *
  *   topk_ids       [T, k] int32 in
  *   expert_offsets [E+1] int32 out: rows of expert e are sorted positions
@@ -172,7 +209,10 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  * projection.  While T <= 512 and T*k <= 6*E (at most about six rows per
  * expert) the call uses the decode path (one fused GEMV kernel streaming each
  * selected expert's packed weights once, rows in passes of four); otherwise
- * grouped bf16-MFMA GEMMs.  The permutation arrays must come from moe_permute
+ * grouped bf16-MFMA GEMMs.  The pages dispatch between a GEMV and
+ * dequantise-then-GEMM at 16 rows (page "Qwen3.8-Flash-Next FP6-INT8",
+ * "Quantization quality"); the crossover used here was measured on MI355X
+ * instead, and the choice is made on the host from the sizes alone.  The permutation arrays must come from moe_permute
  * with the same T, k, E.
  *
  *   x           [T, H] bf16, 16-byte aligned
@@ -318,6 +358,11 @@ moe_status moe_device_address(const void *ptr, uint64_t *out);
 /* ---------------------------------------------------------------- combine
  * moe_combine: y[t] = sum over j = 0..k-1 (ascending) of
  *   topk_weights[t, j] * y_perm[row_pos[t*k + j]]   in float32, stored as bf16.
+ * The pages name top-k routing with softmax gates but do not spell out the
+ * combine; this gate-weighted sum of the k expert outputs is the plainest
+ * reading, accumulated in float32 like every other sum of the layer (page
+ * "Qwen3.8-Flash-Next FP6-INT8", "Precision map": bf16 activations, float32
+ * accumulation).
  * Rows with row_pos < 0 contribute nothing.
  *   y_perm [T*k, H] bf16, row_pos [T*k] int32, topk_weights [T, k] float32,
  *   y [T, H] bf16 out.  y_perm and y 16-byte aligned, H % 8 == 0.

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = bq.lib()
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for s in range(6):
         assert L.moe_status_string(s)
     assert L.moe_status_string(99) == b"unknown status"
@@ -199,3 +199,25 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(bq.MoEError):
         bq.route(torch.zeros((1, 256), dtype=torch.bfloat16), torch.zeros((8, 256), dtype=torch.bfloat16), 2)
+
+
+def test_workspace_status_argument_errors():
+    L = bq.lib()
+    flags = ctypes.c_uint32(7)
+    assert L.moe_workspace_status(None, 4096, 1, ctypes.byref(flags), None) == INVALID
+    assert L.moe_workspace_status(A, 4096, 1, None, None) == INVALID
+    assert L.moe_workspace_status(A + 16, 4096, 1, ctypes.byref(flags), None) == MISALIGNED
+    assert L.moe_workspace_status(A, 1024, 1, ctypes.byref(flags), None) == WS_SMALL
+    assert b"control block" in L.moe_last_error()
+    assert flags.value == 7                            # untouched on an error
+
+
+def test_wait_limit_set_and_restored():
+    L = bq.lib()
+    prev = L.moe_set_wait_limit(5)
+    try:
+        assert prev == 1 << 22
+        assert L.moe_set_wait_limit(-1) == 5           # < 0 restores the default
+        assert L.moe_set_wait_limit(-1) == 1 << 22
+    finally:
+        L.moe_set_wait_limit(-1)

@@ -91,6 +91,20 @@ def test_nvfp4_ffn_small_shapes(T, H, I, E, k):
     _check(sp)
 
 
+@pytest.mark.parametrize("T,H,I,E,k", [(1, 256, 128, 8, 2), (5, 512, 256, 16, 4), (40, 256, 128, 8, 2),
+                                       (300, 1024, 256, 32, 4), (1, 4096, 1024, 8, 2)], ids=lambda v: str(v))
+def test_nvfp4_ffn_full_e4m3_scale_range(T, H, I, E, k):
+    """Group-scale codes over every positive finite E4M3 value (0x01..0x7E:
+    the subnormals 2^-9..7*2^-9 up to 448), through the decode kernel (T = 1,
+    5) and the grouped GEMMs (T = 40, 300)."""
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, I=I, E=E, k=k, bits=4, group=16,
+                       nv_scale_codes=(0x01, 0x7E), seed=5600 + T + H)
+    inp = workload.make_layer_inputs(sp)
+    codes = np.concatenate([inp.weights["w13_scales"].ravel(), inp.weights["w2_scales"].ravel()])
+    assert codes.min() == 0x01 and codes.max() == 0x7E
+    _check(sp)
+
+
 def test_nvfp4_ffn_decode_full_size():
     _check(workload.spec("decode_t1_h4096_e256_k8_i1024_nvfp4"))
 

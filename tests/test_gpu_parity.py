@@ -112,13 +112,14 @@ def test_route_decode_full_size(name):
 
 
 @pytest.mark.parametrize("name", ["prefill_t4096_h4096_e256_k8_i1024_int4", "prefill_t8192_h4096_e256_k8_i1024_int2"])
-def test_route_prefill_full_size_sampled(name):
+def test_route_prefill_full_size_all_tokens(name):
+    """The token-tiled prefill router against the oracle on every token: logit
+    bits, ids and gates (near-ties under the Zipf prior included)."""
     sp = workload.spec(name)
     w_r, bias = workload.make_router(sp)
     x = workload.make_x(sp)
-    tok = np.random.default_rng(5).choice(sp.T, 128, replace=False)
-    tok = np.concatenate([tok, [0, sp.T - 1]])
-    _check_route(x, w_r, bias, sp.k, tokens=tok)
+    ids, _ = _check_route(x, w_r, bias, sp.k)
+    say(f"    {sp.T} tokens: logits, ids and gates match the oracle")
 
 
 # ------------------------------------------------------------------ permutation
@@ -370,15 +371,25 @@ def test_layer_decode_full_size(name):
 @pytest.mark.parametrize("name", ["prefill_t4096_h4096_e256_k8_i1024_int4", "prefill_t8192_h4096_e256_k8_i1024_int2",
                                   "mid_t64_h4096_e256_k8_i1024_int4"])
 def test_layer_prefill_full_size_sampled(name):
+    """Routing and permutation of every token against the oracle's own (logit
+    bits, ids, gates; offsets, sorted_rows, row_pos, active from the oracle's
+    ids); the FFN output on sampled experts and tokens the oracle computes one
+    by one."""
     sp = workload.spec(name)
     inp = workload.make_layer_inputs(sp)
     wd = weights_to_dev(inp.weights)
-    out = bq.moe_layer(to_dev(inp.x), to_dev(inp.w_router), to_dev(inp.logit_bias), wd, sp.k, sp.bits, sp.I)
+    out = bq.moe_layer(to_dev(inp.x), to_dev(inp.w_router), to_dev(inp.logit_bias) if inp.logit_bias is not None
+                       else None, wd, sp.k, sp.bits, sp.I, want_logits=True)
     got = {kk: to_np(v) for kk, v in out.items()}
-    # permutation is a function of the ids: check it in full against the oracle on the GPU ids
-    r_off, r_sr, r_rp, r_act = oracle.permute(got["ids"], sp.E)
+    ref_l = oracle.router_logits(inp.x, inp.w_router, inp.logit_bias)
+    assert np.array_equal(got["logits"].view(np.uint32), ref_l.view(np.uint32)), "router logits differ"
+    ref_ids, ref_g = oracle.topk_softmax(ref_l, sp.k)
+    assert np.array_equal(got["ids"], ref_ids), "ids"
+    assert np.max(np.abs(got["gates"] - ref_g)) <= 1e-6
+    r_off, r_sr, r_rp, r_act = oracle.permute(ref_ids, sp.E)
     for key, r in (("offsets", r_off), ("sorted_rows", r_sr), ("row_pos", r_rp), ("active", r_act)):
         assert np.array_equal(got[key], r), key
+    say(f"    routing and permutation of all {sp.T} tokens bit-exact")
     counts = np.diff(got["offsets"])
     say(f"    rows/expert: max {counts.max()}, empty {(counts == 0).sum()}, <81: {(counts < 81).sum()}")
     # sampled experts: the hottest, a middle one, the coldest non-empty one

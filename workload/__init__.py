@@ -71,6 +71,7 @@ class Spec:
     group: int = 128               # quantisation group along K (128 or 32; 16 marks NVFP4)
     nv_gx: float = 2.0 ** -8       # NVFP4: tensor scales of the activation and h quantisers
     nv_gh: float = 2.0 ** -7
+    nv_scale_codes: tuple = (0x28, 0x47)  # NVFP4: E4M3 group-scale codes drawn uniformly from this range
     n_sets: int = 1                # distinct weight sets cycled by the bench
     note: str = ""
 
@@ -231,14 +232,16 @@ def _fp16_scales(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
 def _nvfp4_weight_set(sp: Spec, set_idx: int) -> Dict[str, np.ndarray]:
     """NVFP4 experts: E2M1 codes uniform over the 16 codes (uniform words, 8
     per word along K), E4M3 group scales drawn uniformly from the codes
-    0x28..0x47 (0.25 .. 3.75), float32 tensor scales 0.004 * U(1, 1.25) per
-    expert and projection."""
+    nv_scale_codes (by default 0x28..0x47, i.e. 0.25 .. 3.75; 0x01..0x7E spans
+    every positive finite E4M3 value, subnormals and 448 included), float32
+    tensor scales 0.004 * U(1, 1.25) per expert and projection."""
     E, H, I = sp.E, sp.H, sp.I
     out = {}
     for name, tc, ts, tz, (N, K) in (("w13", _TAG_W13C, _TAG_W13S, _TAG_W13Z, (2 * I, H)),
                                      ("w2", _TAG_W2C, _TAG_W2S, _TAG_W2Z, (H, I))):
         out[f"{name}_codes"] = _uniform_words(_rng(sp.seed, tc, set_idx), (E, N, K // 8))
-        out[f"{name}_scales"] = _rng(sp.seed, ts, set_idx).integers(0x28, 0x48, size=(E, N, K // 16), dtype=np.uint8)
+        lo, hi = sp.nv_scale_codes
+        out[f"{name}_scales"] = _rng(sp.seed, ts, set_idx).integers(lo, hi + 1, size=(E, N, K // 16), dtype=np.uint8)
         out[f"{name}_gscale"] = (0.004 * _rng(sp.seed, tz, set_idx).uniform(1.0, 1.25, size=E)).astype(np.float32)
     return out
 
