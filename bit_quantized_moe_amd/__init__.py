@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "expert_table", "expert_ffn_table",
     "expert_ffn_nvfp4", "quant_act_nvfp4",
-    "layer", "combine", "unpack_codes",
+    "layer", "layer_noalloc", "combine", "unpack_codes",
     "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH", "workspace_status", "set_wait_limit", "WS_WAIT_TIMEOUT",
 ]
 
@@ -59,6 +59,7 @@ _SIGS = {
                         + [_vp, _c_size, _vp]),
     "moe_layer_wna16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_layer_w2a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
+    "moe_layer_w4a16_noalloc": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp] * 3 + [_vp]),
     "moe_unpack_codes": (_c_int, [_vp, _c_int, _c_i64, _vp, _vp]),
     "moe_dequant_bf16": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_dequant_bf16_grouped": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
@@ -401,6 +402,22 @@ def layer(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Te
         raise MoEError("bits must be 2 or 4")
     _check(s, f"moe_layer_w{bits}a16")
     return (y, ids, gates) if want_routing else y
+
+
+def layer_noalloc(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],
+                  weights: Dict[str, torch.Tensor], k: int, I: int, y: Optional[torch.Tensor] = None,
+                  ids: Optional[torch.Tensor] = None, gates: Optional[torch.Tensor] = None):
+    """The INT4 one-launch layer with the library's own device scratch as its workspace
+    (moe_layer_w4a16_noalloc): no workspace argument; outputs may be passed in preallocated."""
+    dev = _dev(x)
+    T, H = x.shape
+    E = w_router.shape[0]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if y is None else y
+    _check(lib().moe_layer_w4a16_noalloc(_p(x), _p(w_router), _p(logit_bias), T, H, E, k, I,
+                                         _p(weights["w13_codes"]), _p(weights["w13_scales"]),
+                                         _p(weights["w2_codes"]), _p(weights["w2_scales"]), _p(y), _p(ids),
+                                         _p(gates), _stream(dev)), "moe_layer_w4a16_noalloc")
+    return y
 
 
 def layer_nvfp4(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor],

@@ -42,6 +42,34 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 std::atomic<int> g_wait_spins{kDefaultWaitSpins};
 
+// ---- workspace of moe_layer_w4a16_noalloc: a file-scope device array.
+// Each device the library runs on holds its own copy (reserved when the code
+// object is loaded, kept until the process ends).  In host code the name
+// `scratch` is only a host-side stand-in for the symbol, not a device
+// address: host code uses the address hipGetSymbolAddress returns for the
+// current device, looked up once per device on the first call there.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 moe_status check_common_moe(int T, int H, int E, int k) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
   if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E must be in [1, 1024] (got %d)", E);
@@ -423,7 +451,7 @@ static moe_status layer(const char *name, int bits, const uint16_t *x, const uin
                         const uint16_t *w13_scales, const uint8_t *w13_zeros, const uint32_t *w2_codes,
                         const uint16_t *w2_scales, const uint8_t *w2_zeros, uint16_t *y, int32_t *topk_ids,
                         float *topk_weights, void *workspace, size_t workspace_bytes, void *stream,
-                        int group = 128) {
+                        int group = 128, bool use_scratch = false) {
   moe_status s = check_common_moe(T, H, E, k);
   if (s != MOE_OK) return s;
   if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
@@ -433,7 +461,7 @@ static moe_status layer(const char *name, int bits, const uint16_t *x, const uin
                 "%s: one-launch layer needs 1 <= T <= %d and a decode-path shape (T=%d, k=%d, E=%d, H=%d, I=%d); "
                 "call the stages instead",
                 name, kLayerMaxT, T, k, E, H, I);
-  if (!x || !w_router || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !y || !workspace)
+  if (!x || !w_router || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !y || (!workspace && !use_scratch))
     return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
   if (bits == 2 && (!w13_zeros || !w2_zeros)) return fail(MOE_ERR_INVALID_ARG, "%s: zero-points are required", name);
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16))
@@ -441,13 +469,30 @@ static moe_status layer(const char *name, int bits, const uint16_t *x, const uin
   if (!aligned(w13_scales, 2) || !aligned(w2_scales, 2) || !aligned(y, 4) || (topk_ids && !aligned(topk_ids, 4)) ||
       (topk_weights && !aligned(topk_weights, 4)) || (logit_bias && !aligned(logit_bias, 4)))
     return fail(MOE_ERR_MISALIGNED, "%s: array alignment", name);
-  if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
   const size_t need = moe_layer_workspace_size(T, k, E, H, I);
-  if (workspace_bytes < need)
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", name, workspace_bytes, need);
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                  "%s: this shape needs %zu bytes of workspace, more than the %zu-byte scratch; call the entry point "
+                  "that takes a workspace",
+                  name, need, kScratchBytes);
+  } else {
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
+    if (workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", name, workspace_bytes, need);
+  }
   DeviceInfo dev;
   hipError_t he = current_device_info(&dev);
   if (he != hipSuccess) return from_hip(he, name);
+  if (use_scratch) {
+    // The scratch keeps the previous call's contents (left zero unless a wait
+    // timed out), so every call clears the region it uses before its launch;
+    // with a fill kernel, not a memset, since callers may capture the call in
+    // a graph.
+    he = scratch_address(&workspace);
+    if (he == hipSuccess) he = launch_zero16(workspace, need, (hipStream_t)stream);
+    if (he != hipSuccess) return from_hip(he, name);
+  }
   FfnArgs a{x, nullptr, nullptr, nullptr, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
             w2_codes, w2_scales, w2_zeros, nullptr, workspace, nullptr, group};
   LayerArgs l{w_router, logit_bias, y, topk_ids, topk_weights, nullptr};
@@ -518,6 +563,14 @@ moe_status moe_layer_w4a16(const uint16_t *x, const uint16_t *w_router, const fl
                            float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
   return layer("moe_layer_w4a16", 4, x, w_router, logit_bias, T, H, E, k, I, w13_codes, w13_scales, nullptr,
                w2_codes, w2_scales, nullptr, y, topk_ids, topk_weights, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_layer_w4a16_noalloc(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H,
+                                   int E, int k, int I, const uint32_t *w13_codes, const uint16_t *w13_scales,
+                                   const uint32_t *w2_codes, const uint16_t *w2_scales, uint16_t *y,
+                                   int32_t *topk_ids, float *topk_weights, void *stream) {
+  return layer("moe_layer_w4a16_noalloc", 4, x, w_router, logit_bias, T, H, E, k, I, w13_codes, w13_scales, nullptr,
+               w2_codes, w2_scales, nullptr, y, topk_ids, topk_weights, nullptr, 0, stream, 128, true);
 }
 
 moe_status moe_layer_w2a16(const uint16_t *x, const uint16_t *w_router, const float *logit_bias, int T, int H, int E,

@@ -428,6 +428,28 @@ moe_status moe_layer_w2a16(const uint16_t *x, const uint16_t *w_router, const fl
                            uint16_t *y, int32_t *topk_ids, float *topk_weights,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- the layer without a workspace
+ * moe_layer_w4a16_noalloc: moe_layer_w4a16 for callers that cannot allocate
+ * device memory - code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments without the workspace,
+ * same kernels, same results bit for bit.  The workspace is a file-scope
+ * device array of the library (8 MiB, one per GPU, reserved when the library's
+ * code is loaded on that GPU and kept until the process ends); the call
+ * allocates and frees nothing.  Shapes whose moe_layer_workspace_size exceeds
+ * 8 MiB return MOE_ERR_UNSUPPORTED_SHAPE (T*k <= 256 with H = 4096, I = 1024
+ * and E <= 1024 fit).  Every call first clears the part of the array it uses
+ * with a fill kernel on `stream`, then launches the layer.  All calls on one
+ * GPU share that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued.  A wait that timed out
+ * inside such a call is not reported (there is no caller-visible workspace to
+ * read the flag from); the next call starts from a cleared array.
+ */
+moe_status moe_layer_w4a16_noalloc(const uint16_t *x, const uint16_t *w_router, const float *logit_bias,
+                                   int T, int H, int E, int k, int I,
+                                   const uint32_t *w13_codes, const uint16_t *w13_scales,
+                                   const uint32_t *w2_codes, const uint16_t *w2_scales,
+                                   uint16_t *y, int32_t *topk_ids, float *topk_weights, void *stream);
+
 /* ---------------------------------------------------------------- diagnostics
  * moe_unpack_codes: the signed codes of n_words packed words, unpacked by the
  * same device routine the decode kernels use (INT4: q = field - 8; 2-bit:

@@ -221,3 +221,21 @@ def test_wait_limit_set_and_restored():
         assert L.moe_set_wait_limit(-1) == 1 << 22
     finally:
         L.moe_set_wait_limit(-1)
+
+
+def test_layer_noalloc_argument_errors():
+    """Argument errors come back before the library looks up its scratch (no GPU needed)."""
+    L = bq.lib()
+    f = L.moe_layer_w4a16_noalloc
+    args = [A, A, None, 1, 4096, 256, 8, 1024, A, A, A, A, A, None, None, None]
+    assert f(*args[:3], 0, *args[4:]) == OK                          # T = 0: nothing to do
+    bad = list(args); bad[0] = None
+    assert f(*bad) == INVALID
+    bad = list(args); bad[0] = A + 4
+    assert f(*bad) == MISALIGNED
+    bad = list(args); bad[3] = 16; bad[6] = 16                       # T*k = 256 at I = 4096: > 8 MiB
+    bad[7] = 4096
+    assert f(*bad) == SHAPE
+    assert b"scratch" in L.moe_last_error()
+    bad = list(args); bad[3] = 17                                    # one-launch layer: T <= 16
+    assert f(*bad) == SHAPE
