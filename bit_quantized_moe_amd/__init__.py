@@ -61,6 +61,9 @@ _SIGS = {
     "moe_layer_w2a16": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 6 + [_vp] * 3 + [_vp, _c_size, _vp]),
     "moe_layer_w4a16_noalloc": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_vp] * 3 + [_vp]),
     "moe_unpack_codes": (_c_int, [_vp, _c_int, _c_i64, _vp, _vp]),
+    "moe_probe_stream_blocks": (_c_size, [_c_size]),
+    "moe_probe_stream_read": (_c_int, [_vp, _c_size, _vp, _vp]),
+    "moe_probe_mfma": (_c_int, [_c_int, _c_int, _vp, _vp]),
     "moe_dequant_bf16": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_dequant_bf16_grouped": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
 }

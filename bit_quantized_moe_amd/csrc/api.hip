@@ -631,4 +631,19 @@ moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const
   return moe_dequant_bf16_grouped(words, scales, zeros, bits, 128, N, K, out, stream);
 }
 
+size_t moe_probe_stream_blocks(size_t bytes) { return probe_stream_blocks(bytes); }
+
+moe_status moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {
+  if (!buf || !out) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream_read: buf and out are required");
+  if (!aligned(buf, 16) || bytes % 16) return fail(MOE_ERR_MISALIGNED, "moe_probe_stream_read: 16-byte units");
+  if (probe_stream_blocks(bytes) > (1u << 31) - 1) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream_read: too large");
+  return from_hip(launch_probe_stream(buf, bytes, out, (hipStream_t)stream), "moe_probe_stream_read");
+}
+
+moe_status moe_probe_mfma(int blocks, int iters, float *out, void *stream) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "moe_probe_mfma: out is required");
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1) return fail(MOE_ERR_INVALID_ARG, "moe_probe_mfma: sizes");
+  return from_hip(launch_probe_mfma(blocks, iters, out, (hipStream_t)stream), "moe_probe_mfma");
+}
+
 }  // extern "C"

@@ -37,6 +37,10 @@ constexpr int BK = 64;                       // K per tile: half a 128 group, tw
 constexpr int kRowBytes = BK * 2;            // one LDS row: 64 bf16 = 8 chunks of 16 B
 constexpr int kTileBytes = 128 * kRowBytes;  // 16 KiB per operand tile
 constexpr int kBufWord3 = 0x00020000;        // buffer resource word 3: raw 32-bit access
+#ifndef BQ_MGROUP
+#define BQ_MGROUP 1
+#endif
+constexpr int kMGroup = BQ_MGROUP;          // consecutive M-tile slots per XCD, iterated fastest
 
 struct GemmParams {
   const uint16_t *a_src;   // G1: x [T, H]; G2: h [T*k, I]
@@ -127,8 +131,9 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
   // M tile go to consecutive blocks of the same XCD, so the A tile is read
   // into that XCD's L2 once and reused by all of them.
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-  const int nb = local % p.n_blocks;
-  const int mslot = (local / p.n_blocks) * 8 + xcd;
+  const int msub = local % kMGroup;
+  const int nb = (local / kMGroup) % p.n_blocks;
+  const int mslot = (local / kMGroup / p.n_blocks) * (8 * kMGroup) + xcd * kMGroup + msub;
   int e, m0, rows;
   if (!find_tile(p, mslot, &e, &m0, &rows)) return;
   constexpr bool NV = GS == 16;
@@ -387,7 +392,7 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
   const int nrows = a.T * a.k;
   const int Amax = a.E < nrows ? a.E : nrows;
   long slots = ((long)nrows + (long)Amax * (BM - 1)) / BM;
-  slots = (slots + 7) / 8 * 8;  // whole rounds of the 8 XCDs
+  slots = (slots + 8 * kMGroup - 1) / (8 * kMGroup) * (8 * kMGroup);  // whole rounds of the 8 XCDs
   uint16_t *hbuf = (uint16_t *)((char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E));
 
   GemmParams g1;

@@ -109,4 +109,9 @@ hipError_t launch_quant_nvfp4(const uint16_t *x, int64_t n, float G, uint16_t *v
 hipError_t launch_dequant_bf16(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros, int bits,
                                int group, int N, int K, uint16_t *out, hipStream_t st);
 
+// probe.hip: the achievable HBM read rate and bf16 MFMA rate of the device
+size_t probe_stream_blocks(size_t bytes);  // blocks (and words of out) of one stream probe launch
+hipError_t launch_probe_stream(const void *buf, size_t bytes, uint32_t *out, hipStream_t st);
+hipError_t launch_probe_mfma(int blocks, int iters, float *out, hipStream_t st);
+
 }  // namespace bqmoe

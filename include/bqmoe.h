@@ -472,6 +472,20 @@ moe_status moe_dequant_bf16(const uint32_t *words, const uint16_t *scales, const
 moe_status moe_dequant_bf16_grouped(const uint32_t *words, const uint16_t *scales, const uint8_t *zeros,
                                     int bits, int group_size, int N, int K, uint16_t *out, void *stream);
 
+/* ---------------------------------------------------------------- measurement probes
+ * The device's achievable rates, measured by the benchmark next to the spec
+ * sheet's peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16 MFMA):
+ * moe_probe_stream_read: reads `bytes` (a multiple of 16; buf 16-byte
+ *   aligned) once in one launch, each thread eight 16-byte loads all in flight
+ *   together, and writes one folded word per block to out
+ *   [moe_probe_stream_blocks(bytes)] (so the reads cannot be dropped).
+ * moe_probe_mfma: `blocks` blocks of four waves, each wave issuing 8 * iters
+ *   v_mfma_f32_16x16x32_bf16 (16384 flops each) on register operands with eight
+ *   independent accumulators; out [4 * blocks] float32 (the folded sums). */
+size_t moe_probe_stream_blocks(size_t bytes);
+moe_status moe_probe_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream);
+moe_status moe_probe_mfma(int blocks, int iters, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
