@@ -1000,9 +1000,6 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   bool routed = false;  // fused layer: this block has counted itself done with the record
   for (int item = blockIdx.x; item < n1 + n2; item += gridDim.x) {
     if (item < n1) {
-#if defined(BQ_PRIO1) && BQ_PRIO1 > 0
-      __builtin_amdgcn_s_setprio(BQ_PRIO1);
-#endif
       // ============================================================ phase 1
       const int a = item / per1, i0 = (item - a * per1) * kRows1;
       const Meta md = get_meta(a);
@@ -1089,12 +1086,6 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       }
     } else {
       // ============================================================ phase 2
-#if defined(BQ_PRIO1) && BQ_PRIO1 > 0
-      __builtin_amdgcn_s_setprio(0);
-#endif
-#if defined(BQ_P2_SLEEP) && BQ_P2_SLEEP > 0
-      for (int z = 0; z < BQ_P2_SLEEP; ++z) __builtin_amdgcn_s_sleep(16);
-#endif
       const int it = item - n1;
       const int a = it / per2, n0 = (it - a * per2) * kRows2 + wv * 32;
       const Meta md = get_meta(a);

@@ -37,10 +37,7 @@ constexpr int BK = 64;                       // K per tile: half a 128 group, tw
 constexpr int kRowBytes = BK * 2;            // one LDS row: 64 bf16 = 8 chunks of 16 B
 constexpr int kTileBytes = 128 * kRowBytes;  // 16 KiB per operand tile
 constexpr int kBufWord3 = 0x00020000;        // buffer resource word 3: raw 32-bit access
-#ifndef BQ_MGROUP
-#define BQ_MGROUP 1
-#endif
-constexpr int kMGroup = BQ_MGROUP;          // consecutive M-tile slots per XCD, iterated fastest
+constexpr int kMGroup = 1;  // consecutive M-tile slots per XCD, iterated fastest (2-8 measured: no gain)
 
 struct GemmParams {
   const uint16_t *a_src;   // G1: x [T, H]; G2: h [T*k, I]

@@ -142,6 +142,12 @@ SPECS: Dict[str, Spec] = {
         Spec("mid_t64_h4096_e256_k8_i1024_int4", T=64, H=4096, E=256, k=8, I=1024, bits=4,
              seed=1006, router_law="uniform", x_law="ar1_streams", streams=16, n_sets=2,
              note="middle batch: 16 streams x 4 draft tokens (higher-concurrency verify), decode path"),
+        Spec("mid_t256_h4096_e256_k8_i1024_int4", T=256, H=4096, E=256, k=8, I=1024, bits=4,
+             seed=1015, router_law="uniform", x_law="ar1_streams", streams=64, n_sets=2,
+             note="middle batch: 64 streams x 4 draft tokens, about 8 rows per expert"),
+        Spec("mid_t512_h4096_e256_k8_i1024_int4", T=512, H=4096, E=256, k=8, I=1024, bits=4,
+             seed=1016, router_law="uniform", x_law="ar1_streams", streams=128, n_sets=2,
+             note="middle batch: 128 streams x 4 draft tokens, about 16 rows per expert"),
     ]
 }
 
@@ -186,13 +192,17 @@ def make_x(sp: Spec, set_idx: int = 0) -> np.ndarray:
     if sp.x_law == "normal":
         xf = rng.standard_normal((sp.T, sp.H), dtype=np.float32)
     elif sp.x_law == "ar1_streams":
-        # consecutive tokens of a stream: x_{j+1} = a*x_j + sqrt(1-a^2)*eps
-        per = sp.T // sp.streams
+        # consecutive tokens of a stream: x_{j+1} = a*x_j + sqrt(1-a^2)*eps;
+        # streams of ceil(T / streams) tokens fill the rows in order (T rows in all)
+        n_streams = max(1, min(sp.streams, sp.T))
+        per = -(-sp.T // n_streams)
         a = sp.ar1_alpha
         xf = np.empty((sp.T, sp.H), np.float32)
-        for s in range(sp.streams):
+        for s in range(n_streams):
             cur = rng.standard_normal(sp.H, dtype=np.float32)
             for j in range(per):
+                if s * per + j >= sp.T:
+                    break
                 if j:
                     eps = rng.standard_normal(sp.H, dtype=np.float32)
                     cur = (a * cur + math.sqrt(1.0 - a * a) * eps).astype(np.float32)
