@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "expert_table", "expert_ffn_table",
-    "expert_ffn_nvfp4", "quant_act_nvfp4",
+    "expert_ffn_nvfp4_table", "expert_ffn_nvfp4", "quant_act_nvfp4",
     "layer", "layer_noalloc", "combine", "unpack_codes",
     "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH", "workspace_status", "set_wait_limit", "WS_WAIT_TIMEOUT",
 ]
@@ -51,6 +51,9 @@ _SIGS = {
     "moe_quant_act_nvfp4": (_c_int, [_vp, _c_i64, ctypes.c_float, _vp, _vp, _vp]),
     "moe_expert_ffn_w4a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _vp, _c_size, _vp]),
+    "moe_expert_ffn_wna16_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 7 + [_vp, _vp, _vp, _c_size, _vp]),
+    "moe_expert_ffn_nvfp4_table": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [ctypes.c_float] * 2
+                                   + [_vp, _vp, _vp, _c_size, _vp]),
     "moe_device_address": (_c_int, [_vp, ctypes.POINTER(ctypes.c_uint64)]),
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_layer_workspace_size": (_c_size, [_c_int] * 5),
@@ -270,19 +273,36 @@ def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: D
 
 
 _TABLE_FIELDS = ("w13_codes", "w13_scales", "w13_zeros", "w2_codes", "w2_scales", "w2_zeros")
+# NVFP4 rows keep the address of each projection's float32 tensor scale where
+# the other formats keep their zero-points
+_TABLE_FIELDS_NVFP4 = ("w13_codes", "w13_scales", "w13_gscale", "w2_codes", "w2_scales", "w2_gscale")
+_TABLE_ALIGN = {"codes": 16, "scales": 2, "zeros": 1, "gscale": 4}
 
 
-def expert_table(experts, bits: int, device=None) -> torch.Tensor:
-    """Per-expert address table [E, 6] int64 for ``expert_ffn_table``.
+def _device_address(L, ptr: int, what: str) -> int:
+    a = ctypes.c_uint64(0)
+    _check(L.moe_device_address(ctypes.c_void_p(ptr), ctypes.byref(a)), f"moe_device_address ({what})")
+    return a.value
+
+
+def expert_table(experts, bits, device=None) -> torch.Tensor:
+    """Per-expert address table [E, 6] int64 for ``expert_ffn_table`` and
+    ``expert_ffn_nvfp4_table``.
 
     ``experts`` is a list with one dict per expert (the keys of the stacked
     weights, each tensor that expert's own contiguous block, in device memory
     or in pinned host memory), or one stacked weights dict, whose [e] slices
-    are used.  Addresses go through ``moe_device_address``, which rejects
-    memory the kernels cannot read.  The table does not keep the expert
-    tensors alive.  ``device`` is where the table itself lives: a CUDA device
-    (default: the current one) or "pinned" for pinned host memory.
+    are used.  ``bits`` is the format's code width, or "nvfp4" (then entries 2
+    and 5 hold the addresses of the expert's w13 / w2 float32 tensor scales).
+    Zero-point entries are filled for 2-bit experts only.  Addresses go through
+    ``moe_device_address``, which rejects memory the kernels cannot read; code
+    blocks must be 16-byte, scale blocks 2-byte and tensor scales 4-byte
+    aligned.  The table does not keep the expert tensors alive.  ``device`` is
+    where the table itself lives: a CUDA device (default: the current one) or
+    "pinned" for pinned host memory.
     """
+    nv = bits == "nvfp4"
+    fields = _TABLE_FIELDS_NVFP4 if nv else _TABLE_FIELDS
     if isinstance(experts, dict):
         E = experts["w13_codes"].shape[0]
         experts = [{n: t[e] for n, t in experts.items()} for e in range(E)]
@@ -290,61 +310,78 @@ def expert_table(experts, bits: int, device=None) -> torch.Tensor:
     rows = []
     for e, w in enumerate(experts):
         row = []
-        for n in _TABLE_FIELDS:
-            t = w.get(n)
-            if t is None or (bits == 4 and n.endswith("zeros")):
+        for n in fields:
+            kind = n.split("_", 1)[1]
+            if kind == "zeros" and bits != 2:
                 row.append(0)
                 continue
+            t = w.get(n)
+            if t is None:
+                raise MoEError(f"expert_table: expert {e} has no {n}")
             if not t.is_contiguous():
                 raise MoEError(f"expert_table: expert {e} {n} is not contiguous")
-            a = ctypes.c_uint64(0)
-            _check(L.moe_device_address(ctypes.c_void_p(t.data_ptr()), ctypes.byref(a)),
-                   f"moe_device_address (expert {e} {n})")
-            row.append(a.value)
+            if t.data_ptr() % _TABLE_ALIGN[kind]:
+                raise MoEError(f"expert_table: expert {e} {n} needs {_TABLE_ALIGN[kind]}-byte alignment")
+            row.append(_device_address(L, t.data_ptr(), f"expert {e} {n}"))
         rows.append(row)
-    tab = torch.tensor(rows, dtype=torch.int64).view(-1, len(_TABLE_FIELDS))
+    tab = torch.tensor(rows, dtype=torch.int64).view(-1, len(fields))
     if device == "pinned":
         return tab.pin_memory()
     return tab.to(torch.device("cuda", torch.cuda.current_device()) if device is None else device)
 
 
+def _table_arg(L, table: torch.Tensor, E: int, name: str) -> int:
+    if table.dtype != torch.int64 or tuple(table.shape) != (E, len(_TABLE_FIELDS)):
+        raise MoEError(f"{name}: table must be int64 [{E}, {len(_TABLE_FIELDS)}]")
+    if not (table.is_cuda or table.is_pinned()):
+        raise MoEError(f"{name}: the table must be in device or pinned host memory")
+    return _p(table) if table.is_cuda else _device_address(L, _p(table), "table")
+
+
 def expert_ffn_table(x: torch.Tensor, offsets, sorted_rows, active, k: int, table: torch.Tensor, bits: int, I: int,
-                     ws: Optional[Workspaces] = None, y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """``expert_ffn`` with the expert weights found through an address table."""
+                     ws: Optional[Workspaces] = None, y_perm: Optional[torch.Tensor] = None,
+                     group: int = 128) -> torch.Tensor:
+    """``expert_ffn`` with the expert weights found through an address table
+    (bits 4 or 2 with group 128: the w4a16 / w2a16 table calls; other formats
+    the wna16 table call)."""
     dev = _dev(x)
     T, H = x.shape
     E = offsets.numel() - 1
-    if table.dtype != torch.int64 or tuple(table.shape) != (E, len(_TABLE_FIELDS)):
-        raise MoEError(f"expert_ffn_table: table must be int64 [{E}, {len(_TABLE_FIELDS)}]")
-    if not (table.is_cuda or table.is_pinned()):
-        raise MoEError("expert_ffn_table: the table must be in device or pinned host memory")
+    L = lib()
+    tab_ptr = _table_arg(L, table, E, "expert_ffn_table")
     if y_perm is None:
         y_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
-    L = lib()
     nbytes = L.moe_expert_ffn_workspace_size(T, k, E, H, I)
     w = (ws or Workspaces(dev)).get("ffn", nbytes)
-    if bits not in (2, 4):
-        raise MoEError("bits must be 2 or 4")
-    tab_ptr = _p(table)
-    if not table.is_cuda:
-        a = ctypes.c_uint64(0)
-        _check(L.moe_device_address(ctypes.c_void_p(tab_ptr), ctypes.byref(a)), "moe_device_address (table)")
-        tab_ptr = a.value
-    name = "moe_expert_ffn_w4a16_table" if bits == 4 else "moe_expert_ffn_w2a16_table"
-    s = getattr(L, name)(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I, tab_ptr, _p(y_perm),
-                         _p(w), w.numel(), _stream(dev))
+    common = (_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I)
+    tail = (tab_ptr, _p(y_perm), _p(w), w.numel(), _stream(dev))
+    if bits in (2, 4) and group == 128:
+        name = "moe_expert_ffn_w4a16_table" if bits == 4 else "moe_expert_ffn_w2a16_table"
+        s = getattr(L, name)(*common, *tail)
+    else:
+        name = "moe_expert_ffn_wna16_table"
+        s = L.moe_expert_ffn_wna16_table(*common, bits, group, *tail)
     _check(s, name)
     return y_perm
 
 
-def quant_act_nvfp4(x: torch.Tensor, gscale: float, want_scales: bool = False):
-    """NVFP4 activation quantiser: bf16 q * s of each value (and the E4M3 group-scale codes)."""
+def expert_ffn_nvfp4_table(x: torch.Tensor, offsets, sorted_rows, active, k: int, table: torch.Tensor, I: int,
+                           x_gscale: float, h_gscale: float, ws: Optional[Workspaces] = None,
+                           y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``expert_ffn_nvfp4`` with the experts found through an address table
+    (``expert_table(..., "nvfp4")``)."""
     dev = _dev(x)
-    vals = torch.empty_like(x, dtype=torch.bfloat16)
-    sc = torch.empty(x.numel() // 16, dtype=torch.uint8, device=dev) if want_scales else None
-    _check(lib().moe_quant_act_nvfp4(_p(x), x.numel(), float(gscale), _p(vals), _p(sc), _stream(dev)),
-           "moe_quant_act_nvfp4")
-    return (vals, sc) if want_scales else vals
+    T, H = x.shape
+    E = offsets.numel() - 1
+    L = lib()
+    tab_ptr = _table_arg(L, table, E, "expert_ffn_nvfp4_table")
+    if y_perm is None:
+        y_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    w = (ws or Workspaces(dev)).get("ffn_nvfp4", L.moe_expert_ffn_nvfp4_workspace_size(T, k, E, H, I))
+    _check(L.moe_expert_ffn_nvfp4_table(_p(x), _p(offsets), _p(sorted_rows), _p(active), T, k, E, H, I,
+                                        float(x_gscale), float(h_gscale), tab_ptr, _p(y_perm), _p(w), w.numel(),
+                                        _stream(dev)), "moe_expert_ffn_nvfp4_table")
+    return y_perm
 
 
 def expert_ffn_nvfp4(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: Dict[str, torch.Tensor], I: int,

@@ -257,6 +257,12 @@ size_t moe_expert_ffn_workspace_size(int T, int k, int E, int H, int I) {
   return ffn_workspace_bytes(T, k, E, H, I);
 }
 
+// The integer-code and FP6 formats of the wna16 calls: INT4 and INT8 with
+// groups of 128 or 32, 2-bit and FP6 with groups of 128.
+static bool wna16_format_ok(int bits, int group) {
+  return ((bits == 4 || bits == 8) && (group == 128 || group == 32)) || ((bits == 2 || bits == 6) && group == 128);
+}
+
 static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, const int32_t *expert_offsets,
                              const int32_t *sorted_rows, const int32_t *active, int T, int k, int E, int H, int I,
                              const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
@@ -320,14 +326,24 @@ moe_status moe_expert_ffn_wna16(const uint16_t *x, const int32_t *expert_offsets
                                 const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
                                 const uint32_t *w2_codes, const uint16_t *w2_scales, const uint8_t *w2_zeros,
                                 uint16_t *y_perm, void *workspace, size_t workspace_bytes, void *stream) {
-  const bool ok = (bits == 4 && (group_size == 128 || group_size == 32)) ||
-                  (bits == 8 && (group_size == 128 || group_size == 32)) ||
-                  ((bits == 2 || bits == 6) && group_size == 128);
-  if (!ok)
+  if (!wna16_format_ok(bits, group_size))
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wna16: unsupported format: %d bits, group %d", bits, group_size);
   return expert_ffn("moe_expert_ffn_wna16", bits, x, expert_offsets, sorted_rows, active, T, k, E, H, I, w13_codes,
                     w13_scales, bits == 2 ? w13_zeros : nullptr, w2_codes, w2_scales, bits == 2 ? w2_zeros : nullptr,
                     y_perm, workspace, workspace_bytes, stream, nullptr, group_size);
+}
+
+moe_status moe_expert_ffn_wna16_table(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                      const int32_t *active, int T, int k, int E, int H, int I, int bits,
+                                      int group_size, const uint64_t *expert_table, uint16_t *y_perm,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (!wna16_format_ok(bits, group_size))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wna16_table: unsupported format: %d bits, group %d", bits,
+                group_size);
+  if (!expert_table) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wna16_table: expert_table is NULL");
+  return expert_ffn("moe_expert_ffn_wna16_table", bits, x, expert_offsets, sorted_rows, active, T, k, E, H, I,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, y_perm, workspace, workspace_bytes, stream,
+                    expert_table, group_size);
 }
 
 size_t moe_expert_ffn_nvfp4_workspace_size(int T, int k, int E, int H, int I) {
@@ -335,25 +351,32 @@ size_t moe_expert_ffn_nvfp4_workspace_size(int T, int k, int E, int H, int I) {
   return ffn_nvfp4_workspace_bytes(T, k, E, H, I);
 }
 
-moe_status moe_expert_ffn_nvfp4(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
-                                const int32_t *active, int T, int k, int E, int H, int I, float x_gscale,
-                                float h_gscale, const uint32_t *w13_codes, const uint8_t *w13_scales,
-                                const float *w13_gscale, const uint32_t *w2_codes, const uint8_t *w2_scales,
-                                const float *w2_gscale, uint16_t *y_perm, void *workspace, size_t workspace_bytes,
-                                void *stream) {
-  const char *name = "moe_expert_ffn_nvfp4";
+static moe_status expert_ffn_nvfp4(const char *name, const uint16_t *x, const int32_t *expert_offsets,
+                                   const int32_t *sorted_rows, const int32_t *active, int T, int k, int E, int H,
+                                   int I, float x_gscale, float h_gscale, const uint32_t *w13_codes,
+                                   const uint8_t *w13_scales, const float *w13_gscale, const uint32_t *w2_codes,
+                                   const uint8_t *w2_scales, const float *w2_gscale, uint16_t *y_perm,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   const uint64_t *table = nullptr) {
   moe_status s = check_common_moe(T, H, E, k);
   if (s != MOE_OK) return s;
   if (I < 128 || I % 128) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: I must be a positive multiple of 128 (got %d)", name, I);
-  if (!x || !expert_offsets || !sorted_rows || !active || !y_perm || !workspace || !w13_codes || !w13_scales ||
-      !w13_gscale || !w2_codes || !w2_scales || !w2_gscale)
+  if (!x || !expert_offsets || !sorted_rows || !active || !y_perm || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+  if (table) {
+    if (!aligned(table, 8)) return fail(MOE_ERR_MISALIGNED, "%s: the expert table needs 8-byte alignment", name);
+  } else {
+    if (!w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale)
+      return fail(MOE_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+    if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(w13_scales, 2) || !aligned(w2_scales, 2) ||
+        !aligned(w13_gscale, 4) || !aligned(w2_gscale, 4))
+      return fail(MOE_ERR_MISALIGNED, "%s: code arrays need 16-byte, scale arrays 2-byte and tensor-scale arrays "
+                  "4-byte alignment", name);
+  }
   if (!(x_gscale > 0.f) || !(h_gscale > 0.f) || x_gscale > 3.0e38f || h_gscale > 3.0e38f)
     return fail(MOE_ERR_INVALID_ARG, "%s: the tensor scales must be positive and finite", name);
-  if (!aligned(x, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16))
-    return fail(MOE_ERR_MISALIGNED, "%s: x and code arrays need 16-byte alignment", name);
-  if (!aligned(w13_scales, 2) || !aligned(w2_scales, 2) || !aligned(w13_gscale, 4) || !aligned(w2_gscale, 4) ||
-      !aligned(y_perm, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_rows, 4) || !aligned(active, 4))
+  if (!aligned(x, 16)) return fail(MOE_ERR_MISALIGNED, "%s: x needs 16-byte alignment", name);
+  if (!aligned(y_perm, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_rows, 4) || !aligned(active, 4))
     return fail(MOE_ERR_MISALIGNED, "%s: array alignment", name);
   if (!aligned(workspace, 256)) return fail(MOE_ERR_MISALIGNED, "%s: workspace needs 256-byte alignment", name);
   const size_t need = ffn_nvfp4_workspace_bytes(T, k, E, H, I);
@@ -366,7 +389,7 @@ moe_status moe_expert_ffn_nvfp4(const uint16_t *x, const int32_t *expert_offsets
   hipError_t he = current_device_info(&dev);
   if (he != hipSuccess) return from_hip(he, name);
   FfnArgs a{x, expert_offsets, sorted_rows, active, T, k, E, H, I, 4, w13_codes, (const uint16_t *)w13_scales, nullptr,
-            w2_codes, (const uint16_t *)w2_scales, nullptr, y_perm, workspace, nullptr, 16};
+            w2_codes, (const uint16_t *)w2_scales, nullptr, y_perm, workspace, table, 16};
   a.nvfp4 = true;
   a.w13_g = w13_gscale;
   a.w2_g = w2_gscale;
@@ -386,6 +409,27 @@ moe_status moe_expert_ffn_nvfp4(const uint16_t *x, const int32_t *expert_offsets
     return from_hip(e, name);
   }
   return from_hip(launch_ffn_prefill(a, dev, st), name);
+}
+
+moe_status moe_expert_ffn_nvfp4(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                const int32_t *active, int T, int k, int E, int H, int I, float x_gscale,
+                                float h_gscale, const uint32_t *w13_codes, const uint8_t *w13_scales,
+                                const float *w13_gscale, const uint32_t *w2_codes, const uint8_t *w2_scales,
+                                const float *w2_gscale, uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  return expert_ffn_nvfp4("moe_expert_ffn_nvfp4", x, expert_offsets, sorted_rows, active, T, k, E, H, I, x_gscale,
+                          h_gscale, w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, y_perm,
+                          workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_nvfp4_table(const uint16_t *x, const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                      const int32_t *active, int T, int k, int E, int H, int I, float x_gscale,
+                                      float h_gscale, const uint64_t *expert_table, uint16_t *y_perm,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (!expert_table) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4_table: expert_table is NULL");
+  return expert_ffn_nvfp4("moe_expert_ffn_nvfp4_table", x, expert_offsets, sorted_rows, active, T, k, E, H, I,
+                          x_gscale, h_gscale, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, y_perm,
+                          workspace, workspace_bytes, stream, expert_table);
 }
 
 moe_status moe_quant_act_nvfp4(const uint16_t *x, int64_t n, float gscale, uint16_t *values, uint8_t *scales,
@@ -548,9 +592,7 @@ moe_status moe_layer_wna16(const uint16_t *x, const uint16_t *w_router, const fl
                            const uint16_t *w13_scales, const uint8_t *w13_zeros, const uint32_t *w2_codes,
                            const uint16_t *w2_scales, const uint8_t *w2_zeros, uint16_t *y, int32_t *topk_ids,
                            float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
-  const bool ok = ((bits == 4 || bits == 8) && (group_size == 128 || group_size == 32)) ||
-                  ((bits == 2 || bits == 6) && group_size == 128);
-  if (!ok)
+  if (!wna16_format_ok(bits, group_size))
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_wna16: unsupported format: %d bits, group %d", bits, group_size);
   return layer("moe_layer_wna16", bits, x, w_router, logit_bias, T, H, E, k, I, w13_codes, w13_scales,
                bits == 2 ? w13_zeros : nullptr, w2_codes, w2_scales, bits == 2 ? w2_zeros : nullptr, y, topk_ids,

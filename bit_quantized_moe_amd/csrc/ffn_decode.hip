@@ -1074,7 +1074,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
           }
           float hv;
           if constexpr (NV) {  // tensor scales, then h quantised in its group of 16 (lanes 16 mm .. +15)
-            const float osc = p.gx * sload(p.g13 + md.e);
+            const float osc = p.gx * sload(TAB ? (const float *)xw.zeros : p.g13 + md.e);
             hv = quant16_lanes(silu_f(gv * osc) * (uv * osc), p.gh);
           } else {
             hv = silu_f(gv) * uv;
@@ -1099,7 +1099,9 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         o2[1].s += 2 * lsub;
       }
       const int nch = G2 / CG;
-      const float osc2 = NV ? p.gh * sload(p.g2 + md.e) : 1.f;  // NVFP4 output scale
+      // NVFP4 output scale; a table row holds the address of the tensor scale
+      // where other formats keep their zero-points
+      const float osc2 = NV ? p.gh * sload(TAB ? (const float *)xw.zeros : p.g2 + md.e) : 1.f;
       Chunk<BITS, GS> wd[2];
       if constexpr (FAST) {
         load_chunk<BITS, GS>(xw, o2[0], wd[0]);
@@ -1329,9 +1331,19 @@ const void *decode_fn_layer(int bits, bool one, bool fast) {
   return bits == 4 ? decode_fn_fast<4, 128, LAYER, TAB>(one, fast) : decode_fn_fast<2, 128, LAYER, TAB>(one, fast);
 }
 
+// The stage call of every format, with stacked arrays or an address table.
+template <bool TAB>
+const void *decode_fn_stage(int bits, int group, bool one, bool fast) {
+  if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, false, TAB>(one, fast)
+                                    : decode_fn_fast<8, 128, false, TAB>(one, fast);
+  if (bits == 6) return decode_fn_fast<6, 128, false, TAB>(one, fast);
+  if (bits == 4 && group == 16) return decode_fn_fast<5, 128, false, TAB>(one, fast);  // NVFP4
+  if (group == 32) return decode_fn_fast<4, 32, false, TAB>(one, fast);
+  return decode_fn_layer<false, TAB>(bits, one, fast);
+}
+
 // The layer kernel reads stacked arrays only; the address-table variant is a
-// separate instantiation so that the array kernels keep their registers.  The
-// group-32 and INT8 formats take the stage call with stacked arrays.
+// separate instantiation so that the array kernels keep their registers.
 const void *decode_kernel_fn(int bits, int group, bool one, bool fast, bool layer, bool tab) {
   if (layer) {  // every format; the NVFP4 layer quantises x as it stages it
     if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, true, false>(one, fast)
@@ -1341,12 +1353,7 @@ const void *decode_kernel_fn(int bits, int group, bool one, bool fast, bool laye
     if (group == 16) return decode_fn_fast<5, 128, true, false>(one, fast);  // NVFP4
     return decode_fn_layer<true, false>(bits, one, fast);
   }
-  if (bits == 8) return group == 32 ? decode_fn_fast<8, 32, false, false>(one, fast)
-                                    : decode_fn_fast<8, 128, false, false>(one, fast);
-  if (bits == 6) return decode_fn_fast<6, 128, false, false>(one, fast);
-  if (bits == 4 && group == 16) return decode_fn_fast<5, 128, false, false>(one, fast);  // NVFP4
-  if (group == 32) return decode_fn_fast<4, 32, false, false>(one, fast);
-  return tab ? decode_fn_layer<false, true>(bits, one, fast) : decode_fn_layer<false, false>(bits, one, fast);
+  return tab ? decode_fn_stage<true>(bits, group, one, fast) : decode_fn_stage<false>(bits, group, one, fast);
 }
 
 // Units per chunk of a format (kCG on the host).

@@ -333,7 +333,8 @@ __global__ void __launch_bounds__(256, 2) ffn_gemm_kernel(GemmParams p) {
     // ---- epilogue: C[m][n] of (mi, ni, r) is m = 4*(lane/16) + r, n = lane % 16
     // NVFP4: the products carry the A and weight tensor scales; G1 quantises h
     // in groups of 16 columns (the 16 lanes of one m)
-    const float osc = NV ? p.act_g * sload(p.gscale + e) : 1.f;
+    // (a table row holds the address of the tensor scale in the zero-point slot)
+    const float osc = NV ? p.act_g * sload(te ? (const float *)sload(te + 2) : p.gscale + e) : 1.f;
 #pragma unroll
     for (int mi = 0; mi < MV; ++mi)
 #pragma unroll

@@ -16,7 +16,7 @@
  *                   groups of 128 or 32, 2-bit or FP6 e2m3 with groups of 128
  *   moe_expert_ffn_nvfp4 (+ moe_quant_act_nvfp4)
  *                   the same with NVFP4 W4A4 experts (activations quantised too)
- *   moe_expert_ffn_w4a16_table / _w2a16_table
+ *   moe_expert_ffn_w4a16_table / _w2a16_table / _wna16_table / _nvfp4_table
  *                   the same, each expert's weights located through a
  *                   per-expert address table
  *   moe_combine     gate-weighted sum of each token's k expert outputs
@@ -344,6 +344,42 @@ moe_status moe_expert_ffn_w4a16_table(const uint16_t *x, const int32_t *expert_o
 moe_status moe_expert_ffn_w2a16_table(const uint16_t *x, const int32_t *expert_offsets,
                                       const int32_t *sorted_rows, const int32_t *active,
                                       int T, int k, int E, int H, int I,
+                                      const uint64_t *expert_table,
+                                      uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/* moe_expert_ffn_wna16_table: moe_expert_ffn_wna16 (any of its formats,
+ * chosen by bits and group_size as there) with each expert found through the
+ * table above.  Row e holds the addresses of the [e] slices of the six stacked
+ * arrays of moe_expert_ffn_wna16: code blocks [N, K*bits/32] uint32 (FP6: the
+ * row's bit stream, 3 words per 16 codes), 16-byte aligned; scale blocks
+ * [N, K/group] bf16 (FP6: fp16), 2-byte aligned; zero-point blocks
+ * [N, K/group] uint8 for 2-bit only (entries 2 and 5 are not read for the
+ * other formats).  With the same weights the output is bit-identical to
+ * moe_expert_ffn_wna16.  A NULL table returns MOE_ERR_INVALID_ARG, an
+ * unsupported format MOE_ERR_INVALID_ARG. */
+moe_status moe_expert_ffn_wna16_table(const uint16_t *x, const int32_t *expert_offsets,
+                                      const int32_t *sorted_rows, const int32_t *active,
+                                      int T, int k, int E, int H, int I, int bits, int group_size,
+                                      const uint64_t *expert_table,
+                                      uint16_t *y_perm, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/* moe_expert_ffn_nvfp4_table: moe_expert_ffn_nvfp4 with each expert found
+ * through the table above (same page and section).  Row e holds, in order:
+ *   0  w13 codes   [2I, H/8] uint32 E2M1 fields, 16-byte aligned
+ *   1  w13 scales  [2I, H/16] uint8 E4M3 codes
+ *   2  w13 tensor scale: the address of one float32 (4-byte aligned)
+ *   3  w2 codes    [H, I/8] uint32, 16-byte aligned
+ *   4  w2 scales   [H, I/16] uint8
+ *   5  w2 tensor scale: the address of one float32
+ * i.e. the [e] slices and elements of the stacked arrays of
+ * moe_expert_ffn_nvfp4.  Workspace: moe_expert_ffn_nvfp4_workspace_size.  With
+ * the same weights the output is bit-identical to moe_expert_ffn_nvfp4.  A
+ * NULL table returns MOE_ERR_INVALID_ARG. */
+moe_status moe_expert_ffn_nvfp4_table(const uint16_t *x, const int32_t *expert_offsets,
+                                      const int32_t *sorted_rows, const int32_t *active,
+                                      int T, int k, int E, int H, int I, float x_gscale, float h_gscale,
                                       const uint64_t *expert_table,
                                       uint16_t *y_perm, void *workspace, size_t workspace_bytes,
                                       void *stream);

@@ -119,13 +119,17 @@ def test_ffn_argument_errors():
     assert need >= 4096 + 16 * 8 * 1024 * 2 and need % 256 == 0
 
 
-def _ffn_table(bits=4, T=2, k=2, E=8, H=256, I=128, x=A, tab=A, ws=A, wsb=1 << 24):
+def _ffn_table(bits=4, T=2, k=2, E=8, H=256, I=128, x=A, tab=A, ws=A, wsb=1 << 24, group=128):
     L = bq.lib()
+    if bits == "nvfp4":
+        return L.moe_expert_ffn_nvfp4_table(x, A, A, A, T, k, E, H, I, 1.0, 1.0, tab, A, ws, wsb, None)
+    if group != 128 or bits not in (2, 4):
+        return L.moe_expert_ffn_wna16_table(x, A, A, A, T, k, E, H, I, bits, group, tab, A, ws, wsb, None)
     fn = L.moe_expert_ffn_w4a16_table if bits == 4 else L.moe_expert_ffn_w2a16_table
     return fn(x, A, A, A, T, k, E, H, I, tab, A, ws, wsb, None)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 2, 8, 6, "nvfp4"])
 def test_ffn_table_argument_errors(bits):
     assert _ffn_table(bits, tab=None) == INVALID
     assert _ffn_table(bits, tab=A + 4) == MISALIGNED
@@ -134,6 +138,17 @@ def test_ffn_table_argument_errors(bits):
     assert _ffn_table(bits, x=A + 8) == MISALIGNED
     assert _ffn_table(bits, wsb=100) == WS_SMALL
     assert _ffn_table(bits, T=0) == OK        # no weight arrays are needed beside the table
+
+
+def test_ffn_table_format_and_scale_errors():
+    L = bq.lib()
+    assert _ffn_table(4, group=32, T=0) == OK
+    assert _ffn_table(8, group=32, T=0) == OK
+    for bits, group in ((2, 32), (6, 32), (4, 64), (3, 128), (4, 16)):
+        assert _ffn_table(bits, group=group) == INVALID, (bits, group)
+        assert "unsupported format" in L.moe_last_error().decode()
+    for gx, gh in ((0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        assert L.moe_expert_ffn_nvfp4_table(A, A, A, A, 2, 2, 8, 256, 128, gx, gh, A, A, A, 1 << 24, None) == INVALID
 
 
 def test_ffn_wna16_format_errors():
