@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "MoEError", "lib", "route", "permute", "route_permute", "expert_ffn", "expert_table", "expert_ffn_table",
-    "expert_ffn_nvfp4_table", "expert_ffn_nvfp4", "quant_act_nvfp4",
+    "expert_ffn_nvfp4_table", "expert_ffn_nvfp4", "quant_act_nvfp4", "ffn_path",
     "layer", "layer_noalloc", "combine", "unpack_codes",
     "dequant_bf16", "Workspaces", "moe_layer", "LIB_PATH", "workspace_status", "set_wait_limit", "WS_WAIT_TIMEOUT",
 ]
@@ -42,6 +42,7 @@ _SIGS = {
     "moe_route_permute_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_route_permute": (_c_int, [_vp, _vp, _vp] + [_c_int] * 4 + [_vp] * 7 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_workspace_size": (_c_size, [_c_int] * 5),
+    "moe_expert_ffn_path": (_c_int, [_c_int] * 7),
     "moe_expert_ffn_w4a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 5 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_w2a16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 5 + [_vp] * 7 + [_vp, _c_size, _vp]),
     "moe_expert_ffn_wna16": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 7 + [_vp] * 6 + [_vp, _vp, _c_size, _vp]),
@@ -231,6 +232,20 @@ def route_permute(x: torch.Tensor, w_router: torch.Tensor, k: int, logit_bias: O
     if want_logits:
         out["logits"] = logits
     return out
+
+
+FFN_PATHS = {0: "decode", 1: "mid", 2: "gemm"}
+
+
+def ffn_path(T: int, k: int, E: int, H: int, I: int, bits, group: int = 128) -> str:
+    """The expert-FFN path ("decode", "mid" or "gemm") of these sizes and format
+    (bits "nvfp4" for NVFP4)."""
+    if bits == "nvfp4":
+        bits, group = 4, 16
+    p = lib().moe_expert_ffn_path(T, k, E, H, I, bits, group)
+    if p < 0:
+        raise MoEError(f"ffn_path: unsupported sizes or format ({bits} bits, group {group})")
+    return FFN_PATHS[p]
 
 
 def expert_ffn(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: Dict[str, torch.Tensor], bits: int,

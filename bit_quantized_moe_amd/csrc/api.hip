@@ -209,6 +209,8 @@ moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *ex
   const size_t need = moe_permute_workspace_size(T, k, E);
   if (need && (!workspace || workspace_bytes < need))
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_permute: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (need && !aligned(workspace, 256))
+    return fail(MOE_ERR_MISALIGNED, "moe_permute: workspace needs 256-byte alignment");
   if (T == 0) return MOE_OK;
   return from_hip(launch_permute(topk_ids, T, k, E, expert_offsets, sorted_rows, row_pos, active, workspace,
                                  (hipStream_t)stream),
@@ -263,6 +265,15 @@ static bool wna16_format_ok(int bits, int group) {
   return ((bits == 4 || bits == 8) && (group == 128 || group == 32)) || ((bits == 2 || bits == 6) && group == 128);
 }
 
+// The expert-FFN path of a shape and format (MOE_FFN_PATH_*); group 16 with
+// 4 bits is NVFP4, whose decode kernel reads 128-K units of E4M3 pairs.
+static int ffn_path_of(int T, int k, int E, int H, int I, int bits, int group) {
+  const bool nv = bits == 4 && group == 16;
+  if (decode_path(T, k, E) && decode_layout_ok(H, I, bits, nv ? 32 : group)) return MOE_FFN_PATH_DECODE;
+  if (!nv && mid_path(T, k, E) && mid_layout_ok(H, I, bits, group)) return MOE_FFN_PATH_MID;
+  return MOE_FFN_PATH_GEMM;
+}
+
 static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, const int32_t *expert_offsets,
                              const int32_t *sorted_rows, const int32_t *active, int T, int k, int E, int H, int I,
                              const uint32_t *w13_codes, const uint16_t *w13_scales, const uint8_t *w13_zeros,
@@ -296,11 +307,13 @@ static moe_status expert_ffn(const char *name, int bits, const uint16_t *x, cons
   if (he != hipSuccess) return from_hip(he, name);
   FfnArgs a{x, expert_offsets, sorted_rows, active, T, k, E, H, I, bits, w13_codes, w13_scales, w13_zeros,
             w2_codes, w2_scales, w2_zeros, y_perm, workspace, table, group};
-  if (decode_path(T, k, E) && decode_layout_ok(H, I, bits, group))
-    return from_hip(launch_ffn_decode(a, dev, (hipStream_t)stream), name);
-  // the grouped GEMMs address x and one expert's codes with 32-bit byte offsets
+  const int path = ffn_path_of(T, k, E, H, I, bits, group);
+  if (path == MOE_FFN_PATH_DECODE) return from_hip(launch_ffn_decode(a, dev, (hipStream_t)stream), name);
+  // the grouped GEMMs and the middle-batch kernel address x and one expert's
+  // codes with 32-bit offsets
   if ((long long)T * H > (1LL << 30) || (long long)I * H > (1LL << 30))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "%s: T*H and I*H must be <= 2^30 on the grouped-GEMM path (T=%d)", name, T);
+  if (path == MOE_FFN_PATH_MID) return from_hip(launch_ffn_mid(a, (hipStream_t)stream), name);
   return from_hip(launch_ffn_prefill(a, dev, (hipStream_t)stream), name);
 }
 
@@ -344,6 +357,13 @@ moe_status moe_expert_ffn_wna16_table(const uint16_t *x, const int32_t *expert_o
   return expert_ffn("moe_expert_ffn_wna16_table", bits, x, expert_offsets, sorted_rows, active, T, k, E, H, I,
                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, y_perm, workspace, workspace_bytes, stream,
                     expert_table, group_size);
+}
+
+int moe_expert_ffn_path(int T, int k, int E, int H, int I, int bits, int group_size) {
+  if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return -1;
+  const bool nv = bits == 4 && group_size == 16;
+  if (!nv && !wna16_format_ok(bits, group_size)) return -1;
+  return ffn_path_of(T, k, E, H, I, bits, group_size);
 }
 
 size_t moe_expert_ffn_nvfp4_workspace_size(int T, int k, int E, int H, int I) {
@@ -396,7 +416,7 @@ static moe_status expert_ffn_nvfp4(const char *name, const uint16_t *x, const in
   a.gx = x_gscale;
   a.gh = h_gscale;
   const hipStream_t st = (hipStream_t)stream;
-  if (decode_path(T, k, E) && decode_layout_ok(H, I, 4, 32)) {
+  if (ffn_path_of(T, k, E, H, I, 4, 16) == MOE_FFN_PATH_DECODE) {
     // decode path: quantise x after the h words, run the GEMV kernel on it, clear it again
     uint16_t *xq = (uint16_t *)((char *)workspace + ffn_ctl_bytes(T, k, E) + ffn_nvfp4_h_bytes(T, k, E, I));
     hipError_t e = launch_quant_nvfp4(x, (int64_t)T * H, x_gscale, xq, nullptr, st);

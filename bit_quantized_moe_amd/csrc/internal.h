@@ -98,6 +98,17 @@ size_t layer_workspace_bytes(int T, int k, int E, int H, int I);
 hipError_t launch_layer_decode(const FfnArgs &a, const LayerArgs &l, const DeviceInfo &dev, hipStream_t st);
 hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &dev, hipStream_t st);
 
+// ffn_mid.hip: the middle-batch expert FFN (two launches, rows staged per
+// K step, weights read once per 32 rows of an expert) between the decode
+// path and the grouped GEMMs: INT4 and 2-bit with groups of 128, while an
+// active expert averages at most kMidRowsPerExpert rows.
+constexpr int kMidRowsPerExpert = 24;
+inline bool mid_path(int T, int k, int E) {
+  return !decode_path(T, k, E) && (long)T * k <= (long)kMidRowsPerExpert * E;
+}
+bool mid_layout_ok(int H, int I, int bits, int group);
+hipError_t launch_ffn_mid(const FfnArgs &a, hipStream_t st);
+
 // combine.hip
 hipError_t launch_combine(const uint16_t *y_perm, const int32_t *row_pos, const float *gates, int T, int k,
                           int H, uint16_t *y, hipStream_t st);

@@ -173,6 +173,10 @@ moe_status moe_route(const uint16_t *x, const uint16_t *w_router, const float *l
  *                  experts with at least one row, then their ids ascending,
  *                  then -1 padding
  * Rows whose id lies outside [0, E) are dropped (they get no sorted position).
+ * Workspace: moe_permute_workspace_size(T, k, E) bytes, 256-byte aligned,
+ * all-zero and left zero (the conventions above); the size is 0 for
+ * T*k <= 4096, and then workspace may be NULL.  Larger batches keep a block
+ * counter and a table of per-block expert counts there.
  */
 size_t moe_permute_workspace_size(int T, int k, int E);
 moe_status moe_permute(const int32_t *topk_ids, int T, int k, int E,
@@ -206,14 +210,19 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  *     y_perm[p] = W2_e h                down, H outputs, stored as bf16
  * with W = q * s dequantised from INT4 symmetric group-128 codes.  The dot
  * products accumulate in float32; h is rounded to bf16 before the down
- * projection.  While T <= 512 and T*k <= 6*E (at most about six rows per
- * expert) the call uses the decode path (one fused GEMV kernel streaming each
- * selected expert's packed weights once, rows in passes of four); otherwise
- * grouped bf16-MFMA GEMMs.  The pages dispatch between a GEMV and
- * dequantise-then-GEMM at 16 rows (page "Qwen3.8-Flash-Next FP6-INT8",
- * "Quantization quality"); the crossover used here was measured on MI355X
- * instead, and the choice is made on the host from the sizes alone.  The permutation arrays must come from moe_permute
- * with the same T, k, E.
+ * projection.  Three paths, chosen on the host from the sizes alone
+ * (moe_expert_ffn_path reports the choice):
+ *   decode  T <= 512 and T*k <= 6*E (at most about six rows per expert): one
+ *           fused GEMV kernel streaming each selected expert's packed weights
+ *           once, rows in passes of four;
+ *   mid     otherwise while T*k <= 24*E (INT4 / 2-bit g128, H and I
+ *           multiples of 512): two launches that stage up to 32 rows of an
+ *           expert per K step and read its weights once per 32 rows;
+ *   GEMM    otherwise: grouped bf16-MFMA GEMMs on dequantised tiles.
+ * The pages dispatch between a GEMV and dequantise-then-GEMM at 16 rows (page
+ * "Qwen3.8-Flash-Next FP6-INT8", "Quantization quality"); the crossovers used
+ * here were measured on MI355X instead.  The permutation arrays must come
+ * from moe_permute with the same T, k, E.
  *
  *   x           [T, H] bf16, 16-byte aligned
  *   w13_codes   [E, 2I, H/8]  uint32, 16-byte aligned
@@ -229,6 +238,16 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  * on the grouped-GEMM path also T*H <= 2^30 and I*H <= 2^30 (32-bit offsets).
  */
 size_t moe_expert_ffn_workspace_size(int T, int k, int E, int H, int I);
+
+/* moe_expert_ffn_path: the path the expert-FFN calls take for these sizes and
+ * format (bits, group_size as for moe_expert_ffn_wna16; bits 4 with group 16
+ * is NVFP4, which has no mid path): MOE_FFN_PATH_DECODE, _MID or _GEMM, or -1
+ * for a negative size or an unsupported format.  Pure host arithmetic. */
+#define MOE_FFN_PATH_DECODE 0
+#define MOE_FFN_PATH_MID 1
+#define MOE_FFN_PATH_GEMM 2
+int moe_expert_ffn_path(int T, int k, int E, int H, int I, int bits, int group_size);
+
 moe_status moe_expert_ffn_w4a16(const uint16_t *x, const int32_t *expert_offsets,
                                 const int32_t *sorted_rows, const int32_t *active,
                                 int T, int k, int E, int H, int I,

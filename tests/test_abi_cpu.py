@@ -254,3 +254,27 @@ def test_layer_noalloc_argument_errors():
     assert b"scratch" in L.moe_last_error()
     bad = list(args); bad[3] = 17                                    # one-launch layer: T <= 16
     assert f(*bad) == SHAPE
+
+
+def test_expert_ffn_path_rule():
+    """Host-side dispatch: decode up to about six rows per expert, the mid
+    path up to 24 (INT4 / 2-bit g128, H and I multiples of 512), the grouped
+    GEMMs beyond and for every other format."""
+    L = bq.lib()
+    f = L.moe_expert_ffn_path
+    full = (4096, 1024)
+    assert f(1, 8, 256, *full, 4, 128) == 0
+    assert f(192, 8, 256, *full, 4, 128) == 0
+    assert f(193, 8, 256, *full, 4, 128) == 1
+    assert f(256, 8, 256, *full, 2, 128) == 1
+    assert f(768, 8, 256, *full, 4, 128) == 1
+    assert f(769, 8, 256, *full, 4, 128) == 2
+    assert f(4096, 8, 256, *full, 4, 128) == 2
+    assert f(256, 8, 256, *full, 8, 128) == 2 and f(256, 8, 256, *full, 4, 32) == 2
+    assert f(256, 8, 256, *full, 6, 128) == 2 and f(256, 8, 256, *full, 4, 16) == 2
+    assert f(1, 8, 256, *full, 4, 16) == 0
+    assert f(40, 2, 8, 256, 128, 4, 128) == 2          # H, I not multiples of 512
+    assert f(40, 2, 8, 512, 512, 4, 128) == 1
+    assert f(0, 2, 8, 512, 512, 4, 128) == 0
+    assert f(-1, 8, 256, *full, 4, 128) == -1 and f(1, 8, 256, *full, 3, 128) == -1
+    assert bq.ffn_path(256, 8, 256, *full, 4) == "mid" and bq.ffn_path(1, 8, 256, *full, "nvfp4") == "decode"

@@ -123,8 +123,28 @@ def test_route_prefill_full_size_all_tokens(name):
 
 
 # ------------------------------------------------------------------ permutation
+def test_permute_workspace_reused_and_left_zero():
+    """Batches above 4096 rows keep per-block counts in the workspace: three
+    calls of different sizes on one workspace each equal the oracle, and the
+    workspace is zero after each."""
+    ws = bq.Workspaces("cuda")
+    for i, (T, E) in enumerate([(8192, 256), (600, 256), (5000, 256), (8192, 256)]):
+        rng = np.random.default_rng(900 + i)
+        ids = rng.integers(0, E, (T, 8)).astype(np.int32)
+        off, sr, rp, act = [to_np(v) for v in bq.permute(to_dev(ids), E, ws=ws)]
+        r_off, r_sr, r_rp, r_act = oracle.permute(ids, E)
+        assert np.array_equal(off, r_off) and np.array_equal(sr, r_sr) and np.array_equal(rp, r_rp), (T, E)
+        assert np.array_equal(act, r_act), (T, E)
+        torch.cuda.synchronize()
+        if "permute" in ws._bufs:
+            assert int(ws._bufs["permute"].view(torch.int32).abs().sum()) == 0, (T, E)
+
+
+
 @pytest.mark.parametrize("T,k,E,bad", [(1, 8, 256, False), (16, 8, 256, False), (4, 2, 8, True), (4096, 8, 256, False),
-                                       (8192, 8, 256, True), (700, 3, 1024, True), (5, 1, 1, False), (300, 32, 40, False)])
+                                       (8192, 8, 256, True), (700, 3, 1024, True), (5, 1, 1, False), (300, 32, 40, False),
+                                       (4097, 1, 1024, True), (1025, 4, 1, False), (512, 8, 256, False),
+                                       (513, 8, 256, True), (60000, 8, 384, True)])
 def test_permute_bit_exact(T, k, E, bad):
     rng = np.random.default_rng(T * 7 + E)
     ids = np.stack([rng.permutation(E)[:k] if k <= E else rng.integers(0, E, k) for _ in range(T)]).astype(np.int32)
