@@ -399,6 +399,16 @@ def expert_ffn_nvfp4_table(x: torch.Tensor, offsets, sorted_rows, active, k: int
     return y_perm
 
 
+def quant_act_nvfp4(x: torch.Tensor, gscale: float, want_scales: bool = False):
+    """NVFP4 activation quantiser: bf16 q * s of each value (and the E4M3 group-scale codes)."""
+    dev = _dev(x)
+    vals = torch.empty_like(x, dtype=torch.bfloat16)
+    sc = torch.empty(x.numel() // 16, dtype=torch.uint8, device=dev) if want_scales else None
+    _check(lib().moe_quant_act_nvfp4(_p(x), x.numel(), float(gscale), _p(vals), _p(sc), _stream(dev)),
+           "moe_quant_act_nvfp4")
+    return (vals, sc) if want_scales else vals
+
+
 def expert_ffn_nvfp4(x: torch.Tensor, offsets, sorted_rows, active, k: int, weights: Dict[str, torch.Tensor], I: int,
                      x_gscale: float, h_gscale: float, ws: Optional[Workspaces] = None,
                      y_perm: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -17,12 +17,12 @@
 //  * down (mid_kernel<BITS, false>): block (a, tile of 128 output columns),
 //    wave w owns 32 down rows, y_perm rows in sorted order.
 //
-// Per block, K advances in steps of four 128-K units.  Every step the block
-// stages the expert's routed rows (up to 32 per pass) for those 512 K in LDS,
+// Per block, K advances in steps of two 128-K units.  Every step the block
+// stages the expert's routed rows (up to 32 per pass) for those 256 K in LDS,
 // in the K order the unpacked codes come out in, with their per-unit sums;
 // each wave holds the step's packed weights of its two 16-row sets in
 // registers (requested one step ahead) and runs v_mfma_f32_16x16x32_bf16 with
-// up to two 16-row A tiles against them.  Weights are read once per pass and
+// one or two 16-row A tiles (by the pass's row count) against them.  Weights are read once per pass and
 // unpacked once per step (the offset-bf16 codes 128 + u, exact), and each
 // unit's C is corrected as s * (C - (128 + zero) * sum(x)) before it is
 // added in float32.  An expert with more than 32 rows takes further passes.
@@ -34,7 +34,7 @@ namespace bqmoe {
 namespace {
 
 constexpr int kMidWaves = 4;
-constexpr int kMidUnits = 4;                 // 128-K units per step
+constexpr int kMidUnits = 2;                 // 128-K units per step (2 measured faster than 4: 3 blocks per CU)
 constexpr int kMidStepK = kMidUnits * kGroup;
 constexpr int kMidRows = 32;                 // routed rows per pass: two 16-row M tiles
 constexpr int kMidPitch = kMidStepK * 2 + 16;  // LDS bytes per staged row (16 rows hit 16 distinct bank quads)
@@ -58,7 +58,7 @@ template <int BITS>
 struct MidW {
   Word<BITS> w[2][kMidUnits];
   uint32_t s[2][kMidUnits / 2];  // bf16 scales, two per word (unit u: word u / 2, half u & 1)
-  uint32_t z[2];                 // 2-bit: the zero-point bytes of the step's units
+  uint32_t z[2];                 // 2-bit: the zero-point bytes of the step's units (low kMidUnits bytes)
 };
 
 template <int BITS>
@@ -68,10 +68,8 @@ __device__ __forceinline__ void mid_load(const ExpertW &x, const Off (&o)[2], in
   for (int r = 0; r < 2; ++r) {
 #pragma unroll
     for (int u = 0; u < kMidUnits; ++u) b.w[r][u] = load_word<BITS>(x.codes + o[r].c + (u0 + u) * GB);
-    const u32x2 v = *(const u32x2 *)(x.scales + o[r].s + 2 * u0);
-    b.s[r][0] = v[0];
-    b.s[r][1] = v[1];
-    if constexpr (BITS == 2) b.z[r] = *(const uint32_t *)(x.zeros + o[r].z + u0);
+    b.s[r][0] = *(const uint32_t *)(x.scales + o[r].s + 2 * u0);
+    if constexpr (BITS == 2) b.z[r] = *(const uint16_t *)(x.zeros + o[r].z + u0);
   }
 }
 
@@ -167,13 +165,61 @@ __device__ __forceinline__ void mid_step(const MidW<BITS> &b, const uint8_t *act
   }
 }
 
+// One pass over the expert's weights for the R <= 32 rows at sorted positions
+// q0 .. q0 + R - 1, with MT 16-row tiles (MT = 1 while R <= 16).
+template <int BITS, bool G1, int MT>
+__device__ __forceinline__ void mid_pass(const MidParams &p, const ExpertW &xw, const Off (&o)[2], int c0, int q0,
+                                         int R, int steps, uint8_t *act, float *Xs) {
+  const int lane = lane_id(), m = lane % 16, lsub = lane / 16;
+  uint32_t roff[kMidChunks<BITS>];
+  mid_rows<BITS, G1>(p, q0, R, roff);
+  MidW<BITS> wcur, wnext;
+  MidA<BITS> an;
+  mid_load<BITS>(xw, o, 0, wcur);
+  mid_fetch_a<BITS>(p.a, roff, R, 0, an);
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < steps; ++s) {
+    // stage this step's rows (fetched during the previous step) and their sums
+    __syncthreads();
+    mid_store_a<BITS>(act, Xs, R, an);
+    __syncthreads();
+    // next step's weights and rows in flight during this step's MFMAs
+    if (s + 1 < steps) {
+      mid_load<BITS>(xw, o, (s + 1) * kMidUnits, wnext);
+      mid_fetch_a<BITS>(p.a, roff, R, (s + 1) * kMidStepK, an);
+    }
+    mid_step<BITS, MT>(wcur, act, Xs, R, p.magic, acc);
+    wcur = wnext;
+  }
+  // epilogue: C row 4 lsub + i of tile t is staged row 16 t + 4 lsub + i, column m
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = t * 16 + 4 * lsub + i;
+      if (rr >= R) continue;
+      const size_t q = (size_t)(q0 + rr);
+      if constexpr (G1) {
+        const float g = acc[0][t][i], u = acc[1][t][i];
+        p.out[q * p.I + c0 + m] = f32_to_bf16(silu_f(g) * u);
+      } else {
+        p.out[q * p.H + c0 + m] = f32_to_bf16(acc[0][t][i]);
+        p.out[q * p.H + c0 + 16 + m] = f32_to_bf16(acc[1][t][i]);
+      }
+    }
+}
+
 template <int BITS, bool G1>
-__global__ void __launch_bounds__(kMidWaves * kWave, 2) mid_kernel(MidParams p) {
+__global__ void __launch_bounds__(kMidWaves * kWave, 3) mid_kernel(MidParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t act[kMidRows * kMidPitch];
   __shared__ __attribute__((aligned(16))) float Xs[kMidUnits * kMidRows];
   const int a = blockIdx.x / p.n_tiles, tile = blockIdx.x - a * p.n_tiles;
   if (a >= min(max(sload(p.active), 0), min(p.E, p.T * p.k))) return;  // block-uniform
-  const int lane = lane_id(), m = lane % 16, lsub = lane / 16;
+  const int m = lane_id() % 16, lsub = lane_id() / 16;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nrows = p.T * p.k;
   const int e = min(max(sload(p.active + 1 + a), 0), p.E - 1);
@@ -192,51 +238,12 @@ __global__ void __launch_bounds__(kMidWaves * kWave, 2) mid_kernel(MidParams p) 
   const int c0 = G1 ? tile * 64 + wv * 16 : tile * 128 + wv * 32;
   const int rows0 = c0, rows1 = G1 ? p.I + c0 : c0 + 16;
   const Off o[2] = {row_off<1>(rows0 + m, G, 0, GB, lsub), row_off<1>(rows1 + m, G, 0, GB, lsub)};
-
   for (int q0 = o0; q0 < o1; q0 += kMidRows) {
     const int R = min(kMidRows, o1 - q0);
-    uint32_t roff[kMidChunks<BITS>];
-    mid_rows<BITS, G1>(p, q0, R, roff);
-    MidW<BITS> wcur, wnext;
-    MidA<BITS> an;
-    mid_load<BITS>(xw, o, 0, wcur);
-    mid_fetch_a<BITS>(p.a, roff, R, 0, an);
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < steps; ++s) {
-      // stage this step's rows (fetched during the previous step) and their sums
-      __syncthreads();
-      mid_store_a<BITS>(act, Xs, R, an);
-      __syncthreads();
-      // next step's weights and rows in flight during this step's MFMAs
-      if (s + 1 < steps) {
-        mid_load<BITS>(xw, o, (s + 1) * kMidUnits, wnext);
-        mid_fetch_a<BITS>(p.a, roff, R, (s + 1) * kMidStepK, an);
-      }
-      // both row tiles always (a pass of up to 16 rows repeats its last row in
-      // the second): one instantiation keeps the registers at two blocks per CU
-      mid_step<BITS, 2>(wcur, act, Xs, R, p.magic, acc);
-      wcur = wnext;
-    }
-    // epilogue: C row 4 lsub + i of tile t is staged row 16 t + 4 lsub + i, column m
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = t * 16 + 4 * lsub + i;
-        if (rr >= R) continue;
-        const size_t q = (size_t)(q0 + rr);
-        if constexpr (G1) {
-          const float g = acc[0][t][i], u = acc[1][t][i];
-          p.out[q * p.I + c0 + m] = f32_to_bf16(silu_f(g) * u);
-        } else {
-          p.out[q * p.H + c0 + m] = f32_to_bf16(acc[0][t][i]);
-          p.out[q * p.H + c0 + 16 + m] = f32_to_bf16(acc[1][t][i]);
-        }
-      }
+    if (R > 16)
+      mid_pass<BITS, G1, 2>(p, xw, o, c0, q0, R, steps, act, Xs);
+    else
+      mid_pass<BITS, G1, 1>(p, xw, o, c0, q0, R, steps, act, Xs);
   }
 }
 

@@ -380,11 +380,169 @@ __global__ void __launch_bounds__(512) route_tiled2_kernel(const uint16_t *__res
   }
 }
 
+// ------------------------------------------------------------ 32 < T <= 1024, H % 2048 == 0
+// Logits and top-k as two launches, so that a batch spreads over
+// (T / (4 TPW)) x (E / 64) x KS blocks instead of one block per 16 tokens:
+//  * route_tiles_kernel: block (token tile, expert group, K part); wave w owns
+//    tokens 4 TPW b + TPW w .. + TPW - 1 (its x operand is one broadcast LDS
+//    read), lane l owns expert 64 g + l; K part p covers slices
+//    [64 p / KS, 64 (p + 1) / KS), an aligned subtree of the slice tree.
+//    32-h chunks of x and w are converted to float32 into LDS; each thread
+//    keeps the next kPre chunks' loads in flight, so the wait for a chunk is
+//    covered by the work on the kPre before it.  Same order as
+//    above (slice chains, carry merge at each slice end), so each part ends
+//    with its subtree sum, bit-identical to that node of the full tree.
+//  * route_topk_kernel: one wave per token combines the KS subtree sums in
+//    tree order, adds the bias (the logits, written out if asked for), runs
+//    the top-k and softmax, and clears the partial sums in the workspace.
+constexpr int kPre = 8;  // chunks of x and w in flight per thread (a part has a multiple of 8 chunks)
+template <int TPW, int KS>
+__global__ void __launch_bounds__(256) route_tiles_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ w, int T, int H, int E,
+                                                          float *part) {
+  constexpr int TT = 4 * TPW;  // tokens per block
+  constexpr int SUB = KS == 1 ? 6 : KS == 2 ? 5 : 4;  // tree level of a part's subtree
+  __shared__ __attribute__((aligned(16))) float xs[kHC][TT];
+  __shared__ __attribute__((aligned(16))) float wsm[kHC][kWave];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int ngrp = (E + kWave - 1) / kWave;
+  const int kp = blockIdx.x % KS, tile = blockIdx.x / KS;
+  const int t_base = (tile / ngrp) * TT, e0 = (tile % ngrp) * kWave;
+  const int cps = H / 64 / kHC;  // chunks per slice
+  const int nch = H / KS / kHC;  // chunks of this part
+  const int h0 = kp * (H / KS);
+  // staging: thread tid converts 8 h of expert row e0 + tid / 4; threads
+  // < 4 TT one 8-h piece of token tid / 4
+  const int we = tid >> 2, wq = tid & 3;
+  const bool wvalid = e0 + we < E;
+  const u32x4 *wrow = (const u32x4 *)(w + (size_t)min(e0 + we, E - 1) * H + h0) + wq;
+  const int xt = t_base + (tid >> 2);
+  const bool xload = tid < 4 * TT, xvalid = xload && xt < T;
+  const u32x4 *xrow = (const u32x4 *)(x + (size_t)min(xt, T - 1) * H + h0) + wq;
+  // kPre chunks in flight: chunk c sits in register stage c % kPre, so the
+  // loop below is unrolled by kPre and every stage index is a constant
+  u32x4 pw[kPre], px[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    pw[j] = wrow[j * 4];
+    px[j] = xload ? xrow[j * 4] : u32x4{0u, 0u, 0u, 0u};
+  }
+  float acc[TPW], lvl[6][TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = 0.f;
+  int s = 0;
+  const float *xsp = &xs[0][TPW * wave];
+  const float *wsp = &wsm[0][lane];
+  for (int c0 = 0; c0 < nch; c0 += kPre) {
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const int ch = c0 + j;
+      __syncthreads();  // the previous chunk has been consumed
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wsm[wq * 8 + 2 * r][we] = wvalid ? bf16lo(pw[j][r]) : 0.f;
+        wsm[wq * 8 + 2 * r + 1][we] = wvalid ? bf16hi(pw[j][r]) : 0.f;
+      }
+      if (xload)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          xs[wq * 8 + 2 * r][tid >> 2] = xvalid ? bf16lo(px[j][r]) : 0.f;
+          xs[wq * 8 + 2 * r + 1][tid >> 2] = xvalid ? bf16hi(px[j][r]) : 0.f;
+        }
+      __syncthreads();
+      if (ch + kPre < nch) {
+        pw[j] = wrow[(ch + kPre) * 4];
+        if (xload) px[j] = xrow[(ch + kPre) * 4];
+      }
+#pragma unroll
+      for (int i = 0; i < kHC; ++i) {
+        const float wv = wsp[i * kWave];
+        if constexpr (TPW == 4) {
+          const f32x4 xv = *(const f32x4 *)(xsp + i * TT);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) acc[a] = __builtin_fmaf(xv[a], wv, acc[a]);
+        } else {
+          const f32x2 xv = *(const f32x2 *)(xsp + i * TT);
+#pragma unroll
+          for (int a = 0; a < TPW; ++a) acc[a] = __builtin_fmaf(xv[a], wv, acc[a]);
+        }
+      }
+      if ((ch + 1) % cps == 0) {
+        // slice s (of this part) is complete: lev = trailing one bits of s
+        switch (__builtin_ctz(~(unsigned)s)) {
+          case 0: carry_merge<0>(lvl, acc); break;
+          case 1: carry_merge<1>(lvl, acc); break;
+          case 2: carry_merge<2>(lvl, acc); break;
+          case 3: carry_merge<3>(lvl, acc); break;
+          case 4: carry_merge<4>(lvl, acc); break;
+          case 5: carry_merge<5>(lvl, acc); break;
+          default: carry_merge<6>(lvl, acc); break;  // after slice 63
+        }
+        ++s;
+      }
+    }
+  }
+  // the part's subtree sum: the root (acc) for one part, else its top carry level
+  const int e = e0 + lane;
+  if (e < E) {
+#pragma unroll
+    for (int a = 0; a < TPW; ++a) {
+      const int t = t_base + TPW * wave + a;
+      if (t < T) part[((size_t)kp * T + t) * E + e] = SUB == 6 ? acc[a] : lvl[SUB < 6 ? SUB : 0][a];
+    }
+  }
+}
+
+template <int KS>
+__global__ void __launch_bounds__(256) route_topk_kernel(float *part, const float *bias, float *lg_out, int T, int E,
+                                                         int k, int32_t *ids, float *gates) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;  // wave-uniform
+  topk_softmax_any(
+      [&](auto &v) {
+        constexpr int NV = sizeof(v) / sizeof(v[0]);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int ee = lane_id() + kWave * j;
+          v[j] = 0.f;
+          if (ee < E) {
+            float p[KS];
+#pragma unroll
+            for (int q = 0; q < KS; ++q) {
+              float *pp = part + ((size_t)q * T + t) * E + ee;
+              p[q] = *pp;
+              *pp = 0.f;  // the partial sums live in the workspace
+            }
+            float l = p[0];
+            if constexpr (KS == 2) l = p[0] + p[1];
+            if constexpr (KS == 4) l = (p[0] + p[1]) + (p[2] + p[3]);
+            l = l + (bias ? bias[ee] : 0.f);
+            if (lg_out) lg_out[(size_t)t * E + ee] = l;
+            v[j] = l;
+          }
+        }
+      },
+      E, k, ids + (size_t)t * k, gates + (size_t)t * k);
+}
+
 }  // namespace
+
+// Batches of 32 < T <= 1024 tokens (with H % 2048 == 0) run the logits as
+// tiles of tokens x 64 experts x K parts plus a top-k launch; the partial
+// sums live in the workspace.
+constexpr int kRouteTilesMinT = 32, kRouteTilesMaxT = 1024;
+static bool route_tiles(int T, int H) {
+  return T > kRouteTilesMinT && T <= kRouteTilesMaxT && H % (64 * kHC) == 0;  // slices of whole chunks
+}
+constexpr int kRouteKS = 4;  // K parts (subtrees of 16 slices)
 
 size_t route_workspace_bytes(int T, int E) {
   size_t b = kCtlBytes;
   if (T <= kRouteSmallT) b += (size_t)T * E * sizeof(uint64_t);  // tagged logits
+  if (T > kRouteTilesMinT && T <= kRouteTilesMaxT) {              // partial sums of the tiled launch
+    const size_t l = kCtlBytes + (size_t)kRouteKS * T * E * sizeof(float);
+    if (l > b) b = l;
+  }
   return b;
 }
 
@@ -422,7 +580,14 @@ hipError_t launch_route_group(const uint16_t *x, const uint16_t *w_router, const
 
 hipError_t launch_route(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
                         int k, int32_t *ids, float *gates, float *logits, void *ws, hipStream_t st) {
-  if (T <= kRouteSmallT) {
+  if (route_tiles(T, H)) {
+    float *part = (float *)((char *)ws + kCtlBytes);
+    const int ngrp = (E + kWave - 1) / kWave;
+    route_tiles_kernel<2, kRouteKS><<<dim3((unsigned)(((T + 7) / 8) * ngrp * kRouteKS)), 256, 0, st>>>(
+        x, w_router, T, H, E, part);
+    route_topk_kernel<kRouteKS><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(part, bias, logits, T, E, k, ids,
+                                                                               gates);
+  } else if (T <= kRouteSmallT) {
     launch_route_small<false>(x, w_router, bias, T, H, E, k, ids, gates, logits, ws, GroupOut{}, st);
   } else {
     dim3 grid((T + kTileT - 1) / kTileT), block(256);

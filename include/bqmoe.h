@@ -216,7 +216,7 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  *           fused GEMV kernel streaming each selected expert's packed weights
  *           once, rows in passes of four;
  *   mid     otherwise while T*k <= 24*E (INT4 / 2-bit g128, H and I
- *           multiples of 512): two launches that stage up to 32 rows of an
+ *           multiples of 256): two launches that stage up to 32 rows of an
  *           expert per K step and read its weights once per 32 rows;
  *   GEMM    otherwise: grouped bf16-MFMA GEMMs on dequantised tiles.
  * The pages dispatch between a GEMV and dequantise-then-GEMM at 16 rows (page

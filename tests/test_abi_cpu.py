@@ -258,7 +258,7 @@ def test_layer_noalloc_argument_errors():
 
 def test_expert_ffn_path_rule():
     """Host-side dispatch: decode up to about six rows per expert, the mid
-    path up to 24 (INT4 / 2-bit g128, H and I multiples of 512), the grouped
+    path up to 24 (INT4 / 2-bit g128, H and I multiples of 256), the grouped
     GEMMs beyond and for every other format."""
     L = bq.lib()
     f = L.moe_expert_ffn_path
@@ -273,8 +273,15 @@ def test_expert_ffn_path_rule():
     assert f(256, 8, 256, *full, 8, 128) == 2 and f(256, 8, 256, *full, 4, 32) == 2
     assert f(256, 8, 256, *full, 6, 128) == 2 and f(256, 8, 256, *full, 4, 16) == 2
     assert f(1, 8, 256, *full, 4, 16) == 0
-    assert f(40, 2, 8, 256, 128, 4, 128) == 2          # H, I not multiples of 512
-    assert f(40, 2, 8, 512, 512, 4, 128) == 1
+    assert f(40, 2, 8, 256, 128, 4, 128) == 2          # I not a multiple of 256
+    assert f(40, 2, 8, 384, 256, 4, 128) == 2          # H not a multiple of 256
+    assert f(40, 2, 8, 512, 512, 4, 128) == 1 and f(40, 2, 8, 256, 256, 2, 128) == 1
     assert f(0, 2, 8, 512, 512, 4, 128) == 0
     assert f(-1, 8, 256, *full, 4, 128) == -1 and f(1, 8, 256, *full, 3, 128) == -1
     assert bq.ffn_path(256, 8, 256, *full, 4) == "mid" and bq.ffn_path(1, 8, 256, *full, "nvfp4") == "decode"
+
+
+def test_binding_exports_every_public_name():
+    """Every name in the package's __all__ is defined."""
+    assert [n for n in bq.__all__ if not hasattr(bq, n)] == []
+    assert callable(bq.quant_act_nvfp4) and callable(bq.expert_ffn_nvfp4_table) and callable(bq.ffn_path)

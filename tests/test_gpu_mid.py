@@ -65,6 +65,7 @@ def _check(sp, inp, r, got, experts=None):
 
 CASES = [  # T, H, I, E, k, zipf: rows per expert ~10 (one tile), ~20 (two tiles), skewed (several passes)
     (40, 512, 512, 8, 2, 0.0),
+    (40, 256, 256, 8, 2, 0.0),
     (90, 512, 1024, 8, 2, 0.0),
     (120, 1024, 512, 16, 3, 1.2),
     (70, 2048, 512, 32, 8, 0.0),

@@ -103,6 +103,28 @@ def test_route_both_kernels_ragged_shapes(T, H, E, k):
     _check_route(x, w_r, bias, k)
 
 
+@pytest.mark.parametrize("T,H,E,k", [(33, 2048, 300, 8), (1024, 2048, 64, 4), (1025, 2048, 64, 4), (100, 4096, 1, 1),
+                                     (257, 2048, 1024, 32), (40, 4096, 256, 8)])
+def test_route_tiles_kernel_ragged_shapes(T, H, E, k):
+    """32 < T <= 1024 with H % 2048 == 0 runs the logits as tiles of tokens x
+    64 experts x 4 K parts and the top-k (with the tree's top levels) as a
+    second launch: ragged token tiles and expert groups against the oracle,
+    the logits written to the caller's array; then the same call without
+    logits gives the same ids and gates and leaves the workspace zero.
+    T = 1025 checks the token-tiled kernel across the boundary."""
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, E=E, k=k, seed=88 + T)
+    x = workload.make_x(sp)
+    w_r, _ = workload.make_router(sp)
+    bias = (np.random.default_rng(T).standard_normal(E) * 0.01).astype(np.float32)
+    ids, gates = _check_route(x, w_r, bias, k)
+    ws = bq.Workspaces("cuda")
+    for _ in range(2):
+        ids2, gates2 = bq.route(to_dev(x), to_dev(w_r), k, to_dev(bias), ws=ws)
+        assert np.array_equal(to_np(ids2), ids) and np.array_equal(to_np(gates2), gates)
+        torch.cuda.synchronize()
+        assert int(ws._bufs["route"].view(torch.int32).abs().sum()) == 0
+
+
 @pytest.mark.parametrize("name", ["decode_t1_h4096_e256_k8_i1024_int4", "verify_t16_h4096_e256_k8_i1024_int4"])
 def test_route_decode_full_size(name):
     sp = workload.spec(name)
