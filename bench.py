@@ -22,8 +22,9 @@ of the layer (verify T = 16 INT4, prefill T = 4096 INT4, 2-bit decode T = 1,
 2-bit prefill T = 8192) under "configs", each with at least 100 (decode) or
 20 (prefill) timed steps.  For every workload it reports tokens/s, the step
 time's median / p10 / p90 over back-to-back graph replays, the roofline of
-the dominant kernel (decode: HBM-bound on the packed weight bytes of the
-selected experts; prefill: the expert-FFN GEMMs, MFMA-bound on useful FLOPs)
+the dominant kernel (decode and middle batches: HBM-bound on the packed
+weight bytes of the selected experts; prefill: the expert-FFN GEMMs,
+MFMA-bound on useful FLOPs)
 timed with HIP events on the stream it is launched on, that rate also as a
 fraction of the rates this device measurably reaches (a streaming read and an
 MFMA-only loop, "peaks"), and the CPU oracle's rate on a bounded sample of
@@ -101,10 +102,12 @@ def copy_calibration():
 # while these files are unchanged since the counters were taken.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "decode": ["bit_quantized_moe_amd/csrc/ffn_decode.hip", "bit_quantized_moe_amd/csrc/common.cuh",
-               "bit_quantized_moe_amd/csrc/route_dev.cuh"],
-    "layer": ["bit_quantized_moe_amd/csrc/ffn_decode.hip", "bit_quantized_moe_amd/csrc/common.cuh",
-              "bit_quantized_moe_amd/csrc/route_dev.cuh"],
+    "decode": ["bit_quantized_moe_amd/csrc/ffn_decode.hip", "bit_quantized_moe_amd/csrc/gemv_ops.cuh",
+               "bit_quantized_moe_amd/csrc/common.cuh", "bit_quantized_moe_amd/csrc/route_dev.cuh"],
+    "layer": ["bit_quantized_moe_amd/csrc/ffn_decode.hip", "bit_quantized_moe_amd/csrc/gemv_ops.cuh",
+              "bit_quantized_moe_amd/csrc/common.cuh", "bit_quantized_moe_amd/csrc/route_dev.cuh"],
+    "mid": ["bit_quantized_moe_amd/csrc/ffn_mid.hip", "bit_quantized_moe_amd/csrc/gemv_ops.cuh",
+            "bit_quantized_moe_amd/csrc/common.cuh"],
     "prefill": ["bit_quantized_moe_amd/csrc/ffn_prefill.hip", "bit_quantized_moe_amd/csrc/common.cuh"],
 }
 
@@ -500,13 +503,17 @@ def run_workload(name, args, dev, steps, warmup):
     distinct = [int(st["active"][0].item()) for st in plan.sets]
     mean_distinct = sum(distinct) / len(distinct)
     bpe = sp.weight_bytes_per_expert()
-    # the library's decode-path dispatch (HBM-bound): T <= 512 and T*k <= 6E, every format
-    decode = sp.T <= 512 and sp.T * sp.k <= 6 * sp.E
-    ffn_kernel = ("quant_nvfp4_kernel, then " if sp.nvfp4 else "") + (
-        f"ffn_decode_kernel<{5 if sp.nvfp4 else sp.bits}, ...> (expert-FFN stage: gate_up+SwiGLU+down GEMV)"
-        if decode else "ffn_gemm_kernel gate_up+SwiGLU, then ffn_gemm_kernel down (grouped bf16-MFMA GEMMs)")
+    # the library's expert-FFN dispatch: the decode and mid paths stream each
+    # active expert's packed weights (HBM-bound), the grouped GEMMs are MFMA-bound
+    path = bq.ffn_path(sp.T, sp.k, sp.E, sp.H, sp.I, "nvfp4" if sp.nvfp4 else sp.bits, sp.group)
+    decode = path in ("decode", "mid")
+    ffn_kernel = ("quant_nvfp4_kernel, then " if sp.nvfp4 else "") + {
+        "decode": f"ffn_decode_kernel<{5 if sp.nvfp4 else sp.bits}, ...> (expert-FFN stage: gate_up+SwiGLU+down GEMV)",
+        "mid": f"mid_kernel<{sp.bits}, true> gate_up+SwiGLU, then mid_kernel<{sp.bits}, false> down "
+               "(rows staged per K step, each expert's weights streamed once per 32 rows)",
+        "gemm": "ffn_gemm_kernel gate_up+SwiGLU, then ffn_gemm_kernel down (grouped bf16-MFMA GEMMs)"}[path]
     ffn_stage = None
-    if decode and args.experts == "host":
+    if path == "decode" and args.experts == "host":
         alg = mean_distinct * bpe
         achieved = alg / (ffn_ms * 1e-3) / 1e9
         roof = {"bound": "pcie", "achieved": round(achieved, 1), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
@@ -520,7 +527,7 @@ def run_workload(name, args, dev, steps, warmup):
         achieved = alg / (ffn_ms * 1e-3) / 1e9
         ffn_stage = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(sp.name, "decode") if args.experts == "arrays" else None,
+                     "traffic": stored_traffic(sp.name, path) if args.experts == "arrays" else None,
                      "kernel": ffn_kernel, "algorithmic_bytes_per_launch": int(alg),
                      "avg_launch_us": round(ffn_ms * 1e3, 3), "distinct_experts_per_launch": mean_distinct}
         roof = ffn_stage
