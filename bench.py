@@ -108,7 +108,8 @@ KERNEL_SOURCES = {
               "bit_quantized_moe_amd/csrc/common.cuh", "bit_quantized_moe_amd/csrc/route_dev.cuh"],
     "mid": ["bit_quantized_moe_amd/csrc/ffn_mid.hip", "bit_quantized_moe_amd/csrc/gemv_ops.cuh",
             "bit_quantized_moe_amd/csrc/common.cuh"],
-    "prefill": ["bit_quantized_moe_amd/csrc/ffn_prefill.hip", "bit_quantized_moe_amd/csrc/common.cuh"],
+    "prefill": ["bit_quantized_moe_amd/csrc/ffn_prefill.hip", "bit_quantized_moe_amd/csrc/ffn_mid.hip",
+                "bit_quantized_moe_amd/csrc/gemv_ops.cuh", "bit_quantized_moe_amd/csrc/common.cuh"],
 }
 
 
@@ -511,7 +512,8 @@ def run_workload(name, args, dev, steps, warmup):
         "decode": f"ffn_decode_kernel<{5 if sp.nvfp4 else sp.bits}, ...> (expert-FFN stage: gate_up+SwiGLU+down GEMV)",
         "mid": f"mid_kernel<{sp.bits}, true> gate_up+SwiGLU, then mid_kernel<{sp.bits}, false> down "
                "(rows staged per K step, each expert's weights streamed once per 32 rows)",
-        "gemm": "ffn_gemm_kernel gate_up+SwiGLU, then ffn_gemm_kernel down (grouped bf16-MFMA GEMMs)"}[path]
+        "gemm": ("mid_kernel (experts of at most 64 rows), " if not sp.nvfp4 and sp.group == 128 and sp.bits in (2, 4)
+                 else "") + "ffn_gemm_kernel gate_up+SwiGLU, then ffn_gemm_kernel down (grouped bf16-MFMA GEMMs)"}[path]
     ffn_stage = None
     if path == "decode" and args.experts == "host":
         alg = mean_distinct * bpe

@@ -50,6 +50,7 @@ struct MidParams {
   const uint64_t *tab;  // per-expert address table or null; this GEMM's entries start at tab_off
   int tab_off;
   uint16_t *out;        // gate_up: h [T*k, I]; down: y_perm [T*k, H]
+  int max_rows;         // experts with more rows are left to the grouped GEMMs (prefill hybrid)
   uint32_t magic;       // 0x43434343 (the bf16 high byte of 128)
 };
 
@@ -225,6 +226,7 @@ __global__ void __launch_bounds__(kMidWaves * kWave, 3) mid_kernel(MidParams p) 
   const int e = min(max(sload(p.active + 1 + a), 0), p.E - 1);
   const int o0 = min(max(sload(p.offsets + e), 0), nrows);
   const int o1 = min(max(sload(p.offsets + e + 1), o0), nrows);
+  if (o1 - o0 > p.max_rows) return;  // block-uniform
   constexpr int GB = kGroupBytes<BITS>;
   const int G = p.K / kGroup, steps = G / kMidUnits;
   ExpertW xw;
@@ -253,51 +255,65 @@ bool mid_layout_ok(int H, int I, int bits, int group) {
   return (bits == 4 || bits == 2) && group == 128 && H % kMidStepK == 0 && I % kMidStepK == 0;
 }
 
-hipError_t launch_ffn_mid(const FfnArgs &a, hipStream_t st) {
+// The two launches for the experts with at most max_rows rows (gate_up into
+// hbuf, then down into y_perm); h is left for the caller to clear.
+static MidParams mid_params(const FfnArgs &a, uint16_t *hbuf, int max_rows, bool g1) {
+  MidParams m{};
+  m.offsets = a.offsets;
+  m.sorted_rows = a.sorted_rows;
+  m.active = a.active;
+  m.T = a.T;
+  m.k = a.k;
+  m.E = a.E;
+  m.I = a.I;
+  m.H = a.H;
+  m.tab = a.tab;
+  m.max_rows = max_rows;
+  m.magic = 0x43434343u;
+  if (g1) {
+    m.a = a.x;
+    m.K = a.H;
+    m.n_rows_w = 2 * a.I;
+    m.n_tiles = a.I / 64;
+    m.codes = (const uint8_t *)a.w13_codes;
+    m.scales = (const uint8_t *)a.w13_scales;
+    m.zeros = a.w13_zeros;
+    m.tab_off = 0;
+    m.out = hbuf;
+  } else {
+    m.a = hbuf;
+    m.K = a.I;
+    m.n_rows_w = a.H;
+    m.n_tiles = a.H / 128;
+    m.codes = (const uint8_t *)a.w2_codes;
+    m.scales = (const uint8_t *)a.w2_scales;
+    m.zeros = a.w2_zeros;
+    m.tab_off = 3;
+    m.out = a.y_perm;
+  }
+  return m;
+}
+
+hipError_t launch_mid_gemm(const FfnArgs &a, uint16_t *hbuf, int max_rows, bool gate_up, hipStream_t st) {
   const int nrows = a.T * a.k;
   const int amax = a.E < nrows ? a.E : nrows;
+  const MidParams m = mid_params(a, hbuf, max_rows, gate_up);
+  const dim3 grid((unsigned)(amax * m.n_tiles));
+  if (a.bits == 4)
+    gate_up ? mid_kernel<4, true><<<grid, kMidWaves * kWave, 0, st>>>(m)
+            : mid_kernel<4, false><<<grid, kMidWaves * kWave, 0, st>>>(m);
+  else
+    gate_up ? mid_kernel<2, true><<<grid, kMidWaves * kWave, 0, st>>>(m)
+            : mid_kernel<2, false><<<grid, kMidWaves * kWave, 0, st>>>(m);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_mid(const FfnArgs &a, hipStream_t st) {
   uint16_t *hbuf = (uint16_t *)((char *)a.ws + ffn_ctl_bytes(a.T, a.k, a.E));
-  MidParams g1{};
-  g1.a = a.x;
-  g1.offsets = a.offsets;
-  g1.sorted_rows = a.sorted_rows;
-  g1.active = a.active;
-  g1.T = a.T;
-  g1.k = a.k;
-  g1.E = a.E;
-  g1.I = a.I;
-  g1.H = a.H;
-  g1.K = a.H;
-  g1.n_rows_w = 2 * a.I;
-  g1.n_tiles = a.I / 64;
-  g1.codes = (const uint8_t *)a.w13_codes;
-  g1.scales = (const uint8_t *)a.w13_scales;
-  g1.zeros = a.w13_zeros;
-  g1.tab = a.tab;
-  g1.tab_off = 0;
-  g1.out = hbuf;
-  g1.magic = 0x43434343u;
-  MidParams g2 = g1;
-  g2.a = hbuf;
-  g2.K = a.I;
-  g2.n_rows_w = a.H;
-  g2.n_tiles = a.H / 128;
-  g2.codes = (const uint8_t *)a.w2_codes;
-  g2.scales = (const uint8_t *)a.w2_scales;
-  g2.zeros = a.w2_zeros;
-  g2.tab_off = 3;
-  g2.out = a.y_perm;
-  const dim3 grid1((unsigned)(amax * g1.n_tiles)), grid2((unsigned)(amax * g2.n_tiles));
-  if (a.bits == 4) {
-    mid_kernel<4, true><<<grid1, kMidWaves * kWave, 0, st>>>(g1);
-    mid_kernel<4, false><<<grid2, kMidWaves * kWave, 0, st>>>(g2);
-  } else {
-    mid_kernel<2, true><<<grid1, kMidWaves * kWave, 0, st>>>(g1);
-    mid_kernel<2, false><<<grid2, kMidWaves * kWave, 0, st>>>(g2);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_mid_gemm(a, hbuf, a.T * a.k, true, st);
+  if (e == hipSuccess) e = launch_mid_gemm(a, hbuf, a.T * a.k, false, st);
   if (e != hipSuccess) return e;
-  return launch_zero16(hbuf, (size_t)nrows * a.I * sizeof(uint16_t), st);
+  return launch_zero16(hbuf, (size_t)a.T * a.k * a.I * sizeof(uint16_t), st);
 }
 
 }  // namespace bqmoe

@@ -23,7 +23,10 @@
 //    v_mfma_f32_16x16x32_bf16 (float32 accumulation);
 //  * software pipeline with one barrier per K tile of 64: while the MFMAs
 //    read one buffer, the next tile is dequantised into the other and global
-//    loads run S tiles ahead in registers.
+//    loads run S tiles ahead in registers;
+//  * INT4 and 2-bit g128: the experts with at most kHybridRows rows run the
+//    middle-batch kernel instead (their M tile would dequantise a whole
+//    expert's weights for a few rows), so the GEMMs skip them.
 #include <type_traits>
 
 #include "common.cuh"
@@ -38,6 +41,7 @@ constexpr int kRowBytes = BK * 2;            // one LDS row: 64 bf16 = 8 chunks 
 constexpr int kTileBytes = 128 * kRowBytes;  // 16 KiB per operand tile
 constexpr int kBufWord3 = 0x00020000;        // buffer resource word 3: raw 32-bit access
 constexpr int kMGroup = 1;  // consecutive M-tile slots per XCD, iterated fastest (2-8 measured: no gain)
+constexpr int kHybridRows = 64;  // INT4 / 2-bit g128: experts with at most this many rows take the mid kernel (32-128 measured, 64 best)
 
 struct GemmParams {
   const uint16_t *a_src;   // G1: x [T, H]; G2: h [T*k, I]
@@ -54,6 +58,7 @@ struct GemmParams {
   const uint64_t *tab;     // per-expert address table or null; this GEMM's entries start at tab_off
   int tab_off;
   int n_blocks;            // N tiles: I / 64 (G1) or H / BN (G2)
+  int min_rows;            // experts with at most this many rows are left to the mid kernel
   // NVFP4: per-expert float32 tensor scales of the weights, the tensor scale
   // of this GEMM's (quantised) A operand, and G1's h quantiser scale
   const float *gscale;
@@ -84,7 +89,7 @@ __device__ bool find_tile(const GemmParams &p, int slot, int *e_out, int *m0_out
         e = min(max(p.active[1 + a], 0), p.E - 1);
         o0 = min(max(p.offsets[e], 0), nrows);
         o1 = min(max(p.offsets[e + 1], o0), nrows);
-        tiles = (o1 - o0 + BM - 1) / BM;
+        tiles = o1 - o0 > p.min_rows ? (o1 - o0 + BM - 1) / BM : 0;
       }
       int inc = tiles;
 #pragma unroll
@@ -436,26 +441,43 @@ hipError_t launch_ffn_prefill(const FfnArgs &a, const DeviceInfo &, hipStream_t 
 
   g1.n_blocks = a.I / 64;
   g2.n_blocks = a.H / BN;
+  // Hybrid: for INT4 and 2-bit g128 the experts with at most kHybridRows rows
+  // take the middle-batch kernel (weights read once, no per-element
+  // dequantisation) and the GEMMs skip them; the two write disjoint h and
+  // y_perm rows.
+  const bool hybrid = !a.nvfp4 && mid_layout_ok(a.H, a.I, a.bits, a.group);
+  g1.min_rows = g2.min_rows = hybrid ? kHybridRows : 0;
   dim3 grid1((unsigned)(slots * g1.n_blocks)), grid2((unsigned)(slots * g2.n_blocks));
   // two register stages: K % 128 == 0 makes K / BK even
   auto run = [&](auto g1k, auto g2k) {
+    if (hybrid) {
+      const hipError_t e = launch_mid_gemm(a, hbuf, kHybridRows, true, st);
+      if (e != hipSuccess) return e;
+    }
     g1k<<<grid1, 256, 0, st>>>(g1);
+    if (hybrid) {
+      const hipError_t e = launch_mid_gemm(a, hbuf, kHybridRows, false, st);
+      if (e != hipSuccess) return e;
+    }
     g2k<<<grid2, 256, 0, st>>>(g2);
+    return hipGetLastError();
   };
+  hipError_t err;
   if (a.nvfp4)
-    run(ffn_gemm_kernel<4, 16, true, 2>, ffn_gemm_kernel<4, 16, false, 2>);
+    err = run(ffn_gemm_kernel<4, 16, true, 2>, ffn_gemm_kernel<4, 16, false, 2>);
   else if (a.bits == 4 && a.group == 128)
-    run(ffn_gemm_kernel<4, 128, true, 2>, ffn_gemm_kernel<4, 128, false, 2>);
+    err = run(ffn_gemm_kernel<4, 128, true, 2>, ffn_gemm_kernel<4, 128, false, 2>);
   else if (a.bits == 4)
-    run(ffn_gemm_kernel<4, 32, true, 2>, ffn_gemm_kernel<4, 32, false, 2>);
+    err = run(ffn_gemm_kernel<4, 32, true, 2>, ffn_gemm_kernel<4, 32, false, 2>);
   else if (a.bits == 8 && a.group == 128)
-    run(ffn_gemm_kernel<8, 128, true, 2>, ffn_gemm_kernel<8, 128, false, 2>);
+    err = run(ffn_gemm_kernel<8, 128, true, 2>, ffn_gemm_kernel<8, 128, false, 2>);
   else if (a.bits == 8)
-    run(ffn_gemm_kernel<8, 32, true, 2>, ffn_gemm_kernel<8, 32, false, 2>);
+    err = run(ffn_gemm_kernel<8, 32, true, 2>, ffn_gemm_kernel<8, 32, false, 2>);
   else if (a.bits == 6)
-    run(ffn_gemm_kernel<6, 128, true, 2>, ffn_gemm_kernel<6, 128, false, 2>);
+    err = run(ffn_gemm_kernel<6, 128, true, 2>, ffn_gemm_kernel<6, 128, false, 2>);
   else
-    run(ffn_gemm_kernel<2, 128, true, 2>, ffn_gemm_kernel<2, 128, false, 2>);
+    err = run(ffn_gemm_kernel<2, 128, true, 2>, ffn_gemm_kernel<2, 128, false, 2>);
+  if (err != hipSuccess) return err;
   // h is T*k*I bf16 (I % 128 == 0, so a whole number of 16-byte chunks),
   // followed for NVFP4 by the T*H quantised activations
   const size_t n16 = ((size_t)nrows * a.I + (a.nvfp4 ? (size_t)a.T * a.H : 0)) * sizeof(uint16_t) / 16;

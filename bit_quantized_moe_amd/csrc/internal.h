@@ -108,6 +108,10 @@ inline bool mid_path(int T, int k, int E) {
 }
 bool mid_layout_ok(int H, int I, int bits, int group);
 hipError_t launch_ffn_mid(const FfnArgs &a, hipStream_t st);
+// One of the mid path's two launches (gate_up into hbuf, or down from it)
+// for the experts with at most max_rows rows; the grouped-GEMM path uses it
+// for its small experts.
+hipError_t launch_mid_gemm(const FfnArgs &a, uint16_t *hbuf, int max_rows, bool gate_up, hipStream_t st);
 
 // combine.hip
 hipError_t launch_combine(const uint16_t *y_perm, const int32_t *row_pos, const float *gates, int T, int k,

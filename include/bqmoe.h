@@ -218,7 +218,9 @@ moe_status moe_route_permute(const uint16_t *x, const uint16_t *w_router, const 
  *   mid     otherwise while T*k <= 24*E (INT4 / 2-bit g128, H and I
  *           multiples of 256): two launches that stage up to 32 rows of an
  *           expert per K step and read its weights once per 32 rows;
- *   GEMM    otherwise: grouped bf16-MFMA GEMMs on dequantised tiles.
+ *   GEMM    otherwise: grouped bf16-MFMA GEMMs on dequantised tiles; for
+ *           INT4 / 2-bit g128 (H, I multiples of 256) the experts with at
+ *           most 64 rows run the mid kernel inside the same call.
  * The pages dispatch between a GEMV and dequantise-then-GEMM at 16 rows (page
  * "Qwen3.8-Flash-Next FP6-INT8", "Quantization quality"); the crossovers used
  * here were measured on MI355X instead.  The permutation arrays must come

@@ -140,3 +140,29 @@ def test_mid_full_size_sampled(name):
     act = act[1:1 + act[0]]
     by = sorted(act.tolist(), key=lambda e: counts[e])
     _check(sp, inp, r, got, experts=[by[-1], by[len(by) // 2], by[0]])
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_prefill_hybrid_small_experts_take_the_mid_kernel(bits):
+    """On the grouped-GEMM path (T*k > 24 E) INT4 and 2-bit g128 experts with
+    at most 64 rows run the mid kernel and the others the GEMMs, in one call:
+    every row of both kinds against the oracle, twice on one workspace
+    (bit-identical, workspace left zero)."""
+    T, H, I, E, k = 400, 512, 256, 16, 4
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, I=I, E=E, k=k, bits=bits,
+                       scale_sigma=0.02 if bits == 4 else 0.05, seed=4400 + bits, zipf_s=1.1)
+    assert bq.ffn_path(T, k, E, H, I, bits) == "gemm"
+    inp = workload.make_layer_inputs(sp)
+    wd = weights_to_dev(inp.weights)
+    bias = to_dev(inp.logit_bias) if inp.logit_bias is not None else None
+    r = bq.route_permute(to_dev(inp.x), to_dev(inp.w_router), k, bias)
+    ws = bq.Workspaces("cuda")
+    args = (to_dev(inp.x), r["offsets"], r["sorted_rows"], r["active"], k)
+    got = bq.expert_ffn(*args, wd, bits, I, ws=ws)
+    counts = _check(sp, inp, r, got)
+    act = counts[counts > 0]
+    assert (act <= 64).any() and (act > 64).any(), counts
+    again = bq.expert_ffn(*args, wd, bits, I, ws=ws)
+    assert torch.equal(again.view(torch.int16), got.view(torch.int16))
+    torch.cuda.synchronize()
+    assert int(ws._bufs["ffn"].view(torch.int32).abs().sum()) == 0
