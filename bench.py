@@ -49,7 +49,7 @@ DEFAULT_WORKLOAD = "decode_t1_h4096_e256_k8_i1024_int4"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 16 lanes x 32 GT/s x 128/130 / 8
-FUSED_MAX_T = 4  # decode batches up to this size run as one moe_layer launch; larger ones as the stages
+FUSED_MAX_T = 8  # batches up to this size run as one moe_layer launch (measured faster up to 8 tokens); larger ones as the stages
 
 
 CONFIGS = [  # the layer's other configurations, timed after the headline one
