@@ -21,12 +21,10 @@ constexpr int kGroup = 128;  // quantisation group along K
 //   route workspace:
 //   [32]         selector blocks finished (several selectors grouping rows)
 //   expert-FFN workspace:
-//   [32]         fused decode layer: combining blocks finished
 //   [64 ..]      per-active-expert counters, kCtrStride apart, then the fused
 //                layer's "past routing" counters
 constexpr int kCtlError = 2;
 constexpr int kCtlRouteSel = 32;
-constexpr int kCtlLayerDone = 32;
 constexpr int kCtlCounters = 64;
 constexpr int kCtrStride = 32;   // ints between counters: one 128-byte line each
 constexpr int kCtlWords = 1024;  // minimum control block: 4 KiB

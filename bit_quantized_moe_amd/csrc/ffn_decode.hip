@@ -740,6 +740,13 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         load_chunk<BITS, GS>(xw, o2[0], wd[0]);
         load_chunk<BITS, GS>(xw, o2[1], wd[1]);
       }
+      // Fused layer: a phase-2 block counts itself done with the routing
+      // record once its weight loads are issued (the atomic then completes
+      // while the block waits for h, and holds up no load of its own).
+      if (LAYER && !routed) {
+        if (threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
+        routed = true;
+      }
       // One token with full chunks (the host keeps I / 128 <= 4 kHPend for
       // it): the per-group pipeline.
       constexpr bool kPipe = ONE && FAST;
@@ -852,13 +859,6 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         }
         lds_barrier();  // LDS is rewritten by the next pass
       }
-      // Fused layer: a phase-2 block counts itself done with the routing
-      // record once its y is stored (ahead of the done counter below, whose
-      // round trip would otherwise delay the last combiner's clean-up).
-      if (LAYER && !routed) {
-        if (threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
-        routed = true;
-      }
       // The last phase-2 item of the expert clears the expert's h words and
       // its done counter: every phase-2 item has read h by then.
       int *flag = (int *)red;
@@ -875,9 +875,34 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
     }
   }
   if constexpr (LAYER) {
-    // Counted after the items (not right after reading the record): the
-    // atomic's completion would otherwise hold up the first item's loads.
+    // Phase-1 blocks count after their items (not right after reading the
+    // record): the atomic's completion would otherwise hold up the
+    // activation loads of the first item.
     if (!routed && threadIdx.x == 0) atomicAdd(routed_ctr(p.ctl, p.Amax, blockIdx.x % kRoutedN), 1);
+    // Block 0 clears the routing record once every block has counted itself
+    // done with it, and re-zeroes the counters.  By then the phase-2 blocks
+    // have counted long ago and the phase-1 blocks are finishing, so this
+    // wait is over before block 0's combine below would find its y ready.
+    if (blockIdx.x == 0) {
+      if (wv == 0) {
+        for (int spins = 0;; ++spins) {
+          const int c = lane < kRoutedN ? __hip_atomic_load(routed_ctr(p.ctl, p.Amax, lane), __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0;
+          if (__builtin_amdgcn_readfirstlane((int)group_sum((float)c, kRoutedN)) >= (int)gridDim.x) break;
+          if (spins >= p.max_spins) {
+            if (lane == 0) atomicOr(&p.ctl[kCtlError], 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      lds_barrier();
+      for (int i = threadIdx.x; i < nrows; i += 256)
+        __hip_atomic_store(p.rec + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x < kRoutedN)
+        __hip_atomic_store(routed_ctr(p.ctl, p.Amax, threadIdx.x), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if ((int)blockIdx.x < per2) {
       // y[t, c] = sum over j ascending of g[t, j] * y_perm[row_pos[t k + j], c] in float32,
       // rounded once to bf16; each y_perm word is cleared once read.
@@ -919,33 +944,6 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         p.y[(size_t)t * p.H + c] = f32_to_bf16(acc);
       }
       if (!ok) atomicOr(&p.ctl[kCtlError], 1);
-      // The last combining block clears the routing record once every block
-      // has counted itself done with it, and re-zeroes the counters.
-      int *flag = (int *)red;
-      lds_barrier();
-      if (threadIdx.x == 0) *flag = atomicAdd(&p.ctl[kCtlLayerDone], 1) == per2 - 1;
-      lds_barrier();
-      if (*flag) {
-        if (wv == 0) {
-          for (int spins = 0;; ++spins) {
-            const int c = lane < kRoutedN ? __hip_atomic_load(routed_ctr(p.ctl, p.Amax, lane), __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT)
-                                          : 0;
-            if (__builtin_amdgcn_readfirstlane((int)group_sum((float)c, kRoutedN)) >= (int)gridDim.x) break;
-            if (spins >= p.max_spins) {
-              if (lane == 0) atomicOr(&p.ctl[kCtlError], 1);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-        }
-        lds_barrier();
-        for (int i = threadIdx.x; i < nrows; i += 256)
-          __hip_atomic_store(p.rec + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (threadIdx.x < kRoutedN)
-          __hip_atomic_store(routed_ctr(p.ctl, p.Amax, threadIdx.x), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (threadIdx.x == 0) __hip_atomic_store(&p.ctl[kCtlLayerDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
     }
   }
 }
