@@ -94,6 +94,15 @@ constexpr int kRoutedN = 16;
 __device__ __forceinline__ int *routed_ctr(int *ctl, int amax, int i) {
   return ctl + kCtlCounters + (amax + i) * kCtrStride;
 }
+// Item queues (a grid with more items than blocks): queue q hands out, in
+// order, the items past the first round whose index - grid is q modulo the
+// queue count; block b draws from queue b % queues (its XCD under the
+// round-robin dispatch of blocks).  One counter per queue, on its own line
+// after the routed counters.
+constexpr int kQueues = 8;
+__device__ __forceinline__ int *queue_ctr(int *ctl, int amax, int q) {
+  return ctl + kCtlCounters + (amax + kRoutedN + q) * kCtrStride;
+}
 constexpr uint32_t kHReady = 1u << 16;  // tag of a written h word
 constexpr uint64_t kRecTag = 1ull << 63;  // tag of a written routing record word
 
@@ -521,7 +530,8 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   float *red = Xs + 16 * SPU * (G1 > G2 ? G1 : G2);
   // fused layer: routing results in LDS after the FFN's own arrays, or after
   // the router's rows where those are larger (they share the start of LDS)
-  const size_t ffn_bytes = (size_t)((uint8_t *)(red + kRedFloats) - lds);
+  int *s_next = (int *)(red + kRedFloats);  // the block's next item (item queues)
+  const size_t ffn_bytes = (size_t)((uint8_t *)(red + kRedFloats) - lds) + 16;
   const bool lds_router = LAYER && router_lds_ok(p.H);
   const size_t rbytes = lds_router ? router_lds_bytes(p.H) : 0;
   int32_t *s_ids = (int32_t *)(lds + (ffn_bytes > rbytes ? ffn_bytes : rbytes));  // [T*k] selector block only
@@ -631,7 +641,22 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   };
 
   bool routed = false;  // fused layer: this block has counted itself done with the record
-  for (int item = blockIdx.x; item < n1 + n2; item += gridDim.x) {
+  // More items than blocks: after its first item (its own index) a block
+  // draws the next from its queue, so blocks whose items ran fast take more
+  // of them.  Every queue item is phase 2 unless every first item is phase 1,
+  // and a queue hands out its items in index order (phase 1 first), so a
+  // phase-2 item only ever waits for phase-1 items that are being worked on.
+  const int n_items = n1 + n2, grid = gridDim.x;
+  const bool dyn = n_items > grid;
+  const int nq = grid < kQueues ? grid : kQueues, qx = blockIdx.x % nq;
+  const int q_items = n_items - grid > qx ? (n_items - grid - qx + nq - 1) / nq : 0;  // items of this queue
+  const int q_blocks = (grid - qx + nq - 1) / nq;                                    // blocks drawing from it
+  int *qc = queue_ctr(p.ctl, p.Amax, qx);
+  int ticket = -1;  // thread 0: position drawn from the queue while the current item runs
+  auto draw = [&]() {
+    if (dyn && threadIdx.x == 0 && ticket < 0) ticket = atomicAdd(qc, 1);
+  };
+  for (int item = blockIdx.x; item < n_items;) {
     if (item < n1) {
       // ============================================================ phase 1
       const int a = item / per1, i0 = (item - a * per1) * kRows1;
@@ -663,6 +688,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         load_chunk<BITS, GS>(xw, o2[0], wgu[0]);
         load_chunk<BITS, GS>(xw, o2[1], wgu[1]);
       }
+      draw();  // after the weight loads, so the atomic holds none of them up
       for (int rb = md.o0; rb < md.o1; rb += RM) {
         const int R = ONE ? 1 : min(RM, md.o1 - rb);
         // the fused NVFP4 layer quantises the activations it stages (the stage
@@ -740,6 +766,7 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
         load_chunk<BITS, GS>(xw, o2[0], wd[0]);
         load_chunk<BITS, GS>(xw, o2[1], wd[1]);
       }
+      draw();
       // Fused layer: a phase-2 block counts itself done with the routing
       // record once its weight loads are issued (the atomic then completes
       // while the block waits for h, and holds up no load of its own).
@@ -873,6 +900,20 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
       }
       lds_barrier();  // the flag is read before the next item reuses LDS
     }
+    if (!dyn) {
+      item += grid;
+      continue;
+    }
+    // the next item from the ticket; the draw that returns the queue's last
+    // ticket (q_items + q_blocks - 1: every block's final draw is past its
+    // items) re-zeroes the counter for the next call
+    if (threadIdx.x == 0) {
+      *s_next = ticket < q_items ? grid + qx + nq * ticket : n_items;
+      if (ticket == q_items + q_blocks - 1) __hip_atomic_store(qc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ticket = -1;
+    }
+    lds_barrier();
+    item = *s_next;
   }
   if constexpr (LAYER) {
     // Phase-1 blocks count after their items (not right after reading the
@@ -1001,7 +1042,7 @@ size_t layer_lds_bytes(int T, int k, int E) {
 
 size_t decode_lds_bytes(int H, int I, bool one, int group = kGroup) {
   const size_t kmax = H > I ? H : I;
-  return (size_t)(one ? 1 : kRMax) * (kmax * 2 + 16) + 16 * (kmax / group) * 4 + kRedFloats * 4;
+  return (size_t)(one ? 1 : kRMax) * (kmax * 2 + 16) + 16 * (kmax / group) * 4 + kRedFloats * 4 + 16;
 }
 
 // Fused layer: the router rows (shared start of LDS) or the FFN arrays,
@@ -1042,7 +1083,7 @@ bool decode_layout_ok(int H, int I, int bits, int group) {
 
 size_t ffn_ctl_bytes(int T, int k, int E) {
   const long amax = E < (long)T * k ? E : (long)T * k;
-  size_t b = (size_t)(kCtlCounters + (amax + kRoutedN) * kCtrStride) * 4;
+  size_t b = (size_t)(kCtlCounters + (amax + kRoutedN + kQueues) * kCtrStride) * 4;
   if (b < kCtlBytes) b = kCtlBytes;
   return (b + 255) / 256 * 256;
 }
