@@ -36,22 +36,22 @@ struct GroupOut {
   int n_active_slots;
 };
 
-template <int VEC, bool GROUP>
-__global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restrict__ x,
-                                                         const uint16_t *__restrict__ w, const float *bias, int T,
-                                                         int H, int E, int k, int32_t *ids, float *gates,
-                                                         uint64_t *tl, float *lg_out, int *ctl, int max_spins,
-                                                         GroupOut go) {
+constexpr int kSmallMaxWaves = 8;  // waves per block of the small router kernel
+
+// The selection part of the small router launches, run by one wave of block
+// e < min(T, E) once the block's own logits are stored: the top-k and
+// softmax of tokens e, e + nsel, ... and, with GROUP, the grouping of the
+// rows by expert.  group_lds: LDS of (kFusedRows + E) ints.
+template <bool GROUP>
+__device__ void small_selection(int e, int T, int E, int k, int32_t *ids, float *gates, uint64_t *tl, float *lg_out,
+                                int *ctl, int max_spins, const GroupOut &go, int *group_lds) {
   const int lane = lane_id();
-  const int e = blockIdx.x;
-  router_logits_wave<VEC>(x, w, bias, T, H, E, e, tl);
   const int nsel = min(T, E);
   if (e >= nsel) return;
   // token t's logits: poll the tagged words, then clear them for the next call
   auto logits_of = [&](int t) {
     return TaggedLogits{tl + (size_t)t * E, E, max_spins, ctl, true, lg_out ? lg_out + (size_t)t * E : nullptr};
   };
-  extern __shared__ int group_lds[];  // GROUP with several selectors: key[kFusedRows], then cur[E]
   if constexpr (!GROUP) {
     for (int t = e; t < T; t += nsel)
       topk_softmax_any(logits_of(t), E, k, ids + (size_t)t * k, gates + (size_t)t * k);
@@ -101,6 +101,98 @@ __global__ void __launch_bounds__(64) route_small_kernel(const uint16_t *__restr
       wave_group_rows(key, n, E, cur, go.offsets, go.sorted_rows, go.row_pos, go.active, go.n_active_slots);
     }
   }
+}
+
+template <int VEC, bool GROUP>
+__global__ void __launch_bounds__(kSmallMaxWaves * 64) route_small_kernel(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ w, const float *bias, int T,
+                                                         int H, int E, int k, int32_t *ids, float *gates,
+                                                         uint64_t *tl, float *lg_out, int *ctl, int max_spins,
+                                                         GroupOut go) {
+  extern __shared__ int group_lds[];  // GROUP with several selectors: key[kFusedRows], then cur[E]
+  const int e = blockIdx.x;
+  // the block's waves share expert e's tokens, kTB at a time; only wave 0
+  // goes on to the selection
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  router_logits_wave<VEC>(x, w, bias, T, H, E, e, tl, wv, blockDim.x / kWave);
+  if (wv != 0) return;
+  small_selection<GROUP>(e, T, E, k, ids, gates, tl, lg_out, ctl, max_spins, go, group_lds);
+}
+
+// The same launch with the rows staged in LDS (H a power of two from 512 to
+// 4096): a block takes kLdsExperts experts (one per wave) and kLdsTokens
+// tokens.  Its 256 threads load the weight rows and the activation rows with
+// coalesced 16-byte loads (1 KB per instruction), all in flight together,
+// into the padded slice layout; each wave then runs its expert's fixed-order
+// dots (lane s chains slice s, then the pairwise tree, then the bias) for the
+// tokens, two chains interleaved.  Loading a slice per lane from memory
+// instead touches 64 lines per instruction, and with several waves per CU
+// those lines do not stay in the L1.  Blocks past the (expert, token) tiles
+// only select; block b < min(T, E) selects after its own logits.
+constexpr int kLdsExperts = 4, kLdsTokens = 2;
+constexpr int kLdsRows = kLdsExperts + kLdsTokens;
+template <bool GROUP>
+__global__ void __launch_bounds__(256) route_small_lds_kernel(const uint16_t *__restrict__ x,
+                                                             const uint16_t *__restrict__ w, const float *bias,
+                                                             int T, int H, int E, int k, int32_t *ids, float *gates,
+                                                             uint64_t *tl, float *lg_out, int *ctl, int max_spins,
+                                                             GroupOut go) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t rows_lds[];
+  const int sw64 = 64 * router_slice_words(H);
+  int *group_lds = (int *)(rows_lds + kLdsRows * sw64);
+  const int neg = (E + kLdsExperts - 1) / kLdsExperts, ntg = (T + kLdsTokens - 1) / kLdsTokens;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if ((int)blockIdx.x < neg * ntg) {
+    const int e0 = (blockIdx.x % neg) * kLdsExperts, t0 = (blockIdx.x / neg) * kLdsTokens;
+    const int nch = H / 8, sh = __builtin_ctz(H / 512), sw = router_slice_words(H);
+    // rows 0 .. kLdsExperts-1: weight rows e0 + r; then the token rows t0 + r
+    // (clamped to the last expert / token; their results are not stored)
+    u32x4 a[kLdsRows][2];
+#pragma unroll
+    for (int r = 0; r < kLdsRows; ++r) {
+      const uint16_t *row = r < kLdsExperts ? w + (size_t)min(e0 + r, E - 1) * H
+                                            : x + (size_t)min(t0 + r - kLdsExperts, T - 1) * H;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) a[r][q] = ((const u32x4 *)row)[min((int)threadIdx.x + q * 256, nch - 1)];
+    }
+#pragma unroll
+    for (int r = 0; r < kLdsRows; ++r)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + q * 256;
+        if (c < nch) *(u32x4 *)&rows_lds[r * sw64 + (c >> sh) * sw + (c & ((1 << sh) - 1)) * 4] = a[r][q];
+      }
+    __syncthreads();
+    const int e = e0 + wv;
+    if (e < E) {
+      const int lane = lane_id();
+      const uint32_t *wp = rows_lds + wv * sw64 + lane * sw;
+      const uint32_t *xp0 = rows_lds + kLdsExperts * sw64 + lane * sw, *xp1 = xp0 + sw64;
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < H / 128; j += 4) {
+        const u32x4 ww = *(const u32x4 *)(wp + j), x0 = *(const u32x4 *)(xp0 + j), x1 = *(const u32x4 *)(xp1 + j);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc0 = __builtin_fmaf(bf16lo(x0[r]), bf16lo(ww[r]), acc0);
+          acc0 = __builtin_fmaf(bf16hi(x0[r]), bf16hi(ww[r]), acc0);
+          acc1 = __builtin_fmaf(bf16lo(x1[r]), bf16lo(ww[r]), acc1);
+          acc1 = __builtin_fmaf(bf16hi(x1[r]), bf16hi(ww[r]), acc1);
+        }
+      }
+      const float b = bias ? bias[e] : 0.f;
+      const float v0 = group_sum(acc0, kWave) + b, v1 = group_sum(acc1, kWave) + b;
+      if (lane == 0) {
+        __hip_atomic_store(tl + (size_t)t0 * E + e, kLogitTag | __float_as_uint(v0), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (t0 + 1 < T)
+          __hip_atomic_store(tl + (size_t)(t0 + 1) * E + e, kLogitTag | __float_as_uint(v1), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (wv != 0) return;
+  small_selection<GROUP>(blockIdx.x, T, E, k, ids, gates, tl, lg_out, ctl, max_spins, go, group_lds);
 }
 
 // ------------------------------------------------------------ large T
@@ -546,6 +638,13 @@ size_t route_workspace_bytes(int T, int E) {
   return b;
 }
 
+// The LDS-staged small router: H a power of two from 512 to 4096, and its
+// LDS (six padded rows plus the grouping arrays) within 64 KiB.
+static bool small_lds_ok(int T, int H, int E) {
+  (void)T;
+  return router_lds_ok(H) && kLdsRows * router_lds_row_bytes(H) + (size_t)(kFusedRows + E) * sizeof(int) <= 64 * 1024;
+}
+
 template <bool GROUP>
 static void launch_route_small(const uint16_t *x, const uint16_t *w_router, const float *bias, int T, int H, int E,
                                int k, int32_t *ids, float *gates, float *logits, void *ws, const GroupOut &go,
@@ -554,8 +653,19 @@ static void launch_route_small(const uint16_t *x, const uint16_t *w_router, cons
   uint64_t *tl = (uint64_t *)((char *)ws + kCtlBytes);
   const int L = H / 64;
   const int spins = wait_spin_limit();
-  dim3 grid(E), block(kWave);
-  const size_t lds = GROUP ? (size_t)(kFusedRows + E) * sizeof(int) : 0;
+  const size_t glds = GROUP ? (size_t)(kFusedRows + E) * sizeof(int) : 0;
+  if (small_lds_ok(T, H, E)) {
+    const int tiles = ((E + kLdsExperts - 1) / kLdsExperts) * ((T + kLdsTokens - 1) / kLdsTokens);
+    const int nsel = T < E ? T : E;
+    route_small_lds_kernel<GROUP><<<dim3((unsigned)(tiles > nsel ? tiles : nsel)), 256,
+                                    kLdsRows * router_lds_row_bytes(H) + glds, st>>>(
+        x, w_router, bias, T, H, E, k, ids, gates, tl, logits, ctl, spins, go);
+    return;
+  }
+  // one wave per kTB tokens, up to kSmallMaxWaves
+  const int nw = min(kSmallMaxWaves, (T + kTB - 1) / kTB);
+  dim3 grid(E), block(kWave * nw);
+  const size_t lds = glds;
   if (L % 8 == 0)
     route_small_kernel<8, GROUP><<<grid, block, lds, st>>>(x, w_router, bias, T, H, E, k, ids, gates, tl, logits,
                                                            ctl, spins, go);

@@ -264,18 +264,20 @@ __device__ __forceinline__ float fma_vec(const Vec<VEC> &xv, const Vec<VEC> &wv,
 // as a balanced pairwise tree, then the bias is added) and stores each as a
 // tagged 64-bit word tl[t * E + e] with a device-coherent store.  TB tokens'
 // activation slices are loaded together (register cost ~ 16 * VEC * TB / 8).
+// The wave takes the groups of TB tokens g0, g0 + gs, ... (several waves of
+// a block share one expert's tokens this way).
 // FULL: every slice is a whole number of 64-element chunks, so the chunk
 // loop needs no guards (straight-line code; branches are costly here).
 template <int VEC, int TB, bool FULL>
 __device__ __forceinline__ void router_logits_wave_impl(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ w, const float *bias, int T,
-                                                        int H, int E, int e, uint64_t *tl) {
+                                                        int H, int E, int e, uint64_t *tl, int g0, int gs) {
   constexpr int NVC = 64 / VEC;  // loads per 64-element chunk of a slice
   const int lane = lane_id();
   const int L = H / 64;
   const uint16_t *wrow = w + (size_t)e * H + (size_t)lane * L;
   const float b = bias ? bias[e] : 0.f;
-  for (int t0 = 0; t0 < T; t0 += TB) {
+  for (int t0 = g0 * TB; t0 < T; t0 += gs * TB) {
     float acc[TB];
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) acc[tt] = 0.f;
@@ -315,11 +317,12 @@ __device__ __forceinline__ void router_logits_wave_impl(const uint16_t *__restri
 
 template <int VEC, int TB = kTB>
 __device__ __forceinline__ void router_logits_wave(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-                                                   const float *bias, int T, int H, int E, int e, uint64_t *tl) {
+                                                   const float *bias, int T, int H, int E, int e, uint64_t *tl,
+                                                   int g0 = 0, int gs = 1) {
   if ((H / 64) % 64 == 0)
-    router_logits_wave_impl<VEC, TB, true>(x, w, bias, T, H, E, e, tl);
+    router_logits_wave_impl<VEC, TB, true>(x, w, bias, T, H, E, e, tl, g0, gs);
   else
-    router_logits_wave_impl<VEC, TB, false>(x, w, bias, T, H, E, e, tl);
+    router_logits_wave_impl<VEC, TB, false>(x, w, bias, T, H, E, e, tl, g0, gs);
 }
 
 // Router logits from LDS, for H a power of two from 512 to 4096 (slices of

@@ -94,8 +94,12 @@ def test_route_tiny_and_variants():
         assert pos[2] < pos[5] < pos[6]
 
 
-@pytest.mark.parametrize("T,H,E,k", [(33, 512, 300, 8), (100, 256, 64, 6), (17, 1024, 1024, 32), (32, 384, 7, 7)])
+@pytest.mark.parametrize("T,H,E,k", [(33, 512, 300, 8), (100, 256, 64, 6), (17, 1024, 1024, 32), (32, 384, 7, 7),
+                                     (5, 2048, 13, 4), (1, 4096, 6, 2)])
 def test_route_both_kernels_ragged_shapes(T, H, E, k):
+    """The small router with the rows staged in LDS (H a power of two from 512
+    to 4096; ragged expert groups and token pairs) and with slice-per-lane
+    loads (other H)."""
     sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, E=E, k=k, seed=77 + T)
     x = workload.make_x(sp)
     w_r, _ = workload.make_router(sp)
