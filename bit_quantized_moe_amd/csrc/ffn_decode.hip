@@ -659,7 +659,14 @@ __global__ void __launch_bounds__(256, 3) ffn_decode_kernel(DecodeParams p) {
   for (int item = blockIdx.x; item < n_items;) {
     if (item < n1) {
       // ============================================================ phase 1
-      const int a = item / per1, i0 = (item - a * per1) * kRows1;
+      // One token: the experts are interleaved (item = i A + a).  The blocks
+      // dispatched first (one per CU) get their weights first, so every
+      // expert has its early rows there and its phase 2 starts on the early
+      // half of h while the rest streams in (measured 0.2-0.4 us shorter
+      // than expert by expert).  With more tokens the items go expert by
+      // expert, so that early experts finish their phase 1 (and their
+      // phase 2 can start) while later ones run.
+      const int a = ONE ? item % A : item / per1, i0 = (ONE ? item / A : item - a * per1) * kRows1;
       const Meta md = get_meta(a);
       const int g0 = wv * Gw1, ng = max(min(Gw1, G1 - g0), 0);
       const size_t erows = (size_t)md.e * 2 * p.I;  // first row of the expert

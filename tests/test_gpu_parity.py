@@ -414,6 +414,36 @@ def test_layer_decode_full_size(name):
     _full_decode(name, n_sets=2 if "t1_" in name else 1)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_ffn_item_queues_repeatable(bits):
+    """More decode items than co-resident blocks (H = 4096, I = 1024, 32
+    experts, T = 16, top-4: about 3000 items over 768 blocks), so blocks past
+    their first item draw from the per-XCD item queues: y_perm against the
+    oracle on every row, a second call on the same workspace bit-identical,
+    and the workspace (queue counters included) left zero."""
+    T, H, I, E, k = 16, 4096, 1024, 32, 4
+    sp = workload.spec("tiny_t4_h256_e8_k2_i128_int4", T=T, H=H, I=I, E=E, k=k, bits=bits,
+                       scale_sigma=0.02 if bits == 4 else 0.05, seed=5100 + bits)
+    assert bq.ffn_path(T, k, E, H, I, bits) == "decode"
+    inp = workload.make_layer_inputs(sp)
+    wd = weights_to_dev(inp.weights)
+    r = bq.route_permute(to_dev(inp.x), to_dev(inp.w_router), k)
+    act = to_np(r["active"])
+    assert int(act[0]) * (I // 16 + H // 128) > 768, "the case must have more items than one round of blocks"
+    ws = bq.Workspaces("cuda")
+    args = (to_dev(inp.x), r["offsets"], r["sorted_rows"], r["active"], k)
+    got = bq.expert_ffn(*args, wd, bits, I, ws=ws)
+    again = bq.expert_ffn(*args, wd, bits, I, ws=ws)
+    assert torch.equal(again.view(torch.int16), got.view(torch.int16))
+    torch.cuda.synchronize()
+    assert int(ws._bufs["ffn"].view(torch.int32).abs().sum()) == 0
+    ws.check()
+    off, srt = to_np(r["offsets"]), to_np(r["sorted_rows"])
+    ref = oracle.expert_ffn(inp.x, off, srt, k, inp.weights, bits, I)
+    yp = bf16_np_to_f32(to_np(got))
+    assert oracle.rel_fro(yp, ref) <= TOL and row_rel_err(yp, ref).max() <= TOL
+
+
 @pytest.mark.parametrize("name", ["prefill_t4096_h4096_e256_k8_i1024_int4", "prefill_t8192_h4096_e256_k8_i1024_int2",
                                   "mid_t64_h4096_e256_k8_i1024_int4"])
 def test_layer_prefill_full_size_sampled(name):
