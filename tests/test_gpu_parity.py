@@ -228,18 +228,22 @@ def test_route_permute_matches_route_then_permute(T, H, E, k):
             assert np.array_equal(a, b)
 
 
-def test_combine_matches_oracle():
-    rng = np.random.default_rng(3)
-    T, k, H = 37, 8, 4096
+@pytest.mark.parametrize("T,k,H", [(37, 8, 4096), (5, 12, 1000)])
+def test_combine_matches_oracle(T, k, H):
+    """k = 12 reads the rows in a batch of 8 and a ragged one of 4; H = 1000
+    leaves the last block's threads partly past H; invalid row positions (a
+    dropped row, one past the end) add nothing."""
+    rng = np.random.default_rng(3 + k)
     y_perm = workload.bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
     row_pos = rng.permutation(T * k).astype(np.int32)
     row_pos[5] = -1
+    row_pos[min(9, T * k - 1)] = T * k + 3
     g = rng.random((T, k)).astype(np.float32)
     got = bf16_np_to_f32(to_np(bq.combine(to_dev(y_perm), to_dev(row_pos), to_dev(g))))
     yp = bf16_np_to_f32(y_perm)
     rp = row_pos.copy()
     yp_ext = np.concatenate([yp, np.zeros((1, H), np.float32)])
-    rp[rp < 0] = T * k
+    rp[(rp < 0) | (rp >= T * k)] = T * k
     ref = oracle.combine(yp_ext, rp, g)
     assert oracle.rel_fro(got, ref) < 4e-3
     assert np.max(row_rel_err(got, ref)) < 8e-3
