@@ -185,12 +185,22 @@ __device__ __forceinline__ void order_pairs(const uint32_t *d, uint32_t *o) {
 }
 
 // ---------------------------------------------------------------- GEMM-path dequant
+// The masked words below hold one field per byte.  Passed through an empty asm
+// statement, their bits are opaque to the optimizer, which would otherwise
+// fold the mask into every field's extraction (a bit-field extract, then a
+// byte convert); this way each byte converts with one v_cvt_f32_ubyteN.  The
+// asm emits no instruction.
+__device__ __forceinline__ uint32_t field_bytes(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 // Eight 4-bit fields of w -> four packed bf16 pairs of (u - zoff) * s, in K order.
 // (u - zoff) * s is exact in float32 (a small integer times a bf16 value); the
 // conversion to bf16 rounds to nearest even.
 __device__ __forceinline__ void dequant8_int4(uint32_t w, float s, float zs, uint32_t out[4]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;          // fields 0, 2, 4, 6
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // fields 1, 3, 5, 7
+  const uint32_t lo = field_bytes(w & 0x0F0F0F0Fu);          // fields 0, 2, 4, 6
+  const uint32_t hi = field_bytes((w >> 4) & 0x0F0F0F0Fu);   // fields 1, 3, 5, 7
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const float f0 = (float)((lo >> (8 * b)) & 0xFFu);
@@ -212,10 +222,10 @@ __device__ __forceinline__ void dequant4_int8(uint32_t w, float s, float zs, uin
 // Sixteen 2-bit fields of w -> eight packed bf16 pairs of (u - z) * s, in K order.
 // |u - z| <= 2 for z in {1, 2}, so the values are exact in bf16.
 __device__ __forceinline__ void dequant16_int2(uint32_t w, float s, float zs, uint32_t out[8]) {
-  const uint32_t f0 = w & 0x03030303u;          // fields 0, 4, 8, 12
-  const uint32_t f1 = (w >> 2) & 0x03030303u;   // fields 1, 5, 9, 13
-  const uint32_t f2 = (w >> 4) & 0x03030303u;   // fields 2, 6, 10, 14
-  const uint32_t f3 = (w >> 6) & 0x03030303u;   // fields 3, 7, 11, 15
+  const uint32_t f0 = field_bytes(w & 0x03030303u);          // fields 0, 4, 8, 12
+  const uint32_t f1 = field_bytes((w >> 2) & 0x03030303u);   // fields 1, 5, 9, 13
+  const uint32_t f2 = field_bytes((w >> 4) & 0x03030303u);   // fields 2, 6, 10, 14
+  const uint32_t f3 = field_bytes((w >> 6) & 0x03030303u);   // fields 3, 7, 11, 15
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const float a0 = (float)((f0 >> (8 * b)) & 0xFFu);
