@@ -19,15 +19,18 @@ namespace bqmoe {
 namespace {
 
 // ------------------------------------------------------------ small T
-// Grid: E blocks of one wave; block e computes the logits of expert e for
-// every token (lane s = slice s, sequential over its h) and stores each as a
-// 64-bit word, the float bits under a nonzero tag, with a device-coherent
-// store.  Blocks 0 .. nsel-1 (nsel = min(T, E)) run the top-k of tokens
-// b, b + nsel, ...: they read the token's E words until every one carries the
-// tag (each word is self-validating, so no counter and no store wait are
-// needed), then clear them for the next call.  All E one-wave blocks are
-// co-resident, so the wait ends; it is bounded anyway and a timeout only
-// raises the error flag.
+// Two launch shapes compute the logits (lane s = slice s, sequential over its
+// h): route_small_lds_kernel (H a power of two from 512 to 4096) stages four
+// experts' weight rows and two tokens' rows in LDS per block;
+// route_small_kernel (other H) gives each expert a block of up to eight
+// waves, four tokens per wave.  Each logit is stored as a 64-bit word, the
+// float bits under a nonzero tag, with a device-coherent store.  Blocks
+// 0 .. nsel-1 (nsel = min(T, E)) then run the top-k of tokens b, b + nsel,
+// ...: they read the token's E words until every one carries the tag (each
+// word is self-validating, so no counter and no store wait are needed), then
+// clear them for the next call.  Every block of the grid is co-resident (one
+// per expert, or one per 4 experts x 2 tokens, a few waves each), so the
+// wait ends; it is bounded anyway and a timeout only raises the error flag.
 
 // Outputs of the grouping by expert, when the router launch also groups the
 // rows (T*k <= kFusedRows).
